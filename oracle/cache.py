@@ -1,0 +1,275 @@
+"""A whole low-bit KV cache: append, dequantize, decode (test oracle).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The cache is per sequence and grows by one entry per token per layer
+([trefon] "Czym jest cache KV"); it is written at run time, token by token, so
+quantization parameters come from the observed values ([trefon] "Dlaczego cache
+trudniej skwantyzować niż wagi"; [nalar] "Pertumbuhan cache dinamis mengubah
+persoalan kalibrasi").  Two schemes:
+
+``kivi``: keys per channel over 32-token groups, values per token over 32-dim
+  groups, asymmetric, fp16 scale and zero; a fp16 window of recent tokens
+  (tiers.py); optionally a high-bit window with older groups at ``low_bits``
+  ([troisinh] "Ý tưởng cốt lõi", "Mixed Precision"); optionally the Hadamard
+  rotation before quantizing ([troisinh] "Tại sao nó hoạt động", item 2) and
+  keys kept before RoPE (item 3).
+``block128``: every token's 128-vector, optionally Hadamard-rotated, becomes one
+  symmetric 4-bit block with an fp16 scale ([trefon] "Przykład: model 27B przy
+  262K" and "Jak 4-bitowemu cache to uchodzi: najpierw obrót"); no window.
+
+Append order (reading; the pages give none): groups that leave the high-bit
+tier are requantized to ``low_bits`` from their dequantized high-bit values
+(the fp16 source is gone by then); groups quantized for the first time go
+straight from their fp16 source (rotated if configured) to the tier their age
+dictates after the append.  Hence appending in pieces gives the same bytes as
+one append unless a demotion happens in between.
+
+Decode (reading): the attended keys and values are the dequantized cache in
+its stored domain, the fp16 window taken exactly; Hadamard-rotated tokens are
+rotated back with H / sqrt(128) in fp64 (equivalently the query is rotated and
+the output rotated back, q.k = (Hq).(Hk), [trefon] "Jak 4-bitowemu cache to
+uchodzi"); pre-RoPE keys are rotated to their positions and the query to
+``q_pos`` (default: the cache length).  Window tokens are stored unrotated.
+"""
+
+import numpy as np
+
+from . import tiers, quant, layout
+from .hadamard import fwht128_f32, rotate_f64
+from .attention import rope_f64, decode_f64
+
+F16 = np.float16
+F32 = np.float32
+
+DEFAULTS = dict(head_dim=128, group=32, vdims=32, window=128, hi_window=-1,
+                low_bits=2, hadamard=False, pre_rope=False, rope_theta=10000.0)
+
+
+def make_config(**kw):
+    cfg = dict(DEFAULTS)
+    cfg.update(kw)
+    if cfg["scheme"] == "block128":
+        cfg["window"] = 0
+        cfg.setdefault("k_bits", 4)
+        cfg.setdefault("v_bits", 4)
+    return cfg
+
+
+def _tile_token_of_byte(key_tile):
+    """Token index whose codes a 4-bit tile byte holds (the lower token of the
+    pair for a value tile, whose bytes hold two tokens of one channel)."""
+    tok = np.zeros(2048, np.int64)
+    if key_tile:
+        for cb in range(64):
+            for t in range(32):
+                tok[(cb // 16) * 512 + t * 16 + (cb % 16)] = t
+    else:
+        tok[:] = np.tile(2 * np.arange(16), 128)
+    return tok
+
+
+class OracleCache:
+    """Canonical (unpacked) cache state for [batch, num_kv_heads] sequences."""
+
+    def __init__(self, cfg, batch, max_tokens):
+        self.cfg = make_config(**cfg)
+        c = self.cfg
+        if c["head_dim"] != 128:
+            raise ValueError("head_dim must be 128")
+        if c["k_bits"] != c["v_bits"]:
+            raise ValueError("key and value tiers must share bit widths")
+        self.B, self.H = batch, c["num_kv_heads"]
+        self.max_tokens = max_tokens
+        self.length = 0
+        G = layout.gmax(max_tokens)
+        self.G = G
+        B, H = self.B, self.H
+        if c["scheme"] == "kivi":
+            self.k_codes = np.zeros((B, H, G, 32, 128), np.uint8)
+            self.v_codes = np.zeros((B, H, G, 32, 128), np.uint8)
+            self.bits = np.zeros(G, np.int64)            # 0: not quantized
+            self.k_s = np.zeros((B, H, G, 128), F16)
+            self.k_z = np.zeros((B, H, G, 128), F16)
+            self.v_s = np.zeros((B, H, G, 32, 4), F16)
+            self.v_z = np.zeros((B, H, G, 32, 4), F16)
+            self.win_k = np.zeros((B, H, 0, 128), F16)
+            self.win_v = np.zeros((B, H, 0, 128), F16)
+        else:
+            Tp = G * 32
+            self.k_nib = np.zeros((B, H, Tp, 128), np.uint8)
+            self.v_nib = np.zeros((B, H, Tp, 128), np.uint8)
+            self.k_sc = np.zeros((B, H, Tp), F16)
+            self.v_sc = np.zeros((B, H, Tp), F16)
+
+    # -- tiers ---------------------------------------------------------------
+    @property
+    def Tq(self):
+        return tiers.quantized_prefix(self.length, self.cfg["window"])
+
+    def _source_rows(self, x):
+        """fp16 rows -> the float32 values the quantizer sees."""
+        if self.cfg["hadamard"]:
+            return fwht128_f32(x)
+        return np.asarray(x, dtype=F16).astype(F32)
+
+    # -- append --------------------------------------------------------------
+    def append(self, k_new, v_new):
+        """k_new, v_new: fp16 [B, n, H, 128] (token-major, like a projection)."""
+        k_new = np.asarray(k_new, dtype=F16)
+        v_new = np.asarray(v_new, dtype=F16)
+        B, n, H, Dd = k_new.shape
+        if (B, H, Dd) != (self.B, self.H, 128) or v_new.shape != k_new.shape:
+            raise ValueError("shape mismatch")
+        T0, T1 = self.length, self.length + n
+        if T1 > self.max_tokens:
+            raise ValueError("capacity exceeded")
+        kn = np.transpose(k_new, (0, 2, 1, 3))       # [B, H, n, 128]
+        vn = np.transpose(v_new, (0, 2, 1, 3))
+        c = self.cfg
+        if c["scheme"] == "block128":
+            for name, src, nib, sc in (("k", kn, self.k_nib, self.k_sc),
+                                       ("v", vn, self.v_nib, self.v_sc)):
+                y = self._source_rows(src)
+                q, s = quant.quant_sym128(y)
+                nib[:, :, T0:T1] = q
+                sc[:, :, T0:T1] = s
+            self.length = T1
+            return
+        plan = tiers.append_plan(T0, T1, c["hi_window"], c["window"])
+        Tq0, Tq1 = plan["Tq0"], plan["Tq1"]
+        lo = c["low_bits"]
+        for g in plan["demoted"]:
+            xk = quant.dequant_k_group(self.k_codes[:, :, g], self.k_s[:, :, g], self.k_z[:, :, g])
+            xv = quant.dequant_v_group(self.v_codes[:, :, g], self.v_s[:, :, g], self.v_z[:, :, g])
+            self.k_codes[:, :, g], self.k_s[:, :, g], self.k_z[:, :, g] = quant.quant_k_group(xk, lo)
+            self.v_codes[:, :, g], self.v_s[:, :, g], self.v_z[:, :, g] = quant.quant_v_group(xv, lo)
+            self.bits[g] = lo
+        src_k = np.concatenate([self.win_k, kn], axis=2)   # tokens [Tq0, T1)
+        src_v = np.concatenate([self.win_v, vn], axis=2)
+        for g in plan["new_groups"]:
+            a = g * 32 - Tq0
+            bits = tiers.group_bits(g, Tq1, c["hi_window"], c["k_bits"], lo)
+            vbits = tiers.group_bits(g, Tq1, c["hi_window"], c["v_bits"], lo)
+            xk = self._source_rows(src_k[:, :, a:a + 32])
+            xv = self._source_rows(src_v[:, :, a:a + 32])
+            self.k_codes[:, :, g], self.k_s[:, :, g], self.k_z[:, :, g] = quant.quant_k_group(xk, bits)
+            self.v_codes[:, :, g], self.v_s[:, :, g], self.v_z[:, :, g] = quant.quant_v_group(xv, vbits)
+            self.bits[g] = bits
+        self.win_k = src_k[:, :, Tq1 - Tq0:].copy()
+        self.win_v = src_v[:, :, Tq1 - Tq0:].copy()
+        self.length = T1
+
+    # -- dequant -------------------------------------------------------------
+    def dequant(self, t0=0, t1=None):
+        """Stored-domain values: fp32 [B, t1 - t0, H, 128] for keys and values.
+
+        Quantized tokens: the dequantized value (rotated if the config rotates,
+        keys before RoPE).  Window tokens: their fp16 value exactly."""
+        t1 = self.length if t1 is None else t1
+        if not (0 <= t0 <= t1 <= self.length):
+            raise ValueError("bad token range")
+        c = self.cfg
+        B, H = self.B, self.H
+        K = np.zeros((B, H, t1 - t0, 128), F32)
+        V = np.zeros((B, H, t1 - t0, 128), F32)
+        if c["scheme"] == "block128":
+            K[:] = quant.dequant_sym128(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
+            V[:] = quant.dequant_sym128(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
+        else:
+            Tq = self.Tq
+            qa, qb = t0, min(t1, Tq)
+            if qb > qa:
+                g0, g1 = qa // 32, (qb + 31) // 32
+                kd = quant.dequant_k_group(self.k_codes[:, :, g0:g1], self.k_s[:, :, g0:g1],
+                                           self.k_z[:, :, g0:g1])
+                vd = quant.dequant_v_group(self.v_codes[:, :, g0:g1], self.v_s[:, :, g0:g1],
+                                           self.v_z[:, :, g0:g1])
+                kd = kd.reshape(B, H, -1, 128)[:, :, qa - g0 * 32: qb - g0 * 32]
+                vd = vd.reshape(B, H, -1, 128)[:, :, qa - g0 * 32: qb - g0 * 32]
+                K[:, :, :qb - qa] = kd
+                V[:, :, :qb - qa] = vd
+            wa, wb = max(t0, Tq), t1
+            if wb > wa:
+                K[:, :, wa - t0:] = self.win_k[:, :, wa - Tq:wb - Tq].astype(F32)
+                V[:, :, wa - t0:] = self.win_v[:, :, wa - Tq:wb - Tq].astype(F32)
+        return np.transpose(K, (0, 2, 1, 3)), np.transpose(V, (0, 2, 1, 3))
+
+    # -- decode --------------------------------------------------------------
+    def attended_kv(self, q_pos=None):
+        """The fp64 keys and values attention uses, [B, T, H, 128]."""
+        c = self.cfg
+        K, V = self.dequant()
+        K = K.astype(np.float64)
+        V = V.astype(np.float64)
+        if c["hadamard"]:
+            nq = self.length if c["scheme"] == "block128" else self.Tq
+            K[:, :nq] = rotate_f64(K[:, :nq])
+            V[:, :nq] = rotate_f64(V[:, :nq])
+        if c["pre_rope"]:
+            Kt = np.transpose(K, (0, 2, 1, 3))
+            Kt = rope_f64(Kt, np.arange(self.length), c["rope_theta"])
+            K = np.transpose(Kt, (0, 2, 1, 3))
+        return K, V
+
+    def decode(self, q, q_pos=None, sm_scale=None):
+        """q: fp16 [B, Hq, 128] (before RoPE when keys are pre-RoPE)."""
+        c = self.cfg
+        q = np.asarray(q).astype(np.float64)
+        if c["pre_rope"]:
+            pos = self.length if q_pos is None else q_pos
+            q = rope_f64(q[:, :, None, :], np.array([pos]), c["rope_theta"])[:, :, 0, :]
+        K, V = self.attended_kv()
+        return decode_f64(q, K, V, sm_scale)
+
+    # -- byte image ----------------------------------------------------------
+    def plane_images(self):
+        """(images, live): uint8 images of planes 0..7 and masks of defined bytes."""
+        c = self.cfg
+        B, H = self.B, self.H
+        sizes = layout.plane_sizes(c, B, self.max_tokens)
+        img = [np.zeros(s, np.uint8) for s in sizes]
+        live = [np.zeros(s, bool) for s in sizes]
+        pair = lambda a: a.reshape(B, H, -1)
+        T = self.length
+        if c["scheme"] == "block128":
+            G = self.G
+            for plane, nib, sc in ((layout.K_HI, self.k_nib, self.k_sc),
+                                   (layout.V_HI, self.v_nib, self.v_sc)):
+                tiles = nib.reshape(B, H, G, 32, 128)
+                im = pair(img[plane]).reshape(B, H, G, 2048)
+                lv = pair(live[plane]).reshape(B, H, G, 2048)
+                tok = np.arange(G)[:, None] * 32 + _tile_token_of_byte(plane == layout.K_HI)[None, :]
+                im[:] = (layout.k_tile if plane == layout.K_HI else layout.v_tile)(tiles, 4)
+                lv[:] = (tok < T)[None, None]
+                meta = layout.K_META if plane == layout.K_HI else layout.V_META
+                pair(img[meta])[:] = sc.reshape(B, H, -1).astype("<f2").view(np.uint8)
+                ml = np.repeat(np.arange(G * 32) < T, 2)
+                pair(live[meta])[:] = ml[None, None]
+            return img, live
+        hs = layout.hi_slots(c, self.max_tokens)
+        Tq = self.Tq
+        for g in range(Tq // 32):
+            b = int(self.bits[g])
+            if g * 32 >= tiers.hi_start(Tq, c["hi_window"]):
+                kp, vp, slot, tb = layout.K_HI, layout.V_HI, g % hs, 512 * b
+            else:
+                kp, vp, slot, tb = layout.K_LO, layout.V_LO, g, 512 * b
+            for p, im_fn, codes in ((kp, layout.k_tile, self.k_codes), (vp, layout.v_tile, self.v_codes)):
+                im = pair(img[p]).reshape(B, H, -1, tb)
+                lv = pair(live[p]).reshape(B, H, -1, tb)
+                im[:, :, slot] = im_fn(codes[:, :, g], b)
+                lv[:, :, slot] = True
+            km = pair(img[layout.K_META]).reshape(B, H, -1, 512)
+            vm = pair(img[layout.V_META]).reshape(B, H, -1, 512)
+            km[:, :, g] = layout.k_meta(self.k_s[:, :, g], self.k_z[:, :, g])
+            vm[:, :, g] = layout.v_meta(self.v_s[:, :, g], self.v_z[:, :, g])
+            pair(live[layout.K_META]).reshape(B, H, -1, 512)[:, :, g] = True
+            pair(live[layout.V_META]).reshape(B, H, -1, 512)[:, :, g] = True
+        for p, win in ((layout.K_WIN, self.win_k), (layout.V_WIN, self.win_v)):
+            im = pair(img[p]).reshape(B, H, layout.RING, 256)
+            lv = pair(live[p]).reshape(B, H, layout.RING, 256)
+            for i, t in enumerate(range(Tq, T)):
+                im[:, :, t % layout.RING] = win[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 256)
+                lv[:, :, t % layout.RING] = True
+        return img, live

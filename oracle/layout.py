@@ -1,0 +1,177 @@
+"""Byte image of the cache planes (test oracle).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The pages fix only the container of the 128-value block: a 2-byte fp16 scale
+followed by 64 bytes of 4-bit indices, 66 bytes, 4.125 bits per value
+([trefon] "Przykład: model 27B przy 262K").  Everything else below is this
+package's own layout, written out so that a test can compare a device plane
+byte for byte.  It is restated here from the layout's definition, not shared
+with the library.
+
+Packing of codes into bytes (canonical):
+  4 bits: element 2k -> low nibble of byte k, element 2k+1 -> high nibble.
+  2 bits: element 4k+j -> bits [2j, 2j+1] of byte k.
+
+Tiles.  Quantized tokens live in tiles of 32 consecutive tokens (one key group):
+  key tile   -- token-major: row t = packed codes of token t over the 128
+                channels (64 B at 4 bits, 32 B at 2 bits).  Byte c of row t is
+                stored at offset (c // 16) * 512 + t * 16 + (c % 16), so the
+                16-byte chunk j of all 32 rows is one contiguous 512-byte run.
+  value tile -- channel-major: row d = packed codes of channel d over the 32
+                tokens (16 B at 4 bits, 8 B at 2 bits), row d at offset
+                d * rowbytes.
+  A tile holds 512 * bits bytes.
+
+Planes (all [batch][kv_head][...], row-major, little-endian fp16/fp32):
+  0 K_HI   KIVI: key tiles of the high-bit tier.  With a high-bit window of N
+           tokens the plane is a ring of N/32 slots and group g uses slot
+           g mod (N/32); otherwise it has one slot per group.
+           BLOCK128: key tiles of every group.
+  1 V_HI   same for values.
+  2 K_LO   KIVI with a high-bit window only: low-bit key tiles, slot g = group g.
+  3 V_LO   same for values.
+  4 K_META KIVI: 512 B per group: scales s[128] (channel order) then zeros z[128].
+           BLOCK128: one fp16 scale per token.
+  5 V_META KIVI: 512 B per group: s[4][32] ([dim group][token]) then z[4][32].
+           BLOCK128: one fp16 scale per token.
+  6 K_WIN  KIVI: fp16 window ring of 160 rows x 128; token t in row t mod 160.
+  7 V_WIN  same for values.
+  8 ROPE   pre-RoPE keys only: float32 [32 * ceil(max_tokens/32)][64][2],
+           row t = (cos(t * theta_j), sin(t * theta_j)) for j = 0..63.
+Group count Gmax = ceil(max_tokens / 32).  Unused planes have size 0.
+"""
+
+import numpy as np
+
+TILE_TOKENS = 32
+RING = 160
+N_PLANES = 9
+K_HI, V_HI, K_LO, V_LO, K_META, V_META, K_WIN, V_WIN, ROPE = range(N_PLANES)
+PLANE_NAMES = ["K_HI", "V_HI", "K_LO", "V_LO", "K_META", "V_META", "K_WIN",
+               "V_WIN", "ROPE"]
+
+
+def pack_rows(codes, bits):
+    """Pack the last axis of ``codes`` (uint8 values < 2**bits) canonically."""
+    c = np.asarray(codes, dtype=np.uint8)
+    per = 8 // bits
+    if c.shape[-1] % per:
+        raise ValueError("row length not a multiple of codes per byte")
+    if np.any(c >= (1 << bits)):
+        raise ValueError("code out of range")
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // per, per)).astype(np.uint16)
+    out = np.zeros(g.shape[:-1], dtype=np.uint16)
+    for j in range(per):
+        out |= g[..., j] << (bits * j)
+    return out.astype(np.uint8)
+
+
+def unpack_rows(packed, bits, n):
+    """Inverse of pack_rows: bytes -> n codes per row."""
+    p = np.asarray(packed, dtype=np.uint8)
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    parts = [(p >> (bits * j)) & mask for j in range(per)]
+    out = np.stack(parts, axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * per,))
+    return out[..., :n].astype(np.uint8)
+
+
+def k_tile(codes, bits):
+    """Key tile image: codes [..., 32, 128] -> uint8 [..., 512 * bits]."""
+    rows = pack_rows(codes, bits)                    # [..., 32, rowbytes]
+    rb = rows.shape[-1]
+    lead = rows.shape[:-2]
+    out = np.zeros(lead + (TILE_TOKENS * rb,), dtype=np.uint8)
+    for c in range(rb):
+        for t in range(TILE_TOKENS):
+            out[..., (c // 16) * 512 + t * 16 + (c % 16)] = rows[..., t, c]
+    return out
+
+
+def k_tile_decode(tile, bits):
+    """Key tile image -> codes [..., 32, 128]."""
+    tile = np.asarray(tile, dtype=np.uint8)
+    rb = 128 * bits // 8
+    lead = tile.shape[:-1]
+    rows = np.zeros(lead + (TILE_TOKENS, rb), dtype=np.uint8)
+    for c in range(rb):
+        for t in range(TILE_TOKENS):
+            rows[..., t, c] = tile[..., (c // 16) * 512 + t * 16 + (c % 16)]
+    return unpack_rows(rows, bits, 128)
+
+
+def v_tile(codes, bits):
+    """Value tile image: codes [..., 32 tokens, 128 channels] -> [..., 512 * bits]."""
+    ct = np.swapaxes(np.asarray(codes, dtype=np.uint8), -1, -2)   # [..., 128, 32]
+    rows = pack_rows(ct, bits)                                     # [..., 128, rb]
+    return rows.reshape(rows.shape[:-2] + (-1,))
+
+
+def v_tile_decode(tile, bits):
+    tile = np.asarray(tile, dtype=np.uint8)
+    rb = 32 * bits // 8
+    rows = tile.reshape(tile.shape[:-1] + (128, rb))
+    ct = unpack_rows(rows, bits, 32)                               # [..., 128, 32]
+    return np.swapaxes(ct, -1, -2)
+
+
+def k_meta(s_h, z_h):
+    """512-byte key metadata of one group: s[128] then z[128] (fp16 LE)."""
+    s = np.asarray(s_h, dtype="<f2")
+    z = np.asarray(z_h, dtype="<f2")
+    both = np.concatenate([s, z], axis=-1)
+    return both.view(np.uint8).reshape(s.shape[:-1] + (512,))
+
+
+def v_meta(s_h, z_h):
+    """512-byte value metadata of one group from s_h, z_h [..., 32 tokens, 4]."""
+    s = np.swapaxes(np.asarray(s_h, dtype="<f2"), -1, -2)   # [..., 4, 32]
+    z = np.swapaxes(np.asarray(z_h, dtype="<f2"), -1, -2)
+    both = np.concatenate([s.reshape(s.shape[:-2] + (128,)),
+                           z.reshape(z.shape[:-2] + (128,))], axis=-1)
+    return np.ascontiguousarray(both).view(np.uint8).reshape(both.shape[:-1] + (512,))
+
+
+def block66(nibbles, s_h):
+    """The 66-byte block of one 128-value vector: fp16 scale (LE) + 64 code bytes."""
+    s = np.asarray(s_h, dtype="<f2").reshape(-1, 1).view(np.uint8)
+    codes = pack_rows(nibbles, 4).reshape(-1, 64)
+    out = np.concatenate([s.reshape(-1, 2), codes], axis=-1)
+    return out.reshape(np.shape(nibbles)[:-1] + (66,))
+
+
+def gmax(max_tokens):
+    return (max_tokens + TILE_TOKENS - 1) // TILE_TOKENS
+
+
+def hi_slots(cfg, max_tokens):
+    if cfg["scheme"] == "kivi" and cfg["hi_window"] >= 0:
+        return cfg["hi_window"] // TILE_TOKENS
+    return gmax(max_tokens)
+
+
+def plane_sizes(cfg, batch, max_tokens):
+    """Byte size of every plane, indexed like the plane list above."""
+    pairs = batch * cfg["num_kv_heads"]
+    G = gmax(max_tokens)
+    sz = [0] * N_PLANES
+    if cfg["scheme"] == "kivi":
+        hs = hi_slots(cfg, max_tokens)
+        sz[K_HI] = pairs * hs * 512 * cfg["k_bits"]
+        sz[V_HI] = pairs * hs * 512 * cfg["v_bits"]
+        if cfg["hi_window"] >= 0:
+            sz[K_LO] = pairs * G * 512 * cfg["low_bits"]
+            sz[V_LO] = pairs * G * 512 * cfg["low_bits"]
+        sz[K_META] = pairs * G * 512
+        sz[V_META] = pairs * G * 512
+        sz[K_WIN] = pairs * RING * 128 * 2
+        sz[V_WIN] = pairs * RING * 128 * 2
+    else:
+        sz[K_HI] = pairs * G * 512 * 4
+        sz[V_HI] = pairs * G * 512 * 4
+        sz[K_META] = pairs * G * TILE_TOKENS * 2
+        sz[V_META] = pairs * G * TILE_TOKENS * 2
+    if cfg["pre_rope"]:
+        sz[ROPE] = G * TILE_TOKENS * 64 * 2 * 4
+    return sz

@@ -1,0 +1,156 @@
+"""Pins for oracle/quant.py: round-trip error bounds, brute-force nearest level,
+invariants of the asymmetric and symmetric quantizers, dequant exactness."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import quant
+
+F16, F32 = np.float16, np.float32
+SLACK = 1 + 2.0 ** -20   # quotient rounding
+
+
+def fp16_groups(rng, n, size, kind):
+    if kind == "normal":
+        x = rng.standard_normal((n, size))
+    elif kind == "outlier":
+        x = rng.standard_normal((n, size))
+        x[:, 3] *= 20
+    elif kind == "student":
+        x = rng.standard_t(3, size=(n, size))
+    elif kind == "tiny":      # fp16 subnormal range
+        x = rng.standard_normal((n, size)) * 1e-6
+    elif kind == "offset":    # narrow range far from zero
+        x = 50 + rng.standard_normal((n, size)) * 1e-2
+    elif kind == "signed_zero":
+        x = np.where(rng.random((n, size)) < 0.5, -0.0, 0.0)
+        x[:, 0] = 1.0
+    return x.astype(F16)
+
+
+KINDS = ["normal", "outlier", "student", "tiny", "offset", "signed_zero"]
+
+
+@pytest.mark.parametrize("bits,kind", list(itertools.product([4, 2], KINDS)))
+def test_asym_roundtrip_bound_fp16_inputs(bits, kind):
+    rng = np.random.default_rng([bits, KINDS.index(kind)])
+    x = fp16_groups(rng, 2000, 32, kind).astype(F32)
+    c, s, z = quant.quant_asym(x, bits, axis=-1)
+    xh = quant.dequant_asym(c, s, z, axis=-1)
+    err = np.abs(x.astype(np.float64) - xh)
+    Q = 2 ** bits - 1
+    sh = s.astype(np.float64)[:, None]
+    bound = sh / 2 * SLACK
+    # a normal fp16 scale is within 2^-11 of the exact step, so the range
+    # [z, z + Q s_h] covers the group and the error is at most half a step
+    normal = (s.astype(np.float64) >= 2.0 ** -14)[:, None] | (s == 0)[:, None]
+    assert np.all((err <= bound + 1e-30) | ~normal)
+    # a subnormal scale can be far from the exact step; then values past the
+    # top level are clamped: the error is half a step plus the overshoot
+    top = z.astype(np.float64)[:, None] + Q * sh
+    over = np.maximum(0.0, x.astype(np.float64) - top)
+    assert np.all(err <= bound + over + 1e-30)
+    pos = s >= 2.0 ** -14
+    # the min maps to 0 and the max to Q in every group with a nonzero scale
+    assert np.all(c[pos].min(axis=1) == 0)
+    assert np.all(c[pos].max(axis=1) == Q)
+    # codes are monotone in x within a group
+    order = np.argsort(x, axis=1, kind="stable")
+    cs = np.take_along_axis(c, order, axis=1)
+    assert np.all(np.diff(cs.astype(int), axis=1) >= 0)
+
+
+def test_asym_fp32_inputs_bound():
+    # Hadamard-rotated values are fp32: the zero point is fp16(min), so the bound
+    # widens by |z_h - min|
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((5000, 32)) * 3).astype(F32)
+    for bits in (4, 2):
+        c, s, z = quant.quant_asym(x, bits, axis=-1)
+        xh = quant.dequant_asym(c, s, z, axis=-1)
+        mn = x.min(axis=1).astype(np.float64)
+        extra = np.abs(z.astype(np.float64) - mn)
+        bound = (s.astype(np.float64) / 2 * SLACK + extra)[:, None]
+        assert np.all(np.abs(x - xh) <= bound * (1 + 1e-6))
+
+
+def test_asym_constant_and_zero_groups():
+    x = np.full((4, 32), 3.25, F32)
+    x[1] = 0.0
+    x[2] = -0.0
+    x[3] = -7.5
+    c, s, z = quant.quant_asym(x, 4, axis=-1)
+    assert np.all(c == 0) and np.all(s == 0)
+    assert np.array_equal(quant.dequant_asym(c, s, z, axis=-1), x)
+    # -0 is canonicalized to +0
+    assert z.view(np.uint16)[2] == 0x0000
+
+
+def test_asym_brute_force_nearest_level():
+    # tiny groups: every code is the nearest of the 2^b levels z + k s (fp64),
+    # unless two levels are (nearly) tied
+    rng = np.random.default_rng(7)
+    for bits in (4, 2):
+        Q = 2 ** bits - 1
+        x = (rng.standard_normal((3000, 4)) * rng.uniform(0.1, 10, (3000, 1))).astype(F16).astype(F32)
+        c, s, z = quant.quant_asym(x, bits, axis=-1)
+        for g in range(x.shape[0]):
+            sh, zh = float(s[g]), float(z[g])
+            if sh == 0:
+                assert np.all(c[g] == 0)
+                continue
+            levels = zh + sh * np.arange(Q + 1)
+            for i in range(4):
+                d = np.abs(levels - float(x[g, i]))
+                best = np.argsort(d)
+                if d[best[1]] - d[best[0]] < 1e-6 * sh:
+                    continue
+                assert c[g, i] == best[0], (g, i)
+
+
+def test_kivi_group_axes():
+    # keys: one range per channel over the 32 tokens; values: one range per
+    # token over each 32-dim slice
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((32, 128)).astype(F16).astype(F32)
+    x[:, 5] *= 20
+    ck, sk, zk = quant.quant_k_group(x, 4)
+    assert sk.shape == (128,) and zk.shape == (128,)
+    assert zk[5] == F16(x[:, 5].min())
+    assert sk[5] == F16(F32(x[:, 5].max() - x[:, 5].min()) / F32(15))
+    cv, sv, zv = quant.quant_v_group(x, 4)
+    assert sv.shape == (32, 4)
+    assert zv[7, 2] == F16(x[7, 64:96].min())
+    assert np.array_equal(quant.dequant_v_group(cv, sv, zv)[:, :32],
+                          quant.dequant_asym(cv[:, :32], sv[:, 0], zv[:, 0], axis=-1))
+
+
+def test_symmetric_block():
+    rng = np.random.default_rng(11)
+    y = (rng.standard_normal((4000, 128)) * rng.uniform(0.01, 100, (4000, 1))).astype(F32)
+    n, s = quant.quant_sym128(y)
+    yh = quant.dequant_sym128(n, s)
+    assert n.min() >= 1 and n.max() <= 15
+    assert np.all(np.abs(y - yh) <= s.astype(np.float64)[:, None] / 2 * SLACK)
+    # the absmax element maps to +-7
+    am = np.argmax(np.abs(y), axis=1)
+    c_am = n[np.arange(len(y)), am].astype(int) - 8
+    assert np.all(np.abs(c_am) == 7)
+    assert np.all(np.sign(c_am) == np.sign(y[np.arange(len(y)), am]))
+    zn, zs = quant.quant_sym128(np.zeros((1, 128), F32))
+    assert np.all(zn == 8) and zs[0] == 0
+
+
+def test_dequant_exactness():
+    # c * s_h is exact in fp32 (4-bit x 11-bit significands), so mul-then-add
+    # equals the fp64 value rounded once
+    rng = np.random.default_rng(13)
+    c = rng.integers(0, 16, size=100000).astype(np.uint8)
+    s = rng.standard_normal(100000).astype(F16)
+    z = rng.standard_normal(100000).astype(F16)
+    got = quant.dequant_asym(c[:, None], s, z, axis=-1)[:, 0]
+    prod = c.astype(np.float64) * s.astype(np.float64)
+    assert np.array_equal(prod.astype(F32).astype(np.float64), prod)
+    assert np.array_equal(got, (prod + z.astype(np.float64)).astype(F32))
