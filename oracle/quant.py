@@ -18,8 +18,11 @@ What the pages fix:
 Readings where the pages are silent (all float32 one op at a time, RNE):
   asymmetric, b bits, Q = 2**b - 1, over a group x:
     mn, mx = min(x), max(x)
-    s  = fl32(fl32(mx - mn) / Q);  s_h = fp16(s)
-    z_h = fp16(mn) + (+0.0)         (the addition turns -0 into +0)
+    s  = fl32(fl32(mx - mn) / Q);  s_h = fp16(s) + (+0.0)
+    z_h = fp16(mn) + (+0.0)         (the additions turn -0 into +0: over a
+                                     group of signed zeros min and max may be
+                                     either zero, so the sign bits would
+                                     depend on reduction order)
     c  = clamp(rint(fl32(fl32(x - z_h) / s_h)), 0, Q);   c = 0 wherever s_h == 0
     x^ = fl32(c * s_h + z_h)        (c * s_h is exact in fp32)
   symmetric 128-block, 4 bits:
@@ -51,7 +54,7 @@ def quant_asym(x, bits, axis):
     mn = x.min(axis=axis)
     mx = x.max(axis=axis)
     s = (mx - mn).astype(F32) / Q
-    s_h = s.astype(F16)
+    s_h = (s.astype(F16) + F16(0.0)).astype(F16)
     z_h = (mn.astype(F16) + F16(0.0)).astype(F16)
     sx = np.expand_dims(s_h.astype(F32), axis)
     zx = np.expand_dims(z_h.astype(F32), axis)

@@ -86,6 +86,13 @@ def test_asym_constant_and_zero_groups():
     assert np.array_equal(quant.dequant_asym(c, s, z, axis=-1), x)
     # -0 is canonicalized to +0
     assert z.view(np.uint16)[2] == 0x0000
+    # a group of mixed signed zeros: both parameters are +0 whatever min/max pick
+    xz = np.zeros((2, 32), F32)
+    xz[0, ::2] = -0.0
+    xz[1, 1::3] = -0.0
+    cz, sz, zz = quant.quant_asym(xz, 2, axis=-1)
+    assert np.all(sz.view(np.uint16) == 0) and np.all(zz.view(np.uint16) == 0)
+    assert np.all(cz == 0)
 
 
 def test_asym_brute_force_nearest_level():
