@@ -42,7 +42,7 @@ from .attention import rope_f64, decode_f64
 F16 = np.float16
 F32 = np.float32
 
-DEFAULTS = dict(head_dim=128, group=32, vdims=32, window=128, hi_window=-1,
+DEFAULTS = dict(head_dim=128, group=32, vdims=32, window=128, hi_window=-1, k_bits=4, v_bits=4,
                 low_bits=2, hadamard=False, pre_rope=False, rope_theta=10000.0)
 
 

@@ -1,0 +1,60 @@
+"""Build libkvq.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+    python -m quantized_decode_attention_02_amd.build
+
+Flags that matter for correctness:
+  * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32
+    instructions are generated;
+  * ``-fno-gpu-flush-denormals-to-zero`` and
+    ``-fhip-fp32-correctly-rounded-divide-sqrt``: IEEE fp32 division and
+    denormals, which the bit-exact quantizer relies on;
+  * no fast-math of any kind.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(LIBDIR, "libkvq.so")
+SOURCES = ["kvq.cpp", "append.hip", "decode.hip", "dequant.hip"]
+ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libkvq)")
+
+
+def command(out=LIB):
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-fno-fast-math", "-Wall", "-Wno-unused-function",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out] + \
+           [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose=False):
+    """Compile every source into _lib/libkvq.so (always recompiles)."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libkvq.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,437 @@
+// Quantize-on-append kernels.
+//
+// Sources cited here:
+//   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
+//              ultra-long context" (troisinh.com).
+//   [nalar]    "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
+//              (nalar.dev).
+//   [trefon]   "Matematyka cache KV: ile kosztuje długi kontekst i co daje
+//              4-bitowy cache" (trefon.com).
+//
+// Everything that produces stored bytes is bit-exact with the documented
+// float32 round-to-nearest-even arithmetic: one IEEE operation per step,
+// correctly rounded division, rintf, RNE fp32->fp16.  No fused multiply-add
+// contraction in this file (the only products are exact anyway).
+#pragma clang fp contract(off)
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Asymmetric group quantizer ([troisinh] "Tại sao nó hoạt động", item 1;
+// [nalar] "Granularitas kuantisasi mengendalikan rentang yang harus dicakup
+// setiap scale"): over a group x, Q = 2^bits - 1,
+//   s = fl32(fl32(max - min) / Q), s_h = fp16(s) + 0, z_h = fp16(min) + 0,
+//   c = clamp(rint(fl32(fl32(x - z_h) / s_h)), 0, Q), c = 0 when s_h == 0.
+// The full [min, max] range is used (no clipping).
+struct GroupParams {
+  uint16_t s_bits, z_bits;
+  float s, z;
+};
+
+__device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits) {
+  const float Q = (float)((1 << bits) - 1);
+  GroupParams gp;
+  gp.s_bits = canonical_half_bits((mx - mn) / Q);
+  gp.z_bits = canonical_half_bits(mn);
+  gp.s = half_bits_to_float(gp.s_bits);
+  gp.z = half_bits_to_float(gp.z_bits);
+  return gp;
+}
+
+__device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp, int bits) {
+  if (gp.s == 0.0f) return 0;
+  const float Q = (float)((1 << bits) - 1);
+  const float r = rintf((x - gp.z) / gp.s);
+  return (uint8_t)fminf(fmaxf(r, 0.0f), Q);
+}
+
+// One 32-token group in LDS: xk[32][128], xv[32][128] float (the values the
+// quantizer sees: fp16 inputs, or their rotation) -> codes ck, cv and the
+// metadata records (key: s[128], z[128]; value: s[4][32], z[4][32]).
+// Keys use one range per channel over the 32 tokens, values one range per
+// token over each 32-dim slice ([trefon] "Dlaczego cache trudniej
+// skwantyzować niż wagi").  Needs 256 threads.
+__device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uint8_t (*ck)[kD],
+                               uint8_t (*cv)[kD], uint16_t* kmeta, uint16_t* vmeta, int bits,
+                               int tid) {
+  if (tid < kD) {
+    const int c = tid;
+    float mn = xk[0][c], mx = xk[0][c];
+    for (int t = 1; t < kGroup; ++t) {
+      mn = fminf(mn, xk[t][c]);
+      mx = fmaxf(mx, xk[t][c]);
+    }
+    const GroupParams gp = group_params(mn, mx, bits);
+    for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code(xk[t][c], gp, bits);
+    kmeta[c] = gp.s_bits;
+    kmeta[kD + c] = gp.z_bits;
+  } else {
+    const int u = tid - kD;
+    const int t = u >> 2, dg = u & 3;
+    const float* row = xv[t] + dg * 32;
+    float mn = row[0], mx = row[0];
+    for (int i = 1; i < 32; ++i) {
+      mn = fminf(mn, row[i]);
+      mx = fmaxf(mx, row[i]);
+    }
+    const GroupParams gp = group_params(mn, mx, bits);
+    for (int i = 0; i < 32; ++i) cv[t][dg * 32 + i] = quantize_code(row[i], gp, bits);
+    vmeta[dg * 32 + t] = gp.s_bits;
+    vmeta[kD + dg * 32 + t] = gp.z_bits;
+  }
+}
+
+// Pack codes into the tile byte images (canonical nibble/crumb order: element
+// 2k in the low nibble of byte k; element 4k+j in bits 2j..2j+1).
+//   key tile:   token-major rows, byte cb of token t at ktile_offset(t, cb)
+//   value tile: channel-major rows of 32 tokens, row d at d * (4 * bits)
+__device__ void pack_key_tile(const uint8_t (*ck)[kD], uint8_t* dst, int bits, int tid) {
+  const int per_thread = 2 * bits;  // 2048 or 1024 bytes over 256 threads
+  const int o0 = tid * per_thread;
+  uint8_t buf[8];
+  for (int k = 0; k < per_thread; ++k) {
+    const int o = o0 + k;
+    const int t = (o & 511) >> 4;
+    const int cb = (o >> 9) * 16 + (o & 15);
+    uint32_t v = 0;
+    if (bits == 4) {
+      v = ck[t][2 * cb] | (ck[t][2 * cb + 1] << 4);
+    } else {
+      for (int j = 0; j < 4; ++j) v |= (uint32_t)ck[t][4 * cb + j] << (2 * j);
+    }
+    buf[k] = (uint8_t)v;
+  }
+  if (bits == 4) {
+    uint2 w;
+    w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+    w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
+    *reinterpret_cast<uint2*>(dst + o0) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(dst + o0) =
+        buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+  }
+}
+
+__device__ void pack_value_tile(const uint8_t (*cv)[kD], uint8_t* dst, int bits, int tid) {
+  const int per_thread = 2 * bits;
+  const int rb = 4 * bits;  // bytes per channel row
+  const int o0 = tid * per_thread;
+  uint8_t buf[8];
+  for (int k = 0; k < per_thread; ++k) {
+    const int o = o0 + k;
+    const int d = o / rb, kb = o % rb;
+    uint32_t v = 0;
+    if (bits == 4) {
+      v = cv[2 * kb][d] | (cv[2 * kb + 1][d] << 4);
+    } else {
+      for (int j = 0; j < 4; ++j) v |= (uint32_t)cv[4 * kb + j][d] << (2 * j);
+    }
+    buf[k] = (uint8_t)v;
+  }
+  if (bits == 4) {
+    uint2 w;
+    w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+    w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
+    *reinterpret_cast<uint2*>(dst + o0) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(dst + o0) =
+        buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+  }
+}
+
+__device__ __forceinline__ uint8_t* hi_tile(const Geom& g, const Planes& p, int plane,
+                                            int64_t pair, int64_t grp, int bits) {
+  return p.p[plane] + (pair * g.hi_slots + grp % g.hi_slots) * tile_bytes(bits);
+}
+__device__ __forceinline__ uint8_t* lo_tile(const Geom& g, const Planes& p, int plane,
+                                            int64_t pair, int64_t grp, int bits) {
+  return p.p[plane] + (pair * g.gmax + grp) * tile_bytes(bits);
+}
+
+__device__ void store_group(const Geom& g, const Planes& p, int64_t pair, int64_t grp, int bits,
+                            bool hi, const uint8_t (*ck)[kD], const uint8_t (*cv)[kD],
+                            const uint16_t* kmeta, const uint16_t* vmeta, int tid) {
+  uint8_t* kt = hi ? hi_tile(g, p, KVQ_PLANE_K_HI, pair, grp, bits)
+                   : lo_tile(g, p, KVQ_PLANE_K_LO, pair, grp, bits);
+  uint8_t* vt = hi ? hi_tile(g, p, KVQ_PLANE_V_HI, pair, grp, bits)
+                   : lo_tile(g, p, KVQ_PLANE_V_LO, pair, grp, bits);
+  pack_key_tile(ck, kt, bits, tid);
+  pack_value_tile(cv, vt, bits, tid);
+  uint16_t* km = reinterpret_cast<uint16_t*>(p.p[KVQ_PLANE_K_META] + (pair * g.gmax + grp) * 512);
+  uint16_t* vm = reinterpret_cast<uint16_t*>(p.p[KVQ_PLANE_V_META] + (pair * g.gmax + grp) * 512);
+  km[tid] = kmeta[tid];
+  vm[tid] = vmeta[tid];
+}
+
+// ---------------------------------------------------------------------------
+// KIVI: quantize the key groups [g0, g1) of every (sequence, kv head).  A
+// group's tokens come from the fp16 window ring (tokens before T0) or from the
+// new input (tokens from T0 on).  The group goes to the high-bit tier if it
+// starts at or after hi_start_new, else straight to the low-bit tier.
+__global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, const __half* k_new,
+                                                            const __half* v_new, int64_t n_new,
+                                                            int64_t T0, int64_t g0,
+                                                            int64_t hi_start_new) {
+  __shared__ float xs[2][kGroup][kD];
+  __shared__ uint8_t cs[2][kGroup][kD];
+  __shared__ uint16_t meta[2][256];
+  const int tid = threadIdx.x;
+  const int64_t grp = g0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t pair = pair_index(g, b, h);
+
+  for (int e = tid; e < 2 * kGroup * 16; e += 256) {
+    const int tensor = e >> 9, r = e & 511;
+    const int tok = r >> 4, c8 = r & 15;
+    const int64_t t = grp * kGroup + tok;
+    const __half* src;
+    if (t < T0) {
+      const int plane = tensor ? KVQ_PLANE_V_WIN : KVQ_PLANE_K_WIN;
+      src = reinterpret_cast<const __half*>(p.p[plane]) + (pair * kRing + t % kRing) * kD;
+    } else {
+      const __half* base = tensor ? v_new : k_new;
+      src = base + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
+    }
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
+    const __half* hv = reinterpret_cast<const __half*>(&raw);
+    for (int i = 0; i < 8; ++i) xs[tensor][tok][8 * c8 + i] = __half2float(hv[i]);
+  }
+  __syncthreads();
+  if (g.hadamard) fwht128_lds(&xs[0][0][0], 2 * kGroup, tid, 256);
+
+  const bool hi = grp * kGroup >= hi_start_new;
+  const int bits = hi ? g.hi_bits : g.lo_bits;
+  quantize_group(xs[0], xs[1], cs[0], cs[1], meta[0], meta[1], bits, tid);
+  __syncthreads();
+  store_group(g, p, pair, grp, bits, hi, cs[0], cs[1], meta[0], meta[1], tid);
+}
+
+// KIVI: groups [g0, g1) leave the high-bit tier.  Their fp16 source is gone,
+// so they are requantized at low_bits from their dequantized high-bit values
+// x = fl32(c * s_h + z_h) (the product is exact).  Must run before new groups
+// reuse the ring slots.
+__global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int64_t g0) {
+  __shared__ float xs[2][kGroup][kD];
+  __shared__ uint8_t cs[2][kGroup][kD];
+  __shared__ uint16_t meta[2][256];
+  const int tid = threadIdx.x;
+  const int64_t grp = g0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t pair = pair_index(g, b, h);
+  const int hb = g.hi_bits;
+  const uint8_t* kt = hi_tile(g, p, KVQ_PLANE_K_HI, pair, grp, hb);
+  const uint8_t* vt = hi_tile(g, p, KVQ_PLANE_V_HI, pair, grp, hb);
+  const uint16_t* km =
+      reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META] + (pair * g.gmax + grp) * 512);
+  const uint16_t* vm =
+      reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META] + (pair * g.gmax + grp) * 512);
+  const int per = 8 / hb, mask = (1 << hb) - 1;
+  for (int e = tid; e < kGroup * kD; e += 256) {
+    const int t = e >> 7, d = e & 127;
+    const int kcode = (kt[ktile_offset(t, d / per)] >> (hb * (d % per))) & mask;
+    const int vcode = (vt[d * 4 * hb + t / per] >> (hb * (t % per))) & mask;
+    const float ks = half_bits_to_float(km[d]), kz = half_bits_to_float(km[kD + d]);
+    const int dg = d >> 5;
+    const float vs = half_bits_to_float(vm[dg * 32 + t]);
+    const float vz = half_bits_to_float(vm[kD + dg * 32 + t]);
+    xs[0][t][d] = (float)kcode * ks + kz;
+    xs[1][t][d] = (float)vcode * vs + vz;
+  }
+  __syncthreads();
+  quantize_group(xs[0], xs[1], cs[0], cs[1], meta[0], meta[1], g.lo_bits, tid);
+  __syncthreads();
+  store_group(g, p, pair, grp, g.lo_bits, false, cs[0], cs[1], meta[0], meta[1], tid);
+}
+
+// KIVI: copy new tokens [w0, w1) (absolute positions, all >= T0) into the fp16
+// window ring, row t mod 160.  One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, const __half* k_new,
+                                                           const __half* v_new, int64_t n_new,
+                                                           int64_t T0, int64_t w0, int64_t nw) {
+  const int64_t items = (int64_t)g.B * nw * g.Hkv * 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int tensor = i >= items;
+    int64_t r = tensor ? i - items : i;
+    const int c8 = r % 16;
+    r /= 16;
+    const int h = r % g.Hkv;
+    r /= g.Hkv;
+    const int64_t t = w0 + r % nw;
+    const int b = (int)(r / nw);
+    const __half* src = (tensor ? v_new : k_new) + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
+    const int plane = tensor ? KVQ_PLANE_V_WIN : KVQ_PLANE_K_WIN;
+    __half* dst = reinterpret_cast<__half*>(p.p[plane]) +
+                  (pair_index(g, b, h) * kRing + t % kRing) * kD;
+    *reinterpret_cast<uint4*>(dst + 8 * c8) = *reinterpret_cast<const uint4*>(src + 8 * c8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Symmetric 128-value blocks ([trefon] "Przykład: model 27B przy 262K"; "Jak
+// 4-bitowemu cache to uchodzi: najpierw obrót"): per token vector y (rotated
+// when configured) a = max|y|, s_h = fp16(fl32(a / 7)),
+// c = clamp(rint(fl32(y / s_h)), -7, 7) (0 when s_h == 0), stored nibble c + 8.
+// One block per 32-token tile that overlaps [T0, T0 + n_new); tokens of the
+// tile outside that range keep their stored nibbles (value tiles hold two
+// tokens per byte).
+__global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, const __half* k_new,
+                                                              const __half* v_new, int64_t n_new,
+                                                              int64_t T0, int64_t tile0) {
+  __shared__ float xs[2][kGroup][kD];
+  __shared__ uint8_t cs[2][kGroup][kD];
+  __shared__ float sc[2][kGroup];
+  const int tid = threadIdx.x;
+  const int64_t tile = tile0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t pair = pair_index(g, b, h);
+  const int64_t T1 = T0 + n_new;
+  const int64_t tbase = tile * kGroup;
+
+  for (int e = tid; e < 2 * kGroup * 16; e += 256) {
+    const int tensor = e >> 9, r = e & 511;
+    const int tok = r >> 4, c8 = r & 15;
+    const int64_t t = tbase + tok;
+    float* dst = &xs[tensor][tok][8 * c8];
+    if (t >= T0 && t < T1) {
+      const __half* src = (tensor ? v_new : k_new) + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
+      const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
+      const __half* hv = reinterpret_cast<const __half*>(&raw);
+      for (int i = 0; i < 8; ++i) dst[i] = __half2float(hv[i]);
+    } else {
+      for (int i = 0; i < 8; ++i) dst[i] = 0.0f;
+    }
+  }
+  __syncthreads();
+  if (g.hadamard) fwht128_lds(&xs[0][0][0], 2 * kGroup, tid, 256);
+
+  if (tid < 2 * kGroup) {
+    const int tensor = tid >> 5, tok = tid & 31;
+    float a = 0.0f;
+    for (int i = 0; i < kD; ++i) a = fmaxf(a, fabsf(xs[tensor][tok][i]));
+    const uint16_t sb = float_to_half_bits(a / 7.0f);
+    sc[tensor][tok] = half_bits_to_float(sb);
+    const int64_t t = tbase + tok;
+    if (t >= T0 && t < T1) {
+      uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
+      sp[pair * g.gmax * kGroup + t] = sb;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 2 * kGroup * kD; e += 256) {
+    const int tensor = e >> 12, tok = (e >> 7) & 31, d = e & 127;
+    const float s = sc[tensor][tok];
+    float c = 0.0f;
+    if (s != 0.0f) c = fminf(fmaxf(rintf(xs[tensor][tok][d] / s), -7.0f), 7.0f);
+    cs[tensor][tok][d] = (uint8_t)((int)c + 8);
+  }
+  __syncthreads();
+  uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * 2048;
+  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * 2048;
+  // key tile: 8 consecutive bytes belong to one token row
+  {
+    const int o0 = tid * 8;
+    const int t = (o0 & 511) >> 4;
+    const int64_t tt = tbase + t;
+    if (tt >= T0 && tt < T1) {
+      uint8_t buf[8];
+      for (int k = 0; k < 8; ++k) {
+        const int o = o0 + k;
+        const int cb = (o >> 9) * 16 + (o & 15);
+        buf[k] = (uint8_t)(cs[0][t][2 * cb] | (cs[0][t][2 * cb + 1] << 4));
+      }
+      uint2 w;
+      w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+      w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
+      *reinterpret_cast<uint2*>(kt + o0) = w;
+    }
+  }
+  // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k+1 (high)
+  for (int o = tid; o < 2048; o += 256) {
+    const int d = o >> 4, kb = o & 15;
+    const int64_t t0 = tbase + 2 * kb, t1 = t0 + 1;
+    const bool in0 = t0 >= T0 && t0 < T1, in1 = t1 >= T0 && t1 < T1;
+    if (!in0 && !in1) continue;
+    uint8_t v = (in0 && in1) ? 0 : vt[o];
+    if (in0) v = (uint8_t)((v & 0xF0) | cs[1][2 * kb][d]);
+    if (in1) v = (uint8_t)((v & 0x0F) | (cs[1][2 * kb + 1][d] << 4));
+    vt[o] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-half RoPE table for pre-RoPE keys ([troisinh] "Tại sao nó hoạt
+// động", item 3): row t holds (cos, sin) of t * theta_j, theta_j =
+// base^(-2j/128), computed in fp64 and rounded to fp32.
+__global__ __launch_bounds__(256) void rope_table_kernel(Geom g, Planes p, int64_t t0, int64_t n) {
+  float* tab = reinterpret_cast<float*>(p.p[KVQ_PLANE_ROPE]);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * 64;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = t0 + i / 64;
+    const int j = (int)(i % 64);
+    const double theta = pow((double)g.rope_theta, -2.0 * (double)j / 128.0);
+    const double ang = (double)t * theta;
+    tab[t * 128 + 2 * j] = (float)cos(ang);
+    tab[t * 128 + 2 * j + 1] = (float)sin(ang);
+  }
+}
+
+int grid_for(int64_t items) {
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  return (int)(blocks < 1 ? 1 : blocks);
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const Geom& g, const Planes& p, int64_t t0, int64_t t1, hipStream_t s) {
+  if (t1 > t0) {
+    hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((t1 - t0) * 64)), dim3(256), 0, s, g, p, t0,
+                       t1 - t0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kivi_demote(const Geom& g, const Planes& p, int64_t g0, int64_t g1, hipStream_t s) {
+  if (g1 > g0) {
+    hipLaunchKernelGGL(kivi_demote_kernel, dim3((unsigned)(g1 - g0), g.Hkv, g.B), dim3(256), 0, s, g, p,
+                       g0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_new,
+                                const __half* v_new, int64_t n_new, int64_t T0, int64_t g0,
+                                int64_t g1, int64_t hi_start_new, hipStream_t s) {
+  if (g1 > g0) {
+    hipLaunchKernelGGL(kivi_quantize_kernel, dim3((unsigned)(g1 - g0), g.Hkv, g.B), dim3(256), 0, s, g,
+                       p, k_new, v_new, n_new, T0, g0, hi_start_new);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_window_write(const Geom& g, const Planes& p, const __half* k_new,
+                               const __half* v_new, int64_t n_new, int64_t T0, int64_t w0,
+                               int64_t w1, hipStream_t s) {
+  if (w1 > w0) {
+    const int64_t items = 2 * (int64_t)g.B * (w1 - w0) * g.Hkv * 16;
+    hipLaunchKernelGGL(window_write_kernel, dim3(grid_for(items)), dim3(256), 0, s, g, p, k_new, v_new,
+                       n_new, T0, w0, w1 - w0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block128_append(const Geom& g, const Planes& p, const __half* k_new,
+                                  const __half* v_new, int64_t n_new, int64_t T0, hipStream_t s) {
+  if (n_new > 0) {
+    const int64_t tile0 = T0 / kGroup, tile1 = (T0 + n_new + kGroup - 1) / kGroup;
+    hipLaunchKernelGGL(block128_append_kernel, dim3((unsigned)(tile1 - tile0), g.Hkv, g.B), dim3(256), 0,
+                       s, g, p, k_new, v_new, n_new, T0, tile0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

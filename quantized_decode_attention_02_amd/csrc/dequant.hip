@@ -1,0 +1,80 @@
+// Dequantize a token range to fp32 in the stored domain: the
+// dequantize-before-arithmetic path of [nalar] "Kuantisasi KV Cache dengan
+// Error Budget yang Eksplisit", section "Biaya dequantization harus masuk ke
+// model latency" — here only for tests and inspection; decode never uses it.
+//   KIVI:     x = fl32(c * s_h + z_h)   (the product is exact, so fused or not
+//                                        gives the same bits)
+//   BLOCK128: y = fl32((n - 8) * s_h)  (exact)
+//   window:   the fp16 value.
+#pragma clang fp contract(off)
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+__global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t t0, int64_t nt,
+                                                      float* k_out, float* v_out) {
+  const int64_t items = (int64_t)g.B * nt * g.Hkv * kD;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i;
+    const int d = r % kD;
+    r /= kD;
+    const int h = r % g.Hkv;
+    r /= g.Hkv;
+    const int64_t t = t0 + r % nt;
+    const int b = (int)(r / nt);
+    const int64_t pair = pair_index(g, b, h);
+    float kv, vv;
+    if (g.scheme == KVQ_BLOCK128_SYM) {
+      const int64_t grp = t / kGroup;
+      const int row = (int)(t % kGroup);
+      const uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + grp) * 2048;
+      const uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 2048;
+      const int kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
+      const int vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
+      const uint16_t* vs = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
+      kv = (float)(kn - 8) * half_bits_to_float(ks[t]);
+      vv = (float)(vn - 8) * half_bits_to_float(vs[t]);
+    } else if (t < g.Tq) {
+      const int64_t grp = t / kGroup;
+      const int row = (int)(t % kGroup);
+      int bits;
+      const uint8_t* kt = tile_ptr(g, p, KVQ_PLANE_K_HI, KVQ_PLANE_K_LO, pair, grp, &bits);
+      const uint8_t* vt = tile_ptr(g, p, KVQ_PLANE_V_HI, KVQ_PLANE_V_LO, pair, grp, &bits);
+      const int per = 8 / bits, mask = (1 << bits) - 1;
+      const int kc = (kt[ktile_offset(row, d / per)] >> (bits * (d % per))) & mask;
+      const int vc = (vt[d * 4 * bits + row / per] >> (bits * (row % per))) & mask;
+      const uint16_t* km = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META] + (pair * g.gmax + grp) * 512);
+      const uint16_t* vm = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META] + (pair * g.gmax + grp) * 512);
+      const int dg = d >> 5;
+      kv = (float)kc * half_bits_to_float(km[d]) + half_bits_to_float(km[kD + d]);
+      vv = (float)vc * half_bits_to_float(vm[dg * 32 + row]) + half_bits_to_float(vm[kD + dg * 32 + row]);
+    } else {
+      const __half* kr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
+      const __half* vr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + (pair * kRing + t % kRing) * kD;
+      kv = __half2float(kr[d]);
+      vv = __half2float(vr[d]);
+    }
+    k_out[i] = kv;
+    v_out[i] = vv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const Geom& g, const Planes& p, int64_t t0, int64_t t1, float* k_out,
+                          float* v_out, hipStream_t s) {
+  const int64_t items = (int64_t)g.B * (t1 - t0) * g.Hkv * kD;
+  if (items > 0) {
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, p, t0, t1 - t0, k_out,
+                       v_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,304 @@
+// libkvq C ABI: argument validation, plane layout, tier bookkeeping and
+// kernel dispatch.  No device allocation, no synchronization, no global
+// mutable state.  The contract of every function is in include/kvq.h.
+//
+// Sources cited here:
+//   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
+//              ultra-long context" (troisinh.com).
+//   [nalar]    "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
+//              (nalar.dev).
+#include <cmath>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr uint64_t kAlign = 16;
+
+bool aligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) % kAlign) == 0; }
+
+kvq_status validate_config(const kvq_config* c) {
+  if (c == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (c->head_dim <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (c->scheme != KVQ_KIVI_ASYM && c->scheme != KVQ_BLOCK128_SYM) return KVQ_ERR_INVALID_ARG;
+  if (c->k_bits <= 0 || c->v_bits <= 0) return KVQ_ERR_INVALID_ARG;
+  if (c->hadamard != 0 && c->hadamard != 1) return KVQ_ERR_INVALID_ARG;
+  if (c->pre_rope_keys != 0 && c->pre_rope_keys != 1) return KVQ_ERR_INVALID_ARG;
+  if (c->pre_rope_keys && !(c->rope_theta > 0.0f && std::isfinite(c->rope_theta)))
+    return KVQ_ERR_INVALID_ARG;
+  if (c->int4_window != -1 && (c->int4_window <= 0 || c->int4_window % kGroup != 0))
+    return KVQ_ERR_INVALID_ARG;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (c->head_dim != kD) return KVQ_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4) return KVQ_ERR_UNSUPPORTED;
+  if (c->k_group_tokens != kGroup || c->v_group_dims != 32) return KVQ_ERR_UNSUPPORTED;
+  if (c->v_bits != c->k_bits) return KVQ_ERR_UNSUPPORTED;
+  if (c->hadamard && c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
+  if (c->scheme == KVQ_KIVI_ASYM) {
+    if (c->k_bits != 4 && c->k_bits != 2) return KVQ_ERR_UNSUPPORTED;
+    if (c->fp16_window != kWindow) return KVQ_ERR_UNSUPPORTED;
+    if (c->int4_window >= 0 && (c->k_bits != 4 || c->low_bits != 2)) return KVQ_ERR_UNSUPPORTED;
+  } else {
+    if (c->k_bits != 4) return KVQ_ERR_UNSUPPORTED;
+    if (c->fp16_window != 0 || c->int4_window != -1) return KVQ_ERR_UNSUPPORTED;
+    if (c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
+  }
+  return KVQ_OK;
+}
+
+int64_t quantized_prefix(const kvq_config* c, int64_t length) {
+  if (c->scheme == KVQ_BLOCK128_SYM) return length;
+  const int64_t r = length - kWindow;
+  if (r <= 0) return 0;
+  return (r / kGroup) * kGroup;
+}
+
+int64_t groups_for(int64_t max_tokens) { return (max_tokens + kGroup - 1) / kGroup; }
+
+Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t length) {
+  Geom g;
+  g.B = (int)batch;
+  g.Hq = c->num_q_heads;
+  g.Hkv = c->num_kv_heads;
+  g.G = c->num_q_heads / c->num_kv_heads;
+  g.scheme = c->scheme;
+  g.hi_bits = c->k_bits;
+  g.lo_bits = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->low_bits : c->k_bits;
+  g.hadamard = c->hadamard;
+  g.pre_rope = c->pre_rope_keys;
+  g.rope_theta = c->rope_theta;
+  g.gmax = groups_for(max_tokens);
+  g.hi_slots = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->int4_window / kGroup : g.gmax;
+  g.length = length;
+  g.Tq = quantized_prefix(c, length);
+  g.hi_start = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0)
+                   ? (g.Tq > c->int4_window ? g.Tq - c->int4_window : 0)
+                   : 0;
+  return g;
+}
+
+void plane_sizes(const kvq_config* c, int64_t batch, int64_t max_tokens, uint64_t* sz) {
+  for (int i = 0; i < KVQ_MAX_PLANES; ++i) sz[i] = 0;
+  const uint64_t pairs = (uint64_t)batch * c->num_kv_heads;
+  const uint64_t G = (uint64_t)groups_for(max_tokens);
+  if (c->scheme == KVQ_KIVI_ASYM) {
+    const uint64_t hs = c->int4_window >= 0 ? (uint64_t)(c->int4_window / kGroup) : G;
+    sz[KVQ_PLANE_K_HI] = pairs * hs * 512 * c->k_bits;
+    sz[KVQ_PLANE_V_HI] = pairs * hs * 512 * c->v_bits;
+    if (c->int4_window >= 0) {
+      sz[KVQ_PLANE_K_LO] = pairs * G * 512 * c->low_bits;
+      sz[KVQ_PLANE_V_LO] = pairs * G * 512 * c->low_bits;
+    }
+    sz[KVQ_PLANE_K_META] = pairs * G * 512;
+    sz[KVQ_PLANE_V_META] = pairs * G * 512;
+    sz[KVQ_PLANE_K_WIN] = pairs * kRing * kD * 2;
+    sz[KVQ_PLANE_V_WIN] = pairs * kRing * kD * 2;
+  } else {
+    sz[KVQ_PLANE_K_HI] = pairs * G * 2048;
+    sz[KVQ_PLANE_V_HI] = pairs * G * 2048;
+    sz[KVQ_PLANE_K_META] = pairs * G * kGroup * 2;
+    sz[KVQ_PLANE_V_META] = pairs * G * kGroup * 2;
+  }
+  if (c->pre_rope_keys) sz[KVQ_PLANE_ROPE] = G * kGroup * 64 * 2 * 4;
+}
+
+kvq_status validate_cache(const kvq_config* c, const kvq_cache* cache, Planes* planes) {
+  if (cache == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (cache->batch <= 0 || cache->batch > 65535 || cache->max_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (cache->length < 0 || cache->length > cache->max_tokens) return KVQ_ERR_INVALID_ARG;
+  uint64_t sz[KVQ_MAX_PLANES];
+  plane_sizes(c, cache->batch, cache->max_tokens, sz);
+  for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
+    planes->p[i] = static_cast<uint8_t*>(cache->planes[i]);
+    if (sz[i] > 0 && (cache->planes[i] == nullptr || !aligned(cache->planes[i])))
+      return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+struct DecodeSetup {
+  Geom g;
+  Planes p;
+  ChunkPlan cp;
+  float scale;
+};
+
+kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const void* q, void* out,
+                        void* workspace, uint64_t workspace_bytes, float sm_scale, DecodeSetup* st) {
+  kvq_status s = validate_config(cfg);
+  if (s != KVQ_OK) return s;
+  s = validate_cache(cfg, cache, &st->p);
+  if (s != KVQ_OK) return s;
+  if (q == nullptr || out == nullptr || !aligned(q) || !aligned(out)) return KVQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  st->g = make_geom(cfg, cache->batch, cache->max_tokens, cache->length);
+  st->cp = plan_chunks(st->g);
+  const uint64_t need = (uint64_t)st->g.B * st->g.Hq * st->cp.n * kPartial * sizeof(float);
+  if (need > 0 && (workspace == nullptr || !aligned(workspace))) return KVQ_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  st->scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)kD);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+// Split-K plan: quantized key groups are cut into chunks of gpc groups so that
+// a decode call launches a few thousand work-groups (256 CUs); the fp16
+// window, when present, is one more chunk.
+ChunkPlan plan_chunks(const Geom& g) {
+  ChunkPlan cp;
+  const int64_t Gq = (g.Tq + kGroup - 1) / kGroup;
+  const int64_t pairs = (int64_t)g.B * g.Hkv;
+  int64_t gpc = (Gq * pairs + 2047) / 2048;
+  if (gpc < 4) gpc = 4;
+  if (gpc > 64) gpc = 64;
+  cp.gpc = gpc;
+  cp.nq = Gq > 0 ? (Gq + gpc - 1) / gpc : 0;
+  const bool window = g.scheme == KVQ_KIVI_ASYM && g.length > g.Tq;
+  cp.n = cp.nq + (window ? 1 : 0);
+  return cp;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_strerror(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_layout(const kvq_config* cfg, int64_t batch, int64_t max_tokens, kvq_layout_t* out) {
+  kvq_status s = validate_config(cfg);
+  if (s != KVQ_OK) return s;
+  if (out == nullptr || batch <= 0 || batch > 65535 || max_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  plane_sizes(cfg, batch, max_tokens, out->plane_bytes);
+  out->alignment = kAlign;
+  out->groups = groups_for(max_tokens);
+  out->hi_slots = (cfg->scheme == KVQ_KIVI_ASYM && cfg->int4_window >= 0) ? cfg->int4_window / kGroup
+                                                                           : out->groups;
+  return KVQ_OK;
+}
+
+kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t length, uint64_t* bytes) {
+  kvq_status s = validate_config(cfg);
+  if (s != KVQ_OK) return s;
+  if (bytes == nullptr || batch <= 0 || batch > 65535 || length < 0) return KVQ_ERR_INVALID_ARG;
+  const Geom g = make_geom(cfg, batch, length, length);
+  const ChunkPlan cp = plan_chunks(g);
+  *bytes = (uint64_t)g.B * g.Hq * cp.n * kPartial * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
+                      int64_t n_new, void* stream) {
+  kvq_status s = validate_config(cfg);
+  if (s != KVQ_OK) return s;
+  Planes p;
+  s = validate_cache(cfg, cache, &p);
+  if (s != KVQ_OK) return s;
+  if (n_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (n_new == 0) return KVQ_OK;
+  if (k_new == nullptr || v_new == nullptr || !aligned(k_new) || !aligned(v_new))
+    return KVQ_ERR_INVALID_ARG;
+  const int64_t T0 = cache->length, T1 = T0 + n_new;
+  if (T1 > cache->max_tokens) return KVQ_ERR_CAPACITY;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Geom g = make_geom(cfg, cache->batch, cache->max_tokens, T0);
+  const __half* kn = static_cast<const __half*>(k_new);
+  const __half* vn = static_cast<const __half*>(v_new);
+  hipError_t e = hipSuccess;
+  if (cfg->pre_rope_keys) {
+    e = launch_rope_table(g, p, T0, T1, st);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  if (cfg->scheme == KVQ_BLOCK128_SYM) {
+    e = launch_block128_append(g, p, kn, vn, n_new, T0, st);
+  } else {
+    // Tier bookkeeping ([troisinh] "Ý tưởng cốt lõi", "Mixed Precision"): the
+    // quantized prefix grows by whole 32-token groups; groups older than the
+    // high-bit window drop to low_bits.
+    const int64_t Tq0 = quantized_prefix(cfg, T0), Tq1 = quantized_prefix(cfg, T1);
+    int64_t h1 = 0;
+    if (cfg->int4_window >= 0) {
+      const int64_t h0 = Tq0 > cfg->int4_window ? Tq0 - cfg->int4_window : 0;
+      h1 = Tq1 > cfg->int4_window ? Tq1 - cfg->int4_window : 0;
+      const int64_t d1 = (Tq0 < h1 ? Tq0 : h1);
+      e = launch_kivi_demote(g, p, h0 / kGroup, d1 / kGroup, st);
+      if (e != hipSuccess) return from_hip(e);
+    }
+    e = launch_kivi_quantize(g, p, kn, vn, n_new, T0, Tq0 / kGroup, Tq1 / kGroup, h1, st);
+    if (e != hipSuccess) return from_hip(e);
+    const int64_t w0 = T0 > Tq1 ? T0 : Tq1;
+    e = launch_window_write(g, p, kn, vn, n_new, T0, w0, T1, st);
+  }
+  if (e != hipSuccess) return from_hip(e);
+  cache->length = T1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                               int64_t q_pos, float sm_scale, void* out, void* workspace,
+                               uint64_t workspace_bytes, void* stream) {
+  DecodeSetup st;
+  kvq_status s = decode_setup(cfg, cache, q, out, workspace, workspace_bytes, sm_scale, &st);
+  if (s != KVQ_OK) return s;
+  return from_hip(launch_decode_partials(st.g, st.p, st.cp, static_cast<const __half*>(q), q_pos,
+                                         st.scale, static_cast<float*>(workspace),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_merge(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                            int64_t q_pos, float sm_scale, void* out, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  DecodeSetup st;
+  kvq_status s = decode_setup(cfg, cache, q, out, workspace, workspace_bytes, sm_scale, &st);
+  if (s != KVQ_OK) return s;
+  (void)q_pos;
+  return from_hip(launch_decode_merge(st.g, st.cp, static_cast<float*>(workspace),
+                                      static_cast<float*>(out), static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                           int64_t q_pos, float sm_scale, void* out, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
+  kvq_status s = kvq_decode_partials(cfg, cache, q, q_pos, sm_scale, out, workspace, workspace_bytes,
+                                     stream);
+  if (s != KVQ_OK) return s;
+  return kvq_decode_merge(cfg, cache, q, q_pos, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_dequant(const kvq_config* cfg, const kvq_cache* cache, int64_t t0, int64_t t1,
+                       void* k_out, void* v_out, void* stream) {
+  kvq_status s = validate_config(cfg);
+  if (s != KVQ_OK) return s;
+  Planes p;
+  s = validate_cache(cfg, cache, &p);
+  if (s != KVQ_OK) return s;
+  if (t0 < 0 || t1 < t0 || t1 > cache->length) return KVQ_ERR_INVALID_ARG;
+  if (t1 == t0) return KVQ_OK;
+  if (k_out == nullptr || v_out == nullptr || !aligned(k_out) || !aligned(v_out))
+    return KVQ_ERR_INVALID_ARG;
+  const Geom g = make_geom(cfg, cache->batch, cache->max_tokens, cache->length);
+  return from_hip(launch_dequant(g, p, t0, t1, static_cast<float*>(k_out), static_cast<float*>(v_out),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the C ABI (kvq.cpp) and the HIP kernels.
+// Not part of the public interface; see include/kvq.h for the contract.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kD = 128;        // head dim
+constexpr int kGroup = 32;     // tokens per key group / tile
+constexpr int kRing = 160;     // fp16 window ring rows (>= 128 + 31)
+constexpr int kWindow = 128;   // fp16 window length
+
+// Everything a kernel needs to address one cache.  Plain values, passed by
+// value to every launch.
+struct Geom {
+  int B, Hq, Hkv, G;           // G = Hq / Hkv
+  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM
+  int hi_bits, lo_bits;
+  int hadamard, pre_rope;
+  float rope_theta;
+  int64_t gmax;                // groups per (sequence, head)
+  int64_t hi_slots;            // K_HI / V_HI tiles per (sequence, head)
+  int64_t length;              // cached tokens
+  int64_t Tq;                  // quantized tokens [0, Tq)
+  int64_t hi_start;            // first high-bit token (KIVI)
+};
+
+struct Planes {
+  uint8_t* p[KVQ_NUM_PLANES];
+};
+
+// Split-K plan of one decode call.
+struct ChunkPlan {
+  int64_t gpc;        // key groups per quantized chunk
+  int64_t nq;         // quantized chunks
+  int64_t n;          // nq + (1 if a fp16 window chunk exists)
+};
+
+ChunkPlan plan_chunks(const Geom& g);
+
+// Launchers (kernels in append.hip, decode.hip, dequant.hip).  Each returns
+// hipGetLastError() after its launches.
+hipError_t launch_rope_table(const Geom& g, const Planes& p, int64_t t0, int64_t t1,
+                             hipStream_t s);
+hipError_t launch_kivi_demote(const Geom& g, const Planes& p, int64_t g0, int64_t g1,
+                              hipStream_t s);
+hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_new,
+                                const __half* v_new, int64_t n_new, int64_t T0, int64_t g0,
+                                int64_t g1, int64_t hi_start_new, hipStream_t s);
+hipError_t launch_window_write(const Geom& g, const Planes& p, const __half* k_new,
+                               const __half* v_new, int64_t n_new, int64_t T0, int64_t w0,
+                               int64_t w1, hipStream_t s);
+hipError_t launch_block128_append(const Geom& g, const Planes& p, const __half* k_new,
+                                  const __half* v_new, int64_t n_new, int64_t T0,
+                                  hipStream_t s);
+hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPlan& cp,
+                                  const __half* q, int64_t q_pos, float sm_scale, float* ws,
+                                  hipStream_t s);
+hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
+                               hipStream_t s);
+hipError_t launch_dequant(const Geom& g, const Planes& p, int64_t t0, int64_t t1, float* k_out,
+                          float* v_out, hipStream_t s);
+
+// Partial record per (sequence, q head, chunk): m, l, o[128] (fp32, log2 domain).
+constexpr int kPartial = 2 + kD;
+
+}  // namespace kvq

@@ -1,0 +1,120 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Small shapes that span several tiles and chunks plus ragged tails; every
+scheme and option; streaming appends with demotion; edge cases (empty cache,
+all-window caches, one token)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (build_pair, compare_planes, compare_dequant, compare_rope_table,
+                         check_decode, say)
+from quantized_decode_attention_02_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {
+    "int4": dict(),
+    "int2": dict(k_bits=2, v_bits=2),
+    "int4-hadamard": dict(hadamard=True),
+    "int4-prerope": dict(pre_rope=True, rope_theta=500000.0),
+    "mixed-hadamard": dict(hadamard=True, hi_window=96),
+    "mixed": dict(hi_window=64),
+    "block128": None,
+    "block128-plain": dict(hadamard=False),
+}
+
+
+def make_w(wid, variant, T, batch=2, hq=8, hkv=2, dist="normal", outliers=None):
+    kw = VARIANTS[variant]
+    if variant.startswith("block128"):
+        cfg = wl._block128(**(kw or {}))
+    else:
+        cfg = wl._kivi(**kw)
+    return wl.custom(wid, batch, hq, hkv, T, cfg, dist=dist, outliers=outliers)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("T", [1, 31, 33, 128, 129, 159, 160, 161, 300, 4096 + 17])
+def test_one_shot(variant, T):
+    w = make_w(1000 + T, variant, T, outliers=("channels", 3, 20.0))
+    say(f"one-shot {variant} T={T}")
+    g, o, s, h = build_pair(w, [T], max_tokens=T + 40)
+    compare_planes(g, o, s, h)
+    compare_rope_table(g, o)
+    compare_dequant(g, o, s, h)
+    check_decode(g, o, w, s, h)
+
+
+STREAMS = {
+    "decode-steps": [200] + [1] * 70,
+    "ragged": [5, 27, 1, 64, 100, 3, 31, 32, 33, 250, 7],
+    "big-then-steps": [1500] + [1] * 40 + [77],
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("stream", list(STREAMS))
+def test_streaming(variant, stream):
+    chunks = STREAMS[stream]
+    w = make_w(2000 + len(chunks), variant, sum(chunks), hq=4, dist="student3")
+    say(f"streaming {variant} {stream}")
+    g, o, s, h = build_pair(w, chunks, max_tokens=sum(chunks) + 5)
+    compare_planes(g, o, s, h)
+    compare_dequant(g, o, s, h)
+    check_decode(g, o, w, s, h)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 1), (8, 8)])
+def test_gqa_shapes(hq, hkv):
+    w = make_w(3000 + hq * 10 + hkv, "int4", 777, batch=3, hq=hq, hkv=hkv)
+    g, o, s, h = build_pair(w, [777])
+    compare_planes(g, o, s, h)
+    check_decode(g, o, w, s, h)
+
+
+def test_empty_cache_and_query_position():
+    w = make_w(3100, "int4-prerope", 500)
+    from quantized_decode_attention_02_amd import kvq
+    g0 = kvq.KVCache(wl.library_config(w), w["batch"], 64)
+    out = g0.decode(torch.from_numpy(wl.queries(w)).cuda())
+    assert torch.count_nonzero(out).item() == 0
+    g, o, s, h = build_pair(w, [500])
+    check_decode(g, o, w, s, h, q_pos=480)
+    check_decode(g, o, w, s, h, sm_scale=0.03)
+
+
+def test_partial_dequant_ranges():
+    w = make_w(3200, "mixed-hadamard", 1000)
+    g, o, s, h = build_pair(w, [600, 400])
+    for t0, t1 in [(0, 1), (31, 33), (500, 1000), (871, 872), (999, 1000)]:
+        compare_dequant(g, o, s, h, t0, t1)
+
+
+def test_length_rollback_reappend_is_idempotent():
+    # decode-step pattern: cache at T-1, append one token, decode; roll back to
+    # T-1 and append the same token again
+    w = make_w(3300, "int4", 4096)
+    g, o, s, h = build_pair(w, [4095, 1])
+    K1, V1 = wl.kv_tokens(w, 4095, 4096)
+    before = [p.clone() if p is not None else None for p in g.planes]
+    for _ in range(3):
+        g.length = 4095
+        g.append(torch.from_numpy(K1).cuda(), torch.from_numpy(V1).cuda())
+    torch.cuda.synchronize()
+    for a, b in zip(before, g.planes):
+        if a is not None:
+            assert torch.equal(a, b)
+    check_decode(g, o, w, s, h)
+
+
+def test_capacity_error_leaves_cache_untouched():
+    from quantized_decode_attention_02_amd import kvq
+    w = make_w(3400, "int4", 100)
+    g, o, s, h = build_pair(w, [100], max_tokens=120)
+    K, V = wl.kv_tokens(w, 100, 121)
+    with pytest.raises(kvq.KvqError) as ei:
+        g.append(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda())
+    assert ei.value.status == -3 and g.length == 100
+    compare_planes(g, o, s, h)
