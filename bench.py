@@ -1,0 +1,249 @@
+"""Decode-step benchmark: effective KV GB/s of decode attention over the INT4 cache.
+
+One step is one pass of the whole hot path on every sequence of the batch:
+append one fp16 token per sequence (its key/value go to the fp16 window, and
+the 32-token group leaving the window is quantized: per-channel keys,
+per-token values, packed INT4), then single-query decode attention over the
+whole packed cache (split-K kernel + merge).  The cache starts at T - 1 tokens
+and every step rolls the length back to T - 1 before appending the same token,
+so every step does identical work and decode always attends T tokens.
+
+Reported (one JSON line on stdout):
+  value        algorithmic decode bytes (codes + fp16 scales/zeros + fp16
+               window) / step time, GB/s; inputs resident in HBM
+  roofline     the split-K decode kernel alone: algorithmic bytes per launch /
+               its average duration (HIP events on the launch stream) against
+               the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle (dequantize + fp64 attention) on a bounded
+               sample of the same workload's (sequence, kv head) pairs, one
+               process per core
+
+    python bench.py [--steps K] [--warmup W] [--workload ID]
+"""
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from quantized_decode_attention_02_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn effective KV GB/s (% of HBM peak) + attended tokens/s, INT4, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def tier_map(cfg, T):
+    if cfg["scheme"] == "block128":
+        return T, 0
+    Tq = max(0, ((T - 128) // 32) * 32)
+    hi_start = 0 if cfg["hi_window"] < 0 else max(0, Tq - cfg["hi_window"])
+    return Tq, hi_start
+
+
+def decode_bytes(w, T):
+    """Algorithmic bytes one decode call must read: codes, fp16 scales and
+    zeros, the fp16 window; per (sequence, kv head), times all pairs."""
+    cfg = w["cfg"]
+    pairs = w["batch"] * w["num_kv_heads"]
+    Tq, hi_start = tier_map(cfg, T)
+    if cfg["scheme"] == "block128":
+        per_pair = T * 2 * (64 + 2)
+    else:
+        hi = Tq - hi_start
+        lo = hi_start
+        per_pair = hi * 2 * 128 * cfg["k_bits"] // 8 + lo * 2 * 128 * cfg["low_bits"] // 8
+        per_pair += (Tq // 32) * 2 * 512          # key (s, z) per channel + value (s, z) per token
+        per_pair += (T - Tq) * 2 * 128 * 2         # fp16 window, keys and values
+    return pairs * per_pair
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, one process per core.
+
+def _cpu_worker(args):
+    wid, pairs, T, barrier, q_out = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle.cache import OracleCache
+    w = wl.workload(wid)
+    G = w["num_q_heads"] // w["num_kv_heads"]
+    cfg = dict(wl.library_config(w), num_q_heads=G, num_kv_heads=1)
+    built = []
+    for b, h in pairs:
+        K, V = wl.kv_tokens(w, 0, T, seqs=[b], heads=[h], threads=1)
+        oc = OracleCache(cfg, 1, T)
+        t0 = time.perf_counter()
+        oc.append(K, V)
+        t_app = time.perf_counter() - t0
+        q = wl.queries(w, seqs=[b])[:, h * G:(h + 1) * G]
+        built.append((oc, q, t_app))
+    barrier.wait()
+    t0 = time.time()
+    for oc, q, _ in built:
+        oc.decode(q)
+    t1 = time.time()
+    q_out.put((t0, t1, sum(x[2] for x in built), len(built)))
+
+
+def cpu_baseline(w, T, n_pairs, workers):
+    pairs_all = [(b, h) for b in range(w["batch"]) for h in range(w["num_kv_heads"])]
+    rng = np.random.default_rng(12345)
+    pick = [pairs_all[i] for i in sorted(rng.choice(len(pairs_all), min(n_pairs, len(pairs_all)),
+                                                    replace=False))]
+    workers = max(1, min(workers, len(pick)))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(workers + 1)
+    q_out = ctx.Queue()
+    chunks = [pick[i::workers] for i in range(workers)]
+    procs = [ctx.Process(target=_cpu_worker, args=((w["id"], c, T, barrier, q_out),)) for c in chunks]
+    for p in procs:
+        p.start()
+    barrier.wait()
+    res = [q_out.get() for _ in procs]
+    for p in procs:
+        p.join()
+    start = min(r[0] for r in res)
+    end = max(r[1] for r in res)
+    per_pair_bytes = decode_bytes(dict(w, batch=1, num_kv_heads=1), T)
+    nbytes = per_pair_bytes * len(pick)
+    secs = end - start
+    return {
+        "value": nbytes / secs / 1e9,
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{len(pick)} of {len(pairs_all)} (sequence, kv head) pairs at T={T}: "
+                   f"dequantize + fp64 attention over {nbytes / 1e9:.3f} GB of the cache in "
+                   f"{secs:.2f} s wall on {workers} processes; quantize-on-append of the same "
+                   f"pairs took {sum(r[2] for r in res):.2f} CPU-s (untimed here)"),
+        "attended_tokens_per_s": len(pick) * T / secs,
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    w = wl.workload(args.workload)
+    T = w["tokens"]
+    cfg = wl.library_config(w)
+    if w["cfg"]["scheme"] == "kivi" and w["cfg"]["hi_window"] >= 0:
+        raise SystemExit("this workload's decode step demotes a group; bench the INT4 workloads")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        ncores = len(os.sched_getaffinity(0))
+        log(f"cpu baseline: {args.cpu_pairs} pairs on up to {min(16, ncores)} processes")
+        cpu = cpu_baseline(w, T, args.cpu_pairs, min(16, ncores))
+        log(f"cpu baseline {cpu['value']:.3f} GB/s")
+
+    import torch
+    from quantized_decode_attention_02_amd import kvq
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"workload {w['name']}: generating {T} tokens x {w['batch']} seqs x {w['num_kv_heads']} heads")
+    K0, V0 = wl.kv_tokens(w, 0, T - 1)
+    K1, V1 = wl.kv_tokens(w, T - 1, T)
+    q = torch.from_numpy(wl.queries(w)).to(dev)
+    log("uploading")
+    k0, v0 = torch.from_numpy(K0).to(dev), torch.from_numpy(V0).to(dev)
+    del K0, V0
+    k1, v1 = torch.from_numpy(K1).to(dev), torch.from_numpy(V1).to(dev)
+    cache = kvq.KVCache(cfg, w["batch"], T)
+    cache.append(k0, v0)
+    torch.cuda.synchronize()
+    del k0, v0
+    log(f"cache built: {cache.length} tokens")
+
+    cache.length = T - 1
+    cache.append(k1, v1)
+    ws = cache.new_workspace()
+    out = torch.empty((w["batch"], w["num_q_heads"], 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        cache.length = T - 1
+        cache.append(k1, v1)
+        if ev is not None:
+            ev[0].record(stream)
+        cache.decode_partials(q, ws, out)
+        if ev is not None:
+            ev[1].record(stream)
+        cache.decode_merge(q, ws, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = [a.elapsed_time(b) for a, b in events]
+    k_avg = float(np.mean(k_ms))
+
+    nbytes = decode_bytes(w, T)
+    value = nbytes / (ms_step / 1e3) / 1e9
+    achieved = nbytes / (k_avg / 1e3) / 1e9
+    attended = w["batch"] * T / (ms_step / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "batch": w["batch"], "q_heads": w["num_q_heads"],
+                   "kv_heads": w["num_kv_heads"], "head_dim": 128, "tokens": T,
+                   "cache": "KIVI INT4: K per-channel g32, V per-token g32, fp16 scale+zero, "
+                            "128-token fp16 window",
+                   "step": "append 1 token/seq + split-K decode + merge",
+                   "decode_bytes": nbytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "attended_tokens_per_s": round(attended, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_partials", "kernel_ms_avg": round(k_avg, 5),
+                     "kernel_ms_p10_p90": [round(float(np.percentile(k_ms, 10)), 5),
+                                           round(float(np.percentile(k_ms, 90)), 5)]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
