@@ -67,10 +67,11 @@ enum { KVQ_KIVI_ASYM = 0, KVQ_BLOCK128_SYM = 1 };
  *               keys token-major with 16-byte chunks interleaved across the
  *               32 tokens, values channel-major.
  *   K_LO/V_LO   low-bit tiles (KIVI with int4_window >= 0), one per group.
- *   K_META      KIVI: per group fp16 scale[128] then zero[128].
- *               BLOCK128: one fp16 scale per token.
- *   V_META      KIVI: per group fp16 scale[4][32] then zero[4][32]
- *               ([dim group][token]).  BLOCK128: one fp16 scale per token.
+ *   K_META      KIVI: per group 128 fp16 (scale, zero) pairs, one per
+ *               channel.  BLOCK128: one fp16 scale per token.
+ *   V_META      KIVI: per group, token-major: for each of the 32 tokens the
+ *               fp16 (scale, zero) of its four 32-dim slices.  BLOCK128: one
+ *               fp16 scale per token.
  *   K_WIN/V_WIN KIVI: fp16 ring of 160 rows x 128 per (sequence, kv head);
  *               token t lives in row t mod 160.
  *   ROPE        pre-RoPE keys only: fp32 (cos, sin) of t * theta_j, row t,

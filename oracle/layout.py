@@ -31,10 +31,10 @@ Planes (all [batch][kv_head][...], row-major, little-endian fp16/fp32):
   1 V_HI   same for values.
   2 K_LO   KIVI with a high-bit window only: low-bit key tiles, slot g = group g.
   3 V_LO   same for values.
-  4 K_META KIVI: 512 B per group: scales s[128] (channel order) then zeros z[128].
-           BLOCK128: one fp16 scale per token.
-  5 V_META KIVI: 512 B per group: s[4][32] ([dim group][token]) then z[4][32].
-           BLOCK128: one fp16 scale per token.
+  4 K_META KIVI: 512 B per group: (s, z) fp16 pairs per channel, channel d at
+           bytes 4d..4d+3.  BLOCK128: one fp16 scale per token.
+  5 V_META KIVI: 512 B per group: token-major, token t and 32-dim group g at
+           bytes 16t + 4g: (s, z).  BLOCK128: one fp16 scale per token.
   6 K_WIN  KIVI: fp16 window ring of 160 rows x 128; token t in row t mod 160.
   7 V_WIN  same for values.
   8 ROPE   pre-RoPE keys only: float32 [32 * ceil(max_tokens/32)][64][2],
@@ -117,20 +117,20 @@ def v_tile_decode(tile, bits):
 
 
 def k_meta(s_h, z_h):
-    """512-byte key metadata of one group: s[128] then z[128] (fp16 LE)."""
+    """512-byte key metadata of one group: (s, z) per channel (fp16 LE)."""
     s = np.asarray(s_h, dtype="<f2")
     z = np.asarray(z_h, dtype="<f2")
-    both = np.concatenate([s, z], axis=-1)
+    both = np.ascontiguousarray(np.stack([s, z], axis=-1))          # [..., 128, 2]
     return both.view(np.uint8).reshape(s.shape[:-1] + (512,))
 
 
 def v_meta(s_h, z_h):
-    """512-byte value metadata of one group from s_h, z_h [..., 32 tokens, 4]."""
-    s = np.swapaxes(np.asarray(s_h, dtype="<f2"), -1, -2)   # [..., 4, 32]
-    z = np.swapaxes(np.asarray(z_h, dtype="<f2"), -1, -2)
-    both = np.concatenate([s.reshape(s.shape[:-2] + (128,)),
-                           z.reshape(z.shape[:-2] + (128,))], axis=-1)
-    return np.ascontiguousarray(both).view(np.uint8).reshape(both.shape[:-1] + (512,))
+    """512-byte value metadata of one group from s_h, z_h [..., 32 tokens, 4]:
+    token-major, (s, z) per 32-dim group."""
+    s = np.asarray(s_h, dtype="<f2")
+    z = np.asarray(z_h, dtype="<f2")
+    both = np.ascontiguousarray(np.stack([s, z], axis=-1))          # [..., 32, 4, 2]
+    return both.view(np.uint8).reshape(s.shape[:-2] + (512,))
 
 
 def block66(nibbles, s_h):

@@ -50,7 +50,8 @@ __device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp,
 
 // One 32-token group in LDS: xk[32][128], xv[32][128] float (the values the
 // quantizer sees: fp16 inputs, or their rotation) -> codes ck, cv and the
-// metadata records (key: s[128], z[128]; value: s[4][32], z[4][32]).
+// metadata records (key: (s, z) per channel; value: (s, z) per token and
+// 32-dim slice, token-major).
 // Keys use one range per channel over the 32 tokens, values one range per
 // token over each 32-dim slice ([trefon] "Dlaczego cache trudniej
 // skwantyzować niż wagi").  Needs 256 threads.
@@ -66,8 +67,8 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
     }
     const GroupParams gp = group_params(mn, mx, bits);
     for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code(xk[t][c], gp, bits);
-    kmeta[c] = gp.s_bits;
-    kmeta[kD + c] = gp.z_bits;
+    kmeta[2 * c] = gp.s_bits;
+    kmeta[2 * c + 1] = gp.z_bits;
   } else {
     const int u = tid - kD;
     const int t = u >> 2, dg = u & 3;
@@ -79,8 +80,8 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
     }
     const GroupParams gp = group_params(mn, mx, bits);
     for (int i = 0; i < 32; ++i) cv[t][dg * 32 + i] = quantize_code(row[i], gp, bits);
-    vmeta[dg * 32 + t] = gp.s_bits;
-    vmeta[kD + dg * 32 + t] = gp.z_bits;
+    vmeta[2 * (t * 4 + dg)] = gp.s_bits;
+    vmeta[2 * (t * 4 + dg) + 1] = gp.z_bits;
   }
 }
 
@@ -233,10 +234,10 @@ __global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int6
     const int t = e >> 7, d = e & 127;
     const int kcode = (kt[ktile_offset(t, d / per)] >> (hb * (d % per))) & mask;
     const int vcode = (vt[d * 4 * hb + t / per] >> (hb * (t % per))) & mask;
-    const float ks = half_bits_to_float(km[d]), kz = half_bits_to_float(km[kD + d]);
+    const float ks = half_bits_to_float(km[2 * d]), kz = half_bits_to_float(km[2 * d + 1]);
     const int dg = d >> 5;
-    const float vs = half_bits_to_float(vm[dg * 32 + t]);
-    const float vz = half_bits_to_float(vm[kD + dg * 32 + t]);
+    const float vs = half_bits_to_float(vm[2 * (t * 4 + dg)]);
+    const float vz = half_bits_to_float(vm[2 * (t * 4 + dg) + 1]);
     xs[0][t][d] = (float)kcode * ks + kz;
     xs[1][t][d] = (float)vcode * vs + vz;
   }

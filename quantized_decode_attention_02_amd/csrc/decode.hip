@@ -35,6 +35,7 @@ struct DecodeArgs {
   int64_t q_pos;
   float scale_log2;  // sm_scale * log2(e)
   int64_t gpc, nq, n;
+  int64_t c0;  // chunk index of blockIdx.x == 0
 };
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -63,7 +64,8 @@ __device__ __forceinline__ void channels_of(int sl, int* ch) {
 template <int G, bool ROPE>
 __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
   const Geom& g = a.g;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t c = a.c0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t pair = pair_index(g, b, h);
   const bool window_chunk = c >= a.nq;
 
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int d = ch[i];
           const int code = (tile[ktile_offset(tok, d / per)] >> (bits * (d % per))) & mask;
-          kx[i] = (float)code * half_bits_to_float(meta[d]) + half_bits_to_float(meta[kD + d]);
+          kx[i] = (float)code * half_bits_to_float(meta[2 * d]) + half_bits_to_float(meta[2 * d + 1]);
         }
       }
       if (ROPE) {
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
       for (int k = 0; k < 16; ++k) {
         const int j = 16 * vhalf + k;
         const int code = (tile[vd * rb + j / per] >> (bits * (j % per))) & mask;
-        vx[k] = (float)code * half_bits_to_float(meta[dg * 32 + j]) +
-                half_bits_to_float(meta[kD + dg * 32 + j]);
+        vx[k] = (float)code * half_bits_to_float(meta[2 * (j * 4 + dg)]) +
+                half_bits_to_float(meta[2 * (j * 4 + dg) + 1]);
       }
     }
     for (int i = 0; i < G; ++i) {
@@ -288,7 +290,17 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
   a.gpc = cp.gpc;
   a.nq = cp.nq;
   a.n = cp.n;
-  const dim3 grid((unsigned)cp.n, g.Hkv, g.B), block(256);
+  a.c0 = 0;
+  unsigned nblocks = (unsigned)cp.n;
+  if (cp.mode == 1) {
+    // quantized tokens on the MFMA kernel; the fp16 window here
+    const hipError_t e = launch_decode_mfma(g, p, cp, q, sm_scale, ws, s);
+    if (e != hipSuccess) return e;
+    if (cp.n == cp.nq) return hipGetLastError();
+    a.c0 = cp.nq;
+    nblocks = 1;
+  }
+  const dim3 grid(nblocks, g.Hkv, g.B), block(256);
 #define KVQ_LAUNCH(GG, RR) hipLaunchKernelGGL((decode_partials_v0<GG, RR>), grid, block, 0, s, a)
   if (g.pre_rope) {
     if (g.G == 1) KVQ_LAUNCH(1, true);

@@ -50,8 +50,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       const uint16_t* km = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META] + (pair * g.gmax + grp) * 512);
       const uint16_t* vm = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META] + (pair * g.gmax + grp) * 512);
       const int dg = d >> 5;
-      kv = (float)kc * half_bits_to_float(km[d]) + half_bits_to_float(km[kD + d]);
-      vv = (float)vc * half_bits_to_float(vm[dg * 32 + row]) + half_bits_to_float(vm[kD + dg * 32 + row]);
+      kv = (float)kc * half_bits_to_float(km[2 * d]) + half_bits_to_float(km[2 * d + 1]);
+      vv = (float)vc * half_bits_to_float(vm[2 * (row * 4 + dg)]) +
+           half_bits_to_float(vm[2 * (row * 4 + dg) + 1]);
     } else {
       const __half* kr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
       const __half* vr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + (pair * kRing + t % kRing) * kD;

@@ -147,19 +147,47 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 
 }  // namespace
 
-// Split-K plan: quantized key groups are cut into chunks of gpc groups so that
-// a decode call launches a few thousand work-groups (256 CUs); the fp16
-// window, when present, is one more chunk.
+// Split-K plan.  MFMA path: the quantized tokens form up to two ranges of one
+// code width each (low-bit tier, high-bit tier); a wave streams nt tiles of
+// 64 tokens and a work-group of 4 waves covers 4 * nt tiles, with nt chosen
+// so that a call launches on the order of 16K waves.  Pre-RoPE path: chunks
+// of gpc key groups, a few thousand work-groups.  The fp16 window is one
+// more slot either way.
 ChunkPlan plan_chunks(const Geom& g) {
   ChunkPlan cp;
-  const int64_t Gq = (g.Tq + kGroup - 1) / kGroup;
+  cp.nr = 0;
+  cp.gpc = 0;
   const int64_t pairs = (int64_t)g.B * g.Hkv;
-  int64_t gpc = (Gq * pairs + 2047) / 2048;
-  if (gpc < 4) gpc = 4;
-  if (gpc > 64) gpc = 64;
-  cp.gpc = gpc;
-  cp.nq = Gq > 0 ? (Gq + gpc - 1) / gpc : 0;
   const bool window = g.scheme == KVQ_KIVI_ASYM && g.length > g.Tq;
+  if (g.pre_rope) {
+    cp.mode = 0;
+    const int64_t Gq = (g.Tq + kGroup - 1) / kGroup;
+    int64_t gpc = (Gq * pairs + 2047) / 2048;
+    if (gpc < 4) gpc = 4;
+    if (gpc > 64) gpc = 64;
+    cp.gpc = gpc;
+    cp.nq = Gq > 0 ? (Gq + gpc - 1) / gpc : 0;
+  } else {
+    cp.mode = 1;
+    int64_t lo_end = g.scheme == KVQ_KIVI_ASYM ? g.hi_start : 0;
+    if (lo_end > 0) cp.r[cp.nr++] = RangePlan{0, lo_end, g.lo_bits, 0, 1, 0, 0};
+    if (g.Tq > lo_end) cp.r[cp.nr++] = RangePlan{lo_end, g.Tq, g.hi_bits, 1, 1, 0, 0};
+    int64_t tiles = 0;
+    for (int i = 0; i < cp.nr; ++i) tiles += pairs * ((cp.r[i].t_hi - cp.r[i].t_lo + 63) / 64);
+    int64_t nt = (tiles + 16383) / 16384;
+    if (nt < 1) nt = 1;
+    if (nt > 16) nt = 16;
+    int64_t slot = 0;
+    for (int i = 0; i < cp.nr; ++i) {
+      RangePlan& r = cp.r[i];
+      const int64_t t = (r.t_hi - r.t_lo + 63) / 64;
+      r.nt = (int)nt;
+      r.chunks = (t + 4 * nt - 1) / (4 * nt);
+      r.slot_base = slot;
+      slot += r.chunks * 4;
+    }
+    cp.nq = slot;
+  }
   cp.n = cp.nq + (window ? 1 : 0);
   return cp;
 }

@@ -34,10 +34,26 @@ struct Planes {
   uint8_t* p[KVQ_NUM_PLANES];
 };
 
-// Split-K plan of one decode call.
+// One token range of a decode call with a single code width and tier.
+struct RangePlan {
+  int64_t t_lo, t_hi;  // tokens [t_lo, t_hi), t_lo a multiple of 32
+  int bits;            // code bits
+  int hi_tier;         // 1: high-bit planes (ring), 0: low-bit planes
+  int nt;              // 64-token tiles per wave
+  int64_t chunks;      // work-groups along the range (4 waves each)
+  int64_t slot_base;   // first partial slot
+};
+
+// Split-K plan of one decode call.  Quantized tokens go to the MFMA kernel
+// (mode 1) as up to two tier-pure ranges, each wave writing one partial
+// slot; pre-RoPE caches use the VALU kernel (mode 0) with chunks of gpc key
+// groups.  The fp16 window, when present, is the last slot (VALU kernel).
 struct ChunkPlan {
-  int64_t gpc;        // key groups per quantized chunk
-  int64_t nq;         // quantized chunks
+  int mode;
+  int64_t gpc;        // mode 0: key groups per chunk
+  RangePlan r[2];
+  int nr;
+  int64_t nq;         // partial slots of quantized tokens
   int64_t n;          // nq + (1 if a fp16 window chunk exists)
 };
 
@@ -61,6 +77,8 @@ hipError_t launch_block128_append(const Geom& g, const Planes& p, const __half* 
 hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPlan& cp,
                                   const __half* q, int64_t q_pos, float sm_scale, float* ws,
                                   hipStream_t s);
+hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
+                              float sm_scale, float* ws, hipStream_t s);
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
                                hipStream_t s);
 hipError_t launch_dequant(const Geom& g, const Planes& p, int64_t t0, int64_t t1, float* k_out,

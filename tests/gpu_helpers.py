@@ -102,5 +102,6 @@ def check_decode(g, o, w, seqs, heads, q_pos=None, sm_scale=0.0):
     err = np.abs(got.astype(np.float64) - ref)
     lim = ATOL + RTOL * np.abs(ref)
     worst = float(np.max(err / lim)) if err.size else 0.0
+    say(f"  decode: worst {worst:.3f} of tolerance, max abs err {err.max():.2e}")
     assert np.all(err <= lim), f"decode off by {worst:.2f}x the tolerance; max abs {err.max():.3e}"
     return worst, float(err.max()) if err.size else 0.0

@@ -81,8 +81,13 @@ def test_meta_images():
     z = rng.standard_normal(128).astype(np.float16)
     m = layout.k_meta(s, z)
     assert m.shape == (512,)
-    assert np.array_equal(m[:256].view("<f2"), s) and np.array_equal(m[256:].view("<f2"), z)
+    mh = m.view("<f2")
+    assert np.array_equal(mh[0::2], s) and np.array_equal(mh[1::2], z)
+    assert m[4 * 9:4 * 9 + 2].view("<f2")[0] == s[9]
     sv = rng.standard_normal((32, 4)).astype(np.float16)
     zv = rng.standard_normal((32, 4)).astype(np.float16)
-    mv = layout.v_meta(sv, zv).view("<f2")
-    assert mv[2 * 32 + 7] == sv[7, 2] and mv[128 + 3 * 32 + 31] == zv[31, 3]
+    mv = layout.v_meta(sv, zv)
+    assert mv.shape == (512,)
+    # token 7, dim group 2 at bytes 16*7 + 4*2: (s, z)
+    assert mv[16 * 7 + 8:16 * 7 + 10].view("<f2")[0] == sv[7, 2]
+    assert mv[16 * 31 + 14:16 * 31 + 16].view("<f2")[0] == zv[31, 3]
