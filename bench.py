@@ -140,7 +140,19 @@ def main():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--cpu-pairs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for "
+                         "hardware byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

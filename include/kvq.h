@@ -72,8 +72,10 @@ enum { KVQ_KIVI_ASYM = 0, KVQ_BLOCK128_SYM = 1 };
  *   V_META      KIVI: per group, token-major: for each of the 32 tokens the
  *               fp16 (scale, zero) of its four 32-dim slices.  BLOCK128: one
  *               fp16 scale per token.
- *   K_WIN/V_WIN KIVI: fp16 ring of 160 rows x 128 per (sequence, kv head);
- *               token t lives in row t mod 160.
+ *   K_WIN       KIVI: fp16 key ring of 160 rows x 128 channels per
+ *               (sequence, kv head); token t lives in row t mod 160.
+ *   V_WIN       KIVI: fp16 value ring, channel-major: 128 rows x 160 slots
+ *               per (sequence, kv head); token t lives in slot t mod 160.
  *   ROPE        pre-RoPE keys only: fp32 (cos, sin) of t * theta_j, row t,
  *               j = 0..63, written by kvq_append for the appended positions.
  * Every plane is indexed [sequence][kv head][...] except ROPE (shared). */

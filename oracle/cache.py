@@ -266,10 +266,14 @@ class OracleCache:
             vm[:, :, g] = layout.v_meta(self.v_s[:, :, g], self.v_z[:, :, g])
             pair(live[layout.K_META]).reshape(B, H, -1, 512)[:, :, g] = True
             pair(live[layout.V_META]).reshape(B, H, -1, 512)[:, :, g] = True
-        for p, win in ((layout.K_WIN, self.win_k), (layout.V_WIN, self.win_v)):
-            im = pair(img[p]).reshape(B, H, layout.RING, 256)
-            lv = pair(live[p]).reshape(B, H, layout.RING, 256)
-            for i, t in enumerate(range(Tq, T)):
-                im[:, :, t % layout.RING] = win[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 256)
-                lv[:, :, t % layout.RING] = True
+        im = pair(img[layout.K_WIN]).reshape(B, H, layout.RING, 256)
+        lv = pair(live[layout.K_WIN]).reshape(B, H, layout.RING, 256)
+        for i, t in enumerate(range(Tq, T)):
+            im[:, :, t % layout.RING] = self.win_k[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 256)
+            lv[:, :, t % layout.RING] = True
+        im = pair(img[layout.V_WIN]).reshape(B, H, 128, layout.RING, 2)
+        lv = pair(live[layout.V_WIN]).reshape(B, H, 128, layout.RING, 2)
+        for i, t in enumerate(range(Tq, T)):
+            im[:, :, :, t % layout.RING] = self.win_v[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 128, 2)
+            lv[:, :, :, t % layout.RING] = True
         return img, live

@@ -35,8 +35,10 @@ Planes (all [batch][kv_head][...], row-major, little-endian fp16/fp32):
            bytes 4d..4d+3.  BLOCK128: one fp16 scale per token.
   5 V_META KIVI: 512 B per group: token-major, token t and 32-dim group g at
            bytes 16t + 4g: (s, z).  BLOCK128: one fp16 scale per token.
-  6 K_WIN  KIVI: fp16 window ring of 160 rows x 128; token t in row t mod 160.
-  7 V_WIN  same for values.
+  6 K_WIN  KIVI: fp16 key window ring, 160 rows x 128 channels; token t in
+           row t mod 160.
+  7 V_WIN  KIVI: fp16 value window ring, channel-major: 128 rows (channels) x
+           160 slots; token t in slot t mod 160 of every row.
   8 ROPE   pre-RoPE keys only: float32 [32 * ceil(max_tokens/32)][64][2],
            row t = (cos(t * theta_j), sin(t * theta_j)) for j = 0..63.
 Group count Gmax = ceil(max_tokens / 32).  Unused planes have size 0.

@@ -32,8 +32,9 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libkvq)")
 
 
-def command(out=LIB):
+def command(out=LIB, defines=()):
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            *[f"-D{d}" for d in defines],
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-fno-fast-math", "-Wall", "-Wno-unused-function",
@@ -41,19 +42,20 @@ def command(out=LIB):
            [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose=False):
-    """Compile every source into _lib/libkvq.so (always recompiles)."""
-    os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose=False, out=LIB, defines=()):
+    """Compile every source into ``out`` (default _lib/libkvq.so; always
+    recompiles).  ``defines``: tuning macros such as KVQ_DECODE_PREFETCH=1."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
+    cmd = command(tmp, defines)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libkvq.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

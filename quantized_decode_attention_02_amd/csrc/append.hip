@@ -184,21 +184,28 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, co
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t pair = pair_index(g, b, h);
 
-  for (int e = tid; e < 2 * kGroup * 16; e += 256) {
-    const int tensor = e >> 9, r = e & 511;
-    const int tok = r >> 4, c8 = r & 15;
+  // keys: 16-byte chunks of token rows (window ring rows or new input rows)
+  for (int e = tid; e < kGroup * 16; e += 256) {
+    const int tok = e >> 4, c8 = e & 15;
     const int64_t t = grp * kGroup + tok;
     const __half* src;
     if (t < T0) {
-      const int plane = tensor ? KVQ_PLANE_V_WIN : KVQ_PLANE_K_WIN;
-      src = reinterpret_cast<const __half*>(p.p[plane]) + (pair * kRing + t % kRing) * kD;
+      src = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
     } else {
-      const __half* base = tensor ? v_new : k_new;
-      src = base + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
+      src = k_new + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
     }
     const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
     const __half* hv = reinterpret_cast<const __half*>(&raw);
-    for (int i = 0; i < 8; ++i) xs[tensor][tok][8 * c8 + i] = __half2float(hv[i]);
+    for (int i = 0; i < 8; ++i) xs[0][tok][8 * c8 + i] = __half2float(hv[i]);
+  }
+  // values: the window ring is channel-major, new input token-major
+  const __half* vring = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
+  for (int e = tid; e < kGroup * kD; e += 256) {
+    const int tok = e >> 7, d = e & 127;
+    const int64_t t = grp * kGroup + tok;
+    const __half v = t < T0 ? vring[d * kRing + t % kRing]
+                            : v_new[(((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + d];
+    xs[1][tok][d] = __half2float(v);
   }
   __syncthreads();
   if (g.hadamard) fwht128_lds(&xs[0][0][0], 2 * kGroup, tid, 256);
@@ -248,7 +255,8 @@ __global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int6
 }
 
 // KIVI: copy new tokens [w0, w1) (absolute positions, all >= T0) into the fp16
-// window ring, row t mod 160.  One thread per 16-byte chunk.
+// window rings: keys to row t mod 160 (one thread per 16-byte chunk), values
+// to slot t mod 160 of each channel row (one thread per 8 channels).
 __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, const __half* k_new,
                                                            const __half* v_new, int64_t n_new,
                                                            int64_t T0, int64_t w0, int64_t nw) {
@@ -264,10 +272,16 @@ __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, con
     const int64_t t = w0 + r % nw;
     const int b = (int)(r / nw);
     const __half* src = (tensor ? v_new : k_new) + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
-    const int plane = tensor ? KVQ_PLANE_V_WIN : KVQ_PLANE_K_WIN;
-    __half* dst = reinterpret_cast<__half*>(p.p[plane]) +
-                  (pair_index(g, b, h) * kRing + t % kRing) * kD;
-    *reinterpret_cast<uint4*>(dst + 8 * c8) = *reinterpret_cast<const uint4*>(src + 8 * c8);
+    const int64_t pair = pair_index(g, b, h);
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
+    if (tensor == 0) {
+      __half* dst = reinterpret_cast<__half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
+      *reinterpret_cast<uint4*>(dst + 8 * c8) = raw;
+    } else {
+      __half* dst = reinterpret_cast<__half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing + t % kRing;
+      const __half* hv = reinterpret_cast<const __half*>(&raw);
+      for (int k = 0; k < 8; ++k) dst[(8 * c8 + k) * kRing] = hv[k];
+    }
   }
 }
 

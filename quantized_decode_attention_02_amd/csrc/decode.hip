@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
       const __half* ring = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_V_WIN]) + pair * kRing * kD;
       for (int k = 0; k < 16; ++k) {
         const int64_t t = t0 + k;
-        vx[k] = (16 * vhalf + k < nvalid) ? __half2float(ring[(t % kRing) * kD + vd]) : 0.0f;
+        vx[k] = (16 * vhalf + k < nvalid) ? __half2float(ring[vd * kRing + t % kRing]) : 0.0f;
       }
     } else if (g.scheme == KVQ_BLOCK128_SYM) {
       const uint8_t* tile = a.p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 2048;
@@ -246,32 +246,70 @@ __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // M = max m_c, L = sum l_c 2^(m_c - M), out = sum o_c 2^(m_c - M) / L.
-// Hadamard caches: the quantized chunks were attended with the rotated query,
-// so their sum is rotated back once (H/sqrt(128) is its own inverse); the fp16
-// window chunk was attended unrotated.
-__global__ __launch_bounds__(128) void decode_merge_kernel(Geom g, const float* ws, float* out,
+// Hadamard caches: the quantized chunks (slots < nq) were attended with the
+// rotated query, so their sum is rotated back once (H/sqrt(128) is its own
+// inverse); the fp16 window slots were attended unrotated.
+// 256 threads: the slot loops are strided over threads so their loads are
+// independent; two threads per output channel.
+__device__ __forceinline__ float block_reduce(float v, float* red, int tid, bool is_max) {
+  red[tid] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = is_max ? fmaxf(red[tid], red[tid + s]) : red[tid] + red[tid + s];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, const float* ws, float* out,
                                                            int64_t nq, int64_t n) {
-  __shared__ float acc[kD];
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  __shared__ float red[256];
+  __shared__ float wsh[1024];
+  __shared__ float acc[2][2][kD];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const float* base = ws + ((int64_t)b * g.Hq + hq) * n * kPartial;
   float M = -INFINITY;
-  for (int64_t c = 0; c < n; ++c) M = fmaxf(M, base[c * kPartial]);
-  float L = 0.0f, oq = 0.0f, ow = 0.0f;
-  for (int64_t c = 0; c < n; ++c) {
-    const float m = base[c * kPartial];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += base[c * kPartial + 1] * w;
-    const float v = base[c * kPartial + 2 + d] * w;
-    if (c < nq) oq += v; else ow += v;
+  for (int64_t c = tid; c < n; c += 256) M = fmaxf(M, base[c * kPartial]);
+  M = block_reduce(M, red, tid, true);
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (int64_t c = tid; c < n; c += 256) {
+      const float m = base[c * kPartial];
+      if (m != -INFINITY) L += base[c * kPartial + 1] * exp2f(m - M);
+    }
   }
-  if (g.hadamard) {
-    acc[d] = oq;
+  L = block_reduce(L, red, tid, false);
+  const int d = tid & 127, hf = tid >> 7;
+  float oq = 0.0f, ow = 0.0f;
+  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+    const int cnt = (int)min((int64_t)1024, n - c0);
+    for (int i = tid; i < cnt; i += 256) {
+      const float m = base[(c0 + i) * kPartial];
+      wsh[i] = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    }
     __syncthreads();
-    fwht128_lds(acc, 1, d, 128);
-    oq = acc[d];
+#pragma unroll 8
+    for (int i = hf; i < cnt; i += 2) {
+      const float v = base[(c0 + i) * kPartial + 2 + d] * wsh[i];
+      if (c0 + i < nq) oq += v; else ow += v;
+    }
+    __syncthreads();
   }
-  out[((int64_t)b * g.Hq + hq) * kD + d] = L > 0.0f ? (oq + ow) / L : 0.0f;
+  acc[0][hf][d] = oq;
+  acc[1][hf][d] = ow;
+  __syncthreads();
+  if (g.hadamard) {
+    if (tid < kD) red[tid] = acc[0][0][tid] + acc[0][1][tid];
+    __syncthreads();
+    fwht128_lds(red, 1, tid, 256);
+  }
+  if (tid < kD) {
+    const float q_part = g.hadamard ? red[tid] : acc[0][0][tid] + acc[0][1][tid];
+    const float w_part = acc[1][0][tid] + acc[1][1][tid];
+    out[((int64_t)b * g.Hq + hq) * kD + tid] = L > 0.0f ? (q_part + w_part) / L : 0.0f;
+  }
 }
 
 }  // namespace
@@ -292,14 +330,7 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
   a.n = cp.n;
   a.c0 = 0;
   unsigned nblocks = (unsigned)cp.n;
-  if (cp.mode == 1) {
-    // quantized tokens on the MFMA kernel; the fp16 window here
-    const hipError_t e = launch_decode_mfma(g, p, cp, q, sm_scale, ws, s);
-    if (e != hipSuccess) return e;
-    if (cp.n == cp.nq) return hipGetLastError();
-    a.c0 = cp.nq;
-    nblocks = 1;
-  }
+  if (cp.mode == 1) return launch_decode_mfma(g, p, cp, q, sm_scale, ws, s);
   const dim3 grid(nblocks, g.Hkv, g.B), block(256);
 #define KVQ_LAUNCH(GG, RR) hipLaunchKernelGGL((decode_partials_v0<GG, RR>), grid, block, 0, s, a)
   if (g.pre_rope) {
@@ -317,7 +348,7 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
 
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
                                hipStream_t s) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(g.Hq, g.B), dim3(128), 0, s, g, ws, out, cp.nq, cp.n);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(g.Hq, g.B), dim3(256), 0, s, g, ws, out, cp.nq, cp.n);
   return hipGetLastError();
 }
 

@@ -55,9 +55,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
            half_bits_to_float(vm[2 * (row * 4 + dg) + 1]);
     } else {
       const __half* kr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
-      const __half* vr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + (pair * kRing + t % kRing) * kD;
+      const __half* vr = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
       kv = __half2float(kr[d]);
-      vv = __half2float(vr[d]);
+      vv = __half2float(vr[d * kRing + t % kRing]);
     }
     k_out[i] = kv;
     v_out[i] = vv;

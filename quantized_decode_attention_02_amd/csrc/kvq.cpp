@@ -12,6 +12,12 @@
 
 #include "kvq_internal.h"
 
+// Tuning knob: the MFMA decode aims at about this many waves per launch
+// (tiles per wave = all 64-token tiles / this, clamped to [1, 16]).
+#ifndef KVQ_DECODE_TARGET_WAVES
+#define KVQ_DECODE_TARGET_WAVES 16384
+#endif
+
 namespace kvq {
 namespace {
 
@@ -150,9 +156,9 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 // Split-K plan.  MFMA path: the quantized tokens form up to two ranges of one
 // code width each (low-bit tier, high-bit tier); a wave streams nt tiles of
 // 64 tokens and a work-group of 4 waves covers 4 * nt tiles, with nt chosen
-// so that a call launches on the order of 16K waves.  Pre-RoPE path: chunks
-// of gpc key groups, a few thousand work-groups.  The fp16 window is one
-// more slot either way.
+// so that a call launches on the order of 16K waves; the fp16 window rides
+// on the last launch as one more work-group.  Pre-RoPE path: chunks of gpc
+// key groups, a few thousand work-groups, the window one more chunk.
 ChunkPlan plan_chunks(const Geom& g) {
   ChunkPlan cp;
   cp.nr = 0;
@@ -167,28 +173,30 @@ ChunkPlan plan_chunks(const Geom& g) {
     if (gpc > 64) gpc = 64;
     cp.gpc = gpc;
     cp.nq = Gq > 0 ? (Gq + gpc - 1) / gpc : 0;
-  } else {
-    cp.mode = 1;
-    int64_t lo_end = g.scheme == KVQ_KIVI_ASYM ? g.hi_start : 0;
-    if (lo_end > 0) cp.r[cp.nr++] = RangePlan{0, lo_end, g.lo_bits, 0, 1, 0, 0};
-    if (g.Tq > lo_end) cp.r[cp.nr++] = RangePlan{lo_end, g.Tq, g.hi_bits, 1, 1, 0, 0};
-    int64_t tiles = 0;
-    for (int i = 0; i < cp.nr; ++i) tiles += pairs * ((cp.r[i].t_hi - cp.r[i].t_lo + 63) / 64);
-    int64_t nt = (tiles + 16383) / 16384;
-    if (nt < 1) nt = 1;
-    if (nt > 16) nt = 16;
-    int64_t slot = 0;
-    for (int i = 0; i < cp.nr; ++i) {
-      RangePlan& r = cp.r[i];
-      const int64_t t = (r.t_hi - r.t_lo + 63) / 64;
-      r.nt = (int)nt;
-      r.chunks = (t + 4 * nt - 1) / (4 * nt);
-      r.slot_base = slot;
-      slot += r.chunks * 4;
-    }
-    cp.nq = slot;
+    cp.n = cp.nq + (window ? 1 : 0);
+    return cp;
   }
-  cp.n = cp.nq + (window ? 1 : 0);
+  cp.mode = 1;
+  const int64_t lo_end = g.scheme == KVQ_KIVI_ASYM ? g.hi_start : 0;
+  if (lo_end > 0) cp.r[cp.nr++] = RangePlan{0, lo_end, g.lo_bits, 0, 1, 0, 0, 0};
+  if (g.Tq > lo_end || window) cp.r[cp.nr++] = RangePlan{lo_end, g.Tq, g.hi_bits, 1, 1, 0, 0, 0};
+  int64_t tiles = 0;
+  for (int i = 0; i < cp.nr; ++i) tiles += pairs * ((cp.r[i].t_hi - cp.r[i].t_lo + 63) / 64);
+  int64_t nt = (tiles + KVQ_DECODE_TARGET_WAVES - 1) / KVQ_DECODE_TARGET_WAVES;
+  if (nt < 1) nt = 1;
+  if (nt > 16) nt = 16;
+  int64_t slot = 0;
+  for (int i = 0; i < cp.nr; ++i) {
+    RangePlan& r = cp.r[i];
+    const int64_t t = (r.t_hi - r.t_lo + 63) / 64;
+    r.nt = (int)nt;
+    r.chunks = (t + 4 * nt - 1) / (4 * nt);
+    r.slot_base = slot;
+    slot += r.chunks * 4;
+  }
+  cp.nq = slot;
+  if (window) cp.r[cp.nr - 1].window = 1;
+  cp.n = cp.nq + (window ? 4 : 0);
   return cp;
 }
 

@@ -42,19 +42,22 @@ struct RangePlan {
   int nt;              // 64-token tiles per wave
   int64_t chunks;      // work-groups along the range (4 waves each)
   int64_t slot_base;   // first partial slot
+  int window;          // 1: this launch also attends the fp16 window (4 slots
+                       // after its chunks' slots)
 };
 
-// Split-K plan of one decode call.  Quantized tokens go to the MFMA kernel
-// (mode 1) as up to two tier-pure ranges, each wave writing one partial
-// slot; pre-RoPE caches use the VALU kernel (mode 0) with chunks of gpc key
-// groups.  The fp16 window, when present, is the last slot (VALU kernel).
+// Split-K plan of one decode call.  Mode 1 (MFMA kernel): quantized tokens as
+// up to two tier-pure ranges, each wave writing one partial slot; the fp16
+// window is one more work-group of the last range's launch (4 slots).
+// Mode 0 (VALU kernel, pre-RoPE caches): chunks of gpc key groups, the fp16
+// window one more chunk (1 slot).  Slots [0, nq) hold quantized tokens.
 struct ChunkPlan {
   int mode;
   int64_t gpc;        // mode 0: key groups per chunk
   RangePlan r[2];
   int nr;
   int64_t nq;         // partial slots of quantized tokens
-  int64_t n;          // nq + (1 if a fp16 window chunk exists)
+  int64_t n;          // all slots (nq + the window's)
 };
 
 ChunkPlan plan_chunks(const Geom& g);

@@ -11,7 +11,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libkvq.so")
+# KVQ_LIBRARY may point at another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is loaded.
+_LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "_lib", "libkvq.so")
 
 KIVI_ASYM, BLOCK128_SYM = 0, 1
 MAX_PLANES = 16

@@ -126,6 +126,7 @@ def test_workspace_formula():
     c = dict(CASES[1])
     cfg = kvq.make_config(c)
     assert kvq.workspace_bytes(cfg, 8, 0) == 0
-    assert kvq.workspace_bytes(cfg, 8, 100) == 8 * 32 * 1 * 130 * 4
+    # an all-window cache: one work-group of 4 waves, one slot each
+    assert kvq.workspace_bytes(cfg, 8, 100) == 8 * 32 * 4 * 130 * 4
     n = kvq.workspace_bytes(cfg, 8, 32768) // (8 * 32 * 130 * 4)
     assert n >= 2
