@@ -147,15 +147,22 @@ class OracleCache:
             self.bits[g] = lo
         src_k = np.concatenate([self.win_k, kn], axis=2)   # tokens [Tq0, T1)
         src_v = np.concatenate([self.win_v, vn], axis=2)
-        for g in plan["new_groups"]:
-            a = g * 32 - Tq0
-            bits = tiers.group_bits(g, Tq1, c["hi_window"], c["k_bits"], lo)
-            vbits = tiers.group_bits(g, Tq1, c["hi_window"], c["v_bits"], lo)
-            xk = self._source_rows(src_k[:, :, a:a + 32])
-            xv = self._source_rows(src_v[:, :, a:a + 32])
-            self.k_codes[:, :, g], self.k_s[:, :, g], self.k_z[:, :, g] = quant.quant_k_group(xk, bits)
-            self.v_codes[:, :, g], self.v_s[:, :, g], self.v_z[:, :, g] = quant.quant_v_group(xv, vbits)
-            self.bits[g] = bits
+        # every new group at once: [B, H, groups, 32, 128], split by tier
+        ng = len(plan["new_groups"])
+        if ng:
+            g0 = plan["new_groups"][0]
+            rows_k = src_k[:, :, g0 * 32 - Tq0:(g0 + ng) * 32 - Tq0].reshape(B, H, ng, 32, 128)
+            rows_v = src_v[:, :, g0 * 32 - Tq0:(g0 + ng) * 32 - Tq0].reshape(B, H, ng, 32, 128)
+            gbits = np.array([tiers.group_bits(g, Tq1, c["hi_window"], c["k_bits"], lo)
+                              for g in plan["new_groups"]])
+            for bits in np.unique(gbits):
+                sel = np.nonzero(gbits == bits)[0]
+                gs = g0 + sel
+                xk = self._source_rows(rows_k[:, :, sel])
+                xv = self._source_rows(rows_v[:, :, sel])
+                self.k_codes[:, :, gs], self.k_s[:, :, gs], self.k_z[:, :, gs] = quant.quant_k_group(xk, int(bits))
+                self.v_codes[:, :, gs], self.v_s[:, :, gs], self.v_z[:, :, gs] = quant.quant_v_group(xv, int(bits))
+                self.bits[gs] = bits
         self.win_k = src_k[:, :, Tq1 - Tq0:].copy()
         self.win_v = src_v[:, :, Tq1 - Tq0:].copy()
         self.length = T1
@@ -249,31 +256,37 @@ class OracleCache:
             return img, live
         hs = layout.hi_slots(c, self.max_tokens)
         Tq = self.Tq
-        for g in range(Tq // 32):
-            b = int(self.bits[g])
-            if g * 32 >= tiers.hi_start(Tq, c["hi_window"]):
-                kp, vp, slot, tb = layout.K_HI, layout.V_HI, g % hs, 512 * b
-            else:
-                kp, vp, slot, tb = layout.K_LO, layout.V_LO, g, 512 * b
+        gq = np.arange(Tq // 32)
+        hi_mask = gq * 32 >= tiers.hi_start(Tq, c["hi_window"])
+        for is_hi in (True, False):
+            gs = gq[hi_mask == is_hi]
+            if gs.size == 0:
+                continue
+            b = int(self.bits[gs[0]])
+            assert np.all(self.bits[gs] == b)
+            kp, vp = (layout.K_HI, layout.V_HI) if is_hi else (layout.K_LO, layout.V_LO)
+            slots = gs % hs if is_hi else gs
+            tb = 512 * b
             for p, im_fn, codes in ((kp, layout.k_tile, self.k_codes), (vp, layout.v_tile, self.v_codes)):
                 im = pair(img[p]).reshape(B, H, -1, tb)
                 lv = pair(live[p]).reshape(B, H, -1, tb)
-                im[:, :, slot] = im_fn(codes[:, :, g], b)
-                lv[:, :, slot] = True
+                im[:, :, slots] = im_fn(codes[:, :, gs], b)
+                lv[:, :, slots] = True
+        if gq.size:
             km = pair(img[layout.K_META]).reshape(B, H, -1, 512)
             vm = pair(img[layout.V_META]).reshape(B, H, -1, 512)
-            km[:, :, g] = layout.k_meta(self.k_s[:, :, g], self.k_z[:, :, g])
-            vm[:, :, g] = layout.v_meta(self.v_s[:, :, g], self.v_z[:, :, g])
-            pair(live[layout.K_META]).reshape(B, H, -1, 512)[:, :, g] = True
-            pair(live[layout.V_META]).reshape(B, H, -1, 512)[:, :, g] = True
+            km[:, :, gq] = layout.k_meta(self.k_s[:, :, gq], self.k_z[:, :, gq])
+            vm[:, :, gq] = layout.v_meta(self.v_s[:, :, gq], self.v_z[:, :, gq])
+            pair(live[layout.K_META]).reshape(B, H, -1, 512)[:, :, gq] = True
+            pair(live[layout.V_META]).reshape(B, H, -1, 512)[:, :, gq] = True
+        ring = np.arange(Tq, T) % layout.RING
         im = pair(img[layout.K_WIN]).reshape(B, H, layout.RING, 256)
         lv = pair(live[layout.K_WIN]).reshape(B, H, layout.RING, 256)
-        for i, t in enumerate(range(Tq, T)):
-            im[:, :, t % layout.RING] = self.win_k[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 256)
-            lv[:, :, t % layout.RING] = True
+        im[:, :, ring] = np.ascontiguousarray(self.win_k.astype("<f2")).view(np.uint8).reshape(B, H, -1, 256)
+        lv[:, :, ring] = True
         im = pair(img[layout.V_WIN]).reshape(B, H, 128, layout.RING, 2)
         lv = pair(live[layout.V_WIN]).reshape(B, H, 128, layout.RING, 2)
-        for i, t in enumerate(range(Tq, T)):
-            im[:, :, :, t % layout.RING] = self.win_v[:, :, i].astype("<f2").view(np.uint8).reshape(B, H, 128, 2)
-            lv[:, :, :, t % layout.RING] = True
+        wv = np.ascontiguousarray(np.swapaxes(self.win_v.astype("<f2"), 2, 3)).view(np.uint8)
+        im[:, :, :, ring] = wv.reshape(B, H, 128, -1, 2)
+        lv[:, :, :, ring] = True
         return img, live

@@ -79,15 +79,20 @@ def unpack_rows(packed, bits, n):
     return out[..., :n].astype(np.uint8)
 
 
+def _k_tile_perm(bits):
+    """perm[t * rowbytes + c] = offset of canonical byte c of token t."""
+    rb = 128 * bits // 8
+    t = np.arange(TILE_TOKENS)[:, None]
+    c = np.arange(rb)[None, :]
+    return ((c // 16) * 512 + t * 16 + (c % 16)).reshape(-1)
+
+
 def k_tile(codes, bits):
     """Key tile image: codes [..., 32, 128] -> uint8 [..., 512 * bits]."""
     rows = pack_rows(codes, bits)                    # [..., 32, rowbytes]
-    rb = rows.shape[-1]
     lead = rows.shape[:-2]
-    out = np.zeros(lead + (TILE_TOKENS * rb,), dtype=np.uint8)
-    for c in range(rb):
-        for t in range(TILE_TOKENS):
-            out[..., (c // 16) * 512 + t * 16 + (c % 16)] = rows[..., t, c]
+    out = np.zeros(lead + (512 * bits,), dtype=np.uint8)
+    out[..., _k_tile_perm(bits)] = rows.reshape(lead + (-1,))
     return out
 
 
@@ -95,11 +100,7 @@ def k_tile_decode(tile, bits):
     """Key tile image -> codes [..., 32, 128]."""
     tile = np.asarray(tile, dtype=np.uint8)
     rb = 128 * bits // 8
-    lead = tile.shape[:-1]
-    rows = np.zeros(lead + (TILE_TOKENS, rb), dtype=np.uint8)
-    for c in range(rb):
-        for t in range(TILE_TOKENS):
-            rows[..., t, c] = tile[..., (c // 16) * 512 + t * 16 + (c % 16)]
+    rows = tile[..., _k_tile_perm(bits)].reshape(tile.shape[:-1] + (TILE_TOKENS, rb))
     return unpack_rows(rows, bits, 128)
 
 
