@@ -13,12 +13,13 @@ Reported (one JSON line on stdout):
                window) / step time, GB/s; inputs resident in HBM
   roofline     the split-K decode kernel alone: algorithmic bytes per launch /
                its average duration (HIP events on the launch stream) against
-               the 8 TB/s HBM peak
-  cpu_baseline the CPU oracle (dequantize + fp64 attention) on a bounded
-               sample of the same workload's (sequence, kv head) pairs, one
-               process per core
+               the 8 TB/s HBM peak; traffic = counter-measured HBM bytes per
+               launch (null when the kernel sources changed since)
+  cpu_baseline the CPU oracle on the same step (append one token + dequantize
+               + fp64 attention) over a bounded sample of the workload's
+               (sequence, kv head) pairs, one process per core
 
-    python bench.py [--steps K] [--warmup W] [--workload ID]
+    python bench.py [--steps K] [--warmup W] [--workload ID] [--no-cpu-baseline]
 """
 
 import argparse
@@ -38,6 +39,21 @@ from quantized_decode_attention_02_amd import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn effective KV GB/s (% of HBM peak) + attended tokens/s, INT4, 1 GPU"
 
+# HBM bytes of one decode-kernel launch from hardware counters (rocprofv3
+# --pmc FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+# the counter reads for a plain 1 GiB device copy (FETCH_SIZE reads 524300 KiB
+# for 1048576 KiB moved: x2.0; WRITE_SIZE reads 1048576 KiB: x1.0).  Valid only
+# for the kernel sources they were taken with (sha256 over COUNTER_SOURCES);
+# any change there reports traffic as null until the counters are taken again.
+COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
+                   "quantized_decode_attention_02_amd/csrc/kvq_device.h",
+                   "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
+                   "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
+COUNTERS = {
+    1: {"sources_sha256": "94a34706f6369423f77e0b56adc42aa53dfebfd421f96248792cf8660529e9e4", "fetch_kib": 666200, "write_kib": 9020,
+        "fetch_factor": 2.0, "write_factor": 1.0},
+}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -49,6 +65,24 @@ def tier_map(cfg, T):
     Tq = max(0, ((T - 128) // 32) * 32)
     hi_start = 0 if cfg["hi_window"] < 0 else max(0, Tq - cfg["hi_window"])
     return Tq, hi_start
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in COUNTER_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(wid):
+    """Counter-measured HBM bytes per decode launch, or None when the kernel
+    sources differ from those the counters were taken with."""
+    c = COUNTERS.get(wid)
+    if c is None or c["sources_sha256"] != sources_sha256():
+        return None
+    return int((c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"]) * 1024)
 
 
 def decode_bytes(w, T):
@@ -79,23 +113,29 @@ def _cpu_worker(args):
     G = w["num_q_heads"] // w["num_kv_heads"]
     cfg = dict(wl.library_config(w), num_q_heads=G, num_kv_heads=1)
     built = []
+    t_build = 0.0
     for b, h in pairs:
         K, V = wl.kv_tokens(w, 0, T, seqs=[b], heads=[h], threads=1)
         oc = OracleCache(cfg, 1, T)
         t0 = time.perf_counter()
-        oc.append(K, V)
-        t_app = time.perf_counter() - t0
+        oc.append(K[:, :T - 1], V[:, :T - 1])
+        t_build += time.perf_counter() - t0
         q = wl.queries(w, seqs=[b])[:, h * G:(h + 1) * G]
-        built.append((oc, q, t_app))
+        built.append((oc, q, K[:, T - 1:], V[:, T - 1:]))
     barrier.wait()
     t0 = time.time()
-    for oc, q, _ in built:
+    for oc, q, k1, v1 in built:
+        oc.append(k1, v1)
         oc.decode(q)
     t1 = time.time()
-    q_out.put((t0, t1, sum(x[2] for x in built), len(built)))
+    q_out.put((t0, t1, t_build, len(built)))
 
 
 def cpu_baseline(w, T, n_pairs, workers):
+    """The oracle timed on the same step as the GPU (append the last token,
+    which quantizes the group leaving the window, then dequantize + fp64
+    attention over the whole cache) for a sample of (sequence, kv head)
+    pairs, one process per core, all started together."""
     pairs_all = [(b, h) for b in range(w["batch"]) for h in range(w["num_kv_heads"])]
     rng = np.random.default_rng(12345)
     pick = [pairs_all[i] for i in sorted(rng.choice(len(pairs_all), min(n_pairs, len(pairs_all)),
@@ -117,15 +157,17 @@ def cpu_baseline(w, T, n_pairs, workers):
     per_pair_bytes = decode_bytes(dict(w, batch=1, num_kv_heads=1), T)
     nbytes = per_pair_bytes * len(pick)
     secs = end - start
+    cpu_s = sum(r[1] - r[0] for r in res)
     return {
         "value": nbytes / secs / 1e9,
         "unit": "GB/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": (f"{len(pick)} of {len(pairs_all)} (sequence, kv head) pairs at T={T}: "
-                   f"dequantize + fp64 attention over {nbytes / 1e9:.3f} GB of the cache in "
-                   f"{secs:.2f} s wall on {workers} processes; quantize-on-append of the same "
-                   f"pairs took {sum(r[2] for r in res):.2f} CPU-s (untimed here)"),
+        "sample": (f"{len(pick)} of {len(pairs_all)} (sequence, kv head) pairs at T={T}, the same "
+                   f"step as the GPU (append 1 token + dequantize + fp64 attention) over "
+                   f"{nbytes / 1e9:.3f} GB of the cache: {secs:.2f} s wall, {cpu_s:.1f} CPU-s on "
+                   f"{workers} processes; building the {T - 1}-token caches took "
+                   f"{sum(r[2] for r in res):.1f} CPU-s (untimed)"),
         "attended_tokens_per_s": len(pick) * T / secs,
     }
 
@@ -138,7 +180,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--cpu-pairs", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for "
@@ -226,6 +268,7 @@ def main():
     value = nbytes / (ms_step / 1e3) / 1e9
     achieved = nbytes / (k_avg / 1e3) / 1e9
     attended = w["batch"] * T / (ms_step / 1e3)
+    traffic = counter_traffic(w["id"])
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -237,7 +280,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w["name"], "batch": w["batch"], "q_heads": w["num_q_heads"],
                    "kv_heads": w["num_kv_heads"], "head_dim": 128, "tokens": T,
@@ -248,8 +291,11 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "attended_tokens_per_s": round(attended, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_partials", "kernel_ms_avg": round(k_avg, 5),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "decode_mfma_kernel (split-K partials)", "kernel_ms_avg": round(k_avg, 5),
                      "kernel_ms_p10_p90": [round(float(np.percentile(k_ms, 10)), 5),
                                            round(float(np.percentile(k_ms, 90)), 5)]},
         "cpu_baseline": cpu,

@@ -70,16 +70,23 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
     kmeta[2 * c] = gp.s_bits;
     kmeta[2 * c + 1] = gp.z_bits;
   } else {
+    // lane t of a wave walks its slice starting at element t: the 32 lanes
+    // of one slice index hit 32 different LDS banks (min and max do not
+    // depend on the order, and each code depends on its element only)
     const int u = tid - kD;
-    const int t = u >> 2, dg = u & 3;
+    const int t = u & 31, dg = u >> 5;
     const float* row = xv[t] + dg * 32;
-    float mn = row[0], mx = row[0];
+    float mn = row[t], mx = row[t];
     for (int i = 1; i < 32; ++i) {
-      mn = fminf(mn, row[i]);
-      mx = fmaxf(mx, row[i]);
+      const float x = row[(i + t) & 31];
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
     }
     const GroupParams gp = group_params(mn, mx, bits);
-    for (int i = 0; i < 32; ++i) cv[t][dg * 32 + i] = quantize_code(row[i], gp, bits);
+    for (int i = 0; i < 32; ++i) {
+      const int j = (i + t) & 31;
+      cv[t][dg * 32 + j] = quantize_code(row[j], gp, bits);
+    }
     vmeta[2 * (t * 4 + dg)] = gp.s_bits;
     vmeta[2 * (t * 4 + dg) + 1] = gp.z_bits;
   }
@@ -168,67 +175,60 @@ __device__ void store_group(const Geom& g, const Planes& p, int64_t pair, int64_
 }
 
 // ---------------------------------------------------------------------------
-// KIVI: quantize the key groups [g0, g1) of every (sequence, kv head).  A
-// group's tokens come from the fp16 window ring (tokens before T0) or from the
-// new input (tokens from T0 on).  The group goes to the high-bit tier if it
-// starts at or after hi_start_new, else straight to the low-bit tier.
-__global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, const __half* k_new,
-                                                            const __half* v_new, int64_t n_new,
-                                                            int64_t T0, int64_t g0,
-                                                            int64_t hi_start_new) {
-  __shared__ float xs[2][kGroup][kD];
-  __shared__ uint8_t cs[2][kGroup][kD];
-  __shared__ uint16_t meta[2][256];
-  const int tid = threadIdx.x;
-  const int64_t grp = g0 + blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+// KIVI group sources.
+//
+// load_group: the fp16 keys and values of group grp of (b, h) as floats in
+// xk / xv.  A token before T0 is read from the fp16 window rings (keys: row
+// t mod 160, token-major; values: slot t mod 160 of each channel row), a
+// token from T0 on from the new input.  A group never wraps around the ring
+// (160 = 5 * 32), so a group that lies wholly before T0 is 32 consecutive
+// ring rows and 128 runs of 32 consecutive value slots: those are read as
+// 16-byte vectors.
+__device__ void load_group(const Geom& g, const Planes& p, float (*xk)[kD], float (*xv)[kD],
+                           const __half* k_new, const __half* v_new, int64_t n_new, int64_t T0,
+                           int b, int h, int64_t grp, int tid) {
   const int64_t pair = pair_index(g, b, h);
-
-  // keys: 16-byte chunks of token rows (window ring rows or new input rows)
+  const __half* kring = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + pair * kRing * kD;
+  const __half* vring = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
+  if ((grp + 1) * kGroup <= T0) {
+    const int slot0 = (int)(grp % 5) * kGroup;
+    for (int e = tid; e < kGroup * 16; e += 256) {
+      const int tok = e >> 4, c8 = e & 15;
+      const uint4 raw = *reinterpret_cast<const uint4*>(kring + (slot0 + tok) * kD + 8 * c8);
+      const __half* hv = reinterpret_cast<const __half*>(&raw);
+      for (int i = 0; i < 8; ++i) xk[tok][8 * c8 + i] = __half2float(hv[i]);
+    }
+    for (int e = tid; e < kD * 4; e += 256) {
+      const int d = e & 127, c4 = e >> 7;
+      const uint4 raw = *reinterpret_cast<const uint4*>(vring + d * kRing + slot0 + 8 * c4);
+      const __half* hv = reinterpret_cast<const __half*>(&raw);
+      for (int i = 0; i < 8; ++i) xv[8 * c4 + i][d] = __half2float(hv[i]);
+    }
+    return;
+  }
   for (int e = tid; e < kGroup * 16; e += 256) {
     const int tok = e >> 4, c8 = e & 15;
     const int64_t t = grp * kGroup + tok;
-    const __half* src;
-    if (t < T0) {
-      src = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_K_WIN]) + (pair * kRing + t % kRing) * kD;
-    } else {
-      src = k_new + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
-    }
+    const __half* src = t < T0 ? kring + (t % kRing) * kD
+                               : k_new + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
     const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
     const __half* hv = reinterpret_cast<const __half*>(&raw);
-    for (int i = 0; i < 8; ++i) xs[0][tok][8 * c8 + i] = __half2float(hv[i]);
+    for (int i = 0; i < 8; ++i) xk[tok][8 * c8 + i] = __half2float(hv[i]);
   }
-  // values: the window ring is channel-major, new input token-major
-  const __half* vring = reinterpret_cast<const __half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
   for (int e = tid; e < kGroup * kD; e += 256) {
     const int tok = e >> 7, d = e & 127;
     const int64_t t = grp * kGroup + tok;
     const __half v = t < T0 ? vring[d * kRing + t % kRing]
                             : v_new[(((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + d];
-    xs[1][tok][d] = __half2float(v);
+    xv[tok][d] = __half2float(v);
   }
-  __syncthreads();
-  if (g.hadamard) fwht128_lds(&xs[0][0][0], 2 * kGroup, tid, 256);
-
-  const bool hi = grp * kGroup >= hi_start_new;
-  const int bits = hi ? g.hi_bits : g.lo_bits;
-  quantize_group(xs[0], xs[1], cs[0], cs[1], meta[0], meta[1], bits, tid);
-  __syncthreads();
-  store_group(g, p, pair, grp, bits, hi, cs[0], cs[1], meta[0], meta[1], tid);
 }
 
-// KIVI: groups [g0, g1) leave the high-bit tier.  Their fp16 source is gone,
-// so they are requantized at low_bits from their dequantized high-bit values
-// x = fl32(c * s_h + z_h) (the product is exact).  Must run before new groups
-// reuse the ring slots.
-__global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int64_t g0) {
-  __shared__ float xs[2][kGroup][kD];
-  __shared__ uint8_t cs[2][kGroup][kD];
-  __shared__ uint16_t meta[2][256];
-  const int tid = threadIdx.x;
-  const int64_t grp = g0 + blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t pair = pair_index(g, b, h);
+// load_demoted: group grp leaves the high-bit tier; its fp16 source is gone,
+// so the values it is requantized from are its dequantized high-bit values
+// x = fl32(c * s_h + z_h) (the product is exact).
+__device__ void load_demoted(const Geom& g, const Planes& p, float (*xk)[kD], float (*xv)[kD],
+                             int64_t pair, int64_t grp, int tid) {
   const int hb = g.hi_bits;
   const uint8_t* kt = hi_tile(g, p, KVQ_PLANE_K_HI, pair, grp, hb);
   const uint8_t* vt = hi_tile(g, p, KVQ_PLANE_V_HI, pair, grp, hb);
@@ -245,13 +245,115 @@ __global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int6
     const int dg = d >> 5;
     const float vs = half_bits_to_float(vm[2 * (t * 4 + dg)]);
     const float vz = half_bits_to_float(vm[2 * (t * 4 + dg) + 1]);
-    xs[0][t][d] = (float)kcode * ks + kz;
-    xs[1][t][d] = (float)vcode * vs + vz;
+    xk[t][d] = (float)kcode * ks + kz;
+    xv[t][d] = (float)vcode * vs + vz;
   }
+}
+
+// LDS of one group in flight.
+struct GroupLds {
+  float xs[2][kGroup][kD];
+  uint8_t cs[2][kGroup][kD];
+  uint16_t meta[2][256];
+};
+
+// Quantize the group held in gl.xs (already rotated if it is to be) at
+// `bits` and store it in its tier.  Synchronizes before returning, so gl can
+// be reloaded right after.
+__device__ void quantize_store(const Geom& g, const Planes& p, GroupLds& gl, int64_t pair,
+                               int64_t grp, int bits, bool hi, int tid) {
+  quantize_group(gl.xs[0], gl.xs[1], gl.cs[0], gl.cs[1], gl.meta[0], gl.meta[1], bits, tid);
   __syncthreads();
-  quantize_group(xs[0], xs[1], cs[0], cs[1], meta[0], meta[1], g.lo_bits, tid);
+  store_group(g, p, pair, grp, bits, hi, gl.cs[0], gl.cs[1], gl.meta[0], gl.meta[1], tid);
   __syncthreads();
-  store_group(g, p, pair, grp, g.lo_bits, false, cs[0], cs[1], meta[0], meta[1], tid);
+}
+
+// KIVI: quantize the groups [g0, g1) of every (sequence, kv head), one
+// work-group per group.  A group goes to the high-bit tier if it starts at or
+// after hi_start_new, else straight to the low-bit tier.
+__global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, const __half* k_new,
+                                                            const __half* v_new, int64_t n_new,
+                                                            int64_t T0, int64_t g0,
+                                                            int64_t hi_start_new) {
+  __shared__ GroupLds gl;
+  const int tid = threadIdx.x;
+  const int64_t grp = g0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
+  __syncthreads();
+  if (g.hadamard) fwht128_lds(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+  const bool hi = grp * kGroup >= hi_start_new;
+  quantize_store(g, p, gl, pair_index(g, b, h), grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
+}
+
+// KIVI: groups [g0, g1) leave the high-bit tier and are requantized at
+// low_bits.  Must run before new groups reuse their ring slots.
+__global__ __launch_bounds__(256) void kivi_demote_kernel(Geom g, Planes p, int64_t g0) {
+  __shared__ GroupLds gl;
+  const int tid = threadIdx.x;
+  const int64_t grp = g0 + blockIdx.x;
+  const int64_t pair = pair_index(g, blockIdx.z, blockIdx.y);
+  load_demoted(g, p, gl.xs[0], gl.xs[1], pair, grp, tid);
+  __syncthreads();
+  quantize_store(g, p, gl, pair, grp, g.lo_bits, false, tid);
+}
+
+// KIVI appends of at most kSmallAppendMax tokens (decode steps): one work-group
+// per (sequence, kv head) does the whole append of its pair in order: demote
+// the groups [d0, d1) leaving the high-bit tier, quantize the groups [q0, q1)
+// leaving the fp16 window at their tier, copy the new tokens [T0, T0 + n_new)
+// into the rings.  With fewer than 128 new tokens, a group leaving the window
+// lies wholly in the ring; a new token may overwrite the ring slot of a token
+// of such a group, which is why the copies come last, after a barrier that
+// follows every group load.  The new tokens are read into registers first so
+// their latency overlaps the group work.
+__global__ __launch_bounds__(256) void kivi_small_append_kernel(Geom g, Planes p,
+                                                                const __half* k_new,
+                                                                const __half* v_new, int64_t n_new,
+                                                                int64_t T0, int64_t d0, int64_t d1,
+                                                                int64_t q0, int64_t q1,
+                                                                int64_t hi_start_new) {
+  __shared__ GroupLds gl;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t pair = pair_index(g, b, h);
+  // 16-byte pieces per tensor: at most 512, two per thread.  Two named
+  // registers each, not an indexed array, which the compiler could move to LDS.
+  const int items = (int)n_new * 16;
+  const int e0 = tid, e1 = tid + 256;
+  auto piece = [&](int e) { return (((int64_t)b * n_new + (e >> 4)) * g.Hkv + h) * kD + 8 * (e & 15); };
+  uint4 k0 = {}, v0 = {}, k1 = {}, v1 = {};
+  if (e0 < items) {
+    k0 = *reinterpret_cast<const uint4*>(k_new + piece(e0));
+    v0 = *reinterpret_cast<const uint4*>(v_new + piece(e0));
+  }
+  if (e1 < items) {
+    k1 = *reinterpret_cast<const uint4*>(k_new + piece(e1));
+    v1 = *reinterpret_cast<const uint4*>(v_new + piece(e1));
+  }
+  for (int64_t grp = d0; grp < d1; ++grp) {
+    load_demoted(g, p, gl.xs[0], gl.xs[1], pair, grp, tid);
+    __syncthreads();
+    quantize_store(g, p, gl, pair, grp, g.lo_bits, false, tid);
+  }
+  for (int64_t grp = q0; grp < q1; ++grp) {
+    load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
+    __syncthreads();
+    if (g.hadamard) fwht128_lds(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+    const bool hi = grp * kGroup >= hi_start_new;
+    quantize_store(g, p, gl, pair, grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
+  }
+  __half* kring = reinterpret_cast<__half*>(p.p[KVQ_PLANE_K_WIN]) + pair * kRing * kD;
+  __half* vring = reinterpret_cast<__half*>(p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
+  auto put = [&](int e, const uint4& kv, const uint4& vv) {
+    const int c8 = e & 15;
+    const int slot = (int)((T0 + (e >> 4)) % kRing);
+    *reinterpret_cast<uint4*>(kring + slot * kD + 8 * c8) = kv;
+    const __half* hv = reinterpret_cast<const __half*>(&vv);
+    for (int i = 0; i < 8; ++i) vring[(8 * c8 + i) * kRing + slot] = hv[i];
+  };
+  if (e0 < items) put(e0, k0, v0);
+  if (e1 < items) put(e1, k1, v1);
 }
 
 // KIVI: copy new tokens [w0, w1) (absolute positions, all >= T0) into the fp16
@@ -425,6 +527,16 @@ hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_
     hipLaunchKernelGGL(kivi_quantize_kernel, dim3((unsigned)(g1 - g0), g.Hkv, g.B), dim3(256), 0, s, g,
                        p, k_new, v_new, n_new, T0, g0, hi_start_new);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kivi_small_append(const Geom& g, const Planes& p, const __half* k_new,
+                                    const __half* v_new, int64_t n_new, int64_t T0, int64_t d0,
+                                    int64_t d1, int64_t q0, int64_t q1, int64_t hi_start_new,
+                                    hipStream_t s) {
+  if (n_new < 1 || n_new > kSmallAppendMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kivi_small_append_kernel, dim3(g.Hkv, g.B), dim3(256), 0, s, g, p, k_new, v_new,
+                     n_new, T0, d0, d1, q0, q1, hi_start_new);
   return hipGetLastError();
 }
 

@@ -249,66 +249,91 @@ __global__ __launch_bounds__(256) void decode_partials_v0(DecodeArgs a) {
 // Hadamard caches: the quantized chunks (slots < nq) were attended with the
 // rotated query, so their sum is rotated back once (H/sqrt(128) is its own
 // inverse); the fp16 window slots were attended unrotated.
-// 256 threads: the slot loops are strided over threads so their loads are
-// independent; two threads per output channel.
-__device__ __forceinline__ float block_reduce(float v, float* red, int tid, bool is_max) {
-  red[tid] = v;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = is_max ? fmaxf(red[tid], red[tid + s]) : red[tid] + red[tid + s];
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
+//
+// One pass over the workspace: wave w takes slots w, w + 4, w + 8, ... in batches
+// of 64 (lane j reads the (m, l) of the batch's j-th slot), folds a batch into
+// its running (M, L, o) with one max and one sum over the wave, then streams
+// the batch's o[128] rows (two channels per lane) with the weights broadcast
+// from the lane that holds them.  The four waves combine in LDS.  Quantized
+// slots (below nq) and window slots are summed apart so that a Hadamard cache
+// rotates back only the quantized part.
 __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, const float* ws, float* out,
                                                            int64_t nq, int64_t n) {
-  __shared__ float red[256];
-  __shared__ float wsh[1024];
-  __shared__ float acc[2][2][kD];
+  __shared__ float wml[4][2];
+  __shared__ float wo[4][2][kD];
+  __shared__ float rot[kD];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const float* base = ws + ((int64_t)b * g.Hq + hq) * n * kPartial;
-  float M = -INFINITY;
-  for (int64_t c = tid; c < n; c += 256) M = fmaxf(M, base[c * kPartial]);
-  M = block_reduce(M, red, tid, true);
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int64_t c = tid; c < n; c += 256) {
-      const float m = base[c * kPartial];
-      if (m != -INFINITY) L += base[c * kPartial + 1] * exp2f(m - M);
+  float M = -INFINITY, L = 0.0f;
+  float q0 = 0.0f, q1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
+  for (int64_t first = w; first < n; first += 256) {
+    const int64_t mine = first + 4 * (int64_t)lane;
+    float m = -INFINITY, l = 0.0f;
+    if (mine < n) {
+      m = base[mine * kPartial];
+      l = base[mine * kPartial + 1];
+    }
+    const float Mb = fmaxf(M, wave_max64(m));
+    if (Mb == -INFINITY) continue;  // nothing attended so far
+    const float r = M == -INFINITY ? 0.0f : exp2f(M - Mb);
+    const float wt = m == -INFINITY ? 0.0f : exp2f(m - Mb);
+    L = L * r + wave_sum64(l * wt);
+    q0 *= r; q1 *= r; w0 *= r; w1 *= r;
+    M = Mb;
+    // eight rows in flight per step; steps past the batch end reread its
+    // last row with weight 0, so the body has no branch to wait behind
+    const int cnt = (int)min((int64_t)64, (n - first + 3) / 4);
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t slot = first + 4 * (int64_t)min(i0 + k, cnt - 1);
+        v[k] = *reinterpret_cast<const float2*>(base + slot * kPartial + 2 + 2 * lane);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = min(i0 + k, cnt - 1);
+        const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i));
+        const float wi = i0 + k < cnt ? wr : 0.0f;
+        const float wq = first + 4 * (int64_t)i < nq ? wi : 0.0f;
+        const float ww = wi - wq;
+        q0 += wq * v[k].x;
+        q1 += wq * v[k].y;
+        w0 += ww * v[k].x;
+        w1 += ww * v[k].y;
+      }
     }
   }
-  L = block_reduce(L, red, tid, false);
-  const int d = tid & 127, hf = tid >> 7;
-  float oq = 0.0f, ow = 0.0f;
-  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
-    const int cnt = (int)min((int64_t)1024, n - c0);
-    for (int i = tid; i < cnt; i += 256) {
-      const float m = base[(c0 + i) * kPartial];
-      wsh[i] = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int i = hf; i < cnt; i += 2) {
-      const float v = base[(c0 + i) * kPartial + 2 + d] * wsh[i];
-      if (c0 + i < nq) oq += v; else ow += v;
-    }
-    __syncthreads();
+  if (lane == 0) {
+    wml[w][0] = M;
+    wml[w][1] = L;
   }
-  acc[0][hf][d] = oq;
-  acc[1][hf][d] = ow;
+  wo[w][0][2 * lane] = q0;
+  wo[w][0][2 * lane + 1] = q1;
+  wo[w][1][2 * lane] = w0;
+  wo[w][1][2 * lane + 1] = w1;
   __syncthreads();
-  if (g.hadamard) {
-    if (tid < kD) red[tid] = acc[0][0][tid] + acc[0][1][tid];
-    __syncthreads();
-    fwht128_lds(red, 1, tid, 256);
+  float Mt = -INFINITY;
+  for (int i = 0; i < 4; ++i) Mt = fmaxf(Mt, wml[i][0]);
+  float sc[4], Lt = 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = wml[i][0] == -INFINITY ? 0.0f : exp2f(wml[i][0] - Mt);
+    Lt += sc[i] * wml[i][1];
   }
+  float qp = 0.0f, wp = 0.0f;
   if (tid < kD) {
-    const float q_part = g.hadamard ? red[tid] : acc[0][0][tid] + acc[0][1][tid];
-    const float w_part = acc[1][0][tid] + acc[1][1][tid];
-    out[((int64_t)b * g.Hq + hq) * kD + tid] = L > 0.0f ? (q_part + w_part) / L : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      qp += sc[i] * wo[i][0][tid];
+      wp += sc[i] * wo[i][1][tid];
+    }
+    rot[tid] = qp;
+  }
+  __syncthreads();
+  if (g.hadamard) fwht128_lds(rot, 1, tid, 256);
+  if (tid < kD) {
+    const float q_part = g.hadamard ? rot[tid] : qp;
+    out[((int64_t)b * g.Hq + hq) * kD + tid] = Lt > 0.0f ? (q_part + wp) / Lt : 0.0f;
   }
 }
 

@@ -78,39 +78,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// DPP lane permutations within a 16-lane row (full rows, so every lane has a
-// source): xor 1, xor 2, reverse 8, reverse 16.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// ds_swizzle bitmask mode within 32 lanes: partner = lane ^ 16
-__device__ __forceinline__ float swz16(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
-__device__ __forceinline__ float half_sum(float v) {   // over the 32 lanes of a half-wave
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  v += dpp<0x140>(v);
-  return v + swz16(v);
-}
-__device__ __forceinline__ float half_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  return fmaxf(v, swz16(v));
-}
-__device__ __forceinline__ float wave_sum64(float v) {
-  v = half_sum(v);
-  return v + __shfl_xor(v, 32, 64);
-}
-__device__ __forceinline__ float wave_max64(float v) {
-  v = half_max(v);
-  return fmaxf(v, __shfl_xor(v, 32, 64));
-}
-
 __device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
   typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
   u2_t v = {x, y};

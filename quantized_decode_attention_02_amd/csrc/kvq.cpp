@@ -272,18 +272,27 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
     // quantized prefix grows by whole 32-token groups; groups older than the
     // high-bit window drop to low_bits.
     const int64_t Tq0 = quantized_prefix(cfg, T0), Tq1 = quantized_prefix(cfg, T1);
-    int64_t h1 = 0;
+    int64_t h0 = 0, h1 = 0, d1 = 0;
     if (cfg->int4_window >= 0) {
-      const int64_t h0 = Tq0 > cfg->int4_window ? Tq0 - cfg->int4_window : 0;
+      h0 = Tq0 > cfg->int4_window ? Tq0 - cfg->int4_window : 0;
       h1 = Tq1 > cfg->int4_window ? Tq1 - cfg->int4_window : 0;
-      const int64_t d1 = (Tq0 < h1 ? Tq0 : h1);
-      e = launch_kivi_demote(g, p, h0 / kGroup, d1 / kGroup, st);
-      if (e != hipSuccess) return from_hip(e);
+      d1 = (Tq0 < h1 ? Tq0 : h1);
     }
-    e = launch_kivi_quantize(g, p, kn, vn, n_new, T0, Tq0 / kGroup, Tq1 / kGroup, h1, st);
-    if (e != hipSuccess) return from_hip(e);
-    const int64_t w0 = T0 > Tq1 ? T0 : Tq1;
-    e = launch_window_write(g, p, kn, vn, n_new, T0, w0, T1, st);
+    if (n_new <= kSmallAppendMax) {
+      // decode-sized append: one fused launch (the window write starts at T0,
+      // since fewer than 128 new tokens never reach the quantized prefix)
+      e = launch_kivi_small_append(g, p, kn, vn, n_new, T0, h0 / kGroup, d1 / kGroup, Tq0 / kGroup,
+                                   Tq1 / kGroup, h1, st);
+    } else {
+      if (d1 > h0) {
+        e = launch_kivi_demote(g, p, h0 / kGroup, d1 / kGroup, st);
+        if (e != hipSuccess) return from_hip(e);
+      }
+      e = launch_kivi_quantize(g, p, kn, vn, n_new, T0, Tq0 / kGroup, Tq1 / kGroup, h1, st);
+      if (e != hipSuccess) return from_hip(e);
+      const int64_t w0 = T0 > Tq1 ? T0 : Tq1;
+      e = launch_window_write(g, p, kn, vn, n_new, T0, w0, T1, st);
+    }
   }
   if (e != hipSuccess) return from_hip(e);
   cache->length = T1;

@@ -71,6 +71,13 @@ hipError_t launch_kivi_demote(const Geom& g, const Planes& p, int64_t g0, int64_
 hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_new,
                                 const __half* v_new, int64_t n_new, int64_t T0, int64_t g0,
                                 int64_t g1, int64_t hi_start_new, hipStream_t s);
+// Appends of 1..kSmallAppendMax tokens: demote, quantize and window copy
+// fused into one launch of one work-group per (sequence, kv head).
+constexpr int kSmallAppendMax = 32;
+hipError_t launch_kivi_small_append(const Geom& g, const Planes& p, const __half* k_new,
+                                    const __half* v_new, int64_t n_new, int64_t T0, int64_t d0,
+                                    int64_t d1, int64_t q0, int64_t q1, int64_t hi_start_new,
+                                    hipStream_t s);
 hipError_t launch_window_write(const Geom& g, const Planes& p, const __half* k_new,
                                const __half* v_new, int64_t n_new, int64_t T0, int64_t w0,
                                int64_t w1, hipStream_t s);
