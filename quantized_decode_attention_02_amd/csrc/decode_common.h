@@ -1,0 +1,340 @@
+// Pieces shared by the split-K decode kernels on the 4x4x4 fp16 MFMA
+// (decode_mfma.hip: keys stored after RoPE or rotated; decode_rope.hip: keys
+// stored before RoPE).
+//
+// Sources cited here:
+//   [nalar]  "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
+//            (nalar.dev).
+//
+// MFMA 4x4x4 with 16 blocks: block b is lanes 4b..4b+3; A lane 4b+m holds
+// row m, B lane 4b+n holds column n, D lane 4b+n register r holds row r of
+// column n.  A wave streams 64-token tiles; lane l owns token l for the scores
+// and channels l and 64 + l for the output; rows are query heads.
+//
+// Values (both kernels): per-token scales fold into the probabilities,
+// p'_t = p_t s_t, written to LDS in A order as hi + lo fp16 halves (a single
+// fp16 would put a 2^-12 relative error on c * s, i.e. on the group's whole
+// range rather than on the value); zero points add sum_t p_t z_t.  B is the
+// codes of 4 tokens of one channel (value tiles are channel-major): a nibble
+// masked into an fp16 (w & 0x000F000F, ...) is the exact subnormal n * 2^-24,
+// which the epilogue scales back by 2^24 ([nalar] "Error pada value masuk
+// setelah attention probability").
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+struct MfmaArgs {
+  Geom g;
+  Planes p;
+  const __half* q;
+  float* ws;
+  float scale_log2;
+  int64_t q_pos;        // query position (keys stored before RoPE)
+  int64_t t_lo, t_hi;   // token range of this launch; t_lo is 32-aligned
+  int nt;               // 64-token tiles per wave
+  int hi_tier;          // KIVI: tiles in the high-bit planes (ring) or low-bit
+  int64_t chunks;       // work-groups over [t_lo, t_hi)
+  int window;           // 1: one more work-group attends the fp16 window
+  int64_t slot_base;    // first partial slot of this launch
+  int64_t n_slots;      // partial slots per (sequence, query head)
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
+  typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+  u2_t v = {x, y};
+  return __builtin_bit_cast(h4_t, v);
+}
+
+__device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(x, y, c, 0, 0, 0);
+}
+
+// Value token tl (0..31 in its group) -> (k-step within the group, slot).
+template <int BITS>
+__device__ __forceinline__ void value_slot(int tl, int* kk, int* slot) {
+  if (BITS == 4) {
+    const int i = tl >> 3, r = tl & 7, j = r & 3, hp = r >> 2;
+    *kk = 2 * i + (j >> 1);
+    *slot = (j & 1) * 2 + hp;
+  } else {
+    const int i = tl >> 4, e = tl & 15, j = e & 7, hp = e >> 3;
+    *kk = 4 * i + (j >> 1);
+    *slot = (j & 1) * 2 + hp;
+  }
+}
+
+// hi + lo fp16 split of x (x - hi is exact in fp32)
+__device__ __forceinline__ void split_half(float x, _Float16* hi, _Float16* lo) {
+  *hi = (_Float16)x;
+  *lo = (_Float16)(x - (float)*hi);
+}
+
+// Online-softmax update of one head for one tile; returns p for this lane.
+template <int G, int HL, int NDG>
+__device__ __forceinline__ float softmax_step(int m, float s, bool tok_ok, float* m_run, float* l_acc,
+                                              f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3,
+                                              float (*zacc)[NDG]) {
+  if (__any(s > m_run[m])) {
+    const float mnew = fmaxf(m_run[m], wave_max64(s));
+    const float alpha = (m_run[m] == -INFINITY) ? 0.0f : exp2f(m_run[m] - mnew);
+    m_run[m] = mnew;
+    l_acc[m] *= alpha;
+    o0[m] *= alpha; o1[m] *= alpha; o2[m] *= alpha; o3[m] *= alpha;
+    if (HL == 1) {
+      o0[G + m] *= alpha; o1[G + m] *= alpha; o2[G + m] *= alpha; o3[G + m] *= alpha;
+    }
+    for (int d = 0; d < NDG; ++d) zacc[m][d] *= alpha;
+  }
+  const float p = tok_ok ? exp2f(s - m_run[m]) : 0.0f;
+  l_acc[m] += p;
+  return p;
+}
+
+// Raw bytes of one 64-token tile for this lane: its token's key row, the
+// value rows of channels lane and 64 + lane for both groups, the metadata of
+// its token / group.
+template <int BITS, bool BLOCK>
+struct TileRaw {
+  uint4 kc[BITS];
+  uint32_t vc[2][2][BITS];
+  uint2 km0, km1;   // KIVI, keys after RoPE: (s, z) of the key channels of this lane's k-step
+  uint4 kmr;        // KIVI, keys before RoPE: (s, z) of channels 4 (lane % 32) .. + 3
+  uint4 vm;         // KIVI: (s, z) x 4 of this lane's token
+  uint16_t ks16, vs16;   // BLOCK: per-token scales
+};
+
+struct TilePos {
+  int64_t base;
+  int nvalid;
+  uint32_t s0, s1;  // tile slots of the two groups
+  uint32_t grp0;
+};
+
+// Position of tile `it` of wave w in the work-group's chunk; false past the end.
+__device__ __forceinline__ bool tile_pos(const MfmaArgs& a, int64_t chunk_tok0, int it, int w,
+                                         int64_t slots, bool ring, TilePos& tp) {
+  tp.base = chunk_tok0 + ((int64_t)it * 4 + w) * 64;
+  if (it >= a.nt || tp.base >= a.t_hi) return false;
+  tp.nvalid = (int)min((int64_t)64, a.t_hi - tp.base);
+  tp.grp0 = (uint32_t)(tp.base >> 5);
+  tp.s0 = tp.grp0;
+  tp.s1 = tp.grp0 + 1;
+  if (ring) {
+    tp.s0 = tp.grp0 % (uint32_t)slots;
+    tp.s1 = (tp.s0 + 1 == (uint32_t)slots) ? 0 : tp.s0 + 1;
+  }
+  return true;
+}
+
+template <int BITS, bool BLOCK, bool ROPE>
+__device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos& tp, int lane,
+                                          const uint8_t* kpair, const uint8_t* vpair,
+                                          const uint8_t* kmpair, const uint8_t* vmpair,
+                                          const uint16_t* ksc, const uint16_t* vsc, int kch0,
+                                          int kch1) {
+  constexpr int TB = 512 * BITS;
+  constexpr int VROW = 4 * BITS;
+  const int gh = lane >> 5, tl = lane & 31;
+  const bool tok_ok = lane < tp.nvalid;
+  const bool grp1_ok = tp.nvalid > 32;
+  const uint32_t my_slot = gh ? tp.s1 : tp.s0;
+  const uint8_t* kt = kpair + (int64_t)my_slot * TB + tl * 16;
+  for (int j = 0; j < BITS; ++j)
+    r.kc[j] = tok_ok ? *reinterpret_cast<const uint4*>(kt + j * 512) : make_uint4(0, 0, 0, 0);
+  for (int gg = 0; gg < 2; ++gg) {
+    const bool ok = gg == 0 || grp1_ok;
+    const uint8_t* vt = vpair + (int64_t)(gg ? tp.s1 : tp.s0) * TB;
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint8_t* src = vt + (lane + 64 * hf) * VROW;
+      if (BITS == 4) {
+        const uint4 x = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y; r.vc[gg][hf][2] = x.z; r.vc[gg][hf][3] = x.w;
+      } else {
+        const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y;
+      }
+    }
+  }
+  if (BLOCK) {
+    const int64_t t = tp.base + lane;
+    r.ks16 = tok_ok ? ksc[t] : (uint16_t)0;
+    r.vs16 = tok_ok ? vsc[t] : (uint16_t)0;
+  } else {
+    const bool my_grp_ok = gh == 0 || grp1_ok;
+    const uint32_t my_grp = tp.grp0 + gh;
+    const uint8_t* kmeta = kmpair + (int64_t)my_grp * 512;
+    const uint8_t* vmeta = vmpair + (int64_t)my_grp * 512;
+    if (ROPE) {
+      r.kmr = my_grp_ok ? *reinterpret_cast<const uint4*>(kmeta + 16 * tl) : make_uint4(0, 0, 0, 0);
+    } else {
+      r.km0 = my_grp_ok ? *reinterpret_cast<const uint2*>(kmeta + 4 * kch0) : make_uint2(0, 0);
+      r.km1 = my_grp_ok ? *reinterpret_cast<const uint2*>(kmeta + 4 * kch1) : make_uint2(0, 0);
+    }
+    r.vm = tok_ok ? *reinterpret_cast<const uint4*>(vmeta + 16 * tl) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Per-token value scales / zeros of this lane's token from the raw tile.
+template <int BITS, bool BLOCK, int NDG>
+__device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, float* vs, float* vz) {
+  if (BLOCK) {
+    vs[0] = half_bits_to_float(r.vs16);
+    vz[0] = 0.0f;
+  } else {
+    const uint32_t vw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
+    for (int d = 0; d < 4; ++d) {
+      vs[d] = half_bits_to_float((uint16_t)(vw[d] & 0xFFFF));
+      vz[d] = half_bits_to_float((uint16_t)(vw[d] >> 16));
+    }
+  }
+}
+
+// p' = p s into this wave's value A table (PLw = PL[w]); zero-point sums.
+template <int G, int BITS, bool BLOCK, int HL, int NDG>
+__device__ __forceinline__ void stage_probs(const float* p, const float* vs, const float* vz,
+                                            _Float16 (*PLw)[16][HL][4][4], float (*zacc)[NDG],
+                                            int tl, int gh) {
+  int kk, slot;
+  value_slot<BITS>(tl, &kk, &slot);
+  const int ks = 8 * gh + kk;
+  for (int d = 0; d < NDG; ++d)
+    for (int m = 0; m < G; ++m) {
+      const float x = p[m] * vs[d];
+      _Float16 hi, lo;
+      split_half(x, &hi, &lo);
+      PLw[d][ks][0][m][slot] = hi;
+      if (HL == 1) PLw[d][ks][0][G + m][slot] = lo;
+      else PLw[d][ks][1][m][slot] = lo;
+      zacc[m][d] += BLOCK ? x : p[m] * vz[d];
+    }
+}
+
+// O += p' . codes over the tile's value rows: 16 k-steps x 2 halves.
+template <int G, int BITS, bool BLOCK, int HL, int NDG>
+__device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
+                                           _Float16 (*PLw)[16][HL][4][4], int row, int gh,
+                                           f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3) {
+  for (int gg = 0; gg < 2; ++gg) {
+    for (int hf = 0; hf < 2; ++hf) {
+      const int dg = BLOCK ? 0 : (gh + 2 * hf);
+      for (int u = 0; u < BITS; ++u) {
+        const uint32_t x = vc[gg][hf][u];
+        // unpack one dword: 8 tokens (4-bit) or 16 tokens (2-bit) as pairs
+        constexpr int NP = (BITS == 4) ? 4 : 8;
+        uint32_t pr[NP];
+        if (BITS == 4) {
+          pr[0] = x & 0x000F000Fu;
+          pr[1] = (x >> 4) & 0x000F000Fu;
+          pr[2] = (x >> 8) & 0x000F000Fu;
+          pr[3] = (x >> 12) & 0x000F000Fu;
+        } else {
+          for (int j = 0; j < 8; ++j) pr[j] = (x >> (2 * j)) & 0x00030003u;
+        }
+        for (int q2 = 0; q2 < NP / 2; ++q2) {
+          const int ks = 8 * gg + (NP / 2) * u + q2;   // k-step of pairs (2 q2, 2 q2 + 1)
+          const h4_t bv = as_h4(pr[2 * q2], pr[2 * q2 + 1]);
+          for (int hl = 0; hl < HL; ++hl) {
+            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][hl][row][0]);
+            if (hf == 0) {
+              if (q2 & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
+            } else {
+              if (q2 & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// fp16 window values: O += p . V over tokens [base, base + nvalid) of the
+// channel-major value ring, with p in natural token order in PLw[0] (k-step
+// lane/4, slot lane%4).  Halves of tokens past the window are zeroed (stale
+// ring slots may hold anything).
+template <int HL>
+__device__ __forceinline__ void window_value_mfma(const __half* vring, int64_t base, int nvalid,
+                                                  _Float16 (*PLw)[16][HL][4][4], int lane, int row,
+                                                  f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3) {
+  for (int kp = 0; kp < 8; ++kp) {    // 8 tokens (two k-steps) per load
+    const int64_t t0 = base + 8 * kp;
+    const int slot = (int)(t0 % kRing);
+    for (int hf = 0; hf < 2; ++hf) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (8 * kp < nvalid) {
+        x = *reinterpret_cast<const uint4*>(vring + (lane + 64 * hf) * kRing + slot);
+        const int left = nvalid - 8 * kp;
+        if (left < 8) {
+          uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+          for (int k = 0; k < 4; ++k) {
+            if (2 * k >= left) xw[k] = 0;
+            else if (2 * k + 1 >= left) xw[k] &= 0xFFFFu;
+          }
+          x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+        }
+      }
+      for (int hl = 0; hl < HL; ++hl) {
+        const h4_t a0 = *reinterpret_cast<const h4_t*>(&PLw[0][2 * kp][hl][row][0]);
+        const h4_t a1 = *reinterpret_cast<const h4_t*>(&PLw[0][2 * kp + 1][hl][row][0]);
+        if (hf == 0) {
+          o0 = mfma4(a0, as_h4(x.x, x.y), o0);
+          o2 = mfma4(a1, as_h4(x.z, x.w), o2);
+        } else {
+          o1 = mfma4(a0, as_h4(x.x, x.y), o1);
+          o3 = mfma4(a1, as_h4(x.z, x.w), o3);
+        }
+      }
+    }
+  }
+}
+
+// fp16 window probabilities in natural token order (k-step lane/4, slot lane%4).
+template <int G, int HL>
+__device__ __forceinline__ void stage_window_probs(const float* p, _Float16 (*PLw)[16][HL][4][4],
+                                                   int lane) {
+  for (int m = 0; m < G; ++m) {
+    _Float16 hi, lo;
+    split_half(p[m], &hi, &lo);
+    PLw[0][lane >> 2][0][m][lane & 3] = hi;
+    if (HL == 1) PLw[0][lane >> 2][0][G + m][lane & 3] = lo;
+    else PLw[0][lane >> 2][1][m][lane & 3] = lo;
+  }
+}
+
+// The wave's partial (m, l, o[128]) of each head into workspace slot `slot`.
+// `scale` multiplies the MFMA sums (2^24 for code B operands, 1 for fp16),
+// `add0` / `add1` are added to channels lane / 64 + lane of head m.
+template <int G, int HL>
+__device__ __forceinline__ void write_partial(const MfmaArgs& a, int b, int h, int64_t slot, int lane,
+                                              const float* m_run, const float* l_acc,
+                                              const f4_t& o0, const f4_t& o1, const f4_t& o2,
+                                              const f4_t& o3, float scale, const float* add0,
+                                              const float* add1) {
+  for (int m = 0; m < G; ++m) {
+    const float lsum = wave_sum64(l_acc[m]);
+    float* rec = a.ws + (((int64_t)b * a.g.Hq + h * G + m) * a.n_slots + slot) * kPartial;
+    const float a0 = (HL == 1) ? o0[m] + o0[G + m] + o2[m] + o2[G + m] : o0[m] + o2[m];
+    const float a1 = (HL == 1) ? o1[m] + o1[G + m] + o3[m] + o3[G + m] : o1[m] + o3[m];
+    rec[2 + lane] = a0 * scale + add0[m];
+    rec[2 + 64 + lane] = a1 * scale + add1[m];
+    if (lane == 0) {
+      rec[0] = m_run[m];
+      rec[1] = lsum;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kvq

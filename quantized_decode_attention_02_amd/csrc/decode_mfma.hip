@@ -1,4 +1,7 @@
-// Split-K decode over packed 4-bit / 2-bit tiles on the 4x4x4 fp16 MFMA.
+// Split-K decode over packed 4-bit / 2-bit tiles on the 4x4x4 fp16 MFMA, for
+// caches whose keys are stored after RoPE (or Hadamard-rotated).  Value side,
+// softmax, window values and partials are shared with decode_rope.hip
+// (decode_common.h).
 //
 // Sources cited here:
 //   [nalar]  "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
@@ -37,7 +40,7 @@
 // The fp16 window of a KIVI cache is one more work-group of the same launch:
 // keys and values are fp16 already (B operands as stored), the query
 // unrotated.  Each wave writes its own (m, l, o[128]) partial per query head.
-#include "kvq_device.h"
+#include "decode_common.h"
 
 // Tuning knobs (compile-time):
 //   KVQ_DECODE_PREFETCH   1: load tile i+1 into registers while tile i is
@@ -53,40 +56,6 @@
 
 namespace kvq {
 namespace {
-
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-struct MfmaArgs {
-  Geom g;
-  Planes p;
-  const __half* q;
-  float* ws;
-  float scale_log2;
-  int64_t t_lo, t_hi;   // token range of this launch; t_lo is 32-aligned
-  int nt;               // 64-token tiles per wave
-  int hi_tier;          // KIVI: tiles in the high-bit planes (ring) or low-bit
-  int64_t chunks;       // work-groups over [t_lo, t_hi)
-  int window;           // 1: one more work-group attends the fp16 window
-  int64_t slot_base;    // first partial slot of this launch
-  int64_t n_slots;      // partial slots per (sequence, query head)
-};
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
-  typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
-  u2_t v = {x, y};
-  return __builtin_bit_cast(h4_t, v);
-}
-
-__device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
-  return __builtin_amdgcn_mfma_f32_4x4x4f16(x, y, c, 0, 0, 0);
-}
 
 // Key k-step ks (0..31) covers four channels: slot s of the operands holds
 // channel ch[s], whose B value carries the factor 1/inv_f[s] (see the
@@ -105,110 +74,6 @@ __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
     const float f1 = (p1 == 1) ? 4.f : (p1 == 3) ? 64.f : (p1 == 5) ? 1.f : 16.f;   // p1 in {1,3,5,7}
     ch[0] = 16 * i + p0; ch[1] = 16 * i + p0 + 8; ch[2] = 16 * i + p1; ch[3] = 16 * i + p1 + 8;
     inv_f[0] = 1.0f / f0; inv_f[1] = 1.0f / f0; inv_f[2] = 1.0f / f1; inv_f[3] = 1.0f / f1;
-  }
-}
-
-// Value token tl (0..31 in its group) -> (k-step within the group, slot).
-template <int BITS>
-__device__ __forceinline__ void value_slot(int tl, int* kk, int* slot) {
-  if (BITS == 4) {
-    const int i = tl >> 3, r = tl & 7, j = r & 3, hp = r >> 2;
-    *kk = 2 * i + (j >> 1);
-    *slot = (j & 1) * 2 + hp;
-  } else {
-    const int i = tl >> 4, e = tl & 15, j = e & 7, hp = e >> 3;
-    *kk = 4 * i + (j >> 1);
-    *slot = (j & 1) * 2 + hp;
-  }
-}
-
-// hi + lo fp16 split of x (x - hi is exact in fp32)
-__device__ __forceinline__ void split_half(float x, _Float16* hi, _Float16* lo) {
-  *hi = (_Float16)x;
-  *lo = (_Float16)(x - (float)*hi);
-}
-
-// Online-softmax update of one head for one tile; returns p for this lane.
-template <int G, int HL, int NDG>
-__device__ __forceinline__ float softmax_step(int m, float s, bool tok_ok, float* m_run, float* l_acc,
-                                              f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3,
-                                              float (*zacc)[NDG]) {
-  if (__any(s > m_run[m])) {
-    const float mnew = fmaxf(m_run[m], wave_max64(s));
-    const float alpha = (m_run[m] == -INFINITY) ? 0.0f : exp2f(m_run[m] - mnew);
-    m_run[m] = mnew;
-    l_acc[m] *= alpha;
-    o0[m] *= alpha; o1[m] *= alpha; o2[m] *= alpha; o3[m] *= alpha;
-    if (HL == 1) {
-      o0[G + m] *= alpha; o1[G + m] *= alpha; o2[G + m] *= alpha; o3[G + m] *= alpha;
-    }
-    for (int d = 0; d < NDG; ++d) zacc[m][d] *= alpha;
-  }
-  const float p = tok_ok ? exp2f(s - m_run[m]) : 0.0f;
-  l_acc[m] += p;
-  return p;
-}
-
-// Raw bytes of one 64-token tile for this lane: its token's key row, the
-// value rows of channels lane and 64 + lane for both groups, the metadata of
-// its token / group.
-template <int BITS, bool BLOCK>
-struct TileRaw {
-  uint4 kc[BITS];
-  uint32_t vc[2][2][BITS];
-  uint2 km0, km1;   // KIVI: (s, z) of the key channels of this lane's k-step
-  uint4 vm;         // KIVI: (s, z) x 4 of this lane's token
-  uint16_t ks16, vs16;   // BLOCK: per-token scales
-};
-
-struct TilePos {
-  int64_t base;
-  int nvalid;
-  uint32_t s0, s1;  // tile slots of the two groups
-  uint32_t grp0;
-};
-
-template <int BITS, bool BLOCK>
-__device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos& tp, int lane,
-                                          const uint8_t* kpair, const uint8_t* vpair,
-                                          const uint8_t* kmpair, const uint8_t* vmpair,
-                                          const uint16_t* ksc, const uint16_t* vsc, int kch0,
-                                          int kch1) {
-  constexpr int TB = 512 * BITS;
-  constexpr int VROW = 4 * BITS;
-  const int gh = lane >> 5, tl = lane & 31;
-  const bool tok_ok = lane < tp.nvalid;
-  const bool grp1_ok = tp.nvalid > 32;
-  const uint32_t my_slot = gh ? tp.s1 : tp.s0;
-  const uint8_t* kt = kpair + (int64_t)my_slot * TB + tl * 16;
-  for (int j = 0; j < BITS; ++j)
-    r.kc[j] = tok_ok ? *reinterpret_cast<const uint4*>(kt + j * 512) : make_uint4(0, 0, 0, 0);
-  for (int gg = 0; gg < 2; ++gg) {
-    const bool ok = gg == 0 || grp1_ok;
-    const uint8_t* vt = vpair + (int64_t)(gg ? tp.s1 : tp.s0) * TB;
-    for (int hf = 0; hf < 2; ++hf) {
-      const uint8_t* src = vt + (lane + 64 * hf) * VROW;
-      if (BITS == 4) {
-        const uint4 x = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y; r.vc[gg][hf][2] = x.z; r.vc[gg][hf][3] = x.w;
-      } else {
-        const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y;
-      }
-    }
-  }
-  if (BLOCK) {
-    const int64_t t = tp.base + lane;
-    r.ks16 = tok_ok ? ksc[t] : (uint16_t)0;
-    r.vs16 = tok_ok ? vsc[t] : (uint16_t)0;
-  } else {
-    const bool my_grp_ok = gh == 0 || grp1_ok;
-    const uint32_t my_grp = tp.grp0 + gh;
-    const uint8_t* kmeta = kmpair + (int64_t)my_grp * 512;
-    const uint8_t* vmeta = vmpair + (int64_t)my_grp * 512;
-    r.km0 = my_grp_ok ? *reinterpret_cast<const uint2*>(kmeta + 4 * kch0) : make_uint2(0, 0);
-    r.km1 = my_grp_ok ? *reinterpret_cast<const uint2*>(kmeta + 4 * kch1) : make_uint2(0, 0);
-    r.vm = tok_ok ? *reinterpret_cast<const uint4*>(vmeta + 16 * tl) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -307,61 +172,14 @@ void decode_mfma_kernel(MfmaArgs a) {
         const float s = tok_ok ? dv * unscale : -INFINITY;
         p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
       }
-      // probabilities in natural token order: k-step lane/4, slot lane%4
-      for (int m = 0; m < G; ++m) {
-        _Float16 hi, lo;
-        split_half(p[m], &hi, &lo);
-        PL[w][0][lane >> 2][0][m][lane & 3] = hi;
-        if (HL == 1) PL[w][0][lane >> 2][0][G + m][lane & 3] = lo;
-        else PL[w][0][lane >> 2][1][m][lane & 3] = lo;
-      }
+      stage_window_probs<G, HL>(p, PL[w], lane);
       wave_sync();
       const __half* vring = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
-      for (int kp = 0; kp < 8; ++kp) {    // 8 tokens (two k-steps) per load
-        const int64_t t0 = base + 8 * kp;
-        const int slot = (int)(t0 % kRing);
-        for (int hf = 0; hf < 2; ++hf) {
-          uint4 x = make_uint4(0, 0, 0, 0);
-          if (8 * kp < nvalid) {
-            x = *reinterpret_cast<const uint4*>(vring + (lane + 64 * hf) * kRing + slot);
-            // zero the halves of tokens past the window (stale ring slots)
-            const int left = nvalid - 8 * kp;
-            if (left < 8) {
-              uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-              for (int k = 0; k < 4; ++k) {
-                if (2 * k >= left) xw[k] = 0;
-                else if (2 * k + 1 >= left) xw[k] &= 0xFFFFu;
-              }
-              x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-            }
-          }
-          for (int hl = 0; hl < HL; ++hl) {
-            const h4_t a0 = *reinterpret_cast<const h4_t*>(&PL[w][0][2 * kp][hl][row][0]);
-            const h4_t a1 = *reinterpret_cast<const h4_t*>(&PL[w][0][2 * kp + 1][hl][row][0]);
-            if (hf == 0) {
-              o0 = mfma4(a0, as_h4(x.x, x.y), o0);
-              o2 = mfma4(a1, as_h4(x.z, x.w), o2);
-            } else {
-              o1 = mfma4(a0, as_h4(x.x, x.y), o1);
-              o3 = mfma4(a1, as_h4(x.z, x.w), o3);
-            }
-          }
-        }
-      }
+      window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
     }
-    const int64_t slot = a.slot_base + a.chunks * 4 + w;
-    for (int m = 0; m < G; ++m) {
-      const float lsum = wave_sum64(l_acc[m]);
-      float* rec = a.ws + (((int64_t)b * g.Hq + h * G + m) * a.n_slots + slot) * kPartial;
-      const float v0 = (HL == 1) ? o0[m] + o0[G + m] + o2[m] + o2[G + m] : o0[m] + o2[m];
-      const float v1 = (HL == 1) ? o1[m] + o1[G + m] + o3[m] + o3[G + m] : o1[m] + o3[m];
-      rec[2 + lane] = v0;
-      rec[2 + 64 + lane] = v1;
-      if (lane == 0) {
-        rec[0] = m_run[m];
-        rec[1] = lsum;
-      }
-    }
+    const float zero[G] = {};
+    write_partial<G, HL>(a, b, h, a.slot_base + a.chunks * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
+                         1.0f, zero, zero);
     return;
   }
 
@@ -410,34 +228,21 @@ void decode_mfma_kernel(MfmaArgs a) {
   const uint16_t* ksc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
   const uint16_t* vsc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
 
-  auto tile_pos = [&](int it, TilePos& tp) -> bool {
-    tp.base = chunk_tok0 + ((int64_t)it * 4 + w) * 64;
-    if (it >= a.nt || tp.base >= a.t_hi) return false;
-    tp.nvalid = (int)min((int64_t)64, a.t_hi - tp.base);
-    tp.grp0 = (uint32_t)(tp.base >> 5);
-    tp.s0 = tp.grp0;
-    tp.s1 = tp.grp0 + 1;
-    if (ring) {
-      tp.s0 = tp.grp0 % (uint32_t)slots;
-      tp.s1 = (tp.s0 + 1 == (uint32_t)slots) ? 0 : tp.s0 + 1;
-    }
-    return true;
-  };
   TilePos cur_pos, nxt_pos;
   TileRaw<BITS, BLOCK> cur, nxt;
-  bool have = tile_pos(0, cur_pos);
+  bool have = tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
   if (KVQ_DECODE_PREFETCH && have)
-    load_tile<BITS, BLOCK>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
+    load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
   for (int it = 0; have; ++it) {
     bool have_next;
     if (KVQ_DECODE_PREFETCH) {
       // prefetch the next tile of this wave before working on the current one
-      have_next = tile_pos(it + 1, nxt_pos);
+      have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
       if (have_next)
-        load_tile<BITS, BLOCK>(nxt, nxt_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
+        load_tile<BITS, BLOCK, false>(nxt, nxt_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
     } else {
-      load_tile<BITS, BLOCK>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
-      have_next = tile_pos(it + 1, nxt_pos);
+      load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
+      have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
     }
     const int64_t base = cur_pos.base;
     const int nvalid = cur_pos.nvalid;
@@ -445,19 +250,9 @@ void decode_mfma_kernel(MfmaArgs a) {
     const uint4* kc = cur.kc;
     const uint32_t (*vc)[2][BITS] = cur.vc;
     float vs[NDG], vz[NDG];
-    float kscale = 0.0f;
+    value_meta<BITS, BLOCK, NDG>(cur, vs, vz);
+    const float kscale = BLOCK ? half_bits_to_float(cur.ks16) : 0.0f;
     const uint2 km0 = cur.km0, km1 = cur.km1;
-    if (BLOCK) {
-      kscale = half_bits_to_float(cur.ks16);
-      vs[0] = half_bits_to_float(cur.vs16);
-      vz[0] = 0.0f;
-    } else {
-      const uint32_t vw[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
-      for (int d = 0; d < 4; ++d) {
-        vs[d] = half_bits_to_float((uint16_t)(vw[d] & 0xFFFF));
-        vz[d] = half_bits_to_float((uint16_t)(vw[d] >> 16));
-      }
-    }
     (void)base;
 
     // ---------------- KIVI: query table of my group (k-step tl)
@@ -540,56 +335,10 @@ void decode_mfma_kernel(MfmaArgs a) {
       p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
     }
 
-    // ---------------- p' = p s into the value A table; zero-point sums
-    {
-      int kk, slot;
-      value_slot<BITS>(tl, &kk, &slot);
-      const int ks = 8 * gh + kk;
-      for (int d = 0; d < NDG; ++d)
-        for (int m = 0; m < G; ++m) {
-          const float x = p[m] * vs[d];
-          _Float16 hi, lo;
-          split_half(x, &hi, &lo);
-          PL[w][d][ks][0][m][slot] = hi;
-          if (HL == 1) PL[w][d][ks][0][G + m][slot] = lo;
-          else PL[w][d][ks][1][m][slot] = lo;
-          zacc[m][d] += BLOCK ? x : p[m] * vz[d];
-        }
-    }
+    // ---------------- p' = p s into the value A table; values: O += p' . codes
+    stage_probs<G, BITS, BLOCK, HL, NDG>(p, vs, vz, PL[w], zacc, tl, gh);
     wave_sync();
-
-    // ---------------- values: O += p' . codes, 16 k-steps x 2 halves
-    for (int gg = 0; gg < 2; ++gg) {
-      for (int hf = 0; hf < 2; ++hf) {
-        const int dg = BLOCK ? 0 : (gh + 2 * hf);
-        for (int u = 0; u < BITS; ++u) {
-          const uint32_t x = vc[gg][hf][u];
-          // unpack one dword: 8 tokens (4-bit) or 16 tokens (2-bit) as pairs
-          constexpr int NP = (BITS == 4) ? 4 : 8;
-          uint32_t pr[NP];
-          if (BITS == 4) {
-            pr[0] = x & 0x000F000Fu;
-            pr[1] = (x >> 4) & 0x000F000Fu;
-            pr[2] = (x >> 8) & 0x000F000Fu;
-            pr[3] = (x >> 12) & 0x000F000Fu;
-          } else {
-            for (int j = 0; j < 8; ++j) pr[j] = (x >> (2 * j)) & 0x00030003u;
-          }
-          for (int q2 = 0; q2 < NP / 2; ++q2) {
-            const int ks = 8 * gg + (NP / 2) * u + q2;   // k-step of pairs (2 q2, 2 q2 + 1)
-            const h4_t bv = as_h4(pr[2 * q2], pr[2 * q2 + 1]);
-            for (int hl = 0; hl < HL; ++hl) {
-              const h4_t av = *reinterpret_cast<const h4_t*>(&PL[w][dg][ks][hl][row][0]);
-              if (hf == 0) {
-                if (q2 & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
-              } else {
-                if (q2 & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
-              }
-            }
-          }
-        }
-      }
-    }
+    value_mfma<G, BITS, BLOCK, HL, NDG>(vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
     if (KVQ_DECODE_PREFETCH) cur = nxt;
     cur_pos = nxt_pos;
@@ -597,29 +346,15 @@ void decode_mfma_kernel(MfmaArgs a) {
   }
 
   // ---------------- epilogue: per-head partial of this wave
-  const int64_t slot = a.slot_base + chunk * 4 + w;
+  float add0[G], add1[G];
   for (int m = 0; m < G; ++m) {
-    const float lsum = wave_sum64(l_acc[m]);
     float zsum[NDG];
     for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-    float* rec = a.ws + (((int64_t)b * g.Hq + h * G + m) * a.n_slots + slot) * kPartial;
-    const float a0 = (HL == 1) ? o0[m] + o0[G + m] + o2[m] + o2[G + m] : o0[m] + o2[m];
-    const float a1 = (HL == 1) ? o1[m] + o1[G + m] + o3[m] + o3[G + m] : o1[m] + o3[m];
-    float v0, v1;
-    if (BLOCK) {
-      v0 = a0 * 16777216.0f - 8.0f * zsum[0];
-      v1 = a1 * 16777216.0f - 8.0f * zsum[0];
-    } else {
-      v0 = a0 * 16777216.0f + zsum[gh];
-      v1 = a1 * 16777216.0f + zsum[gh + 2];
-    }
-    rec[2 + lane] = v0;
-    rec[2 + 64 + lane] = v1;
-    if (lane == 0) {
-      rec[0] = m_run[m];
-      rec[1] = lsum;
-    }
+    add0[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh];
+    add1[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
   }
+  write_partial<G, HL>(a, b, h, a.slot_base + chunk * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
+                       16777216.0f, add0, add1);
 }
 
 }  // namespace
@@ -636,6 +371,7 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
     a.q = q;
     a.ws = ws;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.q_pos = 0;
     a.t_lo = rp.t_lo;
     a.t_hi = rp.t_hi;
     a.nt = rp.nt;

@@ -1,0 +1,297 @@
+// Split-K decode for KIVI caches whose keys are stored before RoPE.
+//
+// Sources cited here:
+//   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
+//              ultra-long context" (troisinh.com).
+//   [nalar]    "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
+//              (nalar.dev).
+//
+// Keys are quantized per channel before the rotary embedding and rotated at
+// attention time ([troisinh] "Ý tưởng cốt lõi", "RoPE — Cái bẫy tinh vi";
+// "Tại sao nó hoạt động", item 3).  Split-half RoPE rotates each channel pair
+// (j, j + 64) of the key at position t by t * theta_j.  With the query at
+// q_pos rotated the same way, the score of token t is
+//     s_t = (R(q_pos) q) . (R(t) k_t) = (R(-t0) R(q_pos) q) . (R(t - t0) k_t)
+// for any t0.  Here t0 is the first token of the key's 32-token group: the
+// query is rotated once per group, every key by its offset d = t - t0 < 32,
+// with cos / sin from rows 0..31 of the cache's RoPE table (fp64-derived).
+//
+// Precision decides the arithmetic.  Per-channel outliers (the reason keys
+// are quantized per channel) make single terms of the score large, so the
+// rotated key and the query enter the contraction in fp32: the key is
+// dequantized and rotated in fp32 on the VALU (x = n s + z, then the 2 x 2
+// rotation of each pair) and contracted on the fp32 4x4x1 MFMA (16 blocks;
+// lane 4b + n of block b is token column n, rows are query heads, one
+// channel per instruction).  An fp16 key or query would put a 2^-11 relative
+// error on an outlier channel's term ([nalar] "Error pada key mengubah input
+// softmax").  Values, softmax, window and partials are those of the other
+// MFMA decode (decode_common.h).
+#include "decode_common.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ f4_t mfma1(float x, float y, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(x, y, c, 0, 0, 0);
+}
+
+// Codes of one key row as floats, channels [8 i, 8 i + 8) (4-bit word i) or
+// [16 i, 16 i + 16) (2-bit word i), in channel order.
+template <int BITS>
+__device__ __forceinline__ void unpack_word(uint32_t w, float* n) {
+  if (BITS == 4) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    for (int k = 0; k < 4; ++k) {
+      n[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
+      n[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
+    }
+  } else {
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t c = (w >> (2 * r)) & 0x03030303u;
+      for (int k = 0; k < 4; ++k) n[4 * k + r] = (float)((c >> (8 * k)) & 0xFFu);
+    }
+  }
+}
+
+template <int G, int BITS>
+__global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
+  constexpr int HL = (G <= 2) ? 1 : 2;   // value-side MFMAs per k-step (hi/lo of p')
+  constexpr int NDG = 4;                 // value scale groups per token
+  constexpr int TB = 512 * BITS;         // tile bytes
+  constexpr int CPW = 32 / BITS;         // channels per code word
+  const Geom& g = a.g;
+  __shared__ float qs[G][kD];                                      // R(q_pos) q, scaled
+  __shared__ __attribute__((aligned(16))) float DT[32][32][4];     // [j / 2][d]: cos, sin of j, j + 1
+  __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD];   // [wave][group][head][channel]
+  __shared__ __attribute__((aligned(16))) float KSZ[4][2][64][4];  // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
+  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t chunk = blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t pair = pair_index(g, b, h);
+  const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
+  const bool win = a.window && chunk == a.chunks;   // the fp16 window work-group
+  const float* rope_tab = reinterpret_cast<const float*>(a.p.p[KVQ_PLANE_ROPE]);
+
+  // ---------------- prologue: R(q_pos) q with fp64 angles; offset table
+  if (tid < 64) {
+    const double theta = pow((double)g.rope_theta, -2.0 * (double)tid / 128.0);
+    const double ang = (double)a.q_pos * theta;
+    const float c = (float)cos(ang), s = (float)sin(ang);
+    for (int m = 0; m < G; ++m) {
+      const int64_t qb = ((int64_t)b * g.Hq + h * G + m) * kD;
+      const float x = __half2float(a.q[qb + tid]), y = __half2float(a.q[qb + tid + 64]);
+      qs[m][tid] = (x * c - y * s) * a.scale_log2;
+      qs[m][tid + 64] = (x * s + y * c) * a.scale_log2;
+    }
+  }
+  // rows 0..31 of the RoPE table: the plane always holds at least 32 rows;
+  // rows at or past the cache length are only used for masked tokens
+  for (int e = tid; e < 32 * 32; e += 256) {
+    const int jp = e >> 5, d = e & 31;
+    *reinterpret_cast<float4*>(&DT[jp][d][0]) = *reinterpret_cast<const float4*>(rope_tab + d * 128 + 4 * jp);
+  }
+  for (int e = tid; e < (int)(sizeof(QA) / 4); e += 256) (&QA[0][0][0][0])[e] = 0.0f;
+  for (int e = tid; e < (int)(sizeof(PL) / 2); e += 256) (&PL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
+  __syncthreads();
+
+  // query tables of the two groups of a tile (group starts t0 and t0 + 32):
+  // u = R(-t0) qs, lane j writes channels j and j + 64 of every head
+  auto build_query = [&](int64_t t0, bool second) {
+    for (int gg = 0; gg < 2; ++gg) {
+      const int64_t t = (gg && second) ? t0 + 32 : t0;
+      const float2 cs = *reinterpret_cast<const float2*>(rope_tab + t * 128 + 2 * lane);
+      for (int m = 0; m < G; ++m) {
+        const float x = qs[m][lane], y = qs[m][lane + 64];
+        QA[w][gg][m][lane] = x * cs.x + y * cs.y;
+        QA[w][gg][m][lane + 64] = y * cs.x - x * cs.y;
+      }
+    }
+    wave_sync();
+  };
+
+  float m_run[G], l_acc[G];
+  float zacc[G][NDG];
+  for (int m = 0; m < G; ++m) {
+    m_run[m] = -INFINITY;
+    l_acc[m] = 0.0f;
+    for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
+  }
+  f4_t o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0}, o2 = {0, 0, 0, 0}, o3 = {0, 0, 0, 0};
+
+  // Scores of this lane's token from its 128 key values x_c (fp32), rotated
+  // by d = tl: four accumulator chains, one MFMA per channel.
+  auto score_pairs = [&](const float* xl, const float* xh, int j0, int np, f4_t* acc) {
+    for (int k = 0; k < np; k += 2) {
+      const int j = j0 + k;
+      const float4 cs = *reinterpret_cast<const float4*>(&DT[j >> 1][tl][0]);
+      const float4 qa = *reinterpret_cast<const float4*>(&QA[w][gh][row][j & ~3]);
+      const float4 qb = *reinterpret_cast<const float4*>(&QA[w][gh][row][64 + (j & ~3)]);
+      const float qal[4] = {qa.x, qa.y, qa.z, qa.w}, qbl[4] = {qb.x, qb.y, qb.z, qb.w};
+      for (int e = 0; e < 2; ++e) {
+        const float c = e ? cs.z : cs.x, s = e ? cs.w : cs.y;
+        const float x = xl[k + e], y = xh[k + e];
+        const float rl = x * c - y * s, rh = x * s + y * c;
+        acc[2 * e] = mfma1(qal[(j + e) & 3], rl, acc[2 * e]);
+        acc[2 * e + 1] = mfma1(qbl[(j + e) & 3], rh, acc[2 * e + 1]);
+      }
+    }
+  };
+
+  if (win) {
+    // ================= fp16 window: tokens [Tq, length), wave w takes tile w
+    const int64_t base = g.Tq + 64 * (int64_t)w;
+    if (base < g.length) {
+      const int nvalid = (int)min((int64_t)64, g.length - base);
+      build_query(base, nvalid > 32);
+      const bool tok_ok = lane < nvalid;
+      const __half* krow = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_K_WIN]) +
+                           (pair * kRing + (base + lane) % kRing) * kD;
+      f4_t acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+      for (int i = 0; i < 8; ++i) {   // channels 8i..8i+7 and 64 + 8i..
+        float xl[8], xh[8];
+        const uint4 lo = tok_ok ? *reinterpret_cast<const uint4*>(krow + 8 * i) : make_uint4(0, 0, 0, 0);
+        const uint4 hi = tok_ok ? *reinterpret_cast<const uint4*>(krow + 64 + 8 * i) : make_uint4(0, 0, 0, 0);
+        const __half* hl = reinterpret_cast<const __half*>(&lo);
+        const __half* hh = reinterpret_cast<const __half*>(&hi);
+        for (int e = 0; e < 8; ++e) {
+          xl[e] = __half2float(hl[e]);
+          xh[e] = __half2float(hh[e]);
+        }
+        score_pairs(xl, xh, 8 * i, 8, acc);
+      }
+      float p[G];
+      for (int m = 0; m < G; ++m) {
+        const float s = tok_ok ? (acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m]) : -INFINITY;
+        p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
+      }
+      stage_window_probs<G, HL>(p, PL[w], lane);
+      wave_sync();
+      const __half* vring = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
+      window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
+    }
+    const float zero[G] = {};
+    write_partial<G, HL>(a, b, h, a.slot_base + a.chunks * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
+                         1.0f, zero, zero);
+    return;
+  }
+
+  // ================= quantized tiles
+  const int64_t chunk_tok0 = a.t_lo + chunk * 4 * a.nt * 64;
+  const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
+  const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
+  const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
+  const bool ring = slots != g.gmax;
+  const uint8_t* kpair = kplane + pair * slots * TB;
+  const uint8_t* vpair = vplane + pair * slots * TB;
+  const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
+  const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
+
+  TilePos cur_pos, nxt_pos;
+  TileRaw<BITS, false> cur;
+  bool have = tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
+  for (int it = 0; have; ++it) {
+    load_tile<BITS, false, true>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, nullptr, nullptr, 0, 0);
+    const bool have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
+    const int nvalid = cur_pos.nvalid;
+    const bool tok_ok = lane < nvalid;
+    float vs[NDG], vz[NDG];
+    value_meta<BITS, false, NDG>(cur, vs, vz);
+
+    // key (s, z) of both groups into KSZ (channel c -> pair c mod 64, half c / 64)
+    {
+      const uint32_t mw[4] = {cur.kmr.x, cur.kmr.y, cur.kmr.z, cur.kmr.w};
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * tl + e;
+        KSZ[w][gh][c & 63][c >> 6] = half_bits_to_float((uint16_t)(mw[e] & 0xFFFF));
+        KSZ[w][gh][c & 63][2 + (c >> 6)] = half_bits_to_float((uint16_t)(mw[e] >> 16));
+      }
+    }
+    build_query(cur_pos.base, nvalid > 32);   // its wave barrier also covers KSZ
+
+    // ---------------- scores
+    f4_t acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    uint32_t kw[4 * BITS];
+    for (int j = 0; j < BITS; ++j) {
+      kw[4 * j] = cur.kc[j].x; kw[4 * j + 1] = cur.kc[j].y;
+      kw[4 * j + 2] = cur.kc[j].z; kw[4 * j + 3] = cur.kc[j].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; ++i) {   // words of channels [CPW i, CPW (i + 1)) and 64 + ...
+      float nl[CPW], nh[CPW], xl[CPW], xh[CPW];
+      unpack_word<BITS>(kw[i], nl);
+      unpack_word<BITS>(kw[i + 2 * BITS], nh);
+      for (int k = 0; k < CPW; ++k) {
+        const float4 sz = *reinterpret_cast<const float4*>(&KSZ[w][gh][CPW * i + k][0]);
+        xl[k] = nl[k] * sz.x + sz.z;   // exact product, one rounding
+        xh[k] = nh[k] * sz.y + sz.w;
+      }
+      score_pairs(xl, xh, CPW * i, CPW, acc);
+    }
+    float p[G];
+    for (int m = 0; m < G; ++m) {
+      const float s = tok_ok ? (acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m]) : -INFINITY;
+      p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
+    }
+
+    // ---------------- values
+    stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PL[w], zacc, tl, gh);
+    wave_sync();
+    value_mfma<G, BITS, false, HL, NDG>(cur.vc, PL[w], row, gh, o0, o1, o2, o3);
+    wave_sync();
+    cur_pos = nxt_pos;
+    have = have_next;
+  }
+
+  float add0[G], add1[G];
+  for (int m = 0; m < G; ++m) {
+    float zsum[NDG];
+    for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
+    add0[m] = zsum[gh];
+    add1[m] = zsum[gh + 2];
+  }
+  write_partial<G, HL>(a, b, h, a.slot_base + chunk * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
+                       16777216.0f, add0, add1);
+}
+
+}  // namespace
+
+hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
+                              int64_t q_pos, float sm_scale, float* ws, hipStream_t s) {
+  for (int r = 0; r < cp.nr; ++r) {
+    const RangePlan& rp = cp.r[r];
+    const int window = rp.window;
+    if (rp.chunks == 0 && !window) continue;
+    MfmaArgs a;
+    a.g = g;
+    a.p = p;
+    a.q = q;
+    a.ws = ws;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.q_pos = q_pos;
+    a.t_lo = rp.t_lo;
+    a.t_hi = rp.t_hi;
+    a.nt = rp.nt;
+    a.hi_tier = rp.hi_tier;
+    a.chunks = rp.chunks;
+    a.window = window;
+    a.slot_base = rp.slot_base;
+    a.n_slots = cp.n;
+    const dim3 grid((unsigned)(rp.chunks + window), g.Hkv, g.B), block(256);
+#define KVQ_RP(GG, BB) hipLaunchKernelGGL((decode_rope_kernel<GG, BB>), grid, block, 0, s, a)
+    if (rp.bits == 4) {
+      if (g.G == 1) KVQ_RP(1, 4);
+      else if (g.G == 2) KVQ_RP(2, 4);
+      else KVQ_RP(4, 4);
+    } else {
+      if (g.G == 1) KVQ_RP(1, 2);
+      else if (g.G == 2) KVQ_RP(2, 2);
+      else KVQ_RP(4, 2);
+    }
+#undef KVQ_RP
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -153,30 +153,16 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 
 }  // namespace
 
-// Split-K plan.  MFMA path: the quantized tokens form up to two ranges of one
-// code width each (low-bit tier, high-bit tier); a wave streams nt tiles of
-// 64 tokens and a work-group of 4 waves covers 4 * nt tiles, with nt chosen
-// so that a call launches on the order of 16K waves; the fp16 window rides
-// on the last launch as one more work-group.  Pre-RoPE path: chunks of gpc
-// key groups, a few thousand work-groups, the window one more chunk.
+// Split-K plan: the quantized tokens form up to two ranges of one code width
+// each (low-bit tier, high-bit tier); a wave streams nt tiles of 64 tokens and
+// a work-group of 4 waves covers 4 * nt tiles, with nt chosen so that a call
+// launches on the order of 16K waves; the fp16 window rides on the last
+// launch as one more work-group.
 ChunkPlan plan_chunks(const Geom& g) {
   ChunkPlan cp;
   cp.nr = 0;
-  cp.gpc = 0;
   const int64_t pairs = (int64_t)g.B * g.Hkv;
   const bool window = g.scheme == KVQ_KIVI_ASYM && g.length > g.Tq;
-  if (g.pre_rope) {
-    cp.mode = 0;
-    const int64_t Gq = (g.Tq + kGroup - 1) / kGroup;
-    int64_t gpc = (Gq * pairs + 2047) / 2048;
-    if (gpc < 4) gpc = 4;
-    if (gpc > 64) gpc = 64;
-    cp.gpc = gpc;
-    cp.nq = Gq > 0 ? (Gq + gpc - 1) / gpc : 0;
-    cp.n = cp.nq + (window ? 1 : 0);
-    return cp;
-  }
-  cp.mode = 1;
   const int64_t lo_end = g.scheme == KVQ_KIVI_ASYM ? g.hi_start : 0;
   if (lo_end > 0) cp.r[cp.nr++] = RangePlan{0, lo_end, g.lo_bits, 0, 1, 0, 0, 0};
   if (g.Tq > lo_end || window) cp.r[cp.nr++] = RangePlan{lo_end, g.Tq, g.hi_bits, 1, 1, 0, 0, 0};

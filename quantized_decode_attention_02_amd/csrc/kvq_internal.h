@@ -46,14 +46,11 @@ struct RangePlan {
                        // after its chunks' slots)
 };
 
-// Split-K plan of one decode call.  Mode 1 (MFMA kernel): quantized tokens as
-// up to two tier-pure ranges, each wave writing one partial slot; the fp16
-// window is one more work-group of the last range's launch (4 slots).
-// Mode 0 (VALU kernel, pre-RoPE caches): chunks of gpc key groups, the fp16
-// window one more chunk (1 slot).  Slots [0, nq) hold quantized tokens.
+// Split-K plan of one decode call: quantized tokens as up to two tier-pure
+// ranges (one launch each), each wave writing one partial slot; the fp16
+// window is one more work-group of the last range's launch (4 slots).  Slots
+// [0, nq) hold quantized tokens.
 struct ChunkPlan {
-  int mode;
-  int64_t gpc;        // mode 0: key groups per chunk
   RangePlan r[2];
   int nr;
   int64_t nq;         // partial slots of quantized tokens
@@ -89,6 +86,8 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
                                   hipStream_t s);
 hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
                               float sm_scale, float* ws, hipStream_t s);
+hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
+                              int64_t q_pos, float sm_scale, float* ws, hipStream_t s);
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
                                hipStream_t s);
 hipError_t launch_dequant(const Geom& g, const Planes& p, int64_t t0, int64_t t1, float* k_out,
