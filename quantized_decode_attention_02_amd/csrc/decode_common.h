@@ -187,17 +187,102 @@ __device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos
   }
 }
 
-// Per-token value scales / zeros of this lane's token from the raw tile.
-template <int BITS, bool BLOCK, int NDG>
-__device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, float* vs, float* vz) {
+// ---------------------------------------------------------------------------
+// Tile staging.  A wave copies the code bytes of its next tile straight from
+// HBM into its own LDS stage with 16-byte global-to-LDS loads (lane l of one
+// load writes bytes [16 l, 16 l + 16) of a 1 KiB run), and the few metadata
+// bytes into registers, while it computes the current tile: a whole tile is
+// in flight during the compute.  Stage layout (TB = tile bytes of one group):
+//   [0, 2 TB)    key tiles of the two groups
+//   [2 TB, 4 TB) value tiles of the two groups
+// A second group past the tile's tokens is read from the first group's slot
+// (what it brings is never used), and block scales past the end of the
+// pair's region from inside it: every source lies inside the data.
+template <int BITS>
+constexpr int stage_bytes() {
+  return 4 * 512 * BITS;
+}
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_run) {
+  __builtin_amdgcn_global_load_lds(src, lds_run, 16, 0, 0);
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_issue(uint8_t* st, const TilePos& tp, int lane,
+                                            const uint8_t* kpair, const uint8_t* vpair) {
+  constexpr int TB = 512 * BITS;
+  const bool g1 = tp.nvalid > 32;
+  for (int gg = 0; gg < 2; ++gg) {
+    const int64_t slot = (gg && g1) ? tp.s1 : tp.s0;
+    for (int k = 0; k < TB / 1024; ++k) {
+      lds_dma16(kpair + slot * TB + k * 1024 + 16 * lane, st + gg * TB + k * 1024);
+      lds_dma16(vpair + slot * TB + k * 1024 + 16 * lane, st + 2 * TB + gg * TB + k * 1024);
+    }
+  }
+}
+
+// Metadata of the lane's token / group into registers (plain loads).
+template <int BITS, bool BLOCK, bool ROPE>
+__device__ __forceinline__ void meta_issue(TileRaw<BITS, BLOCK>& r, const TilePos& tp, int lane,
+                                           const uint8_t* kmpair, const uint8_t* vmpair,
+                                           const uint16_t* ksc, const uint16_t* vsc, int64_t scale_end,
+                                           int kch0, int kch1) {
+  const int gh = lane >> 5, tl = lane & 31;
   if (BLOCK) {
-    vs[0] = half_bits_to_float(r.vs16);
+    int64_t t = tp.base + lane;
+    if (t >= scale_end) t = scale_end - 1;
+    r.ks16 = ksc[t];
+    r.vs16 = vsc[t];
+  } else {
+    const int64_t grp = tp.grp0 + ((gh && tp.nvalid > 32) ? 1 : 0);
+    const uint8_t* kmeta = kmpair + grp * 512;
+    if (ROPE) {
+      r.kmr = *reinterpret_cast<const uint4*>(kmeta + 16 * tl);
+    } else {
+      r.km0 = *reinterpret_cast<const uint2*>(kmeta + 4 * kch0);
+      r.km1 = *reinterpret_cast<const uint2*>(kmeta + 4 * kch1);
+    }
+    r.vm = *reinterpret_cast<const uint4*>(vmpair + grp * 512 + 16 * tl);
+  }
+}
+
+// This lane's codes from the staged tile (same contents as load_tile).
+template <int BITS, bool BLOCK>
+__device__ __forceinline__ void stage_read(TileRaw<BITS, BLOCK>& r, const uint8_t* st, int lane) {
+  constexpr int TB = 512 * BITS;
+  constexpr int VROW = 4 * BITS;
+  const int gh = lane >> 5, tl = lane & 31;
+  for (int j = 0; j < BITS; ++j) r.kc[j] = *reinterpret_cast<const uint4*>(st + gh * TB + j * 512 + tl * 16);
+  for (int gg = 0; gg < 2; ++gg)
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint8_t* src = st + 2 * TB + gg * TB + (lane + 64 * hf) * VROW;
+      if (BITS == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y; r.vc[gg][hf][2] = x.z; r.vc[gg][hf][3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y;
+      }
+    }
+}
+
+__device__ __forceinline__ void wait_stage_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_stage_read() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Per-token value scales / zeros of this lane's token from the raw tile.
+// Tokens past the tile get 0 (their probability is 0, and 0 * anything
+// non-finite would not be).
+template <int BITS, bool BLOCK, int NDG>
+__device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, bool tok_ok, float* vs,
+                                           float* vz) {
+  if (BLOCK) {
+    vs[0] = tok_ok ? half_bits_to_float(r.vs16) : 0.0f;
     vz[0] = 0.0f;
   } else {
     const uint32_t vw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
     for (int d = 0; d < 4; ++d) {
-      vs[d] = half_bits_to_float((uint16_t)(vw[d] & 0xFFFF));
-      vz[d] = half_bits_to_float((uint16_t)(vw[d] >> 16));
+      vs[d] = tok_ok ? half_bits_to_float((uint16_t)(vw[d] & 0xFFFF)) : 0.0f;
+      vz[d] = tok_ok ? half_bits_to_float((uint16_t)(vw[d] >> 16)) : 0.0f;
     }
   }
 }

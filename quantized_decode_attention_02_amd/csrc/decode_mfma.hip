@@ -43,12 +43,13 @@
 #include "decode_common.h"
 
 // Tuning knobs (compile-time):
-//   KVQ_DECODE_PREFETCH   1: load tile i+1 into registers while tile i is
-//                         processed (more bytes in flight, more VGPRs)
+//   KVQ_DECODE_STAGE      1: tiles reach registers through a per-wave LDS
+//                         stage filled by global-to-LDS loads one tile ahead
+//                         (decode_common.h); 0: plain loads of the current tile
 //   KVQ_DECODE_MIN_WAVES  minimum waves per SIMD the register allocation
 //                         must allow (0: compiler's choice)
-#ifndef KVQ_DECODE_PREFETCH
-#define KVQ_DECODE_PREFETCH 0
+#ifndef KVQ_DECODE_STAGE
+#define KVQ_DECODE_STAGE 1
 #endif
 #ifndef KVQ_DECODE_MIN_WAVES
 #define KVQ_DECODE_MIN_WAVES 0
@@ -93,8 +94,11 @@ void decode_mfma_kernel(MfmaArgs a) {
   const Geom& g = a.g;
   __shared__ float qs[G][kD];
   __shared__ float qmax_s;
-  __shared__ __attribute__((aligned(16))) _Float16 QL[4][2][32][HL][4][4];
+  // query tables: per wave and group half (KIVI, rebuilt per group); one
+  // table for the work-group (BLOCK, fixed for the chunk)
+  __shared__ __attribute__((aligned(16))) _Float16 QL[BLOCK ? 1 : 4][BLOCK ? 1 : 2][32][HL][4][4];
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
+  __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t chunk = blockIdx.x;
@@ -102,23 +106,72 @@ void decode_mfma_kernel(MfmaArgs a) {
   const int64_t pair = pair_index(g, b, h);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
   const bool win = a.window && chunk == a.chunks;   // the fp16 window work-group
+  auto QLw = QL[BLOCK ? 0 : w];
+  const int qh = BLOCK ? 0 : gh;
 
-  // ---------------- prologue: scaled (rotated unless window) queries, zero tables
-  for (int e = tid; e < G * kD; e += 256)
-    qs[e / kD][e % kD] = __half2float(a.q[((int64_t)b * g.Hq + h * G + e / kD) * kD + e % kD]);
+  // Wave 0 fetches the query into LDS before it requests its first tile;
+  // the other waves request theirs at once.  (The compiler waits for every
+  // global load, tile requests included, before a register loaded after one
+  // is used, so the query must not be loaded behind a tile.)
+  if (w == 0) {
+    for (int e = lane; e < G * kD; e += 64)
+      qs[e / kD][e % kD] = __half2float(a.q[((int64_t)b * g.Hq + h * G + e / kD) * kD + e % kD]);
+  }
+
+  // this lane writes key k-step ks = tl of the query table: four channels
+  int kch[4];
+  float kinv[4];
+  key_quad<BITS>(tl, kch, kinv);
+
+  const int64_t chunk_tok0 = a.t_lo + chunk * 4 * a.nt * 64;
+  const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
+  const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
+  const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
+  const bool ring = slots != g.gmax;
+  const uint8_t* kpair = kplane + pair * slots * TB;
+  const uint8_t* vpair = vplane + pair * slots * TB;
+  const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
+  const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
+  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
+  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
+
+  TilePos cur_pos, nxt_pos;
+  TileRaw<BITS, BLOCK> cur, nxt;
+  uint8_t* stage = ST[KVQ_DECODE_STAGE ? w : 0];
+  const int64_t scale_end = g.gmax * kGroup;
+  bool have = !win && tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
+  // The first tile is requested before the prologue, so its latency overlaps
+  // the query set-up.  The request is made by every wave, without a branch
+  // (a branch would make the query's use wait for it too): a wave without a
+  // tile fetches the range's first group instead and waits for it before
+  // leaving.
+  if (KVQ_DECODE_STAGE) {
+    TilePos first = cur_pos;
+    if (!have) {
+      first.base = a.t_lo;
+      first.nvalid = 1;
+      first.grp0 = (uint32_t)(a.t_lo >> 5);
+      first.s0 = first.s1 = ring ? first.grp0 % (uint32_t)slots : first.grp0;
+    }
+    stage_issue<BITS>(stage, first, lane, kpair, vpair);
+    meta_issue<BITS, BLOCK, false>(nxt, first, lane, kmpair, vmpair, ksc, vsc, scale_end, kch[0], kch[1]);
+  }
+
+  // ---------------- prologue: scaled (rotated unless window) queries, zero
+  // tables; LDS-only barriers, so the first tiles stay in flight
   for (int e = tid; e < (int)(sizeof(QL) / 2); e += 256) (&QL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
   for (int e = tid; e < (int)(sizeof(PL) / 2); e += 256) (&PL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
-  __syncthreads();
+  lds_barrier();
   if (g.hadamard && !win) fwht128_lds(&qs[0][0], G, tid, 256);
   for (int e = tid; e < G * kD; e += 256) (&qs[0][0])[e] *= a.scale_log2;
-  __syncthreads();
+  lds_barrier();
   if (tid < 64) {
     float mx = 0.0f;
     for (int e = lane; e < G * kD; e += 64) mx = fmaxf(mx, fabsf((&qs[0][0])[e]));
     mx = wave_max64(mx);
     if (lane == 0) qmax_s = mx;
   }
-  __syncthreads();
+  lds_barrier();
 
   float m_run[G], l_acc[G];
   float zacc[G][NDG];
@@ -142,9 +195,9 @@ void decode_mfma_kernel(MfmaArgs a) {
       _Float16 hi[4], lo[4];
       for (int i = 0; i < 4; ++i) split_half(ldexpf(qs[m][4 * tl + i], e_q), &hi[i], &lo[i]);
       const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-      *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][m][0]) = hv;
-      if (HL == 1) *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][G + m][0]) = lv;
-      else *reinterpret_cast<h4_t*>(&QL[w][gh][tl][1][m][0]) = lv;
+      *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][m][0]) = hv;
+      if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][G + m][0]) = lv;
+      else *reinterpret_cast<h4_t*>(&QLw[qh][tl][1][m][0]) = lv;
     }
     wave_sync();
     const int64_t base = g.Tq + 64 * (int64_t)w;
@@ -161,8 +214,8 @@ void decode_mfma_kernel(MfmaArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int ks = 8 * c + 2 * j;
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][gh][ks][hl][row][0]), as_h4(kr[j].x, kr[j].y), acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][gh][ks + 1][hl][row][0]), as_h4(kr[j].z, kr[j].w), acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), as_h4(kr[j].x, kr[j].y), acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks + 1][hl][row][0]), as_h4(kr[j].z, kr[j].w), acc1);
           }
         }
       }
@@ -180,14 +233,11 @@ void decode_mfma_kernel(MfmaArgs a) {
     const float zero[G] = {};
     write_partial<G, HL>(a, b, h, a.slot_base + a.chunks * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
                          1.0f, zero, zero);
+    if (KVQ_DECODE_STAGE) wait_stage_landed();
     return;
   }
 
   // ================= quantized tiles
-  // this lane writes key k-step ks = tl of the query table: four channels
-  int kch[4];
-  float kinv[4];
-  key_quad<BITS>(tl, kch, kinv);
   float qv[G][4];
   for (int m = 0; m < G; ++m)
     for (int i = 0; i < 4; ++i) qv[m][i] = qs[m][kch[i]];
@@ -205,41 +255,34 @@ void decode_mfma_kernel(MfmaArgs a) {
       for (int i = 0; i < 4; ++i) s += qv[m][i];
       qsum[m] = half_sum(s);   // the 32 lanes of a half cover all 128 channels
     }
-    for (int m = 0; m < G; ++m) {
-      _Float16 hi[4], lo[4];
-      for (int i = 0; i < 4; ++i) split_half(ldexpf(qv[m][i], e_blk) * kinv[i], &hi[i], &lo[i]);
-      const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-      *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][m][0]) = hv;
-      if (HL == 1) *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][G + m][0]) = lv;
-      else *reinterpret_cast<h4_t*>(&QL[w][gh][tl][1][m][0]) = lv;
+    if (w == 0 && gh == 0) {
+      for (int m = 0; m < G; ++m) {
+        _Float16 hi[4], lo[4];
+        for (int i = 0; i < 4; ++i) split_half(ldexpf(qv[m][i], e_blk) * kinv[i], &hi[i], &lo[i]);
+        const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<h4_t*>(&QLw[0][tl][0][m][0]) = hv;
+        if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[0][tl][0][G + m][0]) = lv;
+        else *reinterpret_cast<h4_t*>(&QLw[0][tl][1][m][0]) = lv;
+      }
     }
-    wave_sync();
+    lds_barrier();
   }
 
-  const int64_t chunk_tok0 = a.t_lo + chunk * 4 * a.nt * 64;
-  const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
-  const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
-  const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
-  const bool ring = slots != g.gmax;
-  const uint8_t* kpair = kplane + pair * slots * TB;
-  const uint8_t* vpair = vplane + pair * slots * TB;
-  const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
-  const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
-  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
-  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
-
-  TilePos cur_pos, nxt_pos;
-  TileRaw<BITS, BLOCK> cur, nxt;
-  bool have = tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
-  if (KVQ_DECODE_PREFETCH && have)
-    load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
   for (int it = 0; have; ++it) {
     bool have_next;
-    if (KVQ_DECODE_PREFETCH) {
-      // prefetch the next tile of this wave before working on the current one
+    if (KVQ_DECODE_STAGE) {
+      // this tile has landed: codes from the stage into registers, then the
+      // stage and the metadata registers are refilled with the next tile
+      // while this one is computed
+      wait_stage_landed();
+      stage_read<BITS, BLOCK>(cur, stage, lane);
+      cur.km0 = nxt.km0; cur.km1 = nxt.km1; cur.vm = nxt.vm; cur.ks16 = nxt.ks16; cur.vs16 = nxt.vs16;
       have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
-      if (have_next)
-        load_tile<BITS, BLOCK, false>(nxt, nxt_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
+      wait_stage_read();
+      if (have_next) {
+        stage_issue<BITS>(stage, nxt_pos, lane, kpair, vpair);
+        meta_issue<BITS, BLOCK, false>(nxt, nxt_pos, lane, kmpair, vmpair, ksc, vsc, scale_end, kch[0], kch[1]);
+      }
     } else {
       load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
       have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
@@ -250,7 +293,7 @@ void decode_mfma_kernel(MfmaArgs a) {
     const uint4* kc = cur.kc;
     const uint32_t (*vc)[2][BITS] = cur.vc;
     float vs[NDG], vz[NDG];
-    value_meta<BITS, BLOCK, NDG>(cur, vs, vz);
+    value_meta<BITS, BLOCK, NDG>(cur, tok_ok, vs, vz);
     const float kscale = BLOCK ? half_bits_to_float(cur.ks16) : 0.0f;
     const uint2 km0 = cur.km0, km1 = cur.km1;
     (void)base;
@@ -287,9 +330,9 @@ void decode_mfma_kernel(MfmaArgs a) {
         _Float16 hi[4], lo[4];
         for (int i = 0; i < 4; ++i) split_half(ldexpf(qp[m][i], e_grp) * kinv[i], &hi[i], &lo[i]);
         const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][m][0]) = hv;
-        if (HL == 1) *reinterpret_cast<h4_t*>(&QL[w][gh][tl][0][G + m][0]) = lv;
-        else *reinterpret_cast<h4_t*>(&QL[w][gh][tl][1][m][0]) = lv;
+        *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][m][0]) = hv;
+        if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][G + m][0]) = lv;
+        else *reinterpret_cast<h4_t*>(&QLw[qh][tl][1][m][0]) = lv;
       }
       wave_sync();
     }
@@ -307,8 +350,8 @@ void decode_mfma_kernel(MfmaArgs a) {
           const h4_t b0 = as_h4(x & 0x000F000Fu, x & 0x00F000F0u);
           const h4_t b1 = as_h4(x8 & 0x000F000Fu, x8 & 0x00F000F0u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][2 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][2 * i + 1][hl][row][0]), b1, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][2 * i][hl][row][0]), b0, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][2 * i + 1][hl][row][0]), b1, acc1);
           }
         } else {
           const uint32_t x10 = x >> 10;
@@ -317,10 +360,10 @@ void decode_mfma_kernel(MfmaArgs a) {
           const h4_t b2 = as_h4(x & 0x03000300u, x10 & 0x00030003u);
           const h4_t b3 = as_h4(x10 & 0x000C000Cu, x10 & 0x00300030u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][4 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][4 * i + 1][hl][row][0]), b1, acc1);
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][4 * i + 2][hl][row][0]), b2, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QL[w][qgh][4 * i + 3][hl][row][0]), b3, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i][hl][row][0]), b0, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 1][hl][row][0]), b1, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 2][hl][row][0]), b2, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 3][hl][row][0]), b3, acc1);
           }
         }
       }
@@ -340,10 +383,11 @@ void decode_mfma_kernel(MfmaArgs a) {
     wave_sync();
     value_mfma<G, BITS, BLOCK, HL, NDG>(vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
-    if (KVQ_DECODE_PREFETCH) cur = nxt;
     cur_pos = nxt_pos;
     have = have_next;
   }
+
+  if (KVQ_DECODE_STAGE) wait_stage_landed();   // a wave without tiles still has its request out
 
   // ---------------- epilogue: per-head partial of this wave
   float add0[G], add1[G];

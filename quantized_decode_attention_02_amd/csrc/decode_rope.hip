@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
     const int nvalid = cur_pos.nvalid;
     const bool tok_ok = lane < nvalid;
     float vs[NDG], vz[NDG];
-    value_meta<BITS, false, NDG>(cur, vs, vz);
+    value_meta<BITS, false, NDG>(cur, tok_ok, vs, vz);
 
     // key (s, z) of both groups into KSZ (channel c -> pair c mod 64, half c / 64)
     {

@@ -57,6 +57,15 @@ __host__ __device__ __forceinline__ int ktile_offset(int t, int cb) {
   return (cb >> 4) * 512 + t * 16 + (cb & 15);
 }
 
+// Work-group barrier for data exchanged through LDS only: each wave waits for
+// its own LDS operations, then all waves meet.  Unlike __syncthreads() it
+// does not wait for outstanding global loads (a tile still in flight to LDS
+// or registers stays in flight across it).  The "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Normalized FWHT-128 of `nvec` vectors stored as float rows of 128 in LDS,
 // in the fixed fp32 schedule: for h = 1, 2, ..., 64 in that order every pair
 // (x[i], x[i+h]) with bit log2(h) of i clear becomes (a + b, a - b), each one
@@ -64,7 +73,8 @@ __host__ __device__ __forceinline__ int ktile_offset(int t, int cb) {
 // H in Sylvester order is orthonormal after the scaling, so nothing is lost
 // and dot products are kept ([troisinh] "Tại sao nó hoạt động", item 2;
 // [trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót").
-// All threads of the block must call it; it synchronizes internally.
+// All threads of the block must call it; it synchronizes internally, on LDS
+// only (the vectors are exchanged through LDS and nothing else).
 __device__ __forceinline__ void fwht128_lds(float* x, int nvec, int tid, int nthreads) {
   for (int h = 1; h < kD; h <<= 1) {
     for (int i = tid; i < nvec * 64; i += nthreads) {
@@ -75,11 +85,11 @@ __device__ __forceinline__ void fwht128_lds(float* x, int nvec, int tid, int nth
       row[i0] = a + b;
       row[i0 + h] = a - b;
     }
-    __syncthreads();
+    lds_barrier();
   }
   const float c = c32();
   for (int i = tid; i < nvec * kD; i += nthreads) x[i] = x[i] * c;
-  __syncthreads();
+  lds_barrier();
 }
 
 // Cross-lane reductions without LDS round trips.
