@@ -149,8 +149,13 @@ kvq_status kvq_layout(const kvq_config* cfg, int64_t batch, int64_t max_tokens,
                       kvq_layout_t* out);
 
 /* Bytes of the device workspace kvq_decode_attn needs for `batch` sequences
- * of `length` cached tokens (split-K partials: running max, sum and 128
- * accumulators per query head and token chunk).  Writes *bytes. */
+ * of `length` cached tokens.  Writes *bytes.  The workspace starts with
+ * KVQ_COUNTER_BYTES(batch * num_kv_heads) bytes of work counters, which must
+ * be zero before the workspace is first used; every completed decode call
+ * leaves them zero again, so zero the workspace once when it is allocated.
+ * The split-K partials follow (running max, sum and 128 accumulators per
+ * query head and partial). */
+#define KVQ_COUNTER_BYTES(pairs) (2 * (uint64_t)(pairs) * 256)
 kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t length,
                                uint64_t* bytes);
 
@@ -185,7 +190,9 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
  *   q:   device fp16 [batch][num_q_heads][128] (before RoPE if pre_rope_keys)
  *   out: device fp32 [batch][num_q_heads][128]
  *   sm_scale <= 0 means 1/sqrt(128).
- *   workspace: device, >= kvq_workspace_bytes(cfg, batch, length).
+ *   workspace: device, >= kvq_workspace_bytes(cfg, batch, length), its
+ *              counters zero (see kvq_workspace_bytes).  Calls that overlap
+ *              in time must not share a workspace.
  * Accuracy: within |d| <= 2e-3 + 1e-2 |ref| of fp64 attention over the same
  * dequantized cache.  length == 0 writes zeros. */
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q,

@@ -124,7 +124,8 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
 
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
                                hipStream_t s) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(g.Hq, g.B), dim3(256), 0, s, g, ws, out, cp.nq, cp.n);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(g.Hq, g.B), dim3(256), 0, s, g, ws + cp.ctr_floats, out,
+                     cp.nq, cp.n);
   return hipGetLastError();
 }
 

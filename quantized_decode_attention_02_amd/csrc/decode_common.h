@@ -30,26 +30,68 @@ typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
+// One launch of a partials kernel: one token range of one code width.  The
+// range's tiles (64 tokens each) of pair p = (sequence, kv head) form
+// n_chunks chunks of `chunk` tiles, worked by a team of `team` waves that
+// claim them dynamically, so that a wave which runs faster (older waves win
+// issue priority on a SIMD; some XCDs see more fabric traffic) takes more of
+// them instead of finishing early:
+//   - assignment a in [0, pairs * team) is member k = a / pairs of the team
+//     of pair (a + k) mod pairs; the wave of rank r = w * pwgs + blockIdx.x
+//     - wins takes assignments r, r + 4 pwgs, ...  The skew spreads every team over
+//     all XCDs (blockIdx.x mod 8) and all dispatch rounds.
+//   - member k starts on chunk k; a claim on ctr[pair] returning c then
+//     hands out chunk team + c, if that is below n_chunks.  A member claims
+//     one chunk at a time and stops at its first failed claim, so a pair
+//     sees exactly n_chunks claims (n_chunks - team that succeed, team that
+//     fail); the one returning n_chunks - 1 is the last, and its wave puts
+//     the counter back to zero for the next call.
+//   - member k writes one partial, in slot slot_base + k.
+// The first `wins` work-groups attend the fp16 window, one per pair; they go
+// first so that they run beside the start of the tile work, not after it.
 struct MfmaArgs {
   Geom g;
   Planes p;
   const __half* q;
-  float* ws;
+  float* ws;            // partial records
+  uint32_t* ctr;        // chunk counters of this launch: pair p at p * kCounterStride (zero on entry and exit)
   float scale_log2;
   int64_t q_pos;        // query position (keys stored before RoPE)
   int64_t t_lo, t_hi;   // token range of this launch; t_lo is 32-aligned
-  int nt;               // 64-token tiles per wave
   int hi_tier;          // KIVI: tiles in the high-bit planes (ring) or low-bit
-  int64_t chunks;       // work-groups over [t_lo, t_hi)
-  int window;           // 1: one more work-group attends the fp16 window
-  int64_t slot_base;    // first partial slot of this launch
+  int64_t tiles_pp;     // tiles per (sequence, kv head)
+  int64_t pairs;        // sequences * kv heads
+  int64_t team;         // waves per pair; also the range's partial slots per query head
+  int64_t chunk;        // tiles per chunk
+  int64_t n_chunks;     // chunks per pair, >= team
+  int64_t pwgs;         // work-groups of the quantized tiles
+  int64_t slot_base;    // first partial slot of this range
+  int64_t wins;         // work-groups of the fp16 window (0 or pairs), launched first
+  int64_t win_slot;     // first of the window's 4 slots
   int64_t n_slots;      // partial slots per (sequence, query head)
 };
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// (pair, member) of assignment asg (asg < pairs * team).
+__device__ __forceinline__ void team_member(const MfmaArgs& a, int64_t asg, int64_t* pair,
+                                            int64_t* k) {
+  *k = asg / a.pairs;
+  *pair = (asg + *k) % a.pairs;
+}
+
+// Claims of chunks: lane 0 issues the atomic; the result stays in its
+// register until claim_value() (so the wave does not wait for it earlier).
+__device__ __forceinline__ uint32_t claim_issue(uint32_t* ctr, int lane) {
+  uint32_t v = 0;
+  if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+__device__ __forceinline__ int64_t claim_value(uint32_t v) {
+  return (int64_t)__builtin_amdgcn_readfirstlane(v);
+}
+// After a failed claim that returned `got` (the counter's old value): the
+// last claim of the pair puts its counter back to zero.
+__device__ __forceinline__ void claim_done(const MfmaArgs& a, uint32_t* ctr, int64_t got, int lane) {
+  if (got == a.n_chunks - 1 && lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
@@ -123,11 +165,10 @@ struct TilePos {
   uint32_t grp0;
 };
 
-// Position of tile `it` of wave w in the work-group's chunk; false past the end.
-__device__ __forceinline__ bool tile_pos(const MfmaArgs& a, int64_t chunk_tok0, int it, int w,
-                                         int64_t slots, bool ring, TilePos& tp) {
-  tp.base = chunk_tok0 + ((int64_t)it * 4 + w) * 64;
-  if (it >= a.nt || tp.base >= a.t_hi) return false;
+// Position of tile t (0 .. tiles_pp - 1) of a pair in the range.
+__device__ __forceinline__ void tile_at(const MfmaArgs& a, int64_t t, int64_t slots, bool ring,
+                                       TilePos& tp) {
+  tp.base = a.t_lo + t * 64;
   tp.nvalid = (int)min((int64_t)64, a.t_hi - tp.base);
   tp.grp0 = (uint32_t)(tp.base >> 5);
   tp.s0 = tp.grp0;
@@ -136,6 +177,48 @@ __device__ __forceinline__ bool tile_pos(const MfmaArgs& a, int64_t chunk_tok0, 
     tp.s0 = tp.grp0 % (uint32_t)slots;
     tp.s1 = (tp.s0 + 1 == (uint32_t)slots) ? 0 : tp.s0 + 1;
   }
+}
+
+// A wave's walk over the tiles of its assignments (see MfmaArgs).
+struct TileCursor {
+  int64_t asg;        // assignment
+  int64_t pair, k;    // its pair and member index
+  int64_t t, t_stop;  // tile, end of its chunk
+  uint32_t pend;      // the claim in flight
+};
+
+// First tile of assignment asg: the member's own chunk; its first claim
+// goes out at once.
+__device__ __forceinline__ void cursor_start(const MfmaArgs& a, int64_t asg, TileCursor& c, int lane) {
+  c.asg = asg;
+  team_member(a, asg, &c.pair, &c.k);
+  c.t = c.k * a.chunk;
+  c.t_stop = min(c.t + a.chunk, a.tiles_pp);
+  c.pend = claim_issue(a.ctr + c.pair * kCounterStride, lane);
+}
+
+// Moves c to the tile after the current one.  *ends: the current tile was
+// the last of its assignment (its partial is due).  Returns false when the
+// wave has no tile left.
+__device__ __forceinline__ bool cursor_next(const MfmaArgs& a, TileCursor& c, int lane, bool* ends) {
+  *ends = false;
+  if (c.t + 1 < c.t_stop) {
+    ++c.t;
+    return true;
+  }
+  const int64_t got = claim_value(c.pend);
+  const int64_t ch = a.team + got;
+  if (ch < a.n_chunks) {
+    c.t = ch * a.chunk;
+    c.t_stop = min(c.t + a.chunk, a.tiles_pp);
+    c.pend = claim_issue(a.ctr + c.pair * kCounterStride, lane);
+    return true;
+  }
+  claim_done(a, a.ctr + c.pair * kCounterStride, got, lane);
+  *ends = true;
+  const int64_t nxt = c.asg + 4 * a.pwgs;
+  if (nxt >= a.pairs * a.team) return false;
+  cursor_start(a, nxt, c, lane);
   return true;
 }
 
@@ -419,6 +502,40 @@ __device__ __forceinline__ void write_partial(const MfmaArgs& a, int b, int h, i
       rec[1] = lsum;
     }
   }
+}
+
+// An empty partial (m = -inf, l = 0, o = 0) for every head in `slot`.
+template <int G>
+__device__ __forceinline__ void write_empty(const MfmaArgs& a, int b, int h, int64_t slot, int lane) {
+  for (int m = 0; m < G; ++m) {
+    float* rec = a.ws + (((int64_t)b * a.g.Hq + h * G + m) * a.n_slots + slot) * kPartial;
+    rec[2 + lane] = 0.0f;
+    rec[2 + 64 + lane] = 0.0f;
+    if (lane == 0) {
+      rec[0] = -INFINITY;
+      rec[1] = 0.0f;
+    }
+  }
+}
+
+// The query of (sequence b, kv head h) for one wave: qsw[m][c] = fp32 q of
+// head h G + m, rotated by the normalized Hadamard transform if asked, times
+// scale_log2.  Returns max |qsw| over the wave's heads.
+template <int G>
+__device__ __forceinline__ float wave_query(const MfmaArgs& a, int b, int h, bool rotate,
+                                            float (*qsw)[kD], int lane) {
+  for (int e = lane; e < G * kD; e += 64)
+    qsw[e / kD][e % kD] = __half2float(a.q[((int64_t)b * a.g.Hq + h * G + e / kD) * kD + e % kD]);
+  wave_sync();
+  if (rotate) fwht128_wave(&qsw[0][0], G, lane);
+  float mx = 0.0f;
+  for (int e = lane; e < G * kD; e += 64) {
+    const float v = qsw[e / kD][e % kD] * a.scale_log2;
+    qsw[e / kD][e % kD] = v;
+    mx = fmaxf(mx, fabsf(v));
+  }
+  wave_sync();
+  return wave_max64(mx);
 }
 
 }  // namespace

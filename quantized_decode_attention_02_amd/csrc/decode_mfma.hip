@@ -47,7 +47,7 @@
 //                         stage filled by global-to-LDS loads one tile ahead
 //                         (decode_common.h); 0: plain loads of the current tile
 //   KVQ_DECODE_MIN_WAVES  minimum waves per SIMD the register allocation
-//                         must allow (0: compiler's choice)
+//                         must allow (0: 3, or 2 for the KIVI G = 4 kernels)
 #ifndef KVQ_DECODE_STAGE
 #define KVQ_DECODE_STAGE 1
 #endif
@@ -78,122 +78,65 @@ __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
   }
 }
 
+// Waves per SIMD the register allocation must allow: three work-groups per
+// compute unit wherever the LDS allows it (the KIVI G = 4 tables do not).
+template <int G, bool BLOCK>
+constexpr int decode_min_waves() {
+  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK) ? 2 : 3);
+}
+
 template <int G, int BITS, bool BLOCK>
-__global__
-#if KVQ_DECODE_MIN_WAVES > 0
-__launch_bounds__(256, KVQ_DECODE_MIN_WAVES)
-#else
-__launch_bounds__(256)
-#endif
-void decode_mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256, (decode_min_waves<G, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
   constexpr int NDG = BLOCK ? 1 : 4;     // value scale groups per token
   constexpr int TB = 512 * BITS;         // tile bytes
-  constexpr int VROW = 4 * BITS;         // value row bytes per channel
   const Geom& g = a.g;
-  __shared__ float qs[G][kD];
-  __shared__ float qmax_s;
-  // query tables: per wave and group half (KIVI, rebuilt per group); one
-  // table for the work-group (BLOCK, fixed for the chunk)
-  __shared__ __attribute__((aligned(16))) _Float16 QL[BLOCK ? 1 : 4][BLOCK ? 1 : 2][32][HL][4][4];
+  // everything per wave: waves never wait for each other
+  __shared__ float qs[4][G][kD];
+  // query tables: per group half (KIVI, rebuilt per group) or one (BLOCK,
+  // fixed per pair)
+  __shared__ __attribute__((aligned(16))) _Float16 QL[4][BLOCK ? 1 : 2][32][HL][4][4];
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
   __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t chunk = blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t pair = pair_index(g, b, h);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
-  const bool win = a.window && chunk == a.chunks;   // the fp16 window work-group
-  auto QLw = QL[BLOCK ? 0 : w];
+  auto QLw = QL[w];
+  auto qsw = qs[w];
   const int qh = BLOCK ? 0 : gh;
-
-  // Wave 0 fetches the query into LDS before it requests its first tile;
-  // the other waves request theirs at once.  (The compiler waits for every
-  // global load, tile requests included, before a register loaded after one
-  // is used, so the query must not be loaded behind a tile.)
-  if (w == 0) {
-    for (int e = lane; e < G * kD; e += 64)
-      qs[e / kD][e % kD] = __half2float(a.q[((int64_t)b * g.Hq + h * G + e / kD) * kD + e % kD]);
-  }
-
-  // this lane writes key k-step ks = tl of the query table: four channels
-  int kch[4];
-  float kinv[4];
-  key_quad<BITS>(tl, kch, kinv);
-
-  const int64_t chunk_tok0 = a.t_lo + chunk * 4 * a.nt * 64;
-  const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
-  const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
-  const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
-  const bool ring = slots != g.gmax;
-  const uint8_t* kpair = kplane + pair * slots * TB;
-  const uint8_t* vpair = vplane + pair * slots * TB;
-  const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
-  const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
-  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
-  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
-
-  TilePos cur_pos, nxt_pos;
-  TileRaw<BITS, BLOCK> cur, nxt;
-  uint8_t* stage = ST[KVQ_DECODE_STAGE ? w : 0];
-  const int64_t scale_end = g.gmax * kGroup;
-  bool have = !win && tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
-  // The first tile is requested before the prologue, so its latency overlaps
-  // the query set-up.  The request is made by every wave, without a branch
-  // (a branch would make the query's use wait for it too): a wave without a
-  // tile fetches the range's first group instead and waits for it before
-  // leaving.
-  if (KVQ_DECODE_STAGE) {
-    TilePos first = cur_pos;
-    if (!have) {
-      first.base = a.t_lo;
-      first.nvalid = 1;
-      first.grp0 = (uint32_t)(a.t_lo >> 5);
-      first.s0 = first.s1 = ring ? first.grp0 % (uint32_t)slots : first.grp0;
-    }
-    stage_issue<BITS>(stage, first, lane, kpair, vpair);
-    meta_issue<BITS, BLOCK, false>(nxt, first, lane, kmpair, vmpair, ksc, vsc, scale_end, kch[0], kch[1]);
-  }
-
-  // ---------------- prologue: scaled (rotated unless window) queries, zero
-  // tables; LDS-only barriers, so the first tiles stay in flight
-  for (int e = tid; e < (int)(sizeof(QL) / 2); e += 256) (&QL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
-  for (int e = tid; e < (int)(sizeof(PL) / 2); e += 256) (&PL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
-  lds_barrier();
-  if (g.hadamard && !win) fwht128_lds(&qs[0][0], G, tid, 256);
-  for (int e = tid; e < G * kD; e += 256) (&qs[0][0])[e] *= a.scale_log2;
-  lds_barrier();
-  if (tid < 64) {
-    float mx = 0.0f;
-    for (int e = lane; e < G * kD; e += 64) mx = fmaxf(mx, fabsf((&qs[0][0])[e]));
-    mx = wave_max64(mx);
-    if (lane == 0) qmax_s = mx;
-  }
-  lds_barrier();
+  for (int e = lane; e < (int)(sizeof(QL[0]) / 2); e += 64) (&QLw[0][0][0][0][0])[e] = (_Float16)0.0f;
+  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) (&PL[w][0][0][0][0][0])[e] = (_Float16)0.0f;
+  wave_sync();
 
   float m_run[G], l_acc[G];
   float zacc[G][NDG];
-  for (int m = 0; m < G; ++m) {
-    m_run[m] = -INFINITY;
-    l_acc[m] = 0.0f;
-    for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
-  }
   // output accumulators: channel lane (o0: even value k-steps, o2: odd) and
   // channel 64 + lane (o1, o3); two chains each so dependent MFMAs interleave
-  f4_t o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0}, o2 = {0, 0, 0, 0}, o3 = {0, 0, 0, 0};
+  f4_t o0, o1, o2, o3;
+  auto reset = [&]() {
+    for (int m = 0; m < G; ++m) {
+      m_run[m] = -INFINITY;
+      l_acc[m] = 0.0f;
+      for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
+    }
+    o0 = f4_t{0, 0, 0, 0}; o1 = o0; o2 = o0; o3 = o0;
+  };
+  reset();
 
-  if (win) {
-    // ================= fp16 window: tokens [Tq, length), wave w takes tile w
+  if (blockIdx.x < a.wins) {
+    // ================= fp16 window of one pair: tokens [Tq, length), wave w takes tile w
+    const int64_t pair = blockIdx.x;
+    const int b = (int)(pair / g.Hkv), h = (int)(pair % g.Hkv);
+    const float qmax = wave_query<G>(a, b, h, false, qsw, lane);
     int ex = 0;
-    if (qmax_s > 0.0f) frexpf(qmax_s, &ex);
+    if (qmax > 0.0f) frexpf(qmax, &ex);
     const int e_q = 10 - ex;
     const float unscale = ldexpf(1.0f, -e_q);
     // query table in natural channel order: k-step ks = tl holds 4tl..4tl+3
     for (int m = 0; m < G; ++m) {
       _Float16 hi[4], lo[4];
-      for (int i = 0; i < 4; ++i) split_half(ldexpf(qs[m][4 * tl + i], e_q), &hi[i], &lo[i]);
+      for (int i = 0; i < 4; ++i) split_half(ldexpf(qsw[m][4 * tl + i], e_q), &hi[i], &lo[i]);
       const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
       *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][m][0]) = hv;
       if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][G + m][0]) = lv;
@@ -231,63 +174,125 @@ void decode_mfma_kernel(MfmaArgs a) {
       window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
     }
     const float zero[G] = {};
-    write_partial<G, HL>(a, b, h, a.slot_base + a.chunks * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
-                         1.0f, zero, zero);
-    if (KVQ_DECODE_STAGE) wait_stage_landed();
+    write_partial<G, HL>(a, b, h, a.win_slot + w, lane, m_run, l_acc, o0, o1, o2, o3, 1.0f, zero, zero);
     return;
   }
 
-  // ================= quantized tiles
-  float qv[G][4];
-  for (int m = 0; m < G; ++m)
-    for (int i = 0; i < 4; ++i) qv[m][i] = qs[m][kch[i]];
+  // ================= quantized tiles: this wave's assignments (see MfmaArgs)
+  const int64_t rank = (int64_t)w * a.pwgs + (blockIdx.x - a.wins);
+  if (rank >= a.pairs * a.team) return;
 
-  // BLOCK: per-token key scales, so the query table is fixed for the chunk
+  // this lane writes key k-step ks = tl of the query table: four channels
+  int kch[4];
+  float kinv[4];
+  key_quad<BITS>(tl, kch, kinv);
+
+  const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
+  const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
+  const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
+  const bool ring = slots != g.gmax;
+  const int64_t scale_end = g.gmax * kGroup;
+  // per-pair bases of the planes
+  auto kpair_of = [&](int64_t pr) { return kplane + pr * slots * TB; };
+  auto vpair_of = [&](int64_t pr) { return vplane + pr * slots * TB; };
+  auto kmeta_of = [&](int64_t pr) { return a.p.p[KVQ_PLANE_K_META] + pr * g.gmax * 512; };
+  auto vmeta_of = [&](int64_t pr) { return a.p.p[KVQ_PLANE_V_META] + pr * g.gmax * 512; };
+  auto ksc_of = [&](int64_t pr) {
+    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pr * g.gmax * kGroup;
+  };
+  auto vsc_of = [&](int64_t pr) {
+    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pr * g.gmax * kGroup;
+  };
+
+  TilePos cur_pos, nxt_pos;
+  TileRaw<BITS, BLOCK> cur, nxt;
+  uint8_t* stage = ST[KVQ_DECODE_STAGE ? w : 0];
+  auto issue = [&](const TilePos& tp, int64_t pr) {
+    stage_issue<BITS>(stage, tp, lane, kpair_of(pr), vpair_of(pr));
+    meta_issue<BITS, BLOCK, false>(nxt, tp, lane, kmeta_of(pr), vmeta_of(pr), ksc_of(pr), vsc_of(pr),
+                                   scale_end, kch[0], kch[1]);
+  };
+  TileCursor cs;
+  cursor_start(a, rank, cs, lane);
+  int64_t cur_pair = cs.pair, cur_k = cs.k;
+  tile_at(a, cs.t, slots, ring, cur_pos);
+  if (KVQ_DECODE_STAGE) issue(cur_pos, cur_pair);   // in flight during the first pair's set-up
+
+  // per-assignment state
+  int64_t pair = -1, pk = 0;
+  int pb = 0, ph = 0;
+  float qv[G][4];
   float qsum[G];
   float e_scale_blk = 1.0f;
-  if (BLOCK) {
-    int ex = 0;
-    if (qmax_s > 0.0f) frexpf(qmax_s, &ex);
-    const int e_blk = 10 - ex;
-    e_scale_blk = ldexpf(1.0f, 24 - e_blk);
+
+  // this member's partial of `pair`
+  auto flush = [&]() {
+    float add0[G], add1[G];
     for (int m = 0; m < G; ++m) {
-      float s = 0.0f;
-      for (int i = 0; i < 4; ++i) s += qv[m][i];
-      qsum[m] = half_sum(s);   // the 32 lanes of a half cover all 128 channels
+      float zsum[NDG];
+      for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
+      add0[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh];
+      add1[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
     }
-    if (w == 0 && gh == 0) {
-      for (int m = 0; m < G; ++m) {
-        _Float16 hi[4], lo[4];
-        for (int i = 0; i < 4; ++i) split_half(ldexpf(qv[m][i], e_blk) * kinv[i], &hi[i], &lo[i]);
-        const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<h4_t*>(&QLw[0][tl][0][m][0]) = hv;
-        if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[0][tl][0][G + m][0]) = lv;
-        else *reinterpret_cast<h4_t*>(&QLw[0][tl][1][m][0]) = lv;
+    write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, 16777216.0f,
+                         add0, add1);
+    reset();
+  };
+
+  bool fresh = true;   // the current tile opens an assignment
+  for (;;) {
+    if (fresh) {
+      // ---------------- a new assignment: its pair's query (rotated for Hadamard caches)
+      pair = cur_pair;
+      pk = cur_k;
+      pb = (int)(pair / g.Hkv);
+      ph = (int)(pair % g.Hkv);
+      const float qmax = wave_query<G>(a, pb, ph, g.hadamard != 0, qsw, lane);
+      for (int m = 0; m < G; ++m)
+        for (int i = 0; i < 4; ++i) qv[m][i] = qsw[m][kch[i]];
+      if (BLOCK) {
+        // per-token key scales: the query table is fixed for the pair
+        int ex = 0;
+        if (qmax > 0.0f) frexpf(qmax, &ex);
+        const int e_blk = 10 - ex;
+        e_scale_blk = ldexpf(1.0f, 24 - e_blk);
+        for (int m = 0; m < G; ++m) {
+          float s = 0.0f;
+          for (int i = 0; i < 4; ++i) s += qv[m][i];
+          qsum[m] = half_sum(s);   // the 32 lanes of a half cover all 128 channels
+        }
+        if (gh == 0) {
+          for (int m = 0; m < G; ++m) {
+            _Float16 hi[4], lo[4];
+            for (int i = 0; i < 4; ++i) split_half(ldexpf(qv[m][i], e_blk) * kinv[i], &hi[i], &lo[i]);
+            const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+            *reinterpret_cast<h4_t*>(&QLw[0][tl][0][m][0]) = hv;
+            if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[0][tl][0][G + m][0]) = lv;
+            else *reinterpret_cast<h4_t*>(&QLw[0][tl][1][m][0]) = lv;
+          }
+        }
+        wave_sync();
       }
     }
-    lds_barrier();
-  }
 
-  for (int it = 0; have; ++it) {
-    bool have_next;
+    bool ends = false, more;
     if (KVQ_DECODE_STAGE) {
-      // this tile has landed: codes from the stage into registers, then the
-      // stage and the metadata registers are refilled with the next tile
-      // while this one is computed
+      // this tile has landed (and with it the claim in flight): codes from
+      // the stage into registers, then the stage and the metadata registers
+      // are refilled with the next tile while this one is computed
       wait_stage_landed();
+      more = cursor_next(a, cs, lane, &ends);
+      if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
       stage_read<BITS, BLOCK>(cur, stage, lane);
       cur.km0 = nxt.km0; cur.km1 = nxt.km1; cur.vm = nxt.vm; cur.ks16 = nxt.ks16; cur.vs16 = nxt.vs16;
-      have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
       wait_stage_read();
-      if (have_next) {
-        stage_issue<BITS>(stage, nxt_pos, lane, kpair, vpair);
-        meta_issue<BITS, BLOCK, false>(nxt, nxt_pos, lane, kmpair, vmpair, ksc, vsc, scale_end, kch[0], kch[1]);
-      }
+      if (more) issue(nxt_pos, cs.pair);
     } else {
-      load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, ksc, vsc, kch[0], kch[1]);
-      have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
+      load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair_of(pair), vpair_of(pair), kmeta_of(pair),
+                                    vmeta_of(pair), ksc_of(pair), vsc_of(pair), kch[0], kch[1]);
+      more = cursor_next(a, cs, lane, &ends);
+      if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
     }
-    const int64_t base = cur_pos.base;
     const int nvalid = cur_pos.nvalid;
     const bool tok_ok = lane < nvalid;
     const uint4* kc = cur.kc;
@@ -296,7 +301,6 @@ void decode_mfma_kernel(MfmaArgs a) {
     value_meta<BITS, BLOCK, NDG>(cur, tok_ok, vs, vz);
     const float kscale = BLOCK ? half_bits_to_float(cur.ks16) : 0.0f;
     const uint2 km0 = cur.km0, km1 = cur.km1;
-    (void)base;
 
     // ---------------- KIVI: query table of my group (k-step tl)
     float bias[G];
@@ -339,31 +343,30 @@ void decode_mfma_kernel(MfmaArgs a) {
 
     // ---------------- scores: S = q' . codes over 32 k-steps (two chains)
     f4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    const int qgh = BLOCK ? 0 : gh;  // table half of my block (tokens 0-31 / 32-63)
     for (int j = 0; j < NKW; ++j) {
       const uint32_t dw[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
       for (int u = 0; u < 4; ++u) {
-        const uint32_t x = dw[u];
+        const uint32_t xw = dw[u];
         const int i = 4 * j + u;     // canonical dword index of the row
         if (BITS == 4) {
-          const uint32_t x8 = x >> 8;
-          const h4_t b0 = as_h4(x & 0x000F000Fu, x & 0x00F000F0u);
+          const uint32_t x8 = xw >> 8;
+          const h4_t b0 = as_h4(xw & 0x000F000Fu, xw & 0x00F000F0u);
           const h4_t b1 = as_h4(x8 & 0x000F000Fu, x8 & 0x00F000F0u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][2 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][2 * i + 1][hl][row][0]), b1, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i][hl][row][0]), b0, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i + 1][hl][row][0]), b1, acc1);
           }
         } else {
-          const uint32_t x10 = x >> 10;
-          const h4_t b0 = as_h4(x & 0x00030003u, x & 0x000C000Cu);
-          const h4_t b1 = as_h4(x & 0x00300030u, x & 0x00C000C0u);
-          const h4_t b2 = as_h4(x & 0x03000300u, x10 & 0x00030003u);
+          const uint32_t x10 = xw >> 10;
+          const h4_t b0 = as_h4(xw & 0x00030003u, xw & 0x000C000Cu);
+          const h4_t b1 = as_h4(xw & 0x00300030u, xw & 0x00C000C0u);
+          const h4_t b2 = as_h4(xw & 0x03000300u, x10 & 0x00030003u);
           const h4_t b3 = as_h4(x10 & 0x000C000Cu, x10 & 0x00300030u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 1][hl][row][0]), b1, acc1);
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 2][hl][row][0]), b2, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qgh][4 * i + 3][hl][row][0]), b3, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i][hl][row][0]), b0, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 1][hl][row][0]), b1, acc1);
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 2][hl][row][0]), b2, acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 3][hl][row][0]), b3, acc1);
           }
         }
       }
@@ -383,48 +386,62 @@ void decode_mfma_kernel(MfmaArgs a) {
     wave_sync();
     value_mfma<G, BITS, BLOCK, HL, NDG>(vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
+
+    // ---------------- the member's partial when its assignment ends
+    if (ends) flush();
+    if (!more) break;
     cur_pos = nxt_pos;
-    have = have_next;
+    cur_pair = cs.pair;
+    cur_k = cs.k;
+    fresh = ends;
   }
-
-  if (KVQ_DECODE_STAGE) wait_stage_landed();   // a wave without tiles still has its request out
-
-  // ---------------- epilogue: per-head partial of this wave
-  float add0[G], add1[G];
-  for (int m = 0; m < G; ++m) {
-    float zsum[NDG];
-    for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-    add0[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh];
-    add1[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
-  }
-  write_partial<G, HL>(a, b, h, a.slot_base + chunk * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
-                       16777216.0f, add0, add1);
 }
 
 }  // namespace
+
+int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
+  const void* fn = nullptr;
+  const bool blk = g.scheme == KVQ_BLOCK128_SYM;
+#define KVQ_FN(GG, BB, BL) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, BB, BL>)
+  if (blk) {
+    if (g.G == 1) KVQ_FN(1, 4, true); else if (g.G == 2) KVQ_FN(2, 4, true); else KVQ_FN(4, 4, true);
+  } else if (bits == 4) {
+    if (g.G == 1) KVQ_FN(1, 4, false); else if (g.G == 2) KVQ_FN(2, 4, false); else KVQ_FN(4, 4, false);
+  } else {
+    if (g.G == 1) KVQ_FN(1, 2, false); else if (g.G == 2) KVQ_FN(2, 2, false); else KVQ_FN(4, 2, false);
+  }
+#undef KVQ_FN
+  return occupancy_wgs_per_cu(fn);
+}
 
 hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
                               float sm_scale, float* ws, hipStream_t s) {
   for (int r = 0; r < cp.nr; ++r) {
     const RangePlan& rp = cp.r[r];
-    const int window = rp.window;
-    if (rp.chunks == 0 && !window) continue;
+    const int64_t wins = rp.window ? (int64_t)g.B * g.Hkv : 0;
+    if (rp.pwgs == 0 && wins == 0) continue;
     MfmaArgs a;
     a.g = g;
     a.p = p;
     a.q = q;
-    a.ws = ws;
+    a.ws = ws + cp.ctr_floats;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.q_pos = 0;
     a.t_lo = rp.t_lo;
     a.t_hi = rp.t_hi;
-    a.nt = rp.nt;
     a.hi_tier = rp.hi_tier;
-    a.chunks = rp.chunks;
-    a.window = window;
+    a.ctr = reinterpret_cast<uint32_t*>(ws) + r * (int64_t)g.B * g.Hkv * kCounterStride;
+    a.tiles_pp = rp.tiles_pp;
+    a.pairs = (int64_t)g.B * g.Hkv;
+    a.team = rp.team;
+    a.chunk = rp.chunk;
+    a.n_chunks = rp.n_chunks;
+    a.pwgs = rp.pwgs;
     a.slot_base = rp.slot_base;
+    a.wins = wins;
+    a.win_slot = cp.nq;
     a.n_slots = cp.n;
-    const dim3 grid((unsigned)(rp.chunks + window), g.Hkv, g.B), block(256);
+    const dim3 grid((unsigned)(rp.pwgs + wins)), block(256);
     const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_MF(GG, BB, BL) hipLaunchKernelGGL((decode_mfma_kernel<GG, BB, BL>), grid, block, 0, s, a)
     if (blk) {

@@ -60,41 +60,43 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
   constexpr int TB = 512 * BITS;         // tile bytes
   constexpr int CPW = 32 / BITS;         // channels per code word
   const Geom& g = a.g;
-  __shared__ float qs[G][kD];                                      // R(q_pos) q, scaled
   __shared__ __attribute__((aligned(16))) float DT[32][32][4];     // [j / 2][d]: cos, sin of j, j + 1
+  // per wave: waves never wait for each other after the table above
+  __shared__ float qs[4][G][kD];                                   // R(q_pos) q, scaled
   __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD];   // [wave][group][head][channel]
   __shared__ __attribute__((aligned(16))) float KSZ[4][2][64][4];  // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t chunk = blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t pair = pair_index(g, b, h);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
-  const bool win = a.window && chunk == a.chunks;   // the fp16 window work-group
   const float* rope_tab = reinterpret_cast<const float*>(a.p.p[KVQ_PLANE_ROPE]);
+  auto qsw = qs[w];
 
-  // ---------------- prologue: R(q_pos) q with fp64 angles; offset table
-  if (tid < 64) {
-    const double theta = pow((double)g.rope_theta, -2.0 * (double)tid / 128.0);
-    const double ang = (double)a.q_pos * theta;
-    const float c = (float)cos(ang), s = (float)sin(ang);
-    for (int m = 0; m < G; ++m) {
-      const int64_t qb = ((int64_t)b * g.Hq + h * G + m) * kD;
-      const float x = __half2float(a.q[qb + tid]), y = __half2float(a.q[qb + tid + 64]);
-      qs[m][tid] = (x * c - y * s) * a.scale_log2;
-      qs[m][tid + 64] = (x * s + y * c) * a.scale_log2;
-    }
-  }
-  // rows 0..31 of the RoPE table: the plane always holds at least 32 rows;
-  // rows at or past the cache length are only used for masked tokens
+  // ---------------- offset table (rows 0..31 of the RoPE table: the plane
+  // always holds at least 32 rows; rows at or past the cache length are only
+  // used for masked tokens), zeroed tables
   for (int e = tid; e < 32 * 32; e += 256) {
     const int jp = e >> 5, d = e & 31;
     *reinterpret_cast<float4*>(&DT[jp][d][0]) = *reinterpret_cast<const float4*>(rope_tab + d * 128 + 4 * jp);
   }
-  for (int e = tid; e < (int)(sizeof(QA) / 4); e += 256) (&QA[0][0][0][0])[e] = 0.0f;
-  for (int e = tid; e < (int)(sizeof(PL) / 2); e += 256) (&PL[0][0][0][0][0][0])[e] = (_Float16)0.0f;
-  __syncthreads();
+  for (int e = lane; e < (int)(sizeof(QA[0]) / 4); e += 64) (&QA[w][0][0][0])[e] = 0.0f;
+  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) (&PL[w][0][0][0][0][0])[e] = (_Float16)0.0f;
+  lds_barrier();
+
+  // the query of (b, h) at q_pos: R(q_pos) q (fp64 angles), scaled; lane j
+  // takes channel pair j of every head
+  auto load_query = [&](int b, int h) {
+    const double theta = pow((double)g.rope_theta, -2.0 * (double)lane / 128.0);
+    const double ang = (double)a.q_pos * theta;
+    const float c = (float)cos(ang), s = (float)sin(ang);
+    for (int m = 0; m < G; ++m) {
+      const int64_t qb = ((int64_t)b * g.Hq + h * G + m) * kD;
+      const float x = __half2float(a.q[qb + lane]), y = __half2float(a.q[qb + lane + 64]);
+      qsw[m][lane] = (x * c - y * s) * a.scale_log2;
+      qsw[m][lane + 64] = (x * s + y * c) * a.scale_log2;
+    }
+    wave_sync();
+  };
 
   // query tables of the two groups of a tile (group starts t0 and t0 + 32):
   // u = R(-t0) qs, lane j writes channels j and j + 64 of every head
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
       const int64_t t = (gg && second) ? t0 + 32 : t0;
       const float2 cs = *reinterpret_cast<const float2*>(rope_tab + t * 128 + 2 * lane);
       for (int m = 0; m < G; ++m) {
-        const float x = qs[m][lane], y = qs[m][lane + 64];
+        const float x = qsw[m][lane], y = qsw[m][lane + 64];
         QA[w][gg][m][lane] = x * cs.x + y * cs.y;
         QA[w][gg][m][lane + 64] = y * cs.x - x * cs.y;
       }
@@ -113,12 +115,16 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
 
   float m_run[G], l_acc[G];
   float zacc[G][NDG];
-  for (int m = 0; m < G; ++m) {
-    m_run[m] = -INFINITY;
-    l_acc[m] = 0.0f;
-    for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
-  }
-  f4_t o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0}, o2 = {0, 0, 0, 0}, o3 = {0, 0, 0, 0};
+  f4_t o0, o1, o2, o3;
+  auto reset = [&]() {
+    for (int m = 0; m < G; ++m) {
+      m_run[m] = -INFINITY;
+      l_acc[m] = 0.0f;
+      for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
+    }
+    o0 = f4_t{0, 0, 0, 0}; o1 = o0; o2 = o0; o3 = o0;
+  };
+  reset();
 
   // Scores of this lane's token from its 128 key values x_c (fp32), rotated
   // by d = tl: four accumulator chains, one MFMA per channel.
@@ -139,8 +145,11 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
     }
   };
 
-  if (win) {
-    // ================= fp16 window: tokens [Tq, length), wave w takes tile w
+  if (blockIdx.x < a.wins) {
+    // ================= fp16 window of one pair: tokens [Tq, length), wave w takes tile w
+    const int64_t pair = blockIdx.x;
+    const int b = (int)(pair / g.Hkv), h = (int)(pair % g.Hkv);
+    load_query(b, h);
     const int64_t base = g.Tq + 64 * (int64_t)w;
     if (base < g.length) {
       const int nvalid = (int)min((int64_t)64, g.length - base);
@@ -172,28 +181,55 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
       window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
     }
     const float zero[G] = {};
-    write_partial<G, HL>(a, b, h, a.slot_base + a.chunks * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
-                         1.0f, zero, zero);
+    write_partial<G, HL>(a, b, h, a.win_slot + w, lane, m_run, l_acc, o0, o1, o2, o3, 1.0f, zero, zero);
     return;
   }
 
-  // ================= quantized tiles
-  const int64_t chunk_tok0 = a.t_lo + chunk * 4 * a.nt * 64;
+  // ================= quantized tiles: this wave's assignments (see MfmaArgs)
+  const int64_t rank = (int64_t)w * a.pwgs + (blockIdx.x - a.wins);
+  if (rank >= a.pairs * a.team) return;
+
   const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
   const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
   const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
   const bool ring = slots != g.gmax;
-  const uint8_t* kpair = kplane + pair * slots * TB;
-  const uint8_t* vpair = vplane + pair * slots * TB;
-  const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
-  const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
 
-  TilePos cur_pos, nxt_pos;
+  TilePos cur_pos;
   TileRaw<BITS, false> cur;
-  bool have = tile_pos(a, chunk_tok0, 0, w, slots, ring, cur_pos);
-  for (int it = 0; have; ++it) {
+  int64_t pair = -1, pk = 0;
+  int pb = 0, ph = 0;
+
+  // this member's partial of `pair`
+  auto flush = [&]() {
+    float add0[G], add1[G];
+    for (int m = 0; m < G; ++m) {
+      float zsum[NDG];
+      for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
+      add0[m] = zsum[gh];
+      add1[m] = zsum[gh + 2];
+    }
+    write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, 16777216.0f,
+                         add0, add1);
+    reset();
+  };
+
+  TileCursor cs;
+  cursor_start(a, rank, cs, lane);
+  tile_at(a, cs.t, slots, ring, cur_pos);
+  bool fresh = true;   // the current tile opens an assignment
+  for (;;) {
+    if (fresh) {
+      pair = cs.pair;
+      pk = cs.k;
+      pb = (int)(pair / g.Hkv);
+      ph = (int)(pair % g.Hkv);
+      load_query(pb, ph);
+    }
+    const uint8_t* kpair = kplane + pair * slots * TB;
+    const uint8_t* vpair = vplane + pair * slots * TB;
+    const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
+    const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
     load_tile<BITS, false, true>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, nullptr, nullptr, 0, 0);
-    const bool have_next = tile_pos(a, chunk_tok0, it + 1, w, slots, ring, nxt_pos);
     const int nvalid = cur_pos.nvalid;
     const bool tok_ok = lane < nvalid;
     float vs[NDG], vz[NDG];
@@ -240,45 +276,59 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
     wave_sync();
     value_mfma<G, BITS, false, HL, NDG>(cur.vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
-    cur_pos = nxt_pos;
-    have = have_next;
-  }
 
-  float add0[G], add1[G];
-  for (int m = 0; m < G; ++m) {
-    float zsum[NDG];
-    for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-    add0[m] = zsum[gh];
-    add1[m] = zsum[gh + 2];
+    // the claim went out a tile ago
+    bool ends = false;
+    const bool more = cursor_next(a, cs, lane, &ends);
+    if (ends) flush();
+    if (!more) break;
+    tile_at(a, cs.t, slots, ring, cur_pos);
+    fresh = ends;
   }
-  write_partial<G, HL>(a, b, h, a.slot_base + chunk * 4 + w, lane, m_run, l_acc, o0, o1, o2, o3,
-                       16777216.0f, add0, add1);
 }
 
 }  // namespace
+
+int decode_rope_wgs_per_cu(const Geom& g, int bits) {
+  const void* fn = nullptr;
+#define KVQ_FN(GG, BB) fn = reinterpret_cast<const void*>(&decode_rope_kernel<GG, BB>)
+  if (bits == 4) {
+    if (g.G == 1) KVQ_FN(1, 4); else if (g.G == 2) KVQ_FN(2, 4); else KVQ_FN(4, 4);
+  } else {
+    if (g.G == 1) KVQ_FN(1, 2); else if (g.G == 2) KVQ_FN(2, 2); else KVQ_FN(4, 2);
+  }
+#undef KVQ_FN
+  return occupancy_wgs_per_cu(fn);
+}
 
 hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
                               int64_t q_pos, float sm_scale, float* ws, hipStream_t s) {
   for (int r = 0; r < cp.nr; ++r) {
     const RangePlan& rp = cp.r[r];
-    const int window = rp.window;
-    if (rp.chunks == 0 && !window) continue;
+    const int64_t wins = rp.window ? (int64_t)g.B * g.Hkv : 0;
+    if (rp.pwgs == 0 && wins == 0) continue;
     MfmaArgs a;
     a.g = g;
     a.p = p;
     a.q = q;
-    a.ws = ws;
+    a.ws = ws + cp.ctr_floats;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.q_pos = q_pos;
     a.t_lo = rp.t_lo;
     a.t_hi = rp.t_hi;
-    a.nt = rp.nt;
     a.hi_tier = rp.hi_tier;
-    a.chunks = rp.chunks;
-    a.window = window;
+    a.ctr = reinterpret_cast<uint32_t*>(ws) + r * (int64_t)g.B * g.Hkv * kCounterStride;
+    a.tiles_pp = rp.tiles_pp;
+    a.pairs = (int64_t)g.B * g.Hkv;
+    a.team = rp.team;
+    a.chunk = rp.chunk;
+    a.n_chunks = rp.n_chunks;
+    a.pwgs = rp.pwgs;
     a.slot_base = rp.slot_base;
+    a.wins = wins;
+    a.win_slot = cp.nq;
     a.n_slots = cp.n;
-    const dim3 grid((unsigned)(rp.chunks + window), g.Hkv, g.B), block(256);
+    const dim3 grid((unsigned)(rp.pwgs + wins)), block(256);
 #define KVQ_RP(GG, BB) hipLaunchKernelGGL((decode_rope_kernel<GG, BB>), grid, block, 0, s, a)
     if (rp.bits == 4) {
       if (g.G == 1) KVQ_RP(1, 4);

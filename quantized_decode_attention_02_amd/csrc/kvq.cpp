@@ -1,6 +1,8 @@
 // libkvq C ABI: argument validation, plane layout, tier bookkeeping and
-// kernel dispatch.  No device allocation, no synchronization, no global
-// mutable state.  The contract of every function is in include/kvq.h.
+// kernel dispatch.  No device allocation, no synchronization; the only global
+// state is a mutex-guarded cache of kernel occupancies (a pure function of
+// the kernel binary and the device).  The contract of every function is in
+// include/kvq.h.
 //
 // Sources cited here:
 //   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
@@ -9,14 +11,10 @@
 //              (nalar.dev).
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 
 #include "kvq_internal.h"
-
-// Tuning knob: the MFMA decode aims at about this many waves per launch
-// (tiles per wave = all 64-token tiles / this, clamped to [1, 16]).
-#ifndef KVQ_DECODE_TARGET_WAVES
-#define KVQ_DECODE_TARGET_WAVES 16384
-#endif
 
 namespace kvq {
 namespace {
@@ -127,6 +125,12 @@ kvq_status validate_cache(const kvq_config* c, const kvq_cache* cache, Planes* p
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+// Workspace bytes of a decode call: the chunk counters, then the partials.
+uint64_t workspace_need(const Geom& g, const ChunkPlan& cp) {
+  if (cp.n == 0) return 0;
+  return ((uint64_t)cp.ctr_floats + (uint64_t)g.B * g.Hq * cp.n * kPartial) * sizeof(float);
+}
+
 struct DecodeSetup {
   Geom g;
   Planes p;
@@ -144,7 +148,7 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
   if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
   st->g = make_geom(cfg, cache->batch, cache->max_tokens, cache->length);
   st->cp = plan_chunks(st->g);
-  const uint64_t need = (uint64_t)st->g.B * st->g.Hq * st->cp.n * kPartial * sizeof(float);
+  const uint64_t need = workspace_need(st->g, st->cp);
   if (need > 0 && (workspace == nullptr || !aligned(workspace))) return KVQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
   st->scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)kD);
@@ -153,36 +157,101 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 
 }  // namespace
 
-// Split-K plan: the quantized tokens form up to two ranges of one code width
-// each (low-bit tier, high-bit tier); a wave streams nt tiles of 64 tokens and
-// a work-group of 4 waves covers 4 * nt tiles, with nt chosen so that a call
-// launches on the order of 16K waves; the fp16 window rides on the last
-// launch as one more work-group.
+// Split-K plan.  The quantized tokens form up to two ranges of one code width
+// each (low-bit tier, high-bit tier), one launch each.  A launch runs as many
+// waves as fit on the device at once, as a team of equal size per pair (one
+// wave handles several pairs in turn when pairs outnumber waves); a team is
+// no larger than half its pair's tiles.  Chunks are one tile, or two where
+// every member gets at least 8 chunks on average, so that a claim has a
+// tile's time to come back; teams above 2 * kTeamPerChunkTile waves take
+// team / kTeamPerChunkTile tiles per chunk.  The fp16 window rides on the
+// last launch: one more work-group per pair.
+#ifndef KVQ_DECODE_CHUNK_MIN
+#define KVQ_DECODE_CHUNK_MIN 1
+#endif
+#ifndef KVQ_DECODE_CHUNK_MAX
+#define KVQ_DECODE_CHUNK_MAX 2
+#endif
+constexpr int64_t kMinTilesPerWave = 2;
+#ifndef KVQ_TEAM_PER_CHUNK_TILE
+#define KVQ_TEAM_PER_CHUNK_TILE 16
+#endif
+constexpr int64_t kTeamPerChunkTile = KVQ_TEAM_PER_CHUNK_TILE;
+
+int occupancy_wgs_per_cu(const void* kernel) {
+  static std::mutex mu;
+  static std::map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 2;   // no device: a plan that is valid everywhere, if not the fastest
+  }
+  cache[kernel] = n;
+  return n;
+}
+
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
+}
+
 ChunkPlan plan_chunks(const Geom& g) {
   ChunkPlan cp;
   cp.nr = 0;
   const int64_t pairs = (int64_t)g.B * g.Hkv;
   const bool window = g.scheme == KVQ_KIVI_ASYM && g.length > g.Tq;
   const int64_t lo_end = g.scheme == KVQ_KIVI_ASYM ? g.hi_start : 0;
-  if (lo_end > 0) cp.r[cp.nr++] = RangePlan{0, lo_end, g.lo_bits, 0, 1, 0, 0, 0};
-  if (g.Tq > lo_end || window) cp.r[cp.nr++] = RangePlan{lo_end, g.Tq, g.hi_bits, 1, 1, 0, 0, 0};
-  int64_t tiles = 0;
-  for (int i = 0; i < cp.nr; ++i) tiles += pairs * ((cp.r[i].t_hi - cp.r[i].t_lo + 63) / 64);
-  int64_t nt = (tiles + KVQ_DECODE_TARGET_WAVES - 1) / KVQ_DECODE_TARGET_WAVES;
-  if (nt < 1) nt = 1;
-  if (nt > 16) nt = 16;
+  auto add = [&](int64_t t_lo, int64_t t_hi, int bits, int hi_tier) {
+    RangePlan& r = cp.r[cp.nr++];
+    r.t_lo = t_lo;
+    r.t_hi = t_hi;
+    r.bits = bits;
+    r.hi_tier = hi_tier;
+    r.tiles_pp = (t_hi - t_lo + 63) / 64;
+    r.pwgs = 0;
+    r.window = 0;
+    r.team = 0;
+    r.chunk = 1;
+    r.n_chunks = 0;
+    if (r.tiles_pp > 0) {
+      const int per_cu = g.pre_rope ? decode_rope_wgs_per_cu(g, bits) : decode_mfma_wgs_per_cu(g, bits);
+      const int64_t cap = 4 * (int64_t)per_cu * device_compute_units();   // waves
+      int64_t team = pairs <= cap ? cap / pairs : 1;
+      const int64_t most = (r.tiles_pp + kMinTilesPerWave - 1) / kMinTilesPerWave;
+      if (team > most) team = most;
+      r.chunk = (KVQ_DECODE_CHUNK_MAX >= 2 && r.tiles_pp >= 16 * team) ? 2 : 1;
+      if (r.chunk < KVQ_DECODE_CHUNK_MIN && r.tiles_pp >= 8 * team * KVQ_DECODE_CHUNK_MIN)
+        r.chunk = KVQ_DECODE_CHUNK_MIN;
+      // large teams: fewer, longer chunks, so one counter is not claimed more
+      // often than its atomics can be served
+      const int64_t wide = team / kTeamPerChunkTile;
+      if (wide > r.chunk && r.tiles_pp >= 8 * team * wide) r.chunk = wide;
+      r.n_chunks = (r.tiles_pp + r.chunk - 1) / r.chunk;
+      if (team > r.n_chunks) team = r.n_chunks;
+      r.team = team;
+      const int64_t waves = pairs * team < cap ? pairs * team : cap;
+      r.pwgs = (waves + 3) / 4;
+    }
+  };
+  if (lo_end > 0) add(0, lo_end, g.lo_bits, 0);
+  if (g.Tq > lo_end || window) add(lo_end, g.Tq, g.hi_bits, 1);
   int64_t slot = 0;
   for (int i = 0; i < cp.nr; ++i) {
-    RangePlan& r = cp.r[i];
-    const int64_t t = (r.t_hi - r.t_lo + 63) / 64;
-    r.nt = (int)nt;
-    r.chunks = (t + 4 * nt - 1) / (4 * nt);
-    r.slot_base = slot;
-    slot += r.chunks * 4;
+    cp.r[i].slot_base = slot;
+    slot += cp.r[i].team;
   }
   cp.nq = slot;
   if (window) cp.r[cp.nr - 1].window = 1;
   cp.n = cp.nq + (window ? 4 : 0);
+  cp.ctr_floats = counter_words(pairs);
   return cp;
 }
 
@@ -225,7 +294,7 @@ kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t len
   if (bytes == nullptr || batch <= 0 || batch > 65535 || length < 0) return KVQ_ERR_INVALID_ARG;
   const Geom g = make_geom(cfg, batch, length, length);
   const ChunkPlan cp = plan_chunks(g);
-  *bytes = (uint64_t)g.B * g.Hq * cp.n * kPartial * sizeof(float);
+  *bytes = workspace_need(g, cp);
   return KVQ_OK;
 }
 

@@ -66,6 +66,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Orders the LDS accesses of one wave before and after it.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Normalized FWHT-128 of `nvec` vectors stored as float rows of 128 in LDS,
 // in the fixed fp32 schedule: for h = 1, 2, ..., 64 in that order every pair
 // (x[i], x[i+h]) with bit log2(h) of i clear becomes (a + b, a - b), each one
@@ -90,6 +97,25 @@ __device__ __forceinline__ void fwht128_lds(float* x, int nvec, int tid, int nth
   const float c = c32();
   for (int i = tid; i < nvec * kD; i += nthreads) x[i] = x[i] * c;
   lds_barrier();
+}
+
+// fwht128_lds for one wave (64 lanes, one butterfly each per stage), same
+// schedule and arithmetic.
+__device__ __forceinline__ void fwht128_wave(float* x, int nvec, int lane) {
+  for (int h = 1; h < kD; h <<= 1) {
+    for (int i = lane; i < nvec * 64; i += 64) {
+      const int v = i >> 6, pr = i & 63;
+      const int i0 = (pr / h) * 2 * h + (pr % h);
+      float* row = x + v * kD;
+      const float a = row[i0], b = row[i0 + h];
+      row[i0] = a + b;
+      row[i0 + h] = a - b;
+    }
+    wave_sync();
+  }
+  const float c = c32();
+  for (int i = lane; i < nvec * kD; i += 64) x[i] = x[i] * c;
+  wave_sync();
 }
 
 // Cross-lane reductions without LDS round trips.

@@ -34,28 +34,42 @@ struct Planes {
   uint8_t* p[KVQ_NUM_PLANES];
 };
 
-// One token range of a decode call with a single code width and tier.
+// One token range of a decode call with a single code width and tier.  Each
+// pair's tiles form n_chunks chunks of `chunk` tiles worked by a team of
+// `team` waves (decode_common.h); pwgs work-groups of 4 waves hold them.
 struct RangePlan {
   int64_t t_lo, t_hi;  // tokens [t_lo, t_hi), t_lo a multiple of 32
   int bits;            // code bits
   int hi_tier;         // 1: high-bit planes (ring), 0: low-bit planes
-  int nt;              // 64-token tiles per wave
-  int64_t chunks;      // work-groups along the range (4 waves each)
+  int64_t tiles_pp;    // 64-token tiles per (sequence, kv head)
+  int64_t team;        // waves per pair = partial slots per query head
+  int64_t chunk;       // tiles per chunk
+  int64_t n_chunks;    // chunks per pair (>= team)
+  int64_t pwgs;        // work-groups of the quantized tiles
   int64_t slot_base;   // first partial slot
-  int window;          // 1: this launch also attends the fp16 window (4 slots
-                       // after its chunks' slots)
+  int window;          // 1: this launch also attends the fp16 window (one
+                       // work-group per pair, 4 slots after all ranges')
 };
 
 // Split-K plan of one decode call: quantized tokens as up to two tier-pure
-// ranges (one launch each), each wave writing one partial slot; the fp16
-// window is one more work-group of the last range's launch (4 slots).  Slots
-// [0, nq) hold quantized tokens.
+// ranges (one launch each); the fp16 window rides on the last launch.
+// Slots [0, nq) hold quantized tokens, [nq, n) the window.  The workspace
+// starts with the chunk counters, one per 256-byte line (range r of pair p
+// at uint32 index (r * pairs + p) * kCounterStride), ctr_floats 4-byte words
+// in all; the partials follow.
 struct ChunkPlan {
   RangePlan r[2];
   int nr;
-  int64_t nq;         // partial slots of quantized tokens
-  int64_t n;          // all slots (nq + the window's)
+  int64_t nq;          // partial slots of quantized tokens
+  int64_t n;           // all slots (nq + the window's)
+  int64_t ctr_floats;  // workspace words before the partials
 };
+
+// Counters one to a 256-byte line: claims on one pair do not queue behind
+// claims on its neighbours.
+constexpr int64_t kCounterStride = 64;
+// Workspace words holding the chunk counters of `pairs` pairs.
+inline int64_t counter_words(int64_t pairs) { return 2 * pairs * kCounterStride; }
 
 ChunkPlan plan_chunks(const Geom& g);
 
@@ -86,6 +100,12 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
                                   hipStream_t s);
 hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
                               float sm_scale, float* ws, hipStream_t s);
+// Work-groups of the partials kernel for (g, bits) that fit on one compute
+// unit at once, and the device's compute units (fallbacks when no device).
+int decode_mfma_wgs_per_cu(const Geom& g, int bits);
+int decode_rope_wgs_per_cu(const Geom& g, int bits);
+int occupancy_wgs_per_cu(const void* kernel);
+int device_compute_units();
 hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& cp, const __half* q,
                               int64_t q_pos, float sm_scale, float* ws, hipStream_t s);
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,

@@ -184,7 +184,9 @@ class KVCache:
         return workspace_bytes(self.cfg, self.batch, self.length)
 
     def new_workspace(self):
-        return torch.empty(max(1, self.workspace_bytes() // 4), dtype=torch.float32, device="cuda")
+        # zero: the leading work counters must start at zero (every decode
+        # call leaves them so)
+        return torch.zeros(max(1, self.workspace_bytes() // 4), dtype=torch.float32, device="cuda")
 
     def _decode_args(self, q, q_pos, sm_scale, out, workspace):
         _need(q, torch.float16, (self.batch, self.hq, 128), "q")

@@ -122,11 +122,14 @@ def test_errors_before_launch():
 
 
 def test_workspace_formula():
-    # (m, l, o[128]) fp32 per (sequence, q head, chunk); the window is one chunk
+    # work counters (two 256-byte lines per (sequence, kv head)), then
+    # (m, l, o[128]) fp32 per (sequence, q head, partial)
     c = dict(CASES[1])
     cfg = kvq.make_config(c)
+    counters = 2 * 8 * 32 * 256
     assert kvq.workspace_bytes(cfg, 8, 0) == 0
     # an all-window cache: one work-group of 4 waves, one slot each
-    assert kvq.workspace_bytes(cfg, 8, 100) == 8 * 32 * 4 * 130 * 4
-    n = kvq.workspace_bytes(cfg, 8, 32768) // (8 * 32 * 130 * 4)
-    assert n >= 2
+    assert kvq.workspace_bytes(cfg, 8, 100) == counters + 8 * 32 * 4 * 130 * 4
+    rest = kvq.workspace_bytes(cfg, 8, 32768) - counters
+    assert rest % (8 * 32 * 130 * 4) == 0
+    assert rest // (8 * 32 * 130 * 4) >= 2 + 4
