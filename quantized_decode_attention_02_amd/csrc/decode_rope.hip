@@ -40,37 +40,43 @@ __device__ __forceinline__ f4_t mfma1(float x, float y, f4_t c) {
 template <int BITS>
 __device__ __forceinline__ void unpack_word(uint32_t w, float* n) {
   if (BITS == 4) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so that every code converts with one
+    // byte-select conversion (v_cvt_f32_ubyteN) instead of a bit-field
+    // extract and a conversion
+    asm volatile("" : "+v"(lo), "+v"(hi));
     for (int k = 0; k < 4; ++k) {
       n[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
       n[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
     }
   } else {
     for (int r = 0; r < 4; ++r) {
-      const uint32_t c = (w >> (2 * r)) & 0x03030303u;
+      uint32_t c = (w >> (2 * r)) & 0x03030303u;
+      asm volatile("" : "+v"(c));
       for (int k = 0; k < 4; ++k) n[4 * k + r] = (float)((c >> (8 * k)) & 0xFFu);
     }
   }
 }
 
 template <int G, int BITS>
-__global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // value-side MFMAs per k-step (hi/lo of p')
   constexpr int NDG = 4;                 // value scale groups per token
   constexpr int TB = 512 * BITS;         // tile bytes
   constexpr int CPW = 32 / BITS;         // channels per code word
   const Geom& g = a.g;
   __shared__ __attribute__((aligned(16))) float DT[32][32][4];     // [j / 2][d]: cos, sin of j, j + 1
-  // per wave: waves never wait for each other after the table above
-  __shared__ float qs[4][G][kD];                                   // R(q_pos) q, scaled
-  __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD];   // [wave][group][head][channel]
-  __shared__ __attribute__((aligned(16))) float KSZ[4][2][64][4];  // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
+  // per wave: waves never wait for each other after the table above.  Rows
+  // are padded by 16 bytes so that the rows one read gathers (group and head
+  // of QA, group of KSZ) fall in different banks.
+  __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD + 4];   // [wave][group][head][channel]
+  __shared__ __attribute__((aligned(16))) float KSZ[4][2][65][4];      // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
   const float* rope_tab = reinterpret_cast<const float*>(a.p.p[KVQ_PLANE_ROPE]);
-  auto qsw = qs[w];
+  float qx[G], qy[G];   // R(q_pos) q, scaled: channels lane and lane + 64 of every head
 
   // ---------------- offset table (rows 0..31 of the RoPE table: the plane
   // always holds at least 32 rows; rows at or past the cache length are only
@@ -92,10 +98,9 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
     for (int m = 0; m < G; ++m) {
       const int64_t qb = ((int64_t)b * g.Hq + h * G + m) * kD;
       const float x = __half2float(a.q[qb + lane]), y = __half2float(a.q[qb + lane + 64]);
-      qsw[m][lane] = (x * c - y * s) * a.scale_log2;
-      qsw[m][lane + 64] = (x * s + y * c) * a.scale_log2;
+      qx[m] = (x * c - y * s) * a.scale_log2;
+      qy[m] = (x * s + y * c) * a.scale_log2;
     }
-    wave_sync();
   };
 
   // query tables of the two groups of a tile (group starts t0 and t0 + 32):
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
       const int64_t t = (gg && second) ? t0 + 32 : t0;
       const float2 cs = *reinterpret_cast<const float2*>(rope_tab + t * 128 + 2 * lane);
       for (int m = 0; m < G; ++m) {
-        const float x = qsw[m][lane], y = qsw[m][lane + 64];
+        const float x = qx[m], y = qy[m];
         QA[w][gg][m][lane] = x * cs.x + y * cs.y;
         QA[w][gg][m][lane + 64] = y * cs.x - x * cs.y;
       }
@@ -194,8 +199,8 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
   const int64_t slots = a.hi_tier ? g.hi_slots : g.gmax;
   const bool ring = slots != g.gmax;
 
-  TilePos cur_pos;
-  TileRaw<BITS, false> cur;
+  TilePos cur_pos, nxt_pos;
+  TileRaw<BITS, false> cur, nxt;
   int64_t pair = -1, pk = 0;
   int pb = 0, ph = 0;
 
@@ -212,10 +217,16 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
                          add0, add1);
     reset();
   };
+  auto fetch = [&](TileRaw<BITS, false>& r, const TilePos& tp, int64_t pr) {
+    load_tile<BITS, false, true>(r, tp, lane, kplane + pr * slots * TB, vplane + pr * slots * TB,
+                                 a.p.p[KVQ_PLANE_K_META] + pr * g.gmax * 512,
+                                 a.p.p[KVQ_PLANE_V_META] + pr * g.gmax * 512, nullptr, nullptr, 0, 0);
+  };
 
   TileCursor cs;
   cursor_start(a, rank, cs, lane);
   tile_at(a, cs.t, slots, ring, cur_pos);
+  fetch(cur, cur_pos, cs.pair);
   bool fresh = true;   // the current tile opens an assignment
   for (;;) {
     if (fresh) {
@@ -225,11 +236,13 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
       ph = (int)(pair % g.Hkv);
       load_query(pb, ph);
     }
-    const uint8_t* kpair = kplane + pair * slots * TB;
-    const uint8_t* vpair = vplane + pair * slots * TB;
-    const uint8_t* kmpair = a.p.p[KVQ_PLANE_K_META] + pair * g.gmax * 512;
-    const uint8_t* vmpair = a.p.p[KVQ_PLANE_V_META] + pair * g.gmax * 512;
-    load_tile<BITS, false, true>(cur, cur_pos, lane, kpair, vpair, kmpair, vmpair, nullptr, nullptr, 0, 0);
+    // the next tile's loads go out before this one is computed
+    bool ends = false;
+    const bool more = cursor_next(a, cs, lane, &ends);
+    if (more) {
+      tile_at(a, cs.t, slots, ring, nxt_pos);
+      fetch(nxt, nxt_pos, cs.pair);
+    }
     const int nvalid = cur_pos.nvalid;
     const bool tok_ok = lane < nvalid;
     float vs[NDG], vz[NDG];
@@ -277,12 +290,10 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(MfmaArgs a) {
     value_mfma<G, BITS, false, HL, NDG>(cur.vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
 
-    // the claim went out a tile ago
-    bool ends = false;
-    const bool more = cursor_next(a, cs, lane, &ends);
     if (ends) flush();
     if (!more) break;
-    tile_at(a, cs.t, slots, ring, cur_pos);
+    cur = nxt;
+    cur_pos = nxt_pos;
     fresh = ends;
   }
 }
