@@ -46,11 +46,12 @@ METRIC = "decode-attn effective KV GB/s (% of HBM peak) + attended tokens/s, INT
 # for the kernel sources they were taken with (sha256 over COUNTER_SOURCES);
 # any change there reports traffic as null until the counters are taken again.
 COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
+                   "quantized_decode_attention_02_amd/csrc/decode_common.h",
                    "quantized_decode_attention_02_amd/csrc/kvq_device.h",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "94a34706f6369423f77e0b56adc42aa53dfebfd421f96248792cf8660529e9e4", "fetch_kib": 666200, "write_kib": 9020,
+    1: {"sources_sha256": "143195d65258f59c5b6b6ecc606a54264bf89dac2e967656c728b9f3232ac056", "fetch_kib": 664809, "write_kib": 4210,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
