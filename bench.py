@@ -11,10 +11,17 @@ so every step does identical work and decode always attends T tokens.
 Reported (one JSON line on stdout):
   value        algorithmic decode bytes (codes + fp16 scales/zeros + fp16
                window) / step time, GB/s; inputs resident in HBM
-  roofline     the split-K decode kernel alone: algorithmic bytes per launch /
-               its average duration (HIP events on the launch stream) against
-               the 8 TB/s HBM peak; traffic = counter-measured HBM bytes per
-               launch (null when the kernel sources changed since)
+  value is measured over back-to-back steps, where the tail of one step's
+  reads is still in the 256 MB Infinity Cache when the next step starts.
+  roofline     the split-K decode kernel alone, cold: algorithmic bytes per
+               launch / its average duration (HIP events on the launch
+               stream) over --cold-steps extra steps, each after a 512 MB read
+               that sweeps the Infinity Cache and the L2s, against the 8 TB/s
+               HBM peak (the back-to-back figure is reported beside it);
+               traffic = counter-measured HBM bytes per launch (null when the
+               kernel sources changed since)
+  append       (chunked-prefill workloads) the workload's multi-token append
+               timed apart: (fp16 read + packed write) bytes / time
   cpu_baseline the CPU oracle on the same step (append one token + dequantize
                + fp64 attention) over a bounded sample of the workload's
                (sequence, kv head) pairs, one process per core
@@ -195,6 +202,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps, each after a 512 MB read that sweeps the caches; the "
+                         "roofline figure is their decode kernel's average")
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--cpu-pairs", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,8 +260,35 @@ def main():
     cache = kvq.KVCache(cfg, w["batch"], T)
     cache.append(k0, v0)
     torch.cuda.synchronize()
+    chunk = None
+    if w.get("prefill") and w["cfg"]["scheme"] == "block128":
+        n = w["prefill"]   # the workload's chunked-prefill append: its last n tokens
+        chunk = (n, torch.cat([k0[:, T - n:], k1], 1).contiguous(), torch.cat([v0[:, T - n:], v1], 1).contiguous())
     del k0, v0
     log(f"cache built: {cache.length} tokens")
+
+    append_rec = None
+    if chunk is not None:
+        # the chunked-prefill append timed apart (it rewrites the same blocks)
+        n, kp, vp = chunk
+        ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for i in range(12):
+            cache.length = T - n
+            if i >= 2:
+                ev_a[i - 2][0].record()
+            cache.append(kp, vp)
+            if i >= 2:
+                ev_a[i - 2][1].record()
+        torch.cuda.synchronize()
+        a_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
+        rd = w["batch"] * n * w["num_kv_heads"] * 2 * 128 * 2
+        wr = w["batch"] * n * w["num_kv_heads"] * 2 * 66
+        append_rec = {"tokens_per_seq": n, "ms": round(a_ms, 5), "read_bytes": rd, "write_bytes": wr,
+                      "gbs": round((rd + wr) / (a_ms / 1e3) / 1e9, 2),
+                      "frac": round((rd + wr) / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"chunked append of {n} tokens: {a_ms:.4f} ms")
+        del kp, vp, chunk
+        cache.length = T - 1
 
     cache.append(k1, v1)
     ws = cache.new_workspace()
@@ -285,10 +322,28 @@ def main():
     k_ms = [a.elapsed_time(b) for a, b in events]
     k_avg = float(np.mean(k_ms))
 
+    # The same steps with the 256 MB Infinity Cache and the L2s swept before
+    # each one by reading a 512 MB buffer (clean lines, so no write-back
+    # competes with the kernel), outside the events.  Back to back, the tail
+    # of one step's reads is still cached when the next step starts; the
+    # roofline figure uses these cold launches.
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    ev_c = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.cold_steps)]
+    for e in ev_c:
+        scratch.sum()
+        step(e)
+    torch.cuda.synchronize()
+    k_cold_ms = [a.elapsed_time(b) for a, b in ev_c]
+    k_cold = float(np.mean(k_cold_ms))
+    del scratch
+
     nbytes = decode_bytes(w, T)
     value = nbytes / (ms_step / 1e3) / 1e9
-    achieved = nbytes / (k_avg / 1e3) / 1e9
+    achieved = nbytes / (k_cold / 1e3) / 1e9
+    achieved_warm = nbytes / (k_avg / 1e3) / 1e9
     attended = w["batch"] * T / (ms_step / 1e3)
+    kname = "decode_rope_kernel" if w["cfg"]["pre_rope"] else "decode_mfma_kernel"
     traffic = counter_traffic(w["id"])
     res = {
         "metric": METRIC,
@@ -311,16 +366,23 @@ def main():
                    "decode_bytes": nbytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "attended_tokens_per_s": round(attended, 1),
+        "bytes_per_attended_token": round(nbytes / (w["batch"] * T), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                      "algorithmic_bytes": nbytes,
-                     "kernel": "decode_mfma_kernel (split-K partials)", "kernel_ms_avg": round(k_avg, 5),
-                     "kernel_ms_p10_p90": [round(float(np.percentile(k_ms, 10)), 5),
-                                           round(float(np.percentile(k_ms, 90)), 5)]},
+                     "kernel": f"{kname} (split-K partials)",
+                     "kernel_ms_avg": round(k_cold, 5),
+                     "kernel_ms_p10_p90": [round(float(np.percentile(k_cold_ms, 10)), 5),
+                                           round(float(np.percentile(k_cold_ms, 90)), 5)],
+                     "caches": "Infinity Cache and L2 swept (512 MB read) before each timed launch",
+                     "kernel_ms_avg_back_to_back": round(k_avg, 5),
+                     "achieved_back_to_back": round(achieved_warm, 2)},
         "cpu_baseline": cpu,
     }
+    if append_rec is not None:
+        res["append"] = append_rec
     print(json.dumps(res), flush=True)
 
 

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, co
   const int h = blockIdx.y, b = blockIdx.z;
   load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
   __syncthreads();
-  if (g.hadamard) fwht128_lds(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+  if (g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
   const bool hi = grp * kGroup >= hi_start_new;
   quantize_store(g, p, gl, pair_index(g, b, h), grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
 }
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void kivi_small_append_kernel(Geom g, Planes p
   for (int64_t grp = q0; grp < q1; ++grp) {
     load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
     __syncthreads();
-    if (g.hadamard) fwht128_lds(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+    if (g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
     const bool hi = grp * kGroup >= hi_start_new;
     quantize_store(g, p, gl, pair, grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
   }
@@ -392,89 +392,75 @@ __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, con
 // 4-bitowemu cache to uchodzi: najpierw obrót"): per token vector y (rotated
 // when configured) a = max|y|, s_h = fp16(fl32(a / 7)),
 // c = clamp(rint(fl32(y / s_h)), -7, 7) (0 when s_h == 0), stored nibble c + 8.
-// One block per 32-token tile that overlaps [T0, T0 + n_new); tokens of the
+// One work-group per 32-token tile that overlaps [T0, T0 + n_new); tokens of the
 // tile outside that range keep their stored nibbles (value tiles hold two
 // tokens per byte).
 __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, const __half* k_new,
                                                               const __half* v_new, int64_t n_new,
                                                               int64_t T0, int64_t tile0) {
-  __shared__ float xs[2][kGroup][kD];
-  __shared__ uint8_t cs[2][kGroup][kD];
-  __shared__ float sc[2][kGroup];
-  const int tid = threadIdx.x;
+  // wave w quantizes 16 vectors: tensor w / 2 (keys, values), tokens
+  // 16 (w % 2) .. + 15 of the tile; a vector lives in the wave's registers,
+  // lane l holding elements 2l and 2l + 1, which are also the two nibbles of
+  // byte l of its packed row
+  __shared__ uint8_t vcode[kGroup][kD];   // value nibbles (c + 8), [token][channel]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t tile = tile0 + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t pair = pair_index(g, b, h);
   const int64_t T1 = T0 + n_new;
   const int64_t tbase = tile * kGroup;
+  const int tensor = w >> 1, tok0 = 16 * (w & 1);
+  const __half* src = tensor ? v_new : k_new;
 
-  for (int e = tid; e < 2 * kGroup * 16; e += 256) {
-    const int tensor = e >> 9, r = e & 511;
-    const int tok = r >> 4, c8 = r & 15;
-    const int64_t t = tbase + tok;
-    float* dst = &xs[tensor][tok][8 * c8];
-    if (t >= T0 && t < T1) {
-      const __half* src = (tensor ? v_new : k_new) + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD;
-      const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
-      const __half* hv = reinterpret_cast<const __half*>(&raw);
-      for (int i = 0; i < 8; ++i) dst[i] = __half2float(hv[i]);
-    } else {
-      for (int i = 0; i < 8; ++i) dst[i] = 0.0f;
-    }
+  uint32_t raw[16];   // all 16 vectors in flight at once
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = tbase + tok0 + i;
+    raw[i] = (t >= T0 && t < T1)
+                 ? *reinterpret_cast<const uint32_t*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD +
+                                                      2 * lane)
+                 : 0u;
   }
-  __syncthreads();
-  if (g.hadamard) fwht128_lds(&xs[0][0][0], 2 * kGroup, tid, 256);
-
-  if (tid < 2 * kGroup) {
-    const int tensor = tid >> 5, tok = tid & 31;
-    float a = 0.0f;
-    for (int i = 0; i < kD; ++i) a = fmaxf(a, fabsf(xs[tensor][tok][i]));
-    const uint16_t sb = float_to_half_bits(a / 7.0f);
-    sc[tensor][tok] = half_bits_to_float(sb);
-    const int64_t t = tbase + tok;
-    if (t >= T0 && t < T1) {
-      uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
-      sp[pair * g.gmax * kGroup + t] = sb;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < 2 * kGroup * kD; e += 256) {
-    const int tensor = e >> 12, tok = (e >> 7) & 31, d = e & 127;
-    const float s = sc[tensor][tok];
-    float c = 0.0f;
-    if (s != 0.0f) c = fminf(fmaxf(rintf(xs[tensor][tok][d] / s), -7.0f), 7.0f);
-    cs[tensor][tok][d] = (uint8_t)((int)c + 8);
-  }
-  __syncthreads();
   uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * 2048;
-  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * 2048;
-  // key tile: 8 consecutive bytes belong to one token row
-  {
-    const int o0 = tid * 8;
-    const int t = (o0 & 511) >> 4;
-    const int64_t tt = tbase + t;
-    if (tt >= T0 && tt < T1) {
-      uint8_t buf[8];
-      for (int k = 0; k < 8; ++k) {
-        const int o = o0 + k;
-        const int cb = (o >> 9) * 16 + (o & 15);
-        buf[k] = (uint8_t)(cs[0][t][2 * cb] | (cs[0][t][2 * cb + 1] << 4));
-      }
-      uint2 w;
-      w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
-      w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
-      *reinterpret_cast<uint2*>(kt + o0) = w;
+  uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]) +
+                 pair * g.gmax * kGroup;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = tok0 + i;
+    const int64_t t = tbase + tok;
+    const bool in = t >= T0 && t < T1;   // the same for the whole wave
+    float e0 = __half2float(__ushort_as_half((uint16_t)(raw[i] & 0xFFFFu)));
+    float e1 = __half2float(__ushort_as_half((uint16_t)(raw[i] >> 16)));
+    if (g.hadamard) fwht128_reg(e0, e1, lane);
+    const float a = wave_max64(fmaxf(fabsf(e0), fabsf(e1)));
+    const uint16_t sb = float_to_half_bits(a / 7.0f);
+    const float s = half_bits_to_float(sb);
+    float c0 = 0.0f, c1 = 0.0f;
+    if (s != 0.0f) {
+      c0 = fminf(fmaxf(rintf(e0 / s), -7.0f), 7.0f);
+      c1 = fminf(fmaxf(rintf(e1 / s), -7.0f), 7.0f);
     }
+    const uint32_t nib0 = (uint32_t)((int)c0 + 8), nib1 = (uint32_t)((int)c1 + 8);
+    if (tensor == 0) {
+      if (in) kt[(lane >> 4) * 512 + 16 * tok + (lane & 15)] = (uint8_t)(nib0 | (nib1 << 4));
+    } else {
+      *reinterpret_cast<uint16_t*>(&vcode[tok][2 * lane]) = (uint16_t)(nib0 | (nib1 << 8));
+    }
+    if (in && lane == 0) sp[t] = sb;
   }
-  // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k+1 (high)
+  __syncthreads();
+  // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k + 1 (high)
+  // of channel d; a byte with one token outside [T0, T1) keeps that token's
+  // stored nibble
+  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * 2048;
   for (int o = tid; o < 2048; o += 256) {
     const int d = o >> 4, kb = o & 15;
     const int64_t t0 = tbase + 2 * kb, t1 = t0 + 1;
     const bool in0 = t0 >= T0 && t0 < T1, in1 = t1 >= T0 && t1 < T1;
     if (!in0 && !in1) continue;
     uint8_t v = (in0 && in1) ? 0 : vt[o];
-    if (in0) v = (uint8_t)((v & 0xF0) | cs[1][2 * kb][d]);
-    if (in1) v = (uint8_t)((v & 0x0F) | (cs[1][2 * kb + 1][d] << 4));
+    if (in0) v = (uint8_t)((v & 0xF0) | vcode[2 * kb][d]);
+    if (in1) v = (uint8_t)((v & 0x0F) | (vcode[2 * kb + 1][d] << 4));
     vt[o] = v;
   }
 }

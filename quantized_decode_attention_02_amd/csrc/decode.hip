@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, const float* 
     rot[tid] = qp;
   }
   __syncthreads();
-  if (g.hadamard) fwht128_lds(rot, 1, tid, 256);
+  if (g.hadamard) fwht128_rows(rot, 1, tid, 256);
   if (tid < kD) {
     const float q_part = g.hadamard ? rot[tid] : qp;
     out[((int64_t)b * g.Hq + hq) * kD + tid] = Lt > 0.0f ? (q_part + wp) / Lt : 0.0f;

@@ -73,51 +73,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Normalized FWHT-128 of `nvec` vectors stored as float rows of 128 in LDS,
-// in the fixed fp32 schedule: for h = 1, 2, ..., 64 in that order every pair
-// (x[i], x[i+h]) with bit log2(h) of i clear becomes (a + b, a - b), each one
-// fp32 operation; then every element is multiplied by fp32(1/sqrt(128)).
-// H in Sylvester order is orthonormal after the scaling, so nothing is lost
-// and dot products are kept ([troisinh] "Tại sao nó hoạt động", item 2;
-// [trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót").
-// All threads of the block must call it; it synchronizes internally, on LDS
-// only (the vectors are exchanged through LDS and nothing else).
-__device__ __forceinline__ void fwht128_lds(float* x, int nvec, int tid, int nthreads) {
-  for (int h = 1; h < kD; h <<= 1) {
-    for (int i = tid; i < nvec * 64; i += nthreads) {
-      const int v = i >> 6, pr = i & 63;
-      const int i0 = (pr / h) * 2 * h + (pr % h);
-      float* row = x + v * kD;
-      const float a = row[i0], b = row[i0 + h];
-      row[i0] = a + b;
-      row[i0 + h] = a - b;
-    }
-    lds_barrier();
-  }
-  const float c = c32();
-  for (int i = tid; i < nvec * kD; i += nthreads) x[i] = x[i] * c;
-  lds_barrier();
-}
-
-// fwht128_lds for one wave (64 lanes, one butterfly each per stage), same
-// schedule and arithmetic.
-__device__ __forceinline__ void fwht128_wave(float* x, int nvec, int lane) {
-  for (int h = 1; h < kD; h <<= 1) {
-    for (int i = lane; i < nvec * 64; i += 64) {
-      const int v = i >> 6, pr = i & 63;
-      const int i0 = (pr / h) * 2 * h + (pr % h);
-      float* row = x + v * kD;
-      const float a = row[i0], b = row[i0 + h];
-      row[i0] = a + b;
-      row[i0 + h] = a - b;
-    }
-    wave_sync();
-  }
-  const float c = c32();
-  for (int i = lane; i < nvec * kD; i += 64) x[i] = x[i] * c;
-  wave_sync();
-}
-
 // Cross-lane reductions without LDS round trips.
 // DPP lane permutations within a 16-lane row (full rows, so every lane has a
 // source): xor 1, xor 2, reverse 8, reverse 16.
@@ -150,6 +105,85 @@ __device__ __forceinline__ float wave_sum64(float v) {
 __device__ __forceinline__ float wave_max64(float v) {
   v = half_max(v);
   return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// Value of lane (lane ^ M) of the wave: M = 1, 2 by DPP quad permutes, 4, 8, 16
+// by ds_swizzle in bitmask mode (within 32 lanes), 32 by ds_bpermute.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+  if (M == 1) return dpp<0xB1>(v);
+  if (M == 2) return dpp<0x4E>(v);
+  if (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+  if (M == 8) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+  if (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
+}
+
+// One butterfly stage h = 2M of fwht128_reg: this lane's elements pair with
+// lane (lane ^ M)'s; the lane holding the lower index keeps a + b, the other
+// a - b, a being the lower element.  Both are computed as p + (+-e) (x + y
+// and y + x, and a + (-b) and a - b, are the same IEEE operation), the sign
+// flip an exact xor.
+template <int M>
+__device__ __forceinline__ void fwht_stage(float& e0, float& e1, int lane) {
+  const float p0 = lane_xor<M>(e0, lane), p1 = lane_xor<M>(e1, lane);
+  const uint32_t flip = (lane & M) ? 0x80000000u : 0u;
+  e0 = p0 + __uint_as_float(__float_as_uint(e0) ^ flip);
+  e1 = p1 + __uint_as_float(__float_as_uint(e1) ^ flip);
+}
+
+// Normalized FWHT-128 of one vector held in the registers of a wave, lane l
+// holding elements 2l (e0) and 2l + 1 (e1), in the fixed fp32 schedule: for
+// h = 1, 2, ..., 64 in that order every pair (x[i], x[i+h]) with bit log2(h)
+// of i clear becomes (a + b, a - b), each one fp32 operation; then every
+// element is multiplied by fp32(1/sqrt(128)).  H in Sylvester order is
+// orthonormal after the scaling, so nothing is lost and dot products are kept
+// ([troisinh] "Tại sao nó hoạt động", item 2; [trefon] "Jak 4-bitowemu cache
+// to uchodzi: najpierw obrót").  Stage h = 1 stays in the lane; stage h = 2M
+// exchanges with lane l ^ M through DPP / ds_swizzle / ds_bpermute: no LDS
+// memory, no barrier.
+__device__ __forceinline__ void fwht128_reg(float& e0, float& e1, int lane) {
+  {
+    const float a = e0, b = e1;
+    e0 = a + b;
+    e1 = a - b;
+  }
+  fwht_stage<1>(e0, e1, lane);
+  fwht_stage<2>(e0, e1, lane);
+  fwht_stage<4>(e0, e1, lane);
+  fwht_stage<8>(e0, e1, lane);
+  fwht_stage<16>(e0, e1, lane);
+  fwht_stage<32>(e0, e1, lane);
+  const float c = c32();
+  e0 = e0 * c;
+  e1 = e1 * c;
+}
+
+// fwht128_reg over `nvec` float rows of 128 in LDS by a whole work-group:
+// wave w transforms rows w, w + nthreads / 64, ... in its registers and
+// writes them back.  The rows must be complete when it is called; it ends
+// with a barrier on LDS.
+__device__ __forceinline__ void fwht128_rows(float* x, int nvec, int tid, int nthreads) {
+  const int lane = tid & 63;
+  for (int v = tid >> 6; v < nvec; v += nthreads >> 6) {
+    float2* r = reinterpret_cast<float2*>(x + v * kD) + lane;
+    float2 e = *r;
+    fwht128_reg(e.x, e.y, lane);
+    *r = e;
+  }
+  lds_barrier();
+}
+
+// The same for rows of one wave's own (wave barriers only).
+__device__ __forceinline__ void fwht128_rows_wave(float* x, int nvec, int lane) {
+  wave_sync();
+  for (int v = 0; v < nvec; ++v) {
+    float2* r = reinterpret_cast<float2*>(x + v * kD) + lane;
+    float2 e = *r;
+    fwht128_reg(e.x, e.y, lane);
+    *r = e;
+  }
+  wave_sync();
 }
 
 }  // namespace kvq
