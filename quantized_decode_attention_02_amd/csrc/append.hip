@@ -29,7 +29,23 @@ namespace {
 struct GroupParams {
   uint16_t s_bits, z_bits;
   float s, z;
+  float rs;   // fl32(1 / s) (0 when s == 0)
 };
+
+// rint(fl32(d / s)) without a full IEEE division per element, for
+// quotients a caller clamps to a code range.  q0 = fl32(d * rs) with
+// rs = fl32(1 / s) is within 2^-23 |d / s| + 2^-24 |d / s| <= 2^-19
+// (|q| <= 16) of d / s, and the correctly rounded quotient fl32(d / s) is
+// within 2^-20 of it, so both round to the same integer unless q0 lies within
+// 2^-18 of a half integer.  Such a quotient inside (lo, hi) -- the half
+// integers that can move a clamped code lie there -- sets `risky`, and the
+// caller redoes the group with the division; outside, q0 stands.
+__device__ __forceinline__ float quot_fast(float d, float rs, float lo, float hi, bool& risky) {
+  const float q0 = d * rs;
+  const float r = rintf(q0);
+  risky |= q0 > lo && q0 < hi && fabsf(q0 - r) >= 0.5f - 0x1p-18f;
+  return r;
+}
 
 __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits) {
   const float Q = (float)((1 << bits) - 1);
@@ -38,13 +54,19 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
   gp.z_bits = canonical_half_bits(mn);
   gp.s = half_bits_to_float(gp.s_bits);
   gp.z = half_bits_to_float(gp.z_bits);
+  gp.rs = gp.s == 0.0f ? 0.0f : 1.0f / gp.s;
   return gp;
 }
 
-__device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp, int bits) {
+// Code of x: clamp(rint(fl32(fl32(x - z) / s)), 0, Q), 0 when s == 0, by the
+// reciprocal unless EXACT (see quot_fast; `risky` reports a quotient that
+// needs the division).
+template <bool EXACT>
+__device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp, int bits, bool& risky) {
   if (gp.s == 0.0f) return 0;
   const float Q = (float)((1 << bits) - 1);
-  const float r = rintf((x - gp.z) / gp.s);
+  const float d = x - gp.z;
+  const float r = EXACT ? rintf(d / gp.s) : quot_fast(d, gp.rs, 0.25f, Q - 0.25f, risky);
   return (uint8_t)fminf(fmaxf(r, 0.0f), Q);
 }
 
@@ -66,7 +88,10 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
       mx = fmaxf(mx, xk[t][c]);
     }
     const GroupParams gp = group_params(mn, mx, bits);
-    for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code(xk[t][c], gp, bits);
+    bool risky = false;
+    for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<false>(xk[t][c], gp, bits, risky);
+    if (risky)
+      for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<true>(xk[t][c], gp, bits, risky);
     kmeta[2 * c] = gp.s_bits;
     kmeta[2 * c + 1] = gp.z_bits;
   } else {
@@ -83,10 +108,13 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
       mx = fmaxf(mx, x);
     }
     const GroupParams gp = group_params(mn, mx, bits);
+    bool risky = false;
     for (int i = 0; i < 32; ++i) {
       const int j = (i + t) & 31;
-      cv[t][dg * 32 + j] = quantize_code(row[j], gp, bits);
+      cv[t][dg * 32 + j] = quantize_code<false>(row[j], gp, bits, risky);
     }
+    if (risky)
+      for (int j = 0; j < 32; ++j) cv[t][dg * 32 + j] = quantize_code<true>(row[j], gp, bits, risky);
     vmeta[2 * (t * 4 + dg)] = gp.s_bits;
     vmeta[2 * (t * 4 + dg) + 1] = gp.z_bits;
   }
@@ -214,6 +242,18 @@ __device__ void load_group(const Geom& g, const Planes& p, float (*xk)[kD], floa
     const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c8);
     const __half* hv = reinterpret_cast<const __half*>(&raw);
     for (int i = 0; i < 8; ++i) xk[tok][8 * c8 + i] = __half2float(hv[i]);
+  }
+  if (grp * kGroup >= T0) {
+    // wholly new: token-major rows like the keys, 16-byte pieces
+    for (int e = tid; e < kGroup * 16; e += 256) {
+      const int tok = e >> 4, c8 = e & 15;
+      const int64_t t = grp * kGroup + tok;
+      const uint4 raw =
+          *reinterpret_cast<const uint4*>(v_new + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + 8 * c8);
+      const __half* hv = reinterpret_cast<const __half*>(&raw);
+      for (int i = 0; i < 8; ++i) xv[tok][8 * c8 + i] = __half2float(hv[i]);
+    }
+    return;
   }
   for (int e = tid; e < kGroup * kD; e += 256) {
     const int tok = e >> 7, d = e & 127;
@@ -398,70 +438,102 @@ __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, con
 __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, const __half* k_new,
                                                               const __half* v_new, int64_t n_new,
                                                               int64_t T0, int64_t tile0) {
-  // wave w quantizes 16 vectors: tensor w / 2 (keys, values), tokens
-  // 16 (w % 2) .. + 15 of the tile; a vector lives in the wave's registers,
-  // lane l holding elements 2l and 2l + 1, which are also the two nibbles of
-  // byte l of its packed row
-  __shared__ uint8_t vcode[kGroup][kD];   // value nibbles (c + 8), [token][channel]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The tile's 64 vectors (32 tokens x keys, values) go through 16 rows of
+  // 16 lanes in four passes: vector 16 pass + row, lane i of a row holding
+  // elements 8i .. 8i + 7, which are also its four packed bytes 4i .. 4i + 3.
+  __shared__ uint32_t vnib[kGroup][16];   // value nibbles of a token, 8 channels a word
+  const int tid = threadIdx.x, row = tid >> 4, i = tid & 15;
   const int64_t tile = tile0 + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t pair = pair_index(g, b, h);
   const int64_t T1 = T0 + n_new;
   const int64_t tbase = tile * kGroup;
-  const int tensor = w >> 1, tok0 = 16 * (w & 1);
-  const __half* src = tensor ? v_new : k_new;
 
-  uint32_t raw[16];   // all 16 vectors in flight at once
+  uint4 raw[4];   // all four passes in flight at once
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t t = tbase + tok0 + i;
-    raw[i] = (t >= T0 && t < T1)
-                 ? *reinterpret_cast<const uint32_t*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD +
-                                                      2 * lane)
-                 : 0u;
+  for (int ps = 0; ps < 4; ++ps) {
+    const int v = 16 * ps + row, tensor = v >> 5, tok = v & 31;
+    const int64_t t = tbase + tok;
+    const __half* src = tensor ? v_new : k_new;
+    raw[ps] = (t >= T0 && t < T1)
+                  ? *reinterpret_cast<const uint4*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + 8 * i)
+                  : make_uint4(0, 0, 0, 0);
   }
   uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * 2048;
-  uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]) +
-                 pair * g.gmax * kGroup;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tok = tok0 + i;
+  for (int ps = 0; ps < 4; ++ps) {
+    const int v = 16 * ps + row, tensor = v >> 5, tok = v & 31;
     const int64_t t = tbase + tok;
-    const bool in = t >= T0 && t < T1;   // the same for the whole wave
-    float e0 = __half2float(__ushort_as_half((uint16_t)(raw[i] & 0xFFFFu)));
-    float e1 = __half2float(__ushort_as_half((uint16_t)(raw[i] >> 16)));
-    if (g.hadamard) fwht128_reg(e0, e1, lane);
-    const float a = wave_max64(fmaxf(fabsf(e0), fabsf(e1)));
+    const bool in = t >= T0 && t < T1;
+    const uint32_t w[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __half2float(__ushort_as_half((uint16_t)(w[j] & 0xFFFFu)));
+      x[2 * j + 1] = __half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
+    }
+    if (g.hadamard) fwht128_row16(x, i);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+    const float a = __uint_as_float(row_max_u32(m));
     const uint16_t sb = float_to_half_bits(a / 7.0f);
     const float s = half_bits_to_float(sb);
-    float c0 = 0.0f, c1 = 0.0f;
-    if (s != 0.0f) {
-      c0 = fminf(fmaxf(rintf(e0 / s), -7.0f), 7.0f);
-      c1 = fminf(fmaxf(rintf(e1 / s), -7.0f), 7.0f);
+    // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
+    // code clamped to [-7, 7] lie in (-6.75, 6.75).  If any lane came close
+    // to one, the wave redoes its vectors with the division.
+    float r[8];
+    bool risky = false;
+    const float rs = s != 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, -6.75f, 6.75f, risky);
+    if (__any(risky)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
     }
-    const uint32_t nib0 = (uint32_t)((int)c0 + 8), nib1 = (uint32_t)((int)c1 + 8);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -7.0f), 7.0f) : 0;
+      packed |= (uint32_t)(c + 8) << (4 * j);
+    }
     if (tensor == 0) {
-      if (in) kt[(lane >> 4) * 512 + 16 * tok + (lane & 15)] = (uint8_t)(nib0 | (nib1 << 4));
+      if (in) *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;
     } else {
-      *reinterpret_cast<uint16_t*>(&vcode[tok][2 * lane]) = (uint16_t)(nib0 | (nib1 << 8));
+      vnib[tok][i] = packed;
     }
-    if (in && lane == 0) sp[t] = sb;
+    if (in && i == 0) {
+      uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
+      sp[pair * g.gmax * kGroup + t] = sb;
+    }
   }
   __syncthreads();
   // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k + 1 (high)
   // of channel d; a byte with one token outside [T0, T1) keeps that token's
-  // stored nibble
+  // stored nibble.  Thread tid builds bytes 8 tid .. 8 tid + 7 (one row d).
   uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * 2048;
-  for (int o = tid; o < 2048; o += 256) {
-    const int d = o >> 4, kb = o & 15;
-    const int64_t t0 = tbase + 2 * kb, t1 = t0 + 1;
-    const bool in0 = t0 >= T0 && t0 < T1, in1 = t1 >= T0 && t1 < T1;
-    if (!in0 && !in1) continue;
-    uint8_t v = (in0 && in1) ? 0 : vt[o];
-    if (in0) v = (uint8_t)((v & 0xF0) | vcode[2 * kb][d]);
-    if (in1) v = (uint8_t)((v & 0x0F) | (vcode[2 * kb + 1][d] << 4));
-    vt[o] = v;
+  {
+    const int d = tid >> 1, kb0 = 8 * (tid & 1);
+    const int wd = d >> 3, sh = 4 * (d & 7);
+    const bool whole = tbase + 2 * kb0 >= T0 && tbase + 2 * kb0 + 16 <= T1;
+    uint32_t out[2] = {0, 0};
+    if (!whole) {
+      const uint2 old = *reinterpret_cast<const uint2*>(vt + 8 * tid);
+      out[0] = old.x;
+      out[1] = old.y;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int kb = kb0 + k;
+      const int64_t t0 = tbase + 2 * kb, t1 = t0 + 1;
+      const bool in0 = t0 >= T0 && t0 < T1, in1 = t1 >= T0 && t1 < T1;
+      uint32_t byte = (out[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      if (in0) byte = (byte & 0xF0u) | ((vnib[2 * kb][wd] >> sh) & 0xFu);
+      if (in1) byte = (byte & 0x0Fu) | (((vnib[2 * kb + 1][wd] >> sh) & 0xFu) << 4);
+      out[k >> 2] = (out[k >> 2] & ~(0xFFu << (8 * (k & 3)))) | (byte << (8 * (k & 3)));
+    }
+    const bool any_in = tbase + 2 * kb0 + 16 > T0 && tbase + 2 * kb0 < T1;
+    if (any_in) *reinterpret_cast<uint2*>(vt + 8 * tid) = make_uint2(out[0], out[1]);
   }
 }
 

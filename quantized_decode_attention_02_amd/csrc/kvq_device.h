@@ -159,6 +159,62 @@ __device__ __forceinline__ void fwht128_reg(float& e0, float& e1, int lane) {
   e1 = e1 * c;
 }
 
+// Value of lane (lane ^ M) within a 16-lane row: M = 1, 2 by DPP quad
+// permutes, 4, 8 by ds_swizzle in bitmask mode.
+template <int M>
+__device__ __forceinline__ uint32_t row_xor(uint32_t v) {
+  if (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  if (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  if (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);
+}
+
+// Cross-lane butterfly stage h = 8M of fwht128_row16: with p the partner's
+// element, the lower lane keeps e + p and the upper one p - e, both as one
+// exactly rounded fma(e, +-1, p).
+template <int M>
+__device__ __forceinline__ void fwht_row_stage(float* x, int i) {
+  const float sgn = (i & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __uint_as_float(row_xor<M>(__float_as_uint(x[j])));
+    x[j] = fmaf(x[j], sgn, p);
+  }
+}
+
+// fwht128_reg for a vector spread over a 16-lane row, lane i of the row
+// holding elements 8i .. 8i + 7 in x[0..7] (four vectors per wave).  Same
+// schedule and fp32 operations: stages h = 1, 2, 4 inside the lane, h = 8,
+// 16, 32, 64 with lanes i ^ 1, i ^ 2, i ^ 4, i ^ 8; then the scaling.
+__device__ __forceinline__ void fwht128_row16(float* x, int i) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+      const float a = x[j], b = x[j + h];
+      x[j] = a + b;
+      x[j + h] = a - b;
+    }
+  }
+  fwht_row_stage<1>(x, i);
+  fwht_row_stage<2>(x, i);
+  fwht_row_stage<4>(x, i);
+  fwht_row_stage<8>(x, i);
+  const float c = c32();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = x[j] * c;
+}
+
+// Maximum of a non-negative float over a 16-lane row, on its bit pattern
+// (for non-negative floats the integer order is the numeric order).
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, row_xor<1>(v));
+  v = max(v, row_xor<2>(v));
+  v = max(v, row_xor<4>(v));
+  return max(v, row_xor<8>(v));
+}
+
 // fwht128_reg over `nvec` float rows of 128 in LDS by a whole work-group:
 // wave w transforms rows w, w + nthreads / 64, ... in its registers and
 // writes them back.  The rows must be complete when it is called; it ends

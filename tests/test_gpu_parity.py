@@ -118,3 +118,70 @@ def test_capacity_error_leaves_cache_untouched():
         g.append(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda())
     assert ei.value.status == -3 and g.length == 100
     compare_planes(g, o, s, h)
+
+
+def tie_tokens(rng, T, hkv, q_levels, s, base):
+    """fp16 keys and values [1, T, hkv, 128] whose quantization hits exact
+    rounding ties: in every 32-token key group (per channel) and every 32-dim
+    value slice (per token) one element is the minimum `base`, one is
+    base + q_levels * s, and the rest are base + (k + 1/2) s, so that
+    (x - z) / s = k + 1/2 exactly and round-to-nearest-even decides."""
+    k = rng.integers(0, q_levels, size=(1, T, hkv, 128))
+    x = base + (k + 0.5) * s
+    kx = x.copy()
+    kx[:, 0::32] = base                       # per-channel group minimum
+    kx[:, 1::32] = base + q_levels * s        # and maximum
+    vx = x.copy()
+    vx[..., 0::32] = base                     # per-token slice minimum
+    vx[..., 1::32] = base + q_levels * s      # and maximum
+    assert np.all(kx.astype(np.float16).astype(np.float64) == kx)
+    assert np.all(vx.astype(np.float16).astype(np.float64) == vx)
+    return kx.astype(np.float16), vx.astype(np.float16)
+
+
+@pytest.mark.parametrize("variant", ["int4", "int2", "block128-plain"])
+def test_rounding_ties(variant):
+    """Quotients exactly halfway between two codes: the kernels' reciprocal
+    fast path must fall back to the division and round to even like the
+    oracle (fp32 round-to-nearest-even on fl32((x - z) / s))."""
+    from oracle.cache import OracleCache
+    from quantized_decode_attention_02_amd import kvq
+    T, hkv = 32 * 6 + 128, 2
+    s = 3.0 / 32.0   # an fp16 scale that is not a power of two
+    if variant == "block128-plain":
+        # symmetric: a = max |y| = 7 s, y = (k + 1/2) s with k in -7 .. 6
+        rng = np.random.default_rng(7)
+        k = rng.integers(-7, 7, size=(1, T, hkv, 128))
+        y = (k + 0.5) * s
+        y[..., 0] = 7 * s
+        K = y.astype(np.float16)
+        V = (-y).astype(np.float16)
+        assert np.all(K.astype(np.float64) == y)
+    else:
+        q = 15 if variant == "int4" else 3
+        K, V = tie_tokens(np.random.default_rng(5), T, hkv, q, s, base=-0.75)
+    w = make_w(3000, variant, T, batch=1, hq=2 * hkv, hkv=hkv)
+    cfg = wl.library_config(w)
+    g = kvq.KVCache(cfg, 1, T)
+    g.append(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda())
+    o = OracleCache(cfg, 1, T)
+    o.append(K, V)
+    torch.cuda.synchronize()
+    say(f"rounding ties {variant}")
+    compare_planes(g, o, [0], list(range(hkv)))
+    compare_dequant(g, o, [0], list(range(hkv)))
+
+
+@pytest.mark.parametrize("variant", ["int4", "int4-prerope"])
+def test_pairs_outnumber_waves(variant):
+    """4096 (sequence, kv head) pairs: more than the waves one launch keeps
+    resident (at most 3 work-groups of 4 waves on each of 256 compute
+    units), so a wave works several pairs in turn, one at a time.  Sampled
+    pairs, first and last included, against the oracle."""
+    B, hkv, T = 512, 8, 32 * 4 + 128 + 5
+    w = make_w(4000, variant, T, batch=B, hq=8, hkv=hkv)
+    seqs, heads = [0, 1, 255, B - 1], [0, hkv - 1]
+    g, o, s, h = build_pair(w, [T], seqs=seqs, heads=heads)
+    say(f"{B * hkv} pairs {variant}")
+    compare_planes(g, o, s, h)
+    check_decode(g, o, w, s, h)
