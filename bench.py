@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "143195d65258f59c5b6b6ecc606a54264bf89dac2e967656c728b9f3232ac056", "fetch_kib": 664809, "write_kib": 4210,
+    1: {"sources_sha256": "b1e1fe98984ca5ce9b60afbf57ec1cd281bb6a9c1966cb16e32007d15048f86d", "fetch_kib": 664938, "write_kib": 4211,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
