@@ -378,11 +378,16 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
   int kk, slot;
   value_slot<BITS>(tl, &kk, &slot);
   const int ks = 8 * gh + kk;
+  // value_mfma masks codes in place, so this token's code carries the factor
+  // 16^(j & 1) (4-bit) or 4^(j & 3) (2-bit), j its nibble / crumb position
+  // within a 16-bit half of its word; its probability takes the inverse (a
+  // power of two: exact)
+  const float inv_f = BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
   for (int d = 0; d < NDG; ++d)
     for (int m = 0; m < G; ++m) {
       const float x = p[m] * vs[d];
       _Float16 hi, lo;
-      split_half(x, &hi, &lo);
+      split_half(x * inv_f, &hi, &lo);
       PLw[d][ks][0][m][slot] = hi;
       if (HL == 1) PLw[d][ks][0][G + m][slot] = lo;
       else PLw[d][ks][1][m][slot] = lo;
@@ -400,16 +405,23 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
       const int dg = BLOCK ? 0 : (gh + 2 * hf);
       for (int u = 0; u < BITS; ++u) {
         const uint32_t x = vc[gg][hf][u];
-        // unpack one dword: 8 tokens (4-bit) or 16 tokens (2-bit) as pairs
+        // one dword: 8 tokens (4-bit) or 16 tokens (2-bit), two per pr[] (one
+        // per 16-bit half), masked in place in the low byte of each half: the
+        // code of position j enters as n * 2^-24 times 16^(j & 1) or
+        // 4^(j & 3), which stage_probs divided out of its probability
         constexpr int NP = (BITS == 4) ? 4 : 8;
         uint32_t pr[NP];
+        const uint32_t x8 = x >> 8;
         if (BITS == 4) {
           pr[0] = x & 0x000F000Fu;
-          pr[1] = (x >> 4) & 0x000F000Fu;
-          pr[2] = (x >> 8) & 0x000F000Fu;
-          pr[3] = (x >> 12) & 0x000F000Fu;
+          pr[1] = x & 0x00F000F0u;
+          pr[2] = x8 & 0x000F000Fu;
+          pr[3] = x8 & 0x00F000F0u;
         } else {
-          for (int j = 0; j < 8; ++j) pr[j] = (x >> (2 * j)) & 0x00030003u;
+          for (int j = 0; j < 4; ++j) {
+            pr[j] = x & (0x00030003u << (2 * j));
+            pr[4 + j] = x8 & (0x00030003u << (2 * j));
+          }
         }
         for (int q2 = 0; q2 < NP / 2; ++q2) {
           const int ks = 8 * gg + (NP / 2) * u + q2;   // k-step of pairs (2 q2, 2 q2 + 1)
