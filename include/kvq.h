@@ -150,11 +150,12 @@ kvq_status kvq_layout(const kvq_config* cfg, int64_t batch, int64_t max_tokens,
 
 /* Bytes of the device workspace kvq_decode_attn needs for `batch` sequences
  * of `length` cached tokens.  Writes *bytes.  The workspace starts with
- * KVQ_COUNTER_BYTES(batch * num_kv_heads) bytes of work counters, which must
- * be zero before the workspace is first used; every completed decode call
- * leaves them zero again, so zero the workspace once when it is allocated.
- * The split-K partials follow (running max, sum and 128 accumulators per
- * query head and partial). */
+ * KVQ_COUNTER_BYTES(batch * num_kv_heads) bytes of work counters; the split-K
+ * partials follow (running max, sum and 128 accumulators per query head and
+ * partial).  The workspace must be all zero before its first use: every
+ * completed decode (kvq_decode_attn, or kvq_decode_partials followed by
+ * kvq_decode_merge) leaves every byte it used zero again, so one workspace,
+ * zeroed once when it is allocated, serves caches of any shape. */
 #define KVQ_COUNTER_BYTES(pairs) (2 * (uint64_t)(pairs) * 256)
 kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t length,
                                uint64_t* bytes);
@@ -194,7 +195,9 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
  *              counters zero (see kvq_workspace_bytes).  Calls that overlap
  *              in time must not share a workspace.
  * Accuracy: within |d| <= 2e-3 + 1e-2 |ref| of fp64 attention over the same
- * dequantized cache.  length == 0 writes zeros. */
+ * dequantized cache.  length == 0 writes zeros.  Waves take token chunks
+ * dynamically, so the grouping of the fp32 partial sums, and with it the
+ * last bits of out, can differ from call to call. */
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                            int64_t q_pos, float sm_scale, void* out, void* workspace,
                            uint64_t workspace_bytes, void* stream);

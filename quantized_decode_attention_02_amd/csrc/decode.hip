@@ -32,14 +32,14 @@ namespace {
 // from the lane that holds them.  The four waves combine in LDS.  Quantized
 // slots (below nq) and window slots are summed apart so that a Hadamard cache
 // rotates back only the quantized part.
-__global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, const float* ws, float* out,
+__global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, float* ws, float* out,
                                                            int64_t nq, int64_t n) {
   __shared__ float wml[4][2];
   __shared__ float wo[4][2][kD];
   __shared__ float rot[kD];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const float* base = ws + ((int64_t)b * g.Hq + hq) * n * kPartial;
+  float* base = ws + ((int64_t)b * g.Hq + hq) * n * kPartial;
   float M = -INFINITY, L = 0.0f;
   float q0 = 0.0f, q1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
   for (int64_t first = w; first < n; first += 256) {
@@ -89,6 +89,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, const float* 
   wo[w][1][2 * lane] = w0;
   wo[w][1][2 * lane + 1] = w1;
   __syncthreads();
+  // every record of this head has been read: zero them, so that a finished
+  // call leaves the whole workspace zero (the chunk counters of any later
+  // call, whatever its cache, start from zero)
+  for (int64_t e = tid; e < n * kPartial / 2; e += 256) reinterpret_cast<float2*>(base)[e] = make_float2(0.0f, 0.0f);
   float Mt = -INFINITY;
   for (int i = 0; i < 4; ++i) Mt = fmaxf(Mt, wml[i][0]);
   float sc[4], Lt = 0.0f;

@@ -185,3 +185,48 @@ def test_pairs_outnumber_waves(variant):
     say(f"{B * hkv} pairs {variant}")
     compare_planes(g, o, s, h)
     check_decode(g, o, w, s, h)
+
+
+def counter_bytes(cache):
+    # two 256-byte lines per (sequence, kv head): the decode chunk counters
+    return 2 * cache.batch * cache.hkv * 256
+
+
+@pytest.mark.parametrize("variant", ["int4", "mixed-hadamard", "int4-prerope", "block128"])
+def test_workspace_counters_left_zero(variant):
+    """Every decode call hands the workspace back with its chunk counters at
+    zero, also when the partials launch runs several times before a merge;
+    a workspace reused across caches of other sizes and tiers gives the same
+    output as a fresh one.  The partial records are filled with garbage
+    first: every slot must be written by the call that reads it."""
+    w = make_w(5000, variant, 4096 + 300, batch=3, hq=8, hkv=2)
+    g, o, s, h = build_pair(w, [4096 + 300])
+    q = torch.from_numpy(wl.queries(w)).cuda()
+    ref = g.decode(q).clone()
+    ws = g.new_workspace()
+    nctr = counter_bytes(g) // 4
+    for rep in range(3):
+        ws[nctr:].fill_(float("nan"))
+        for _ in range(rep + 1):
+            g.decode_partials(q, ws, torch.empty_like(ref))
+        out = torch.empty_like(ref)
+        g.decode_merge(q, ws, out)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws.view(torch.int32)).item() == 0, "workspace not left zero"
+        # waves claim chunks dynamically, so partials group tokens differently
+        # from call to call: equal up to the last bits of the fp32 sums
+        assert torch.allclose(out, ref, rtol=1e-4, atol=1e-5), f"repeat {rep}: output differs from a fresh workspace"
+    # the same workspace (large enough) serves a smaller cache of another scheme
+    w2 = make_w(5001, "int2", 700, batch=2, hq=4, hkv=1)
+    g2, o2, s2, h2 = build_pair(w2, [700])
+    assert g2.workspace_bytes() <= ws.numel() * 4
+    q2 = torch.from_numpy(wl.queries(w2)).cuda()
+    out2 = g2.decode(q2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws.view(torch.int32)).item() == 0
+    # and back to the first cache, whose counter area the second one's
+    # partials covered
+    out3 = g.decode(q, workspace=ws)
+    assert torch.allclose(out3, ref, rtol=1e-4, atol=1e-5)
+    assert torch.allclose(out2, g2.decode(q2), rtol=1e-4, atol=1e-5)
+    say(f"workspace counters {variant}: clean")
