@@ -43,7 +43,7 @@ struct GroupParams {
 __device__ __forceinline__ float quot_fast(float d, float rs, float lo, float hi, bool& risky) {
   const float q0 = d * rs;
   const float r = rintf(q0);
-  risky |= q0 > lo && q0 < hi && fabsf(q0 - r) >= 0.5f - 0x1p-18f;
+  risky |= (q0 > lo) & (q0 < hi) & (fabsf(q0 - r) >= 0.5f - 0x1p-18f);
   return r;
 }
 
@@ -61,12 +61,19 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
 // Code of x: clamp(rint(fl32(fl32(x - z) / s)), 0, Q), 0 when s == 0, by the
 // reciprocal unless EXACT (see quot_fast; `risky` reports a quotient that
 // needs the division).
+// Branch-free: with s == 0, rs is 0 and the fast path gives 0; the exact
+// path's quotient (inf or NaN) is discarded by the select.
 template <bool EXACT>
 __device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp, int bits, bool& risky) {
-  if (gp.s == 0.0f) return 0;
   const float Q = (float)((1 << bits) - 1);
   const float d = x - gp.z;
-  const float r = EXACT ? rintf(d / gp.s) : quot_fast(d, gp.rs, 0.25f, Q - 0.25f, risky);
+  float r;
+  if (EXACT) {
+    const float e = rintf(d / gp.s);
+    r = gp.s == 0.0f ? 0.0f : e;
+  } else {
+    r = quot_fast(d, gp.rs, 0.25f, Q - 0.25f, risky);
+  }
   return (uint8_t)fminf(fmaxf(r, 0.0f), Q);
 }
 
@@ -371,16 +378,21 @@ __global__ __launch_bounds__(256) void kivi_small_append_kernel(Geom g, Planes p
     k1 = *reinterpret_cast<const uint4*>(k_new + piece(e1));
     v1 = *reinterpret_cast<const uint4*>(v_new + piece(e1));
   }
-  for (int64_t grp = d0; grp < d1; ++grp) {
-    load_demoted(g, p, gl.xs[0], gl.xs[1], pair, grp, tid);
+  // demotions first, then the groups leaving the window: one quantize_store
+  // for both (the group quantizer is large; a single copy of it keeps the
+  // kernel's code small)
+  const int64_t nd = d1 - d0, nq = q1 - q0;
+  for (int64_t i = 0; i < nd + nq; ++i) {
+    const bool demote = i < nd;
+    const int64_t grp = demote ? d0 + i : q0 + (i - nd);
+    if (demote) {
+      load_demoted(g, p, gl.xs[0], gl.xs[1], pair, grp, tid);
+    } else {
+      load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
+    }
     __syncthreads();
-    quantize_store(g, p, gl, pair, grp, g.lo_bits, false, tid);
-  }
-  for (int64_t grp = q0; grp < q1; ++grp) {
-    load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
-    __syncthreads();
-    if (g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
-    const bool hi = grp * kGroup >= hi_start_new;
+    if (!demote && g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+    const bool hi = !demote && grp * kGroup >= hi_start_new;
     quantize_store(g, p, gl, pair, grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
   }
   __half* kring = reinterpret_cast<__half*>(p.p[KVQ_PLANE_K_WIN]) + pair * kRing * kD;
