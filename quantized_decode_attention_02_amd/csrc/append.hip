@@ -87,18 +87,24 @@ __device__ __forceinline__ uint8_t quantize_code(float x, const GroupParams& gp,
 __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uint8_t (*ck)[kD],
                                uint8_t (*cv)[kD], uint16_t* kmeta, uint16_t* vmeta, int bits,
                                int tid) {
+  // each thread reads its 32 elements from LDS once, into registers
+  float x[kGroup];
   if (tid < kD) {
     const int c = tid;
-    float mn = xk[0][c], mx = xk[0][c];
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) x[t] = xk[t][c];
+    float mn = x[0], mx = x[0];
+#pragma unroll
     for (int t = 1; t < kGroup; ++t) {
-      mn = fminf(mn, xk[t][c]);
-      mx = fmaxf(mx, xk[t][c]);
+      mn = fminf(mn, x[t]);
+      mx = fmaxf(mx, x[t]);
     }
     const GroupParams gp = group_params(mn, mx, bits);
     bool risky = false;
-    for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<false>(xk[t][c], gp, bits, risky);
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<false>(x[t], gp, bits, risky);
     if (risky)
-      for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<true>(xk[t][c], gp, bits, risky);
+      for (int t = 0; t < kGroup; ++t) ck[t][c] = quantize_code<true>(x[t], gp, bits, risky);
     kmeta[2 * c] = gp.s_bits;
     kmeta[2 * c + 1] = gp.z_bits;
   } else {
@@ -108,20 +114,22 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
     const int u = tid - kD;
     const int t = u & 31, dg = u >> 5;
     const float* row = xv[t] + dg * 32;
-    float mn = row[t], mx = row[t];
+    // x[i] = element (i + t) mod 32 of the slice: the 32 lanes of one slice
+    // index hit 32 different LDS banks on every read
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = row[(i + t) & 31];
+    float mn = x[0], mx = x[0];
+#pragma unroll
     for (int i = 1; i < 32; ++i) {
-      const float x = row[(i + t) & 31];
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
     }
     const GroupParams gp = group_params(mn, mx, bits);
     bool risky = false;
-    for (int i = 0; i < 32; ++i) {
-      const int j = (i + t) & 31;
-      cv[t][dg * 32 + j] = quantize_code<false>(row[j], gp, bits, risky);
-    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cv[t][dg * 32 + ((i + t) & 31)] = quantize_code<false>(x[i], gp, bits, risky);
     if (risky)
-      for (int j = 0; j < 32; ++j) cv[t][dg * 32 + j] = quantize_code<true>(row[j], gp, bits, risky);
+      for (int i = 0; i < 32; ++i) cv[t][dg * 32 + ((i + t) & 31)] = quantize_code<true>(x[i], gp, bits, risky);
     vmeta[2 * (t * 4 + dg)] = gp.s_bits;
     vmeta[2 * (t * 4 + dg) + 1] = gp.z_bits;
   }
@@ -310,9 +318,10 @@ struct GroupLds {
 __device__ void quantize_store(const Geom& g, const Planes& p, GroupLds& gl, int64_t pair,
                                int64_t grp, int bits, bool hi, int tid) {
   quantize_group(gl.xs[0], gl.xs[1], gl.cs[0], gl.cs[1], gl.meta[0], gl.meta[1], bits, tid);
-  __syncthreads();
+  lds_barrier();
   store_group(g, p, pair, grp, bits, hi, gl.cs[0], gl.cs[1], gl.meta[0], gl.meta[1], tid);
-  __syncthreads();
+  // LDS only: the group's global stores need not land before gl is reused
+  lds_barrier();
 }
 
 // KIVI: quantize the groups [g0, g1) of every (sequence, kv head), one

@@ -161,7 +161,7 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 // each (low-bit tier, high-bit tier), one launch each.  A launch runs as many
 // waves as fit on the device at once, as a team of equal size per pair (one
 // wave handles several pairs in turn when pairs outnumber waves); a team is
-// no larger than half its pair's tiles.  Chunks are one tile, or two where
+// no larger than its pair's tile count.  Chunks are one tile, or two where
 // every member gets at least 8 chunks on average, so that a claim has a
 // tile's time to come back; teams above 2 * kTeamPerChunkTile waves take
 // team / kTeamPerChunkTile tiles per chunk.  The fp16 window rides on the
@@ -172,7 +172,10 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 #ifndef KVQ_DECODE_CHUNK_MAX
 #define KVQ_DECODE_CHUNK_MAX 2
 #endif
-constexpr int64_t kMinTilesPerWave = 2;
+#ifndef KVQ_MIN_TILES_PER_WAVE
+#define KVQ_MIN_TILES_PER_WAVE 1
+#endif
+constexpr int64_t kMinTilesPerWave = KVQ_MIN_TILES_PER_WAVE;
 #ifndef KVQ_TEAM_PER_CHUNK_TILE
 #define KVQ_TEAM_PER_CHUNK_TILE 16
 #endif
