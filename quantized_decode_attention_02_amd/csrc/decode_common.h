@@ -131,7 +131,7 @@ __device__ __forceinline__ float softmax_step(int m, float s, bool tok_ok, float
                                               float (*zacc)[NDG]) {
   if (__any(s > m_run[m])) {
     const float mnew = fmaxf(m_run[m], wave_max64(s));
-    const float alpha = (m_run[m] == -INFINITY) ? 0.0f : exp2f(m_run[m] - mnew);
+    const float alpha = (m_run[m] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[m] - mnew);
     m_run[m] = mnew;
     l_acc[m] *= alpha;
     o0[m] *= alpha; o1[m] *= alpha; o2[m] *= alpha; o3[m] *= alpha;
@@ -140,7 +140,10 @@ __device__ __forceinline__ float softmax_step(int m, float s, bool tok_ok, float
     }
     for (int d = 0; d < NDG; ++d) zacc[m][d] *= alpha;
   }
-  const float p = tok_ok ? exp2f(s - m_run[m]) : 0.0f;
+  // the hardware exp2 (v_exp_f32, about 1 ulp): it flushes results below
+  // 2^-126 to zero, a probability mass the fp32 sums could not hold anyway;
+  // exp2f would add a denormal-preserving range reduction around it
+  const float p = tok_ok ? __builtin_amdgcn_exp2f(s - m_run[m]) : 0.0f;
   l_acc[m] += p;
   return p;
 }
