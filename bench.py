@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "b1e1fe98984ca5ce9b60afbf57ec1cd281bb6a9c1966cb16e32007d15048f86d", "fetch_kib": 664938, "write_kib": 4211,
+    1: {"sources_sha256": "52bc9e932ae4da9f13671d15b9a48473faf310cbf1302ba0c5abb557d0130d2c", "fetch_kib": 665414, "write_kib": 4211,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
