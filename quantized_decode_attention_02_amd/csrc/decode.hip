@@ -44,6 +44,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, float* ws, fl
   float q0 = 0.0f, q1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
   for (int64_t first = w; first < n; first += 256) {
     const int64_t mine = first + 4 * (int64_t)lane;
+    // eight rows in flight per step; steps past the batch end reread its
+    // last row with weight 0, so the body has no branch to wait behind.
+    // The first step's rows go out with the (m, l) loads, so a head with at
+    // most 32 partials needs one round trip.
+    const int cnt = (int)min((int64_t)64, (n - first + 3) / 4);
+    float2 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t slot = first + 4 * (int64_t)min(k, cnt - 1);
+      v[k] = *reinterpret_cast<const float2*>(base + slot * kPartial + 2 + 2 * lane);
+    }
     float m = -INFINITY, l = 0.0f;
     if (mine < n) {
       m = base[mine * kPartial];
@@ -56,15 +67,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, float* ws, fl
     L = L * r + wave_sum64(l * wt);
     q0 *= r; q1 *= r; w0 *= r; w1 *= r;
     M = Mb;
-    // eight rows in flight per step; steps past the batch end reread its
-    // last row with weight 0, so the body has no branch to wait behind
-    const int cnt = (int)min((int64_t)64, (n - first + 3) / 4);
     for (int i0 = 0; i0 < cnt; i0 += 8) {
-      float2 v[8];
+      if (i0 > 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int64_t slot = first + 4 * (int64_t)min(i0 + k, cnt - 1);
-        v[k] = *reinterpret_cast<const float2*>(base + slot * kPartial + 2 + 2 * lane);
+        for (int k = 0; k < 8; ++k) {
+          const int64_t slot = first + 4 * (int64_t)min(i0 + k, cnt - 1);
+          v[k] = *reinterpret_cast<const float2*>(base + slot * kPartial + 2 + 2 * lane);
+        }
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
