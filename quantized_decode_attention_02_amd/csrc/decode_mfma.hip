@@ -100,7 +100,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BLOCK>())) void decode_mf
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
   __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: read it into a scalar register, so that the
+  // tile walk and its addresses stay on the scalar unit
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
   auto QLw = QL[w];
   auto qsw = qs[w];

@@ -35,27 +35,32 @@ __device__ __forceinline__ f4_t mfma1(float x, float y, f4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(x, y, c, 0, 0, 0);
 }
 
-// Codes of one key row as floats, channels [8 i, 8 i + 8) (4-bit word i) or
-// [16 i, 16 i + 16) (2-bit word i), in channel order.
+// Code c of one key row, channels [8 i, 8 i + 8) (4-bit word i) or
+// [16 i, 16 i + 16) (2-bit word i) in channel order, as the fp16 subnormal
+// c * f * 2^-24 masked in place: part p of the word holds two channels, k and
+// k + CPW / 2, in its low and high halves.  The factor f of channel k is
+// 16^(k & 1) (4-bit) or 4^(k & 3) (2-bit); key_scale_shift() gives the power
+// of two that cancels it together with 2^-24, so that fma(code, s', z) with
+// s' = s * 2^shift is the dequantized key n s + z with one rounding (the
+// product is exact), and the conversion of the code folds into the fma.
 template <int BITS>
-__device__ __forceinline__ void unpack_word(uint32_t w, float* n) {
+__device__ __forceinline__ h2_t key_part(uint32_t w, int p) {
   if (BITS == 4) {
-    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    // opaque to the optimizer, so that every code converts with one
-    // byte-select conversion (v_cvt_f32_ubyteN) instead of a bit-field
-    // extract and a conversion
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    for (int k = 0; k < 4; ++k) {
-      n[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
-      n[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
-    }
+    const uint32_t src = (p & 2) ? (w >> 8) : w;
+    return __builtin_bit_cast(h2_t, src & ((p & 1) ? 0x00F000F0u : 0x000F000Fu));
   } else {
-    for (int r = 0; r < 4; ++r) {
-      uint32_t c = (w >> (2 * r)) & 0x03030303u;
-      asm volatile("" : "+v"(c));
-      for (int k = 0; k < 4; ++k) n[4 * k + r] = (float)((c >> (8 * k)) & 0xFFu);
-    }
+    const uint32_t src = (p & 4) ? (w >> 8) : w;
+    return __builtin_bit_cast(h2_t, src & (0x00030003u << (2 * (p & 3))));
   }
+}
+template <int BITS>
+__device__ __forceinline__ _Float16 key_code(const h2_t* parts, int k) {
+  constexpr int HALF = 16 / BITS;   // channels per half of the word's parts
+  return (k < HALF) ? parts[k % HALF].x : parts[k % HALF].y;
+}
+template <int BITS>
+constexpr int key_scale_shift(int c) {
+  return BITS == 4 ? 24 - 4 * (c & 1) : 24 - 2 * (c & 3);
 }
 
 template <int G, int BITS>
@@ -73,7 +78,10 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) float KSZ[4][2][65][4];      // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: read it into a scalar register, so that the
+  // tile walk and its addresses stay on the scalar unit
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
   const float* rope_tab = reinterpret_cast<const float*>(a.p.p[KVQ_PLANE_ROPE]);
   float qx[G], qy[G];   // R(q_pos) q, scaled: channels lane and lane + 64 of every head
@@ -103,12 +111,17 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     }
   };
 
-  // query tables of the two groups of a tile (group starts t0 and t0 + 32):
-  // u = R(-t0) qs, lane j writes channels j and j + 64 of every head
-  auto build_query = [&](int64_t t0, bool second) {
+  // RoPE table rows of a tile's group starts t0 and t0 + 32 (t0 twice when
+  // the tile has one group): lane j loads the cos / sin of pair j
+  auto group_rows = [&](int64_t t0, bool second, float2* cs) {
+    cs[0] = *reinterpret_cast<const float2*>(rope_tab + t0 * 128 + 2 * lane);
+    cs[1] = *reinterpret_cast<const float2*>(rope_tab + (second ? t0 + 32 : t0) * 128 + 2 * lane);
+  };
+  // query tables of the two groups of a tile from their rows: u = R(-t0) qs,
+  // lane j writes channels j and j + 64 of every head
+  auto build_query_rows = [&](const float2* rows) {
     for (int gg = 0; gg < 2; ++gg) {
-      const int64_t t = (gg && second) ? t0 + 32 : t0;
-      const float2 cs = *reinterpret_cast<const float2*>(rope_tab + t * 128 + 2 * lane);
+      const float2 cs = rows[gg];
       for (int m = 0; m < G; ++m) {
         const float x = qx[m], y = qy[m];
         QA[w][gg][m][lane] = x * cs.x + y * cs.y;
@@ -116,6 +129,11 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
       }
     }
     wave_sync();
+  };
+  auto build_query = [&](int64_t t0, bool second) {
+    float2 rows[2];
+    group_rows(t0, second, rows);
+    build_query_rows(rows);
   };
 
   float m_run[G], l_acc[G];
@@ -201,6 +219,7 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
 
   TilePos cur_pos, nxt_pos;
   TileRaw<BITS, false> cur, nxt;
+  float2 cur_rows[2], nxt_rows[2];   // group_rows() of the tile, loaded with it
   int64_t pair = -1, pk = 0;
   int pb = 0, ph = 0;
 
@@ -227,8 +246,12 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   cursor_start(a, rank, cs, lane);
   tile_at(a, cs.t, slots, ring, cur_pos);
   fetch(cur, cur_pos, cs.pair);
+  group_rows(cur_pos.base, cur_pos.nvalid > 32, cur_rows);
   bool fresh = true;   // the current tile opens an assignment
-  for (;;) {
+  // One tile: the next one's loads go out into n, then c is computed.  The
+  // loop below alternates the two buffers, so no tile is copied.
+  auto tile_step = [&](TileRaw<BITS, false>& c, const TilePos& c_pos, const float2* c_rows,
+                       TileRaw<BITS, false>& n, TilePos& n_pos, float2* n_rows) -> bool {
     if (fresh) {
       pair = cs.pair;
       pk = cs.k;
@@ -240,41 +263,46 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     bool ends = false;
     const bool more = cursor_next(a, cs, lane, &ends);
     if (more) {
-      tile_at(a, cs.t, slots, ring, nxt_pos);
-      fetch(nxt, nxt_pos, cs.pair);
+      tile_at(a, cs.t, slots, ring, n_pos);
+      fetch(n, n_pos, cs.pair);
+      group_rows(n_pos.base, n_pos.nvalid > 32, n_rows);
     }
-    const int nvalid = cur_pos.nvalid;
+    const int nvalid = c_pos.nvalid;
     const bool tok_ok = lane < nvalid;
     float vs[NDG], vz[NDG];
-    value_meta<BITS, false, NDG>(cur, tok_ok, vs, vz);
+    value_meta<BITS, false, NDG>(c, tok_ok, vs, vz);
 
-    // key (s, z) of both groups into KSZ (channel c -> pair c mod 64, half c / 64)
+    // key (s, z) of both groups into KSZ (channel ch -> pair ch mod 64, half ch / 64)
     {
-      const uint32_t mw[4] = {cur.kmr.x, cur.kmr.y, cur.kmr.z, cur.kmr.w};
+      const uint32_t mw[4] = {c.kmr.x, c.kmr.y, c.kmr.z, c.kmr.w};
       for (int e = 0; e < 4; ++e) {
-        const int c = 4 * tl + e;
-        KSZ[w][gh][c & 63][c >> 6] = half_bits_to_float((uint16_t)(mw[e] & 0xFFFF));
-        KSZ[w][gh][c & 63][2 + (c >> 6)] = half_bits_to_float((uint16_t)(mw[e] >> 16));
+        const int ch = 4 * tl + e;   // ch & 3 == e
+        KSZ[w][gh][ch & 63][ch >> 6] =
+            half_bits_to_float((uint16_t)(mw[e] & 0xFFFF)) * (float)(1 << key_scale_shift<BITS>(e));
+        KSZ[w][gh][ch & 63][2 + (ch >> 6)] = half_bits_to_float((uint16_t)(mw[e] >> 16));
       }
     }
-    build_query(cur_pos.base, nvalid > 32);   // its wave barrier also covers KSZ
+    build_query_rows(c_rows);   // its wave barrier also covers KSZ
 
     // ---------------- scores
     f4_t acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
     uint32_t kw[4 * BITS];
     for (int j = 0; j < BITS; ++j) {
-      kw[4 * j] = cur.kc[j].x; kw[4 * j + 1] = cur.kc[j].y;
-      kw[4 * j + 2] = cur.kc[j].z; kw[4 * j + 3] = cur.kc[j].w;
+      kw[4 * j] = c.kc[j].x; kw[4 * j + 1] = c.kc[j].y;
+      kw[4 * j + 2] = c.kc[j].z; kw[4 * j + 3] = c.kc[j].w;
     }
 #pragma unroll
     for (int i = 0; i < 2 * BITS; ++i) {   // words of channels [CPW i, CPW (i + 1)) and 64 + ...
-      float nl[CPW], nh[CPW], xl[CPW], xh[CPW];
-      unpack_word<BITS>(kw[i], nl);
-      unpack_word<BITS>(kw[i + 2 * BITS], nh);
+      h2_t pl[CPW / 2], ph[CPW / 2];
+      for (int pp = 0; pp < CPW / 2; ++pp) {
+        pl[pp] = key_part<BITS>(kw[i], pp);
+        ph[pp] = key_part<BITS>(kw[i + 2 * BITS], pp);
+      }
+      float xl[CPW], xh[CPW];
       for (int k = 0; k < CPW; ++k) {
         const float4 sz = *reinterpret_cast<const float4*>(&KSZ[w][gh][CPW * i + k][0]);
-        xl[k] = nl[k] * sz.x + sz.z;   // exact product, one rounding
-        xh[k] = nh[k] * sz.y + sz.w;
+        xl[k] = __builtin_fmaf((float)key_code<BITS>(pl, k), sz.x, sz.z);   // exact product, one rounding
+        xh[k] = __builtin_fmaf((float)key_code<BITS>(ph, k), sz.y, sz.w);
       }
       score_pairs(xl, xh, CPW * i, CPW, acc);
     }
@@ -287,14 +315,16 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     // ---------------- values
     stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PL[w], zacc, tl, gh);
     wave_sync();
-    value_mfma<G, BITS, false, HL, NDG>(cur.vc, PL[w], row, gh, o0, o1, o2, o3);
+    value_mfma<G, BITS, false, HL, NDG>(c.vc, PL[w], row, gh, o0, o1, o2, o3);
     wave_sync();
 
     if (ends) flush();
-    if (!more) break;
-    cur = nxt;
-    cur_pos = nxt_pos;
     fresh = ends;
+    return more;
+  };
+  for (;;) {
+    if (!tile_step(cur, cur_pos, cur_rows, nxt, nxt_pos, nxt_rows)) break;
+    if (!tile_step(nxt, nxt_pos, nxt_rows, cur, cur_pos, cur_rows)) break;
   }
 }
 
