@@ -78,22 +78,31 @@ __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
   }
 }
 
-// Waves per SIMD the register allocation must allow: three work-groups per
-// compute unit wherever the LDS allows it (the KIVI G = 4 tables do not).
+// The KIVI G = 4 kernels keep a wave's fp32 query in its probability table
+// (the query is read only while an assignment opens, and every tile rewrites
+// the whole table), which saves 8 KiB of LDS per work-group.
 template <int G, bool BLOCK>
+constexpr bool query_in_prob_table() {
+  return G == 4 && !BLOCK;
+}
+
+// Waves per SIMD the register allocation must allow: three work-groups per
+// compute unit wherever the LDS allows it (the KIVI G = 4 4-bit stages do not).
+template <int G, int BITS, bool BLOCK>
 constexpr int decode_min_waves() {
-  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK) ? 2 : 3);
+  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK && BITS == 4) ? 2 : 3);
 }
 
 template <int G, int BITS, bool BLOCK>
-__global__ __launch_bounds__(256, (decode_min_waves<G, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
   constexpr int NDG = BLOCK ? 1 : 4;     // value scale groups per token
   constexpr int TB = 512 * BITS;         // tile bytes
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
-  __shared__ float qs[4][G][kD];
+  constexpr bool QP = query_in_prob_table<G, BLOCK>();
+  __shared__ __attribute__((aligned(16))) float qs[QP ? 1 : 4][G][kD];
   // query tables: per group half (KIVI, rebuilt per group) or one (BLOCK,
   // fixed per pair)
   __shared__ __attribute__((aligned(16))) _Float16 QL[4][BLOCK ? 1 : 2][32][HL][4][4];
@@ -106,7 +115,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BLOCK>())) void decode_mf
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
   auto QLw = QL[w];
-  auto qsw = qs[w];
+  float (*qsw)[kD] = QP ? reinterpret_cast<float (*)[kD]>(&PL[w][0][0][0][0][0]) : qs[QP ? 0 : w];
+  static_assert(!QP || sizeof(PL[0]) >= sizeof(qs[0]), "the query must fit the probability table");
   const int qh = BLOCK ? 0 : gh;
   for (int e = lane; e < (int)(sizeof(QL[0]) / 2); e += 64) (&QLw[0][0][0][0][0])[e] = (_Float16)0.0f;
   for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) (&PL[w][0][0][0][0][0])[e] = (_Float16)0.0f;
@@ -253,6 +263,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BLOCK>())) void decode_mf
       const float qmax = wave_query<G>(a, pb, ph, g.hadamard != 0, qsw, lane);
       for (int m = 0; m < G; ++m)
         for (int i = 0; i < 4; ++i) qv[m][i] = qsw[m][kch[i]];
+      wave_sync();   // the query is read before stage_probs() may overwrite it
       if (BLOCK) {
         // per-token key scales: the query table is fixed for the pair
         int ex = 0;
