@@ -12,8 +12,9 @@ persoalan kalibrasi").  Two schemes:
   groups, asymmetric, fp16 scale and zero; a fp16 window of recent tokens
   (tiers.py); optionally a high-bit window with older groups at ``low_bits``
   ([troisinh] "Ý tưởng cốt lõi", "Mixed Precision"); optionally the Hadamard
-  rotation before quantizing ([troisinh] "Tại sao nó hoạt động", item 2) and
-  keys kept before RoPE (item 3).
+  rotation before quantizing ([troisinh] "Tại sao nó hoạt động", item 2),
+  plain or randomized by the sign masks ``sign_in`` / ``sign_out``
+  (hadamard.py), and keys kept before RoPE (item 3).
 ``block128``: every token's 128-vector, optionally Hadamard-rotated, becomes one
   symmetric 4-bit block with an fp16 scale ([trefon] "Przykład: model 27B przy
   262K" and "Jak 4-bitowemu cache to uchodzi: najpierw obrót"); no window.
@@ -27,7 +28,8 @@ one append unless a demotion happens in between.
 
 Decode (reading): the attended keys and values are the dequantized cache in
 its stored domain, the fp16 window taken exactly; Hadamard-rotated tokens are
-rotated back with H / sqrt(128) in fp64 (equivalently the query is rotated and
+rotated back with H / sqrt(128) in fp64 (D_in H D_out / sqrt(128) for the
+randomized form; equivalently the query is rotated and
 the output rotated back, q.k = (Hq).(Hk), [trefon] "Jak 4-bitowemu cache to
 uchodzi"); pre-RoPE keys are rotated to their positions and the query to
 ``q_pos`` (default: the cache length).  Window tokens are stored unrotated.
@@ -43,7 +45,8 @@ F16 = np.float16
 F32 = np.float32
 
 DEFAULTS = dict(head_dim=128, group=32, vdims=32, window=128, hi_window=-1, k_bits=4, v_bits=4,
-                low_bits=2, hadamard=False, pre_rope=False, rope_theta=10000.0)
+                low_bits=2, hadamard=False, pre_rope=False, rope_theta=10000.0,
+                sign_in=None, sign_out=None)
 
 
 def make_config(**kw):
@@ -110,7 +113,7 @@ class OracleCache:
     def _source_rows(self, x):
         """fp16 rows -> the float32 values the quantizer sees."""
         if self.cfg["hadamard"]:
-            return fwht128_f32(x)
+            return fwht128_f32(x, self.cfg["sign_in"], self.cfg["sign_out"])
         return np.asarray(x, dtype=F16).astype(F32)
 
     # -- append --------------------------------------------------------------
@@ -211,8 +214,8 @@ class OracleCache:
         V = V.astype(np.float64)
         if c["hadamard"]:
             nq = self.length if c["scheme"] == "block128" else self.Tq
-            K[:, :nq] = rotate_f64(K[:, :nq])
-            V[:, :nq] = rotate_f64(V[:, :nq])
+            K[:, :nq] = rotate_f64(K[:, :nq], c["sign_in"], c["sign_out"])
+            V[:, :nq] = rotate_f64(V[:, :nq], c["sign_in"], c["sign_out"])
         if c["pre_rope"]:
             Kt = np.transpose(K, (0, 2, 1, 3))
             Kt = rope_f64(Kt, np.arange(self.length), c["rope_theta"])

@@ -11,7 +11,15 @@ nor the floating-point schedule.  Readings used here:
 
   * H is the 128x128 Sylvester matrix in natural order,
     H[i, j] = (-1) ** popcount(i & j), applied as H / sqrt(128); H is symmetric
-    and (H / sqrt(128)) is its own inverse.  No random sign flips.
+    and (H / sqrt(128)) is its own inverse.
+  * The randomized form flips signs, transforms, and flips signs again
+    ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót"):
+    y = D_out H D_in x / sqrt(128) with D = diag(+-1).  The two sign vectors
+    are inputs (128-bit masks, four little-endian uint32 words; bit i of word
+    i // 32 set negates coordinate i).  With both masks zero this is the plain
+    transform above.  Sign flips are exact, so the fp32 schedule is the
+    plain one with x negated where D_in says before it and y negated where
+    D_out says after it.  The inverse is D_in H D_out / sqrt(128).
   * Because codes must be bit-exact, the float32 schedule is fixed:
     x <- float32(input); for h = 1, 2, 4, ..., 64 in that order, every pair
     (x[i], x[i + h]) with bit log2(h) of i clear becomes (a + b, a - b), each a
@@ -25,9 +33,25 @@ D = 128
 C32 = np.float32(np.frombuffer(bytes.fromhex("f304b53d"), dtype="<f4")[0])
 
 
-def fwht128_f32(x):
-    """Normalized FWHT over the last axis (length 128), fixed fp32 schedule."""
-    y = np.array(x, dtype=np.float32, copy=True)
+def mask_signs(words):
+    """float32 +-1 vector of a 128-bit sign mask (four uint32 words, word
+    i // 32, bit i % 32 negates coordinate i); None or zeros give all +1."""
+    s = np.ones(D, dtype=np.float32)
+    if words is None:
+        return s
+    words = [int(w) & 0xFFFFFFFF for w in words]
+    if len(words) != 4:
+        raise ValueError("a sign mask is four uint32 words")
+    for i in range(D):
+        if (words[i // 32] >> (i % 32)) & 1:
+            s[i] = -1.0
+    return s
+
+
+def fwht128_f32(x, sign_in=None, sign_out=None):
+    """Normalized FWHT over the last axis (length 128), fixed fp32 schedule;
+    with sign masks, the randomized form D_out H D_in / sqrt(128)."""
+    y = np.array(x, dtype=np.float32, copy=True) * mask_signs(sign_in)
     if y.shape[-1] != D:
         raise ValueError("last axis must be 128")
     shape = y.shape
@@ -41,7 +65,7 @@ def fwht128_f32(x):
         v[:, :, 1, :] = a - b
         h *= 2
     y = y * C32
-    return y.reshape(shape)
+    return y.reshape(shape) * mask_signs(sign_out)
 
 
 def fwht128_unnormalized_exact(x):
@@ -73,7 +97,11 @@ def sylvester(n=D):
     return h
 
 
-def rotate_f64(x):
-    """x -> x (H / sqrt(128)) in float64 over the last axis; its own inverse."""
+def rotate_f64(x, sign_in=None, sign_out=None):
+    """x -> x (H / sqrt(128)) in float64 over the last axis (its own inverse);
+    with sign masks, x -> x (D_out H D_in / sqrt(128)): the inverse of the
+    randomized rotation for row vectors (R = D_out H D_in / sqrt(128) maps a
+    column k to R k, and x R = (R^T x^T)^T undoes it)."""
     H = sylvester(D).astype(np.float64) / np.sqrt(D)
-    return np.asarray(x, dtype=np.float64) @ H
+    R = np.diag(mask_signs(sign_out).astype(np.float64)) @ H @ np.diag(mask_signs(sign_in).astype(np.float64))
+    return np.asarray(x, dtype=np.float64) @ R

@@ -95,6 +95,16 @@ def library_config(w):
     return c
 
 
+def random_signs(seed):
+    """Sign masks of a randomized Hadamard rotation: dict(sign_in=[4 words],
+    sign_out=[4 words]), 128 seeded fair coin flips each (bit i of word i // 32
+    set: coordinate i negated).  Inputs only; what they do is the library's and
+    the oracle's business."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, 0x5167, seed])))
+    words = rng.integers(0, 1 << 32, size=8, dtype=np.uint64)
+    return dict(sign_in=[int(x) for x in words[:4]], sign_out=[int(x) for x in words[4:]])
+
+
 def _rng(wid, b, h, tensor, blk):
     ss = np.random.SeedSequence([BASE_SEED, wid, b, h, tensor, blk])
     return np.random.Generator(np.random.PCG64(ss))

@@ -50,7 +50,12 @@ def build(w, chunks):
     return oc
 
 
+SIGNS = wl.random_signs(7)
+
+
 @pytest.mark.parametrize("scheme,kw", [("kivi", {}), ("kivi", dict(hadamard=True)),
+                                       ("kivi", dict(hadamard=True, **SIGNS)),
+                                       ("block128", dict(**SIGNS)),
                                        ("kivi", dict(k_bits=2, v_bits=2)),
                                        ("kivi", dict(pre_rope=True, rope_theta=500000.0)),
                                        ("block128", {})])
@@ -114,6 +119,32 @@ def test_rotated_domain_decode_identity():
     rq = rotate_f64(q.astype(np.float64))
     out_rot = rotate_f64(decode_f64(rq, kd, vd))
     assert np.allclose(out_rot, oc.decode(q), atol=1e-12)
+
+
+@pytest.mark.parametrize("scheme", ["block128", "kivi"])
+def test_randomized_rotation_decode_identity(scheme):
+    # the same with the randomized rotation R = D_out H D_in / sqrt(128): the
+    # query goes forward (q R^T for rows), the output comes back (o R); for
+    # KIVI only the quantized part is rotated, so attend it alone
+    kw = dict(hadamard=True, **SIGNS) if scheme == "kivi" else dict(SIGNS)
+    w = small_workload(905, scheme, 300, **kw)
+    oc = build(w, [300])
+    q = wl.queries(w)
+    kd, vd = oc.dequant()
+    n = oc.Tq
+    si, so = SIGNS["sign_in"], SIGNS["sign_out"]
+    rq = rotate_f64(q.astype(np.float64), so, si)          # q R^T
+    out = rotate_f64(decode_f64(rq, kd[:, :n], vd[:, :n]), si, so)
+    ref = decode_f64(q.astype(np.float64), rotate_f64(kd[:, :n], si, so), rotate_f64(vd[:, :n], si, so))
+    assert np.allclose(out, ref, atol=1e-12)
+    if scheme == "block128":
+        assert np.allclose(out, oc.decode(q), atol=1e-12)
+    # the signs change the stored codes (same source, plain rotation)
+    plain = build(small_workload(905, scheme, 300, **(dict(hadamard=True) if scheme == "kivi" else {})), [300])
+    assert not np.array_equal(plain.dequant()[0], kd)
+    # and the round trip is close to the fp16 source
+    K, _ = wl.kv_tokens(w, 0, 300)
+    assert np.max(np.abs(rotate_f64(kd[:, :n], si, so) - K[:, :n].astype(np.float64))) < 1.0
 
 
 def test_prerope_query_position_and_short_cache():

@@ -57,3 +57,77 @@ def test_norm_involution_and_dot_identity():
     e[17] = 100.0
     r = hd.rotate_f64(e)
     assert np.allclose(np.abs(r), 100.0 / np.sqrt(128))
+
+
+# ---------------------------------------------------------------------------
+# Randomized form D_out H D_in / sqrt(128): signs, transform, signs ([trefon]
+# "Jak 4-bitowemu cache to uchodzi: najpierw obrót").  The sign vectors here
+# are built from the mask words by byte unpacking, independently of the
+# oracle's bit loop.
+
+def _signs(words):
+    bits = np.unpackbits(np.array(words, dtype="<u4").view(np.uint8), bitorder="little")
+    return 1 - 2 * bits.astype(np.int64)
+
+
+MASK_IN = [0x9E3779B9, 0x7F4A7C15, 0x00000001, 0x80000000]
+MASK_OUT = [0x12345678, 0xDEADBEEF, 0xFFFFFFFF, 0x0F0F0F0F]
+
+
+def test_signed_fp32_schedule_exact_on_integers():
+    rng = np.random.default_rng(3)
+    x = rng.integers(-1000, 1000, size=(64, 128))
+    y = hd.fwht128_f32(x.astype(np.float16), MASK_IN, MASK_OUT)
+    sin, sout = _signs(MASK_IN), _signs(MASK_OUT)
+    H = scipy.linalg.hadamard(128)
+    exact = ((x * sin) @ H) * sout          # D_out H D_in x, rows as vectors (H symmetric)
+    assert np.array_equal(y, (exact.astype(np.float32) * hd.C32))
+    # the sides matter: D_in H D_out is another matrix
+    swapped = ((x * sout) @ H) * sin
+    assert not np.array_equal(y, swapped.astype(np.float32) * hd.C32)
+
+
+def test_signed_zero_masks_are_the_plain_transform():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((32, 128)).astype(np.float16)
+    plain = hd.fwht128_f32(x)
+    assert np.array_equal(hd.fwht128_f32(x, [0, 0, 0, 0], [0, 0, 0, 0]).view(np.uint32), plain.view(np.uint32))
+    assert np.array_equal(hd.fwht128_f32(x, None, None).view(np.uint32), plain.view(np.uint32))
+
+
+def test_signed_mask_bit_order():
+    # bit 37 = word 1, bit 5: negates input coordinate 37 only
+    m = [0, 1 << 5, 0, 0]
+    e37 = np.zeros((1, 128), np.float16)
+    e37[0, 37] = 1
+    e36 = np.zeros((1, 128), np.float16)
+    e36[0, 36] = 1
+    assert np.array_equal(hd.fwht128_f32(e37, m, None), -hd.fwht128_f32(e37))
+    assert np.array_equal(hd.fwht128_f32(e36, m, None), hd.fwht128_f32(e36))
+    # on the output side it negates output coordinate 37 only
+    x = np.random.default_rng(5).standard_normal((1, 128)).astype(np.float16)
+    y, z = hd.fwht128_f32(x), hd.fwht128_f32(x, None, m)
+    flip = np.ones(128, np.float32)
+    flip[37] = -1
+    assert np.array_equal(z, y * flip)
+    assert hd.mask_signs(m)[37] == -1 and np.sum(hd.mask_signs(m) < 0) == 1
+
+
+def test_signed_orthogonal_inverse_and_dot_identity():
+    rng = np.random.default_rng(6)
+    sin, sout = _signs(MASK_IN).astype(np.float64), _signs(MASK_OUT).astype(np.float64)
+    R = np.diag(sout) @ scipy.linalg.hadamard(128).astype(np.float64) @ np.diag(sin) / np.sqrt(128)
+    assert np.allclose(R @ R.T, np.eye(128), atol=1e-13)
+    x = rng.standard_normal((128, 128)).astype(np.float16)
+    y = hd.fwht128_f32(x, MASK_IN, MASK_OUT)
+    # forward = R x for column vectors
+    assert np.allclose(y, x.astype(np.float64) @ R.T, atol=1e-5, rtol=1e-5)
+    # rotate_f64 with the same masks undoes it (rows: x R)
+    assert np.allclose(hd.rotate_f64(y, MASK_IN, MASK_OUT), x.astype(np.float64), atol=1e-4)
+    q, k = rng.standard_normal((8, 128)), rng.standard_normal((8, 128))
+    lhs = np.sum((q @ R.T) * (k @ R.T), axis=1)
+    assert np.allclose(lhs, np.sum(q * k, axis=1), rtol=1e-12, atol=1e-12)
+    # an outlier still spreads over every coordinate
+    e = np.zeros((1, 128), np.float16)
+    e[0, 100] = 64
+    assert np.allclose(np.abs(hd.fwht128_f32(e, MASK_IN, MASK_OUT)), 64 / np.sqrt(128), rtol=1e-6)
