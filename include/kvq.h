@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_MAX_PLANES 16
 
 typedef enum kvq_status {
@@ -113,13 +113,26 @@ typedef struct kvq_config {
                              (Sylvester order, fixed fp32 butterfly order
                              h = 1,2,...,64) before quantizing ([troisinh]
                              "Tại sao nó hoạt động", item 2; [trefon] "Jak
-                             4-bitowemu cache to uchodzi: najpierw obrót") */
+                             4-bitowemu cache to uchodzi: najpierw obrót"),
+                             randomized by the sign masks below */
   int32_t pre_rope_keys;  /* 1: keys are stored before RoPE and rotated on the
                              fly at decode, split-half pairs (j, j+64)
                              ([troisinh] "Tại sao nó hoạt động", item 3;
                              [nexus] "Các mô hình được hỗ trợ").  Not with
                              hadamard. */
   float rope_theta;       /* RoPE base (> 0 when pre_rope_keys) */
+  uint32_t hadamard_sign_in[4];  /* randomized Hadamard ([trefon] "Jak
+                             4-bitowemu cache to uchodzi: najpierw obrót":
+                             signs, transform, signs): the rotation is
+                             D_out H D_in / sqrt(128) with D = diag(+-1); bit
+                             i of word i / 32 set negates coordinate i of the
+                             input (D_in) ... */
+  uint32_t hadamard_sign_out[4]; /* ... and of the output (D_out).  Sign flips
+                             are exact, so codes stay bit-exact.  All zero:
+                             the plain rotation.  Must be all zero unless
+                             hadamard (else KVQ_ERR_INVALID_ARG).  The masks
+                             are part of the cache's format: append, decode
+                             and dequant of one cache take the same ones. */
 } kvq_config;
 
 typedef struct kvq_layout_t {

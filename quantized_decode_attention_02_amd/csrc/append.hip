@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(Geom g, Planes p, co
   const int h = blockIdx.y, b = blockIdx.z;
   load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
   __syncthreads();
-  if (g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+  if (g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256, g.sign_in, g.sign_out, g.hsigned);
   const bool hi = grp * kGroup >= hi_start_new;
   quantize_store(g, p, gl, pair_index(g, b, h), grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
 }
@@ -400,7 +400,8 @@ __global__ __launch_bounds__(256) void kivi_small_append_kernel(Geom g, Planes p
       load_group(g, p, gl.xs[0], gl.xs[1], k_new, v_new, n_new, T0, b, h, grp, tid);
     }
     __syncthreads();
-    if (!demote && g.hadamard) fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256);
+    if (!demote && g.hadamard)
+      fwht128_rows(&gl.xs[0][0][0], 2 * kGroup, tid, 256, g.sign_in, g.sign_out, g.hsigned);
     const bool hi = !demote && grp * kGroup >= hi_start_new;
     quantize_store(g, p, gl, pair, grp, hi ? g.hi_bits : g.lo_bits, hi, tid);
   }
@@ -493,7 +494,10 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       x[2 * j] = __half2float(__ushort_as_half((uint16_t)(w[j] & 0xFFFFu)));
       x[2 * j + 1] = __half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
     }
-    if (g.hadamard) fwht128_row16(x, i);
+    if (g.hadamard) {
+      if (g.hsigned) fwht128_row16_signed(x, i, g.sign_in, g.sign_out);
+      else fwht128_row16(x, i);
+    }
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);

@@ -22,8 +22,10 @@ namespace {
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // M = max m_c, L = sum l_c 2^(m_c - M), out = sum o_c 2^(m_c - M) / L.
 // Hadamard caches: the quantized chunks (slots < nq) were attended with the
-// rotated query, so their sum is rotated back once (H/sqrt(128) is its own
-// inverse); the fp16 window slots were attended unrotated.
+// rotated query R q, so their sum is rotated back once with R^T (R =
+// D_out H D_in / sqrt(128), R^T = D_in H D_out / sqrt(128); the plain H /
+// sqrt(128) is its own inverse); the fp16 window slots were attended
+// unrotated.
 //
 // One pass over the workspace: wave w takes slots w, w + 4, w + 8, ... in batches
 // of 64 (lane j reads the (m, l) of the batch's j-th slot), folds a batch into
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(Geom g, float* ws, fl
     rot[tid] = qp;
   }
   __syncthreads();
-  if (g.hadamard) fwht128_rows(rot, 1, tid, 256);
+  // the inverse of D_out H D_in / sqrt(128) is D_in H D_out / sqrt(128)
+  if (g.hadamard) fwht128_rows(rot, 1, tid, 256, g.sign_out, g.sign_in, g.hsigned);
   if (tid < kD) {
     const float q_part = g.hadamard ? rot[tid] : qp;
     out[((int64_t)b * g.Hq + hq) * kD + tid] = Lt > 0.0f ? (q_part + wp) / Lt : 0.0f;

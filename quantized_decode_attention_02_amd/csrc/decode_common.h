@@ -542,7 +542,7 @@ __device__ __forceinline__ float wave_query(const MfmaArgs& a, int b, int h, boo
   for (int e = lane; e < G * kD; e += 64)
     qsw[e / kD][e % kD] = __half2float(a.q[((int64_t)b * a.g.Hq + h * G + e / kD) * kD + e % kD]);
   wave_sync();
-  if (rotate) fwht128_rows_wave(&qsw[0][0], G, lane);
+  if (rotate) fwht128_rows_wave(&qsw[0][0], G, lane, a.g.sign_in, a.g.sign_out, a.g.hsigned);
   float mx = 0.0f;
   for (int e = lane; e < G * kD; e += 64) {
     const float v = qsw[e / kD][e % kD] * a.scale_log2;

@@ -41,6 +41,9 @@ kvq_status validate_config(const kvq_config* c) {
   if (c->k_group_tokens != kGroup || c->v_group_dims != 32) return KVQ_ERR_UNSUPPORTED;
   if (c->v_bits != c->k_bits) return KVQ_ERR_UNSUPPORTED;
   if (c->hadamard && c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
+  if (!c->hadamard)
+    for (int i = 0; i < 4; ++i)
+      if (c->hadamard_sign_in[i] != 0 || c->hadamard_sign_out[i] != 0) return KVQ_ERR_INVALID_ARG;
   if (c->scheme == KVQ_KIVI_ASYM) {
     if (c->k_bits != 4 && c->k_bits != 2) return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != kWindow) return KVQ_ERR_UNSUPPORTED;
@@ -72,6 +75,12 @@ Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t l
   g.hi_bits = c->k_bits;
   g.lo_bits = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->low_bits : c->k_bits;
   g.hadamard = c->hadamard;
+  g.hsigned = 0;
+  for (int i = 0; i < 4; ++i) {
+    g.sign_in.w[i] = c->hadamard_sign_in[i];
+    g.sign_out.w[i] = c->hadamard_sign_out[i];
+    if (c->hadamard_sign_in[i] != 0 || c->hadamard_sign_out[i] != 0) g.hsigned = 1;
+  }
   g.pre_rope = c->pre_rope_keys;
   g.rope_theta = c->rope_theta;
   g.gmax = groups_for(max_tokens);

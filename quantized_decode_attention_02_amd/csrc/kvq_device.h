@@ -206,6 +206,47 @@ __device__ __forceinline__ void fwht128_row16(float* x, int i) {
   for (int j = 0; j < 8; ++j) x[j] = x[j] * c;
 }
 
+// Sign flips of the randomized rotation D_post H D_pre / sqrt(128) ([trefon]
+// "Jak 4-bitowemu cache to uchodzi: najpierw obrót": signs, transform,
+// signs): coordinate i is negated when bit i of the mask (word i / 32) is
+// set, by an exact xor of its sign bit, so the fp32 schedule is unchanged.
+__device__ __forceinline__ uint32_t mask_word(const Mask128& m, int word) {
+  const uint32_t a = (word & 1) ? m.w[1] : m.w[0];
+  const uint32_t b = (word & 1) ? m.w[3] : m.w[2];
+  return (word & 2) ? b : a;
+}
+__device__ __forceinline__ float flip_by(float v, uint32_t bits, int bit) {
+  return __uint_as_float(__float_as_uint(v) ^ (((bits >> bit) & 1u) << 31));
+}
+
+// fwht128_reg between the flips of `pre` and `post` (elements 2 lane and
+// 2 lane + 1: word lane / 16, bits 2 lane mod 32 and the next).
+__device__ __forceinline__ void fwht128_reg_signed(float& e0, float& e1, int lane, const Mask128& pre,
+                                                   const Mask128& post) {
+  const int word = lane >> 4, bit = (2 * lane) & 31;
+  uint32_t m = mask_word(pre, word);
+  e0 = flip_by(e0, m, bit);
+  e1 = flip_by(e1, m, bit + 1);
+  fwht128_reg(e0, e1, lane);
+  m = mask_word(post, word);
+  e0 = flip_by(e0, m, bit);
+  e1 = flip_by(e1, m, bit + 1);
+}
+
+// fwht128_row16 between the flips of `pre` and `post` (row lane i holds
+// elements 8i .. 8i + 7: word i / 4, bits 8 (i mod 4) ..).
+__device__ __forceinline__ void fwht128_row16_signed(float* x, int i, const Mask128& pre,
+                                                     const Mask128& post) {
+  const int word = i >> 2, b0 = 8 * (i & 3);
+  uint32_t m = mask_word(pre, word);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = flip_by(x[j], m, b0 + j);
+  fwht128_row16(x, i);
+  m = mask_word(post, word);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = flip_by(x[j], m, b0 + j);
+}
+
 // Maximum of a non-negative float over a 16-lane row, on its bit pattern
 // (for non-negative floats the integer order is the numeric order).
 __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
@@ -217,26 +258,31 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
 
 // fwht128_reg over `nvec` float rows of 128 in LDS by a whole work-group:
 // wave w transforms rows w, w + nthreads / 64, ... in its registers and
-// writes them back.  The rows must be complete when it is called; it ends
+// writes them back.  With `sgn`, each row goes through D_post H D_pre /
+// sqrt(128) instead.  The rows must be complete when it is called; it ends
 // with a barrier on LDS.
-__device__ __forceinline__ void fwht128_rows(float* x, int nvec, int tid, int nthreads) {
+__device__ __forceinline__ void fwht128_rows(float* x, int nvec, int tid, int nthreads,
+                                             const Mask128& pre, const Mask128& post, bool sgn) {
   const int lane = tid & 63;
   for (int v = tid >> 6; v < nvec; v += nthreads >> 6) {
     float2* r = reinterpret_cast<float2*>(x + v * kD) + lane;
     float2 e = *r;
-    fwht128_reg(e.x, e.y, lane);
+    if (sgn) fwht128_reg_signed(e.x, e.y, lane, pre, post);
+    else fwht128_reg(e.x, e.y, lane);
     *r = e;
   }
   lds_barrier();
 }
 
 // The same for rows of one wave's own (wave barriers only).
-__device__ __forceinline__ void fwht128_rows_wave(float* x, int nvec, int lane) {
+__device__ __forceinline__ void fwht128_rows_wave(float* x, int nvec, int lane, const Mask128& pre,
+                                                  const Mask128& post, bool sgn) {
   wave_sync();
   for (int v = 0; v < nvec; ++v) {
     float2* r = reinterpret_cast<float2*>(x + v * kD) + lane;
     float2 e = *r;
-    fwht128_reg(e.x, e.y, lane);
+    if (sgn) fwht128_reg_signed(e.x, e.y, lane, pre, post);
+    else fwht128_reg(e.x, e.y, lane);
     *r = e;
   }
   wave_sync();

@@ -15,6 +15,11 @@ constexpr int kGroup = 32;     // tokens per key group / tile
 constexpr int kRing = 160;     // fp16 window ring rows (>= 128 + 31)
 constexpr int kWindow = 128;   // fp16 window length
 
+// 128 sign bits: bit i of w[i / 32] negates coordinate i.
+struct Mask128 {
+  uint32_t w[4];
+};
+
 // Everything a kernel needs to address one cache.  Plain values, passed by
 // value to every launch.
 struct Geom {
@@ -22,6 +27,8 @@ struct Geom {
   int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM
   int hi_bits, lo_bits;
   int hadamard, pre_rope;
+  int hsigned;                 // 1: the rotation is randomized (a mask is nonzero)
+  Mask128 sign_in, sign_out;   // D_in, D_out of D_out H D_in / sqrt(128)
   float rope_theta;
   int64_t gmax;                // groups per (sequence, head)
   int64_t hi_slots;            // K_HI / V_HI tiles per (sequence, head)

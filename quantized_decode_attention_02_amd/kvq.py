@@ -41,7 +41,8 @@ class Config(ctypes.Structure):
                 ("k_group_tokens", ctypes.c_int32), ("v_group_dims", ctypes.c_int32),
                 ("fp16_window", ctypes.c_int32), ("int4_window", ctypes.c_int32),
                 ("low_bits", ctypes.c_int32), ("hadamard", ctypes.c_int32),
-                ("pre_rope_keys", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+                ("pre_rope_keys", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("hadamard_sign_in", ctypes.c_uint32 * 4), ("hadamard_sign_out", ctypes.c_uint32 * 4)]
 
 
 class Layout(ctypes.Structure):
@@ -101,7 +102,9 @@ def make_config(d):
                   int4_window=d.get("hi_window", -1), low_bits=d.get("low_bits", 2),
                   hadamard=int(bool(d.get("hadamard", False))),
                   pre_rope_keys=int(bool(d.get("pre_rope", False))),
-                  rope_theta=float(d.get("rope_theta", 10000.0)))
+                  rope_theta=float(d.get("rope_theta", 10000.0)),
+                  hadamard_sign_in=(ctypes.c_uint32 * 4)(*(d.get("sign_in") or [0, 0, 0, 0])),
+                  hadamard_sign_out=(ctypes.c_uint32 * 4)(*(d.get("sign_out") or [0, 0, 0, 0])))
 
 
 def layout(cfg, batch, max_tokens):

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(kvq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert kvq.LIB.kvq_abi_version() == 1
+    assert kvq.LIB.kvq_abi_version() == 2
     assert kvq.strerror(0) == "ok" and kvq.strerror(-3) == "cache capacity exceeded"
 
 
@@ -77,6 +77,13 @@ def test_config_validation():
     assert status_of(pre_rope_keys=1, rope_theta=0.0) == -1
     assert status_of(scheme=1, fp16_window=0, int4_window=-1) == 0
     assert status_of(scheme=1, fp16_window=128) == -2
+    # randomized Hadamard: sign masks only with the rotation on
+    signs = (ctypes.c_uint32 * 4)(0, 1 << 5, 0, 0)
+    assert status_of(hadamard=1, hadamard_sign_in=signs) == 0
+    assert status_of(hadamard=1, hadamard_sign_out=signs) == 0
+    assert status_of(hadamard_sign_in=signs) == -1
+    assert status_of(hadamard_sign_out=signs) == -1
+    assert status_of(scheme=1, fp16_window=0, int4_window=-1, hadamard=0, hadamard_sign_out=signs) == -1
 
 
 def fake_cache(cfg, batch, max_tokens, length=0, misalign=None):

@@ -14,6 +14,8 @@ from quantized_decode_attention_02_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+SIGNS = wl.random_signs(11)
+
 VARIANTS = {
     "int4": dict(),
     "int2": dict(k_bits=2, v_bits=2),
@@ -21,8 +23,10 @@ VARIANTS = {
     "int4-prerope": dict(pre_rope=True, rope_theta=500000.0),
     "mixed-hadamard": dict(hadamard=True, hi_window=96),
     "mixed": dict(hi_window=64),
+    "mixed-hadamard-signed": dict(hadamard=True, hi_window=96, **SIGNS),
     "block128": None,
     "block128-plain": dict(hadamard=False),
+    "block128-signed": dict(SIGNS),
 }
 
 
