@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "52bc9e932ae4da9f13671d15b9a48473faf310cbf1302ba0c5abb557d0130d2c", "fetch_kib": 665414, "write_kib": 4211,
+    1: {"sources_sha256": "417bee24f3aa62cf67cc50b2d790c1b41286db1167ebb031f81c05e7206531de", "fetch_kib": 665005, "write_kib": 4210,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
