@@ -28,6 +28,7 @@ Modules:
   tiers      -- which tokens are fp16 / high-bit / low-bit for a cache length
   hadamard   -- fixed-order fp32 FWHT-128 and the dense fp64 Sylvester matrix
   quant      -- asymmetric group quantizer, symmetric 128-block quantizer, dequant
+  codebook   -- TBQ4: Lloyd-Max levels of N(0, 1/sqrt(128)), norm + index blocks
   layout     -- the documented byte image of every cache plane, plane sizes
   attention  -- fp64 split-half RoPE and scaled-dot-product decode attention
   cache      -- a whole cache: append (with demotion), dequant, decode
@@ -41,4 +42,4 @@ package's own, stated in each docstring) and model quality (perplexity, task
 scores), which needs trained weights.
 """
 
-from . import tiers, hadamard, quant, layout, attention, cache, sizes  # noqa: F401
+from . import tiers, hadamard, quant, codebook, layout, attention, cache, sizes  # noqa: F401

@@ -6,7 +6,7 @@ The cache is per sequence and grows by one entry per token per layer
 ([trefon] "Czym jest cache KV"); it is written at run time, token by token, so
 quantization parameters come from the observed values ([trefon] "Dlaczego cache
 trudniej skwantyzować niż wagi"; [nalar] "Pertumbuhan cache dinamis mengubah
-persoalan kalibrasi").  Two schemes:
+persoalan kalibrasi").  Three schemes:
 
 ``kivi``: keys per channel over 32-token groups, values per token over 32-dim
   groups, asymmetric, fp16 scale and zero; a fp16 window of recent tokens
@@ -18,6 +18,9 @@ persoalan kalibrasi").  Two schemes:
 ``block128``: every token's 128-vector, optionally Hadamard-rotated, becomes one
   symmetric 4-bit block with an fp16 scale ([trefon] "Przykład: model 27B przy
   262K" and "Jak 4-bitowemu cache to uchodzi: najpierw obrót"); no window.
+``tbq4``: every token's 128-vector, always rotated, becomes 16 Lloyd-Max
+  indices and an fp16 norm in the same 66-byte container (codebook.py); no
+  window.
 
 Append order (reading; the pages give none): groups that leave the high-bit
 tier are requantized to ``low_bits`` from their dequantized high-bit values
@@ -37,7 +40,7 @@ uchodzi"); pre-RoPE keys are rotated to their positions and the query to
 
 import numpy as np
 
-from . import tiers, quant, layout
+from . import tiers, quant, layout, codebook
 from .hadamard import fwht128_f32, rotate_f64
 from .attention import rope_f64, decode_f64
 
@@ -52,11 +55,17 @@ DEFAULTS = dict(head_dim=128, group=32, vdims=32, window=128, hi_window=-1, k_bi
 def make_config(**kw):
     cfg = dict(DEFAULTS)
     cfg.update(kw)
-    if cfg["scheme"] == "block128":
+    if cfg["scheme"] in BLOCK_SCHEMES:
         cfg["window"] = 0
         cfg.setdefault("k_bits", 4)
         cfg.setdefault("v_bits", 4)
+    if cfg["scheme"] == "tbq4" and not cfg["hadamard"]:
+        raise ValueError("tbq4 quantizes rotated blocks: hadamard must be on")
     return cfg
+
+
+# per-token 128-value block schemes: nibbles + one fp16 per token and tensor
+BLOCK_SCHEMES = ("block128", "tbq4")
 
 
 def _tile_token_of_byte(key_tile):
@@ -130,11 +139,12 @@ class OracleCache:
         kn = np.transpose(k_new, (0, 2, 1, 3))       # [B, H, n, 128]
         vn = np.transpose(v_new, (0, 2, 1, 3))
         c = self.cfg
-        if c["scheme"] == "block128":
+        if c["scheme"] in BLOCK_SCHEMES:
+            quantize = quant.quant_sym128 if c["scheme"] == "block128" else codebook.quant_tbq4
             for name, src, nib, sc in (("k", kn, self.k_nib, self.k_sc),
                                        ("v", vn, self.v_nib, self.v_sc)):
                 y = self._source_rows(src)
-                q, s = quant.quant_sym128(y)
+                q, s = quantize(y)
                 nib[:, :, T0:T1] = q
                 sc[:, :, T0:T1] = s
             self.length = T1
@@ -183,9 +193,10 @@ class OracleCache:
         B, H = self.B, self.H
         K = np.zeros((B, H, t1 - t0, 128), F32)
         V = np.zeros((B, H, t1 - t0, 128), F32)
-        if c["scheme"] == "block128":
-            K[:] = quant.dequant_sym128(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
-            V[:] = quant.dequant_sym128(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
+        if c["scheme"] in BLOCK_SCHEMES:
+            deq = quant.dequant_sym128 if c["scheme"] == "block128" else codebook.dequant_tbq4
+            K[:] = deq(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
+            V[:] = deq(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
         else:
             Tq = self.Tq
             qa, qb = t0, min(t1, Tq)
@@ -213,7 +224,7 @@ class OracleCache:
         K = K.astype(np.float64)
         V = V.astype(np.float64)
         if c["hadamard"]:
-            nq = self.length if c["scheme"] == "block128" else self.Tq
+            nq = self.length if c["scheme"] in BLOCK_SCHEMES else self.Tq
             K[:, :nq] = rotate_f64(K[:, :nq], c["sign_in"], c["sign_out"])
             V[:, :nq] = rotate_f64(V[:, :nq], c["sign_in"], c["sign_out"])
         if c["pre_rope"]:
@@ -242,7 +253,7 @@ class OracleCache:
         live = [np.zeros(s, bool) for s in sizes]
         pair = lambda a: a.reshape(B, H, -1)
         T = self.length
-        if c["scheme"] == "block128":
+        if c["scheme"] in BLOCK_SCHEMES:
             G = self.G
             for plane, nib, sc in ((layout.K_HI, self.k_nib, self.k_sc),
                                    (layout.V_HI, self.v_nib, self.v_sc)):

@@ -53,6 +53,13 @@ def _block128(**kw):
     return c
 
 
+def _tbq4(**kw):
+    c = dict(scheme="tbq4", k_bits=4, v_bits=4, low_bits=2, hi_window=-1,
+             window=0, hadamard=True, pre_rope=False, rope_theta=10000.0)
+    c.update(kw)
+    return c
+
+
 WORKLOADS = [
     dict(id=0, name="int4-kivi-b1-h1-t4096-outlier4x20",
          batch=1, num_q_heads=1, num_kv_heads=1, tokens=4096, prefill=0,

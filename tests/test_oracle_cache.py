@@ -36,7 +36,7 @@ def test_append_plan_demotion_sets():
 
 
 def small_workload(wid, scheme, T, **kw):
-    cfg = (wl._kivi if scheme == "kivi" else wl._block128)(**kw)
+    cfg = {"kivi": wl._kivi, "block128": wl._block128, "tbq4": wl._tbq4}[scheme](**kw)
     return wl.custom(wid, 2, 4, 2, T, cfg)
 
 
@@ -56,6 +56,7 @@ SIGNS = wl.random_signs(7)
 @pytest.mark.parametrize("scheme,kw", [("kivi", {}), ("kivi", dict(hadamard=True)),
                                        ("kivi", dict(hadamard=True, **SIGNS)),
                                        ("block128", dict(**SIGNS)),
+                                       ("tbq4", {}), ("tbq4", dict(**SIGNS)),
                                        ("kivi", dict(k_bits=2, v_bits=2)),
                                        ("kivi", dict(pre_rope=True, rope_theta=500000.0)),
                                        ("block128", {})])
@@ -121,7 +122,7 @@ def test_rotated_domain_decode_identity():
     assert np.allclose(out_rot, oc.decode(q), atol=1e-12)
 
 
-@pytest.mark.parametrize("scheme", ["block128", "kivi"])
+@pytest.mark.parametrize("scheme", ["block128", "kivi", "tbq4"])
 def test_randomized_rotation_decode_identity(scheme):
     # the same with the randomized rotation R = D_out H D_in / sqrt(128): the
     # query goes forward (q R^T for rows), the output comes back (o R); for
@@ -137,7 +138,7 @@ def test_randomized_rotation_decode_identity(scheme):
     out = rotate_f64(decode_f64(rq, kd[:, :n], vd[:, :n]), si, so)
     ref = decode_f64(q.astype(np.float64), rotate_f64(kd[:, :n], si, so), rotate_f64(vd[:, :n], si, so))
     assert np.allclose(out, ref, atol=1e-12)
-    if scheme == "block128":
+    if scheme != "kivi":
         assert np.allclose(out, oc.decode(q), atol=1e-12)
     # the signs change the stored codes (same source, plain rotation)
     plain = build(small_workload(905, scheme, 300, **(dict(hadamard=True) if scheme == "kivi" else {})), [300])
