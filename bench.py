@@ -67,8 +67,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+BLOCK_SCHEMES = ("block128", "tbq4")   # one 66-byte block per token and tensor
+
+
 def tier_map(cfg, T):
-    if cfg["scheme"] == "block128":
+    if cfg["scheme"] in BLOCK_SCHEMES:
         return T, 0
     Tq = max(0, ((T - 128) // 32) * 32)
     hi_start = 0 if cfg["hi_window"] < 0 else max(0, Tq - cfg["hi_window"])
@@ -94,6 +97,10 @@ def counter_traffic(wid):
 
 
 def describe_cache(cfg):
+    if cfg["scheme"] == "tbq4":
+        return ("TBQ4: 4-bit indices into 16 Lloyd-Max levels of N(0, 1/sqrt(128)) + fp16 norm "
+                "(66 B/128) after a " + ("randomized " if cfg.get("sign_in") else "")
+                + "Hadamard-128 rotation, no fp16 window")
     if cfg["scheme"] == "block128":
         return ("symmetric 4-bit blocks of 128 values + fp16 scale (66 B/128)"
                 + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")
@@ -114,7 +121,7 @@ def decode_bytes(w, T):
     cfg = w["cfg"]
     pairs = w["batch"] * w["num_kv_heads"]
     Tq, hi_start = tier_map(cfg, T)
-    if cfg["scheme"] == "block128":
+    if cfg["scheme"] in BLOCK_SCHEMES:
         per_pair = T * 2 * (64 + 2)
     else:
         hi = Tq - hi_start
@@ -261,7 +268,7 @@ def main():
     cache.append(k0, v0)
     torch.cuda.synchronize()
     chunk = None
-    if w.get("prefill") and w["cfg"]["scheme"] == "block128":
+    if w.get("prefill") and w["cfg"]["scheme"] in BLOCK_SCHEMES:
         n = w["prefill"]   # the workload's chunked-prefill append: its last n tokens
         chunk = (n, torch.cat([k0[:, T - n:], k1], 1).contiguous(), torch.cat([v0[:, T - n:], v1], 1).contiguous())
     del k0, v0

@@ -449,6 +449,22 @@ __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, con
   }
 }
 
+// Sum of a double over a 16-lane row by an xor butterfly: every lane ends with
+// the same bits (each stage adds the same two partial sums, in either order).
+__device__ __forceinline__ double row_sum_f64(double v) {
+  auto add = [&](auto tag) {
+    constexpr int M = decltype(tag)::value;
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = row_xor<M>((uint32_t)u), hi = row_xor<M>((uint32_t)(u >> 32));
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  add(std::integral_constant<int, 1>{});
+  add(std::integral_constant<int, 2>{});
+  add(std::integral_constant<int, 4>{});
+  add(std::integral_constant<int, 8>{});
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Symmetric 128-value blocks ([trefon] "Przykład: model 27B przy 262K"; "Jak
 // 4-bitowemu cache to uchodzi: najpierw obrót"): per token vector y (rotated
@@ -498,29 +514,52 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       if (g.hsigned) fwht128_row16_signed(x, i, g.sign_in, g.sign_out);
       else fwht128_row16(x, i);
     }
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-    const float a = __uint_as_float(row_max_u32(m));
-    const uint16_t sb = float_to_half_bits(a / 7.0f);
-    const float s = half_bits_to_float(sb);
-    // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
-    // code clamped to [-7, 7] lie in (-6.75, 6.75).  If any lane came close
-    // to one, the wave redoes its vectors with the division.
-    float r[8];
-    bool risky = false;
-    const float rs = s != 0.0f ? 1.0f / s : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, -6.75f, 6.75f, risky);
-    if (__any(risky)) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
-    }
+    uint16_t sb;
     uint32_t packed = 0;
+    if (g.tbq4) {
+      // TBQ4 ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót"):
+      // norm = fp16(min(fl32(sqrt(sum y^2)), 65504)), the sum and the root in
+      // fp64 (squares of fp32 values are exact there; the row's xor
+      // butterfly gives every lane the same sum); index = the number of
+      // level midpoints strictly below fl32(y / norm).
+      double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -7.0f), 7.0f) : 0;
-      packed |= (uint32_t)(c + 8) << (4 * j);
+      for (int j = 0; j < 8; ++j) ss = fma((double)x[j], (double)x[j], ss);
+      ss = row_sum_f64(ss);
+      sb = float_to_half_bits(fminf((float)sqrt(ss), 65504.0f));
+      const float nrm = half_bits_to_float(sb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = nrm != 0.0f ? x[j] / nrm : 0.0f;
+        uint32_t idx = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) idx += u > g.cb_bound[k] ? 1u : 0u;
+        packed |= idx << (4 * j);
+      }
+    } else {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+      const float a = __uint_as_float(row_max_u32(m));
+      sb = float_to_half_bits(a / 7.0f);
+      const float s = half_bits_to_float(sb);
+      // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
+      // code clamped to [-7, 7] lie in (-6.75, 6.75).  If any lane came close
+      // to one, the wave redoes its vectors with the division.
+      float r[8];
+      bool risky = false;
+      const float rs = s != 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, -6.75f, 6.75f, risky);
+      if (__any(risky)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -7.0f), 7.0f) : 0;
+        packed |= (uint32_t)(c + 8) << (4 * j);
+      }
     }
     if (tensor == 0) {
       if (in) *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;

@@ -100,6 +100,43 @@ __device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
   return __builtin_bit_cast(h4_t, v);
 }
 
+// TBQ4 levels of the eight 4-bit codes of a dword, as fp16 pairs in the
+// order the code masks take them: out[0] = (code 0, code 4), out[1] =
+// (1, 5), out[2] = (2, 6), out[3] = (3, 7) (code k = bits 4k .. 4k + 3).
+// A level is carried as hi + lo, two fp16 values (hi = fp16(level), lo =
+// fp16(level - hi)): a single fp16 would put a 2^-12 relative error on every
+// key and value, systematic per level, which the tolerance does not absorb
+// on large norms.  The 16 levels are symmetric (level[15 - k] = -level[k],
+// ascending), so a code n is the magnitude level[8 + m] with m = n - 8
+// (n >= 8) or 7 - n, negated for n < 8.  Byte lookups by v_perm: lut[0..1]
+// hold the low bytes of the eight magnitudes' hi halves, lut[2..3] their high
+// bytes, lut[4..7] the same for the lo halves; the magnitude nibbles
+// themselves are the selectors.  No memory is read.
+__device__ __forceinline__ void tbq4_levels(uint32_t w, const uint32_t* lut, uint32_t* hi, uint32_t* lo) {
+  const uint32_t neg = (~w >> 3) & 0x11111111u;                 // code < 8
+  const uint32_t mag = (w & 0x77777777u) ^ ((neg << 3) - neg);  // m per nibble
+  const uint32_t s_even = mag & 0x0F0F0F0Fu;                    // m of codes 0, 2, 4, 6
+  const uint32_t s_odd = (mag >> 4) & 0x0F0F0F0Fu;              // m of codes 1, 3, 5, 7
+  // the sign of code k moves from bit 4k to bit 15 or 31 of its pair
+  const uint32_t sg[4] = {(neg & 0x00010001u) << 15, (neg & 0x00100010u) << 11,
+                          (neg & 0x01000100u) << 7, (neg & 0x10001000u) << 3};
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const uint32_t* t = lut + 4 * part;
+    uint32_t* out = part ? lo : hi;
+    const uint32_t lb_e = __builtin_amdgcn_perm(t[1], t[0], s_even);
+    const uint32_t hb_e = __builtin_amdgcn_perm(t[3], t[2], s_even);
+    const uint32_t lb_o = __builtin_amdgcn_perm(t[1], t[0], s_odd);
+    const uint32_t hb_o = __builtin_amdgcn_perm(t[3], t[2], s_odd);
+    // [low, high] byte of selector bytes 0 and 2 (codes 0, 4 / 1, 5), 1 and
+    // 3 (codes 2, 6 / 3, 7); xor for the sign, as a lo half may be negative
+    out[0] = __builtin_amdgcn_perm(hb_e, lb_e, 0x06020400u) ^ sg[0];
+    out[1] = __builtin_amdgcn_perm(hb_o, lb_o, 0x06020400u) ^ sg[1];
+    out[2] = __builtin_amdgcn_perm(hb_e, lb_e, 0x07030501u) ^ sg[2];
+    out[3] = __builtin_amdgcn_perm(hb_o, lb_o, 0x07030501u) ^ sg[3];
+  }
+}
+
 __device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(x, y, c, 0, 0, 0);
 }
@@ -374,7 +411,7 @@ __device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, bool t
 }
 
 // p' = p s into this wave's value A table (PLw = PL[w]); zero-point sums.
-template <int G, int BITS, bool BLOCK, int HL, int NDG>
+template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false>
 __device__ __forceinline__ void stage_probs(const float* p, const float* vs, const float* vz,
                                             _Float16 (*PLw)[16][HL][4][4], float (*zacc)[NDG],
                                             int tl, int gh) {
@@ -385,7 +422,7 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
   // 16^(j & 1) (4-bit) or 4^(j & 3) (2-bit), j its nibble / crumb position
   // within a 16-bit half of its word; its probability takes the inverse (a
   // power of two: exact)
-  const float inv_f = BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
+  const float inv_f = TBQ ? 1.0f : BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
   for (int d = 0; d < NDG; ++d)
     for (int m = 0; m < G; ++m) {
       const float x = p[m] * vs[d];
@@ -399,10 +436,11 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
 }
 
 // O += p' . codes over the tile's value rows: 16 k-steps x 2 halves.
-template <int G, int BITS, bool BLOCK, int HL, int NDG>
+template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false>
 __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
                                            _Float16 (*PLw)[16][HL][4][4], int row, int gh,
-                                           f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3) {
+                                           f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3,
+                                           const uint32_t* lut = nullptr) {
   for (int gg = 0; gg < 2; ++gg) {
     for (int hf = 0; hf < 2; ++hf) {
       const int dg = BLOCK ? 0 : (gh + 2 * hf);
@@ -415,7 +453,10 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
         constexpr int NP = (BITS == 4) ? 4 : 8;
         uint32_t pr[NP];
         const uint32_t x8 = x >> 8;
-        if (BITS == 4) {
+        uint32_t prl[4] = {0, 0, 0, 0};
+        if (TBQ) {
+          tbq4_levels(x, lut, pr, prl);   // the levels themselves, no factors
+        } else if (BITS == 4) {
           pr[0] = x & 0x000F000Fu;
           pr[1] = x & 0x00F000F0u;
           pr[2] = x8 & 0x000F000Fu;
@@ -429,12 +470,16 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
         for (int q2 = 0; q2 < NP / 2; ++q2) {
           const int ks = 8 * gg + (NP / 2) * u + q2;   // k-step of pairs (2 q2, 2 q2 + 1)
           const h4_t bv = as_h4(pr[2 * q2], pr[2 * q2 + 1]);
-          for (int hl = 0; hl < HL; ++hl) {
-            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][hl][row][0]);
+          // TBQ: one more pass for the levels' lo halves against the hi half
+          // of p' (rows G.. of a HL = 1 table carry p's lo half: included)
+          for (int hl = 0; hl < HL + (TBQ ? 1 : 0); ++hl) {
+            const bool lo_lv = TBQ && hl == HL;
+            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][lo_lv ? 0 : hl][row][0]);
+            const h4_t b = lo_lv ? as_h4(prl[2 * q2], prl[2 * q2 + 1]) : bv;
             if (hf == 0) {
-              if (q2 & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
+              if (q2 & 1) o2 = mfma4(av, b, o2); else o0 = mfma4(av, b, o0);
             } else {
-              if (q2 & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
+              if (q2 & 1) o3 = mfma4(av, b, o3); else o1 = mfma4(av, b, o1);
             }
           }
         }

@@ -93,7 +93,10 @@ constexpr int decode_min_waves() {
   return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK && BITS == 4) ? 2 : 3);
 }
 
-template <int G, int BITS, bool BLOCK>
+// TBQ (with BLOCK): TBQ4 blocks; codes become their fp16 levels through
+// tbq4_levels() instead of entering as subnormals, and the block scale is the
+// norm, so there is neither a code offset nor a position factor.
+template <int G, int BITS, bool BLOCK, bool TBQ = false>
 __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
@@ -199,6 +202,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   int kch[4];
   float kinv[4];
   key_quad<BITS>(tl, kch, kinv);
+  if (TBQ)
+    for (int i = 0; i < 4; ++i) kinv[i] = 1.0f;
+  uint32_t lut[8];
+  for (int i = 0; i < 8; ++i) lut[i] = a.g.cb_lut[i];
 
   const uint8_t* kplane = a.p.p[a.hi_tier ? KVQ_PLANE_K_HI : KVQ_PLANE_K_LO];
   const uint8_t* vplane = a.p.p[a.hi_tier ? KVQ_PLANE_V_HI : KVQ_PLANE_V_LO];
@@ -244,10 +251,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
       for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-      add0[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh];
-      add1[m] = BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
+      add0[m] = TBQ ? 0.0f : BLOCK ? -8.0f * zsum[0] : zsum[gh];
+      add1[m] = TBQ ? 0.0f : BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
     }
-    write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, 16777216.0f,
+    write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, TBQ ? 1.0f : 16777216.0f,
                          add0, add1);
     reset();
   };
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         int ex = 0;
         if (qmax > 0.0f) frexpf(qmax, &ex);
         const int e_blk = 10 - ex;
-        e_scale_blk = ldexpf(1.0f, 24 - e_blk);
+        e_scale_blk = ldexpf(1.0f, (TBQ ? 0 : 24) - e_blk);
         for (int m = 0; m < G; ++m) {
           float s = 0.0f;
           for (int i = 0; i < 4; ++i) s += qv[m][i];
@@ -364,11 +371,17 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         const int i = 4 * j + u;     // canonical dword index of the row
         if (BITS == 4) {
           const uint32_t x8 = xw >> 8;
-          const h4_t b0 = as_h4(xw & 0x000F000Fu, xw & 0x00F000F0u);
-          const h4_t b1 = as_h4(x8 & 0x000F000Fu, x8 & 0x00F000F0u);
+          uint32_t lv[4], ll[4];
+          if (TBQ) tbq4_levels(xw, lut, lv, ll);
+          const h4_t b0 = TBQ ? as_h4(lv[0], lv[1]) : as_h4(xw & 0x000F000Fu, xw & 0x00F000F0u);
+          const h4_t b1 = TBQ ? as_h4(lv[2], lv[3]) : as_h4(x8 & 0x000F000Fu, x8 & 0x00F000F0u);
           for (int hl = 0; hl < HL; ++hl) {
             acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i][hl][row][0]), b0, acc0);
             acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i + 1][hl][row][0]), b1, acc1);
+          }
+          if (TBQ) {   // the levels' lo halves against the query's hi half
+            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i][0][row][0]), as_h4(ll[0], ll[1]), acc0);
+            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i + 1][0][row][0]), as_h4(ll[2], ll[3]), acc1);
           }
         } else {
           const uint32_t x10 = xw >> 10;
@@ -389,16 +402,17 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     for (int m = 0; m < G; ++m) {
       const float dotv = (HL == 1) ? acc0[m] + acc0[G + m] + acc1[m] + acc1[G + m] : acc0[m] + acc1[m];
       float s;
-      if (BLOCK) s = kscale * (dotv * e_scale_blk - 8.0f * qsum[m]);
+      if (TBQ) s = kscale * (dotv * e_scale_blk);
+      else if (BLOCK) s = kscale * (dotv * e_scale_blk - 8.0f * qsum[m]);
       else s = dotv * kscale_grp + bias[m];
       if (!tok_ok) s = -INFINITY;
       p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
     }
 
     // ---------------- p' = p s into the value A table; values: O += p' . codes
-    stage_probs<G, BITS, BLOCK, HL, NDG>(p, vs, vz, PL[w], zacc, tl, gh);
+    stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PL[w], zacc, tl, gh);
     wave_sync();
-    value_mfma<G, BITS, BLOCK, HL, NDG>(vc, PL[w], row, gh, o0, o1, o2, o3);
+    value_mfma<G, BITS, BLOCK, HL, NDG, TBQ>(vc, PL[w], row, gh, o0, o1, o2, o3, lut);
     wave_sync();
 
     // ---------------- the member's partial when its assignment ends
@@ -417,7 +431,10 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
   const void* fn = nullptr;
   const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_FN(GG, BB, BL) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, BB, BL>)
-  if (blk) {
+#define KVQ_FT(GG) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, 4, true, true>)
+  if (g.tbq4) {
+    if (g.G == 1) KVQ_FT(1); else if (g.G == 2) KVQ_FT(2); else KVQ_FT(4);
+  } else if (blk) {
     if (g.G == 1) KVQ_FN(1, 4, true); else if (g.G == 2) KVQ_FN(2, 4, true); else KVQ_FN(4, 4, true);
   } else if (bits == 4) {
     if (g.G == 1) KVQ_FN(1, 4, false); else if (g.G == 2) KVQ_FN(2, 4, false); else KVQ_FN(4, 4, false);
@@ -425,6 +442,7 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
     if (g.G == 1) KVQ_FN(1, 2, false); else if (g.G == 2) KVQ_FN(2, 2, false); else KVQ_FN(4, 2, false);
   }
 #undef KVQ_FN
+#undef KVQ_FT
   return occupancy_wgs_per_cu(fn);
 }
 
@@ -458,7 +476,12 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
     const dim3 grid((unsigned)(rp.pwgs + wins)), block(256);
     const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_MF(GG, BB, BL) hipLaunchKernelGGL((decode_mfma_kernel<GG, BB, BL>), grid, block, 0, s, a)
-    if (blk) {
+#define KVQ_MT(GG) hipLaunchKernelGGL((decode_mfma_kernel<GG, 4, true, true>), grid, block, 0, s, a)
+    if (g.tbq4) {
+      if (g.G == 1) KVQ_MT(1);
+      else if (g.G == 2) KVQ_MT(2);
+      else KVQ_MT(4);
+    } else if (blk) {
       if (g.G == 1) KVQ_MF(1, 4, true);
       else if (g.G == 2) KVQ_MF(2, 4, true);
       else KVQ_MF(4, 4, true);
@@ -472,6 +495,7 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
       else KVQ_MF(4, 2, false);
     }
 #undef KVQ_MF
+#undef KVQ_MT
   }
   return hipGetLastError();
 }

@@ -5,6 +5,7 @@
 //   KIVI:     x = fl32(c * s_h + z_h)   (the product is exact, so fused or not
 //                                        gives the same bits)
 //   BLOCK128: y = fl32((n - 8) * s_h)  (exact)
+//   TBQ4:     y = fl32(norm * level[n])
 //   window:   the fp16 value.
 #pragma clang fp contract(off)
 
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
     const int b = (int)(r / nt);
     const int64_t pair = pair_index(g, b, h);
     float kv, vv;
-    if (g.scheme == KVQ_BLOCK128_SYM) {
+    if (block_scheme(g.scheme)) {
       const int64_t grp = t / kGroup;
       const int row = (int)(t % kGroup);
       const uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + grp) * 2048;
@@ -36,8 +37,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       const int vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
       const uint16_t* ks = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
       const uint16_t* vs = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
-      kv = (float)(kn - 8) * half_bits_to_float(ks[t]);
-      vv = (float)(vn - 8) * half_bits_to_float(vs[t]);
+      if (g.tbq4) {
+        float kl = g.cb_level[0], vl = g.cb_level[0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) {
+          kl = kn == k ? g.cb_level[k] : kl;
+          vl = vn == k ? g.cb_level[k] : vl;
+        }
+        kv = half_bits_to_float(ks[t]) * kl;
+        vv = half_bits_to_float(vs[t]) * vl;
+      } else {
+        kv = (float)(kn - 8) * half_bits_to_float(ks[t]);
+        vv = (float)(vn - 8) * half_bits_to_float(vs[t]);
+      }
     } else if (t < g.Tq) {
       const int64_t grp = t / kGroup;
       const int row = (int)(t % kGroup);

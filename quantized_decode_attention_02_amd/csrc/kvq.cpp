@@ -9,6 +9,7 @@
 //              ultra-long context" (troisinh.com).
 //   [nalar]    "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
 //              (nalar.dev).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -27,7 +28,7 @@ kvq_status validate_config(const kvq_config* c) {
   if (c == nullptr) return KVQ_ERR_INVALID_ARG;
   if (c->head_dim <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
-  if (c->scheme != KVQ_KIVI_ASYM && c->scheme != KVQ_BLOCK128_SYM) return KVQ_ERR_INVALID_ARG;
+  if (c->scheme != KVQ_KIVI_ASYM && !block_scheme(c->scheme)) return KVQ_ERR_INVALID_ARG;
   if (c->k_bits <= 0 || c->v_bits <= 0) return KVQ_ERR_INVALID_ARG;
   if (c->hadamard != 0 && c->hadamard != 1) return KVQ_ERR_INVALID_ARG;
   if (c->pre_rope_keys != 0 && c->pre_rope_keys != 1) return KVQ_ERR_INVALID_ARG;
@@ -52,18 +53,83 @@ kvq_status validate_config(const kvq_config* c) {
     if (c->k_bits != 4) return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != 0 || c->int4_window != -1) return KVQ_ERR_UNSUPPORTED;
     if (c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
+    // TBQ4's levels assume the near-normal coordinates of a rotated block
+    if (c->scheme == KVQ_TBQ4 && !c->hadamard) return KVQ_ERR_UNSUPPORTED;
   }
   return KVQ_OK;
 }
 
 int64_t quantized_prefix(const kvq_config* c, int64_t length) {
-  if (c->scheme == KVQ_BLOCK128_SYM) return length;
+  if (block_scheme(c->scheme)) return length;
   const int64_t r = length - kWindow;
   if (r <= 0) return 0;
   return (r / kGroup) * kGroup;
 }
 
 int64_t groups_for(int64_t max_tokens) { return (max_tokens + kGroup - 1) / kGroup; }
+
+// The TBQ4 codebook ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw
+// obrót": 16 Lloyd-Max levels fitted to N(0, 1/sqrt(128))).  Lloyd's
+// iteration on the unit normal in fp64 from evenly spaced levels on [-3, 3]:
+// every boundary the midpoint of its neighbours, every level the normal's
+// mean over its cell, (phi(a) - phi(b)) / (Phi(b) - Phi(a)), until no level
+// moves by 1e-14 (the iteration contracts by ~0.965 a step, so the levels end
+// ~3e-13 from the fixed point, far inside their fp32 rounding margins).  Then
+// level_k = fl32(unit level * 1/sqrt(128)), boundary_k = fl32 of the exact
+// midpoint of two fp32 levels.  Computed once, immutable afterwards.
+struct Tbq4Codebook {
+  float level[16];
+  float bound[15];
+  uint32_t lut[8];
+};
+
+const Tbq4Codebook& tbq4_codebook() {
+  static const Tbq4Codebook cb = [] {
+    const double inv_sqrt2 = 1.0 / std::sqrt(2.0);
+    auto phi = [](double x) { return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI); };
+    // Phi(b) - Phi(a), from the tail that keeps it accurate
+    auto mass = [&](double a, double b) {
+      if (a >= 0.0) return 0.5 * (std::erfc(a * inv_sqrt2) - std::erfc(b * inv_sqrt2));
+      if (b <= 0.0) return 0.5 * (std::erfc(-b * inv_sqrt2) - std::erfc(-a * inv_sqrt2));
+      return 1.0 - 0.5 * std::erfc(-a * inv_sqrt2) - 0.5 * std::erfc(b * inv_sqrt2);
+    };
+    double c[16];
+    for (int k = 0; k < 16; ++k) c[k] = -3.0 + 6.0 * (k + 0.5) / 16.0;
+    for (int it = 0; it < 10000; ++it) {
+      double b[17];
+      b[0] = -HUGE_VAL;
+      b[16] = HUGE_VAL;
+      for (int k = 0; k < 15; ++k) b[k + 1] = 0.5 * (c[k] + c[k + 1]);
+      double moved = 0.0;
+      double nc[16];
+      for (int k = 0; k < 16; ++k) {
+        const double plo = std::isinf(b[k]) ? 0.0 : phi(b[k]);
+        const double phi_ = std::isinf(b[k + 1]) ? 0.0 : phi(b[k + 1]);
+        nc[k] = (plo - phi_) / mass(b[k], b[k + 1]);
+        moved = std::max(moved, std::fabs(nc[k] - c[k]));
+      }
+      for (int k = 0; k < 16; ++k) c[k] = nc[k];
+      if (moved < 1e-14) break;
+    }
+    Tbq4Codebook r{};
+    const double sigma = 1.0 / std::sqrt(128.0);
+    for (int k = 0; k < 16; ++k) r.level[k] = (float)(c[k] * sigma);
+    for (int k = 0; k < 15; ++k) r.bound[k] = (float)(((double)r.level[k] + (double)r.level[k + 1]) / 2.0);
+    // decode's v_perm tables: each magnitude as hi = fp16(level) and
+    // lo = fp16(level - hi), split into low and high bytes
+    for (int m = 0; m < 8; ++m) {
+      const __half hh = __float2half_rn(r.level[8 + m]);
+      const uint16_t h = __half_as_ushort(hh);
+      const uint16_t l = __half_as_ushort(__float2half_rn(r.level[8 + m] - __half2float(hh)));
+      r.lut[m >> 2] |= (uint32_t)(h & 0xFF) << (8 * (m & 3));
+      r.lut[2 + (m >> 2)] |= (uint32_t)(h >> 8) << (8 * (m & 3));
+      r.lut[4 + (m >> 2)] |= (uint32_t)(l & 0xFF) << (8 * (m & 3));
+      r.lut[6 + (m >> 2)] |= (uint32_t)(l >> 8) << (8 * (m & 3));
+    }
+    return r;
+  }();
+  return cb;
+}
 
 Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t length) {
   Geom g;
@@ -75,6 +141,13 @@ Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t l
   g.hi_bits = c->k_bits;
   g.lo_bits = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->low_bits : c->k_bits;
   g.hadamard = c->hadamard;
+  g.tbq4 = c->scheme == KVQ_TBQ4;
+  {
+    const Tbq4Codebook& cb = tbq4_codebook();
+    for (int k = 0; k < 16; ++k) g.cb_level[k] = cb.level[k];
+    for (int k = 0; k < 15; ++k) g.cb_bound[k] = cb.bound[k];
+    for (int k = 0; k < 8; ++k) g.cb_lut[k] = cb.lut[k];
+  }
   g.hsigned = 0;
   for (int i = 0; i < 4; ++i) {
     g.sign_in.w[i] = c->hadamard_sign_in[i];
@@ -332,7 +405,7 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
     e = launch_rope_table(g, p, T0, T1, st);
     if (e != hipSuccess) return from_hip(e);
   }
-  if (cfg->scheme == KVQ_BLOCK128_SYM) {
+  if (block_scheme(cfg->scheme)) {
     e = launch_block128_append(g, p, kn, vn, n_new, T0, st);
   } else {
     // Tier bookkeeping ([troisinh] "Ý tưởng cốt lõi", "Mixed Precision"): the

@@ -43,7 +43,7 @@ __host__ __device__ __forceinline__ int64_t tile_bytes(int bits) { return 512 * 
 __device__ __forceinline__ const uint8_t* tile_ptr(const Geom& g, const Planes& p, int plane_hi,
                                                    int plane_lo, int64_t pair, int64_t grp,
                                                    int* bits_out) {
-  if (g.scheme == KVQ_BLOCK128_SYM || grp * kGroup >= g.hi_start) {
+  if (block_scheme(g.scheme) || grp * kGroup >= g.hi_start) {
     *bits_out = g.hi_bits;
     return p.p[plane_hi] + (pair * g.hi_slots + grp % g.hi_slots) * tile_bytes(g.hi_bits);
   }

@@ -24,11 +24,18 @@ struct Mask128 {
 // value to every launch.
 struct Geom {
   int B, Hq, Hkv, G;           // G = Hq / Hkv
-  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM
+  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM / KVQ_TBQ4
   int hi_bits, lo_bits;
   int hadamard, pre_rope;
   int hsigned;                 // 1: the rotation is randomized (a mask is nonzero)
   Mask128 sign_in, sign_out;   // D_in, D_out of D_out H D_in / sqrt(128)
+  int tbq4;                    // 1: KVQ_TBQ4 blocks (norm + Lloyd-Max indices)
+  float cb_bound[15];          // TBQ4 decision boundaries (fp32 midpoints)
+  float cb_level[16];          // TBQ4 levels, ascending
+  uint32_t cb_lut[8];          // levels 8..15 (the magnitudes) as hi + lo
+                               // fp16: low bytes of hi of 8..11, of 12..15,
+                               // high bytes of hi of 8..11, of 12..15, then
+                               // the same four for lo (v_perm tables)
   float rope_theta;
   int64_t gmax;                // groups per (sequence, head)
   int64_t hi_slots;            // K_HI / V_HI tiles per (sequence, head)
@@ -79,6 +86,9 @@ constexpr int64_t kCounterStride = 64;
 inline int64_t counter_words(int64_t pairs) { return 2 * pairs * kCounterStride; }
 
 ChunkPlan plan_chunks(const Geom& g);
+
+// Schemes with one 128-value block per token (no window, no tiers).
+__host__ __device__ inline bool block_scheme(int scheme) { return scheme == KVQ_BLOCK128_SYM || scheme == KVQ_TBQ4; }
 
 // Launchers (kernels in append.hip, decode.hip, dequant.hip).  Each returns
 // hipGetLastError() after its launches.

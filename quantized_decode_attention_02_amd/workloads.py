@@ -60,6 +60,16 @@ def _tbq4(**kw):
     return c
 
 
+def random_signs(seed):
+    """Sign masks of a randomized Hadamard rotation: dict(sign_in=[4 words],
+    sign_out=[4 words]), 128 seeded fair coin flips each (bit i of word i // 32
+    set: coordinate i negated).  Inputs only; what they do is the library's and
+    the oracle's business."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, 0x5167, seed])))
+    words = rng.integers(0, 1 << 32, size=8, dtype=np.uint64)
+    return dict(sign_in=[int(x) for x in words[:4]], sign_out=[int(x) for x in words[4:]])
+
+
 WORKLOADS = [
     dict(id=0, name="int4-kivi-b1-h1-t4096-outlier4x20",
          batch=1, num_q_heads=1, num_kv_heads=1, tokens=4096, prefill=0,
@@ -77,6 +87,11 @@ WORKLOADS = [
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_block128(), dist="normal", outliers=None),
 ]
+# TBQ4 proper (Lloyd-Max levels, randomized Hadamard) at the block-128 shape
+WORKLOADS.append(
+    dict(id=5, name="tbq4-randomized-hadamard-gqa32x8-b32-t65536+8192",
+         batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
+         cfg=_tbq4(**random_signs(5)), dist="normal", outliers=None))
 
 
 def workload(key):
@@ -100,16 +115,6 @@ def library_config(w):
     c = dict(w["cfg"])
     c.update(head_dim=D, num_q_heads=w["num_q_heads"], num_kv_heads=w["num_kv_heads"])
     return c
-
-
-def random_signs(seed):
-    """Sign masks of a randomized Hadamard rotation: dict(sign_in=[4 words],
-    sign_out=[4 words]), 128 seeded fair coin flips each (bit i of word i // 32
-    set: coordinate i negated).  Inputs only; what they do is the library's and
-    the oracle's business."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, 0x5167, seed])))
-    words = rng.integers(0, 1 << 32, size=8, dtype=np.uint64)
-    return dict(sign_in=[int(x) for x in words[:4]], sign_out=[int(x) for x in words[4:]])
 
 
 def _rng(wid, b, h, tensor, blk):

@@ -30,6 +30,7 @@ SCHEDULES = {
     2: [65536, 65535, 1],
     3: [131072, 131032] + [1] * 40,
     4: [8192] * 9,
+    5: [8192] * 9,
 }
 
 

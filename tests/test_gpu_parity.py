@@ -27,6 +27,8 @@ VARIANTS = {
     "block128": None,
     "block128-plain": dict(hadamard=False),
     "block128-signed": dict(SIGNS),
+    "tbq4": dict(),
+    "tbq4-signed": dict(SIGNS),
 }
 
 
@@ -34,6 +36,8 @@ def make_w(wid, variant, T, batch=2, hq=8, hkv=2, dist="normal", outliers=None):
     kw = VARIANTS[variant]
     if variant.startswith("block128"):
         cfg = wl._block128(**(kw or {}))
+    elif variant.startswith("tbq4"):
+        cfg = wl._tbq4(**kw)
     else:
         cfg = wl._kivi(**kw)
     return wl.custom(wid, batch, hq, hkv, T, cfg, dist=dist, outliers=outliers)
