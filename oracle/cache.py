@@ -6,7 +6,7 @@ The cache is per sequence and grows by one entry per token per layer
 ([trefon] "Czym jest cache KV"); it is written at run time, token by token, so
 quantization parameters come from the observed values ([trefon] "Dlaczego cache
 trudniej skwantyzować niż wagi"; [nalar] "Pertumbuhan cache dinamis mengubah
-persoalan kalibrasi").  Three schemes:
+persoalan kalibrasi").  Four schemes:
 
 ``kivi``: keys per channel over 32-token groups, values per token over 32-dim
   groups, asymmetric, fp16 scale and zero; a fp16 window of recent tokens
@@ -21,6 +21,9 @@ persoalan kalibrasi").  Three schemes:
 ``tbq4``: every token's 128-vector, always rotated, becomes 16 Lloyd-Max
   indices and an fp16 norm in the same 66-byte container (codebook.py); no
   window.
+``q4_0``: every token's 128-vector, optionally rotated, becomes four
+  symmetric 4-bit 32-value blocks with an fp16 scale each (18 B per 32 values,
+  [trefon] "Przykład: model 27B przy 262K"); no window.
 
 Append order (reading; the pages give none): groups that leave the high-bit
 tier are requantized to ``low_bits`` from their dequantized high-bit values
@@ -65,7 +68,7 @@ def make_config(**kw):
 
 
 # per-token 128-value block schemes: nibbles + one fp16 per token and tensor
-BLOCK_SCHEMES = ("block128", "tbq4")
+BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")
 
 
 def _tile_token_of_byte(key_tile):
@@ -111,8 +114,9 @@ class OracleCache:
             Tp = G * 32
             self.k_nib = np.zeros((B, H, Tp, 128), np.uint8)
             self.v_nib = np.zeros((B, H, Tp, 128), np.uint8)
-            self.k_sc = np.zeros((B, H, Tp), F16)
-            self.v_sc = np.zeros((B, H, Tp), F16)
+            sc_shape = (B, H, Tp, 4) if c["scheme"] == "q4_0" else (B, H, Tp)
+            self.k_sc = np.zeros(sc_shape, F16)
+            self.v_sc = np.zeros(sc_shape, F16)
 
     # -- tiers ---------------------------------------------------------------
     @property
@@ -140,7 +144,8 @@ class OracleCache:
         vn = np.transpose(v_new, (0, 2, 1, 3))
         c = self.cfg
         if c["scheme"] in BLOCK_SCHEMES:
-            quantize = quant.quant_sym128 if c["scheme"] == "block128" else codebook.quant_tbq4
+            quantize = {"block128": quant.quant_sym128, "tbq4": codebook.quant_tbq4,
+                        "q4_0": quant.quant_sym32}[c["scheme"]]
             for name, src, nib, sc in (("k", kn, self.k_nib, self.k_sc),
                                        ("v", vn, self.v_nib, self.v_sc)):
                 y = self._source_rows(src)
@@ -194,7 +199,8 @@ class OracleCache:
         K = np.zeros((B, H, t1 - t0, 128), F32)
         V = np.zeros((B, H, t1 - t0, 128), F32)
         if c["scheme"] in BLOCK_SCHEMES:
-            deq = quant.dequant_sym128 if c["scheme"] == "block128" else codebook.dequant_tbq4
+            deq = {"block128": quant.dequant_sym128, "tbq4": codebook.dequant_tbq4,
+                   "q4_0": quant.dequant_sym32}[c["scheme"]]
             K[:] = deq(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
             V[:] = deq(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
         else:
@@ -265,7 +271,7 @@ class OracleCache:
                 lv[:] = (tok < T)[None, None]
                 meta = layout.K_META if plane == layout.K_HI else layout.V_META
                 pair(img[meta])[:] = sc.reshape(B, H, -1).astype("<f2").view(np.uint8)
-                ml = np.repeat(np.arange(G * 32) < T, 2)
+                ml = np.repeat(np.arange(G * 32) < T, 2 * (4 if c["scheme"] == "q4_0" else 1))
                 pair(live[meta])[:] = ml[None, None]
             return img, live
         hs = layout.hi_slots(c, self.max_tokens)

@@ -144,6 +144,15 @@ def block66(nibbles, s_h):
     return out.reshape(np.shape(nibbles)[:-1] + (66,))
 
 
+def block18(nibbles, s_h):
+    """The 18-byte blocks of one 128-value vector's four 32-value slices: per
+    slice an fp16 scale (LE) + 16 code bytes (element 2k low nibble of byte k)."""
+    n = np.asarray(nibbles)
+    codes = pack_rows(n.reshape(n.shape[:-1] + (4, 32)), 4)          # [..., 4, 16]
+    s = np.asarray(s_h, dtype="<f2").reshape(n.shape[:-1] + (4, 1)).view(np.uint8)
+    return np.concatenate([s, codes], axis=-1)                       # [..., 4, 18]
+
+
 def gmax(max_tokens):
     return (max_tokens + TILE_TOKENS - 1) // TILE_TOKENS
 
@@ -171,10 +180,11 @@ def plane_sizes(cfg, batch, max_tokens):
         sz[K_WIN] = pairs * RING * 128 * 2
         sz[V_WIN] = pairs * RING * 128 * 2
     else:
+        per_token = 4 if cfg["scheme"] == "q4_0" else 1     # fp16 per token
         sz[K_HI] = pairs * G * 512 * 4
         sz[V_HI] = pairs * G * 512 * 4
-        sz[K_META] = pairs * G * TILE_TOKENS * 2
-        sz[V_META] = pairs * G * TILE_TOKENS * 2
+        sz[K_META] = pairs * G * TILE_TOKENS * 2 * per_token
+        sz[V_META] = pairs * G * TILE_TOKENS * 2 * per_token
     if cfg["pre_rope"]:
         sz[ROPE] = G * TILE_TOKENS * 64 * 2 * 4
     return sz

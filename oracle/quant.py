@@ -29,6 +29,9 @@ Readings where the pages are silent (all float32 one op at a time, RNE):
     a = max|y|;  s_h = fp16(fl32(a / 7))
     c = clamp(rint(fl32(y / s_h)), -7, 7);  c = 0 wherever s_h == 0
     stored nibble n = c + 8 (1..15);  y^ = fl32((n - 8) * s_h)  (exact)
+  symmetric 32-value blocks, 4 bits ("Q4_0", 18 B per 32 values in the
+  format table of [trefon] "Przykład: model 27B przy 262K"): the same
+  quantizer over each 32-value slice of a vector, one fp16 scale per slice.
   No clipping: the full [min, max] range is used.
 """
 
@@ -96,6 +99,32 @@ def dequant_sym128(nibbles, s_h):
     """y^ = fl32((n - 8) * s_h), exact."""
     c = np.asarray(nibbles).astype(np.int16) - 8
     return (c.astype(F32) * np.asarray(s_h, dtype=F16).astype(F32)[..., None]).astype(F32)
+
+
+def quant_sym32(y):
+    """Symmetric 4-bit quantization of float32 vectors (last axis 128) in four
+    32-value slices: (nibbles uint8 1..15, s_h fp16 [..., 4])."""
+    y = np.asarray(y, dtype=F32)
+    _check_finite(y)
+    if y.shape[-1] != 128:
+        raise ValueError("vector length must be 128")
+    ys = y.reshape(y.shape[:-1] + (4, 32))
+    a = np.abs(ys).max(axis=-1)
+    s_h = (a / F32(7)).astype(F32).astype(F16)
+    sx = s_h.astype(F32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quo = (ys / sx).astype(F32)
+    quo = np.where(sx == 0, F32(0), quo)
+    c = np.clip(np.rint(quo), F32(-7), F32(7)).astype(np.int16)
+    return (c + 8).astype(np.uint8).reshape(y.shape), s_h
+
+
+def dequant_sym32(nibbles, s_h):
+    """y^ = fl32((n - 8) * s_h of the value's slice), exact."""
+    n = np.asarray(nibbles)
+    c = (n.astype(np.int16) - 8).reshape(n.shape[:-1] + (4, 32)).astype(F32)
+    y = c * np.asarray(s_h, dtype=F16).astype(F32)[..., None]
+    return y.astype(F32).reshape(n.shape)
 
 
 # --- KIVI groups -------------------------------------------------------------

@@ -53,6 +53,13 @@ def _block128(**kw):
     return c
 
 
+def _q4_0(**kw):
+    c = dict(scheme="q4_0", k_bits=4, v_bits=4, low_bits=2, hi_window=-1,
+             window=0, hadamard=False, pre_rope=False, rope_theta=10000.0)
+    c.update(kw)
+    return c
+
+
 def _tbq4(**kw):
     c = dict(scheme="tbq4", k_bits=4, v_bits=4, low_bits=2, hi_window=-1,
              window=0, hadamard=True, pre_rope=False, rope_theta=10000.0)

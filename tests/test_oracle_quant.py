@@ -161,3 +161,31 @@ def test_dequant_exactness():
     prod = c.astype(np.float64) * s.astype(np.float64)
     assert np.array_equal(prod.astype(F32).astype(np.float64), prod)
     assert np.array_equal(got, (prod + z.astype(np.float64)).astype(F32))
+
+
+def test_symmetric_32_value_blocks():
+    """Q4_0-style slices: the 128-block quantizer applied to each 32-value
+    slice on its own (embedded in zeros, so its absmax is the slice's) must
+    give the same codes and scale; bound, absmax level, byte image."""
+    from oracle import layout
+    rng = np.random.default_rng(12)
+    y = (rng.standard_normal((500, 128)) * rng.uniform(0.01, 100, (500, 4)).repeat(32, axis=1)).astype(F32)
+    n, s = quant.quant_sym32(y)
+    assert n.shape == y.shape and s.shape == (500, 4)
+    for g in range(4):
+        emb = np.zeros_like(y)
+        emb[:, 32 * g:32 * g + 32] = y[:, 32 * g:32 * g + 32]
+        n1, s1 = quant.quant_sym128(emb)
+        assert np.array_equal(s1.view(np.uint16), s[:, g].view(np.uint16))
+        assert np.array_equal(n1[:, 32 * g:32 * g + 32], n[:, 32 * g:32 * g + 32])
+    yh = quant.dequant_sym32(n, s)
+    bound = np.repeat(s.astype(np.float64), 32, axis=1) / 2 * SLACK
+    assert np.all(np.abs(y - yh) <= bound)
+    img = layout.block18(n[:3], s[:3])
+    assert img.shape == (3, 4, 18)
+    assert np.array_equal(img[..., :2].copy().view("<f2")[..., 0], s[:3])
+    # element 2k in the low nibble of byte k of its slice
+    assert np.array_equal(img[..., 2:] & 0xF, n[:3].reshape(3, 4, 32)[..., 0::2])
+    assert np.array_equal(img[..., 2:] >> 4, n[:3].reshape(3, 4, 32)[..., 1::2])
+    # 18 B per 32 values = 4.5 bits per value (the page's Q4_0 row)
+    assert img.shape[-1] * 8 / 32 == 4.5

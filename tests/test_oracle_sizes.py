@@ -101,3 +101,6 @@ def test_plane_sizes_match_per_token_bytes(bits):
     cfgb = make_config(scheme="block128", num_q_heads=4, num_kv_heads=2)
     szb = layout.plane_sizes(cfgb, B, T)
     assert sum(szb) == B * 2 * T * sizes.block128_bytes_per_token_head()
+    # four 18-byte blocks per token and tensor
+    cfgq = make_config(scheme="q4_0", num_q_heads=4, num_kv_heads=2)
+    assert sum(layout.plane_sizes(cfgq, B, T)) == B * 2 * T * 2 * 4 * 18   # K and V
