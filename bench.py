@@ -67,7 +67,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-BLOCK_SCHEMES = ("block128", "tbq4")   # one 66-byte block per token and tensor
+BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")   # per-token blocks, no window
+
+
+def block_bytes(cfg):
+    """Bytes of one token's 128 values of one tensor in a block scheme."""
+    return 4 * 18 if cfg["scheme"] == "q4_0" else 66
 
 
 def tier_map(cfg, T):
@@ -97,6 +102,9 @@ def counter_traffic(wid):
 
 
 def describe_cache(cfg):
+    if cfg["scheme"] == "q4_0":
+        return ("Q4_0-style symmetric 4-bit blocks of 32 values + fp16 scale (18 B/32)"
+                + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")
     if cfg["scheme"] == "tbq4":
         return ("TBQ4: 4-bit indices into 16 Lloyd-Max levels of N(0, 1/sqrt(128)) + fp16 norm "
                 "(66 B/128) after a " + ("randomized " if cfg.get("sign_in") else "")
@@ -122,7 +130,7 @@ def decode_bytes(w, T):
     pairs = w["batch"] * w["num_kv_heads"]
     Tq, hi_start = tier_map(cfg, T)
     if cfg["scheme"] in BLOCK_SCHEMES:
-        per_pair = T * 2 * (64 + 2)
+        per_pair = T * 2 * block_bytes(cfg)
     else:
         hi = Tq - hi_start
         lo = hi_start
@@ -289,7 +297,7 @@ def main():
         torch.cuda.synchronize()
         a_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
         rd = w["batch"] * n * w["num_kv_heads"] * 2 * 128 * 2
-        wr = w["batch"] * n * w["num_kv_heads"] * 2 * 66
+        wr = w["batch"] * n * w["num_kv_heads"] * 2 * block_bytes(w["cfg"])
         append_rec = {"tokens_per_seq": n, "ms": round(a_ms, 5), "read_bytes": rd, "write_bytes": wr,
                       "gbs": round((rd + wr) / (a_ms / 1e3) / 1e9, 2),
                       "frac": round((rd + wr) / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}

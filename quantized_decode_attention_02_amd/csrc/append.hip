@@ -540,7 +540,9 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-      const float a = __uint_as_float(row_max_u32(m));
+      // Q4_0: the absmax of this lane's 32-value slice (lanes 4s .. 4s + 3 of
+      // the row); the 128-block scheme: of the whole row
+      const float a = __uint_as_float(g.q40 ? quad_max_u32(m) : row_max_u32(m));
       sb = float_to_half_bits(a / 7.0f);
       const float s = half_bits_to_float(sb);
       // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
@@ -566,7 +568,12 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
     } else {
       vnib[tok][i] = packed;
     }
-    if (in && i == 0) {
+    if (g.q40) {
+      if (in && (i & 3) == 0) {   // one scale per 32-value slice, slices in order
+        uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
+        sp[(pair * g.gmax * kGroup + t) * 4 + (i >> 2)] = sb;
+      }
+    } else if (in && i == 0) {
       uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
       sp[pair * g.gmax * kGroup + t] = sb;
     }

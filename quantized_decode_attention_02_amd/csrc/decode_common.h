@@ -196,6 +196,7 @@ struct TileRaw {
   uint4 kmr;        // KIVI, keys before RoPE: (s, z) of channels 4 (lane % 32) .. + 3
   uint4 vm;         // KIVI: (s, z) x 4 of this lane's token
   uint16_t ks16, vs16;   // BLOCK: per-token scales
+  uint2 kq4, vq4;        // BLOCK, Q4_0: the four 32-value slice scales of the token
 };
 
 struct TilePos {
@@ -262,7 +263,7 @@ __device__ __forceinline__ bool cursor_next(const MfmaArgs& a, TileCursor& c, in
   return true;
 }
 
-template <int BITS, bool BLOCK, bool ROPE>
+template <int BITS, bool BLOCK, bool ROPE, bool Q40 = false>
 __device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos& tp, int lane,
                                           const uint8_t* kpair, const uint8_t* vpair,
                                           const uint8_t* kmpair, const uint8_t* vmpair,
@@ -291,7 +292,11 @@ __device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos
       }
     }
   }
-  if (BLOCK) {
+  if (BLOCK && Q40) {
+    const int64_t t = tp.base + lane;
+    r.kq4 = tok_ok ? reinterpret_cast<const uint2*>(ksc)[t] : make_uint2(0, 0);
+    r.vq4 = tok_ok ? reinterpret_cast<const uint2*>(vsc)[t] : make_uint2(0, 0);
+  } else if (BLOCK) {
     const int64_t t = tp.base + lane;
     r.ks16 = tok_ok ? ksc[t] : (uint16_t)0;
     r.vs16 = tok_ok ? vsc[t] : (uint16_t)0;
@@ -345,7 +350,7 @@ __device__ __forceinline__ void stage_issue(uint8_t* st, const TilePos& tp, int 
 }
 
 // Metadata of the lane's token / group into registers (plain loads).
-template <int BITS, bool BLOCK, bool ROPE>
+template <int BITS, bool BLOCK, bool ROPE, bool Q40 = false>
 __device__ __forceinline__ void meta_issue(TileRaw<BITS, BLOCK>& r, const TilePos& tp, int lane,
                                            const uint8_t* kmpair, const uint8_t* vmpair,
                                            const uint16_t* ksc, const uint16_t* vsc, int64_t scale_end,
@@ -354,8 +359,13 @@ __device__ __forceinline__ void meta_issue(TileRaw<BITS, BLOCK>& r, const TilePo
   if (BLOCK) {
     int64_t t = tp.base + lane;
     if (t >= scale_end) t = scale_end - 1;
-    r.ks16 = ksc[t];
-    r.vs16 = vsc[t];
+    if (Q40) {
+      r.kq4 = reinterpret_cast<const uint2*>(ksc)[t];
+      r.vq4 = reinterpret_cast<const uint2*>(vsc)[t];
+    } else {
+      r.ks16 = ksc[t];
+      r.vs16 = vsc[t];
+    }
   } else {
     const int64_t grp = tp.grp0 + ((gh && tp.nvalid > 32) ? 1 : 0);
     const uint8_t* kmeta = kmpair + grp * 512;
@@ -395,10 +405,17 @@ __device__ __forceinline__ void wait_stage_read() { asm volatile("s_waitcnt lgkm
 // Per-token value scales / zeros of this lane's token from the raw tile.
 // Tokens past the tile get 0 (their probability is 0, and 0 * anything
 // non-finite would not be).
-template <int BITS, bool BLOCK, int NDG>
+template <int BITS, bool BLOCK, int NDG, bool Q40 = false>
 __device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, bool tok_ok, float* vs,
                                            float* vz) {
-  if (BLOCK) {
+  if (BLOCK && Q40) {   // a scale per 32-dim slice; the code offset 8 comes back in the flush
+    const uint32_t vw[2] = {r.vq4.x, r.vq4.y};
+    for (int d = 0; d < NDG; ++d) {
+      const uint16_t h = (uint16_t)((vw[d >> 1] >> (16 * (d & 1))) & 0xFFFF);
+      vs[d] = tok_ok ? half_bits_to_float(h) : 0.0f;
+      vz[d] = 0.0f;
+    }
+  } else if (BLOCK) {
     vs[0] = tok_ok ? half_bits_to_float(r.vs16) : 0.0f;
     vz[0] = 0.0f;
   } else {
@@ -443,7 +460,7 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
                                            const uint32_t* lut = nullptr) {
   for (int gg = 0; gg < 2; ++gg) {
     for (int hf = 0; hf < 2; ++hf) {
-      const int dg = BLOCK ? 0 : (gh + 2 * hf);
+      const int dg = NDG == 1 ? 0 : (gh + 2 * hf);   // the 32-dim slice of channel lane + 64 hf
       for (int u = 0; u < BITS; ++u) {
         const uint32_t x = vc[gg][hf][u];
         // one dword: 8 tokens (4-bit) or 16 tokens (2-bit), two per pr[] (one

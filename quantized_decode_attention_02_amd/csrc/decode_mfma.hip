@@ -96,11 +96,14 @@ constexpr int decode_min_waves() {
 // TBQ (with BLOCK): TBQ4 blocks; codes become their fp16 levels through
 // tbq4_levels() instead of entering as subnormals, and the block scale is the
 // norm, so there is neither a code offset nor a position factor.
-template <int G, int BITS, bool BLOCK, bool TBQ = false>
+// Q40 (with BLOCK): Q4_0 blocks; every token has a scale per 32-value slice,
+// so key scores are summed slice by slice (a slice is one uint4 of the key
+// row) and values use four scale groups, as KIVI's per-token values do.
+template <int G, int BITS, bool BLOCK, bool TBQ = false, bool Q40 = false>
 __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
-  constexpr int NDG = BLOCK ? 1 : 4;     // value scale groups per token
+  constexpr int NDG = (BLOCK && !Q40) ? 1 : 4;   // value scale groups per token
   constexpr int TB = 512 * BITS;         // tile bytes
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
@@ -217,11 +220,12 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   auto vpair_of = [&](int64_t pr) { return vplane + pr * slots * TB; };
   auto kmeta_of = [&](int64_t pr) { return a.p.p[KVQ_PLANE_K_META] + pr * g.gmax * 512; };
   auto vmeta_of = [&](int64_t pr) { return a.p.p[KVQ_PLANE_V_META] + pr * g.gmax * 512; };
+  constexpr int SPT = Q40 ? 4 : 1;   // fp16 scales per token (block schemes)
   auto ksc_of = [&](int64_t pr) {
-    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pr * g.gmax * kGroup;
+    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_K_META]) + pr * g.gmax * kGroup * SPT;
   };
   auto vsc_of = [&](int64_t pr) {
-    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pr * g.gmax * kGroup;
+    return reinterpret_cast<const uint16_t*>(a.p.p[KVQ_PLANE_V_META]) + pr * g.gmax * kGroup * SPT;
   };
 
   TilePos cur_pos, nxt_pos;
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   uint8_t* stage = ST[KVQ_DECODE_STAGE ? w : 0];
   auto issue = [&](const TilePos& tp, int64_t pr) {
     stage_issue<BITS>(stage, tp, lane, kpair_of(pr), vpair_of(pr));
-    meta_issue<BITS, BLOCK, false>(nxt, tp, lane, kmeta_of(pr), vmeta_of(pr), ksc_of(pr), vsc_of(pr),
-                                   scale_end, kch[0], kch[1]);
+    meta_issue<BITS, BLOCK, false, Q40>(nxt, tp, lane, kmeta_of(pr), vmeta_of(pr), ksc_of(pr), vsc_of(pr),
+                                        scale_end, kch[0], kch[1]);
   };
   TileCursor cs;
   cursor_start(a, rank, cs, lane);
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   int pb = 0, ph = 0;
   float qv[G][4];
   float qsum[G];
+  float qsum4[G][4];   // Q40: sums of the query over each 32-channel slice
   float e_scale_blk = 1.0f;
 
   // this member's partial of `pair`
@@ -251,8 +256,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
       for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-      add0[m] = TBQ ? 0.0f : BLOCK ? -8.0f * zsum[0] : zsum[gh];
-      add1[m] = TBQ ? 0.0f : BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
+      add0[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh] : BLOCK ? -8.0f * zsum[0] : zsum[gh];
+      add1[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh + 2] : BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
     }
     write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, TBQ ? 1.0f : 16777216.0f,
                          add0, add1);
@@ -281,6 +286,15 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
           float s = 0.0f;
           for (int i = 0; i < 4; ++i) s += qv[m][i];
           qsum[m] = half_sum(s);   // the 32 lanes of a half cover all 128 channels
+          if (Q40) {
+            // k-step tl covers channels of slice tl / 8: sum over those 8 lanes
+            float s8 = s;
+            s8 += lane_xor<1>(s8, lane);
+            s8 += lane_xor<2>(s8, lane);
+            s8 += lane_xor<4>(s8, lane);
+            for (int j = 0; j < 4; ++j)
+              qsum4[m][j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s8), 8 * j));
+          }
         }
         if (gh == 0) {
           for (int m = 0; m < G; ++m) {
@@ -306,11 +320,12 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
       stage_read<BITS, BLOCK>(cur, stage, lane);
       cur.km0 = nxt.km0; cur.km1 = nxt.km1; cur.vm = nxt.vm; cur.ks16 = nxt.ks16; cur.vs16 = nxt.vs16;
+      cur.kq4 = nxt.kq4; cur.vq4 = nxt.vq4;
       wait_stage_read();
       if (more) issue(nxt_pos, cs.pair);
     } else {
-      load_tile<BITS, BLOCK, false>(cur, cur_pos, lane, kpair_of(pair), vpair_of(pair), kmeta_of(pair),
-                                    vmeta_of(pair), ksc_of(pair), vsc_of(pair), kch[0], kch[1]);
+      load_tile<BITS, BLOCK, false, Q40>(cur, cur_pos, lane, kpair_of(pair), vpair_of(pair), kmeta_of(pair),
+                                         vmeta_of(pair), ksc_of(pair), vsc_of(pair), kch[0], kch[1]);
       more = cursor_next(a, cs, lane, &ends);
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
     }
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     const uint4* kc = cur.kc;
     const uint32_t (*vc)[2][BITS] = cur.vc;
     float vs[NDG], vz[NDG];
-    value_meta<BITS, BLOCK, NDG>(cur, tok_ok, vs, vz);
+    value_meta<BITS, BLOCK, NDG, Q40>(cur, tok_ok, vs, vz);
     const float kscale = BLOCK ? half_bits_to_float(cur.ks16) : 0.0f;
     const uint2 km0 = cur.km0, km1 = cur.km1;
 
@@ -364,6 +379,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
 
     // ---------------- scores: S = q' . codes over 32 k-steps (two chains)
     f4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    float sq[G];   // Q40: the score so far, slice by slice
+    for (int m = 0; m < G; ++m) sq[m] = 0.0f;
     for (int j = 0; j < NKW; ++j) {
       const uint32_t dw[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
       for (int u = 0; u < 4; ++u) {
@@ -397,12 +414,24 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
           }
         }
       }
+      if (Q40) {
+        // slice j done: its scale times (q'.codes - 8 sum q), then the next
+        const uint32_t kw2 = j < 2 ? cur.kq4.x : cur.kq4.y;
+        const float ksj = half_bits_to_float((uint16_t)((kw2 >> (16 * (j & 1))) & 0xFFFF));
+        for (int m = 0; m < G; ++m) {
+          const float dj = (HL == 1) ? acc0[m] + acc0[G + m] + acc1[m] + acc1[G + m] : acc0[m] + acc1[m];
+          sq[m] += ksj * (dj * e_scale_blk - 8.0f * qsum4[m][j]);
+        }
+        acc0 = f4_t{0, 0, 0, 0};
+        acc1 = f4_t{0, 0, 0, 0};
+      }
     }
     float p[G];
     for (int m = 0; m < G; ++m) {
       const float dotv = (HL == 1) ? acc0[m] + acc0[G + m] + acc1[m] + acc1[G + m] : acc0[m] + acc1[m];
       float s;
-      if (TBQ) s = kscale * (dotv * e_scale_blk);
+      if (Q40) s = sq[m];
+      else if (TBQ) s = kscale * (dotv * e_scale_blk);
       else if (BLOCK) s = kscale * (dotv * e_scale_blk - 8.0f * qsum[m]);
       else s = dotv * kscale_grp + bias[m];
       if (!tok_ok) s = -INFINITY;
@@ -432,8 +461,11 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
   const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_FN(GG, BB, BL) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, BB, BL>)
 #define KVQ_FT(GG) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, 4, true, true>)
+#define KVQ_FQ(GG) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, 4, true, false, true>)
   if (g.tbq4) {
     if (g.G == 1) KVQ_FT(1); else if (g.G == 2) KVQ_FT(2); else KVQ_FT(4);
+  } else if (g.q40) {
+    if (g.G == 1) KVQ_FQ(1); else if (g.G == 2) KVQ_FQ(2); else KVQ_FQ(4);
   } else if (blk) {
     if (g.G == 1) KVQ_FN(1, 4, true); else if (g.G == 2) KVQ_FN(2, 4, true); else KVQ_FN(4, 4, true);
   } else if (bits == 4) {
@@ -443,6 +475,7 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
   }
 #undef KVQ_FN
 #undef KVQ_FT
+#undef KVQ_FQ
   return occupancy_wgs_per_cu(fn);
 }
 
@@ -477,10 +510,15 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
     const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_MF(GG, BB, BL) hipLaunchKernelGGL((decode_mfma_kernel<GG, BB, BL>), grid, block, 0, s, a)
 #define KVQ_MT(GG) hipLaunchKernelGGL((decode_mfma_kernel<GG, 4, true, true>), grid, block, 0, s, a)
+#define KVQ_MQ(GG) hipLaunchKernelGGL((decode_mfma_kernel<GG, 4, true, false, true>), grid, block, 0, s, a)
     if (g.tbq4) {
       if (g.G == 1) KVQ_MT(1);
       else if (g.G == 2) KVQ_MT(2);
       else KVQ_MT(4);
+    } else if (g.q40) {
+      if (g.G == 1) KVQ_MQ(1);
+      else if (g.G == 2) KVQ_MQ(2);
+      else KVQ_MQ(4);
     } else if (blk) {
       if (g.G == 1) KVQ_MF(1, 4, true);
       else if (g.G == 2) KVQ_MF(2, 4, true);
@@ -496,6 +534,7 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
     }
 #undef KVQ_MF
 #undef KVQ_MT
+#undef KVQ_MQ
   }
   return hipGetLastError();
 }

@@ -6,6 +6,7 @@
 //                                        gives the same bits)
 //   BLOCK128: y = fl32((n - 8) * s_h)  (exact)
 //   TBQ4:     y = fl32(norm * level[n])
+//   Q4_0:     y = fl32((n - 8) * s_h of the value's 32-value slice)  (exact)
 //   window:   the fp16 value.
 #pragma clang fp contract(off)
 
@@ -35,8 +36,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       const uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 2048;
       const int kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
       const int vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
-      const uint16_t* ks = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup;
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup;
+      const int per = g.q40 ? 4 : 1;   // fp16 scales per token
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup * per;
+      const uint16_t* vs = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup * per;
       if (g.tbq4) {
         float kl = g.cb_level[0], vl = g.cb_level[0];
 #pragma unroll
@@ -46,6 +48,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
         }
         kv = half_bits_to_float(ks[t]) * kl;
         vv = half_bits_to_float(vs[t]) * vl;
+      } else if (g.q40) {
+        kv = (float)(kn - 8) * half_bits_to_float(ks[4 * t + (d >> 5)]);
+        vv = (float)(vn - 8) * half_bits_to_float(vs[4 * t + (d >> 5)]);
       } else {
         kv = (float)(kn - 8) * half_bits_to_float(ks[t]);
         vv = (float)(vn - 8) * half_bits_to_float(vs[t]);

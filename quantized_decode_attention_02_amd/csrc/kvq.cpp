@@ -142,6 +142,7 @@ Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t l
   g.lo_bits = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->low_bits : c->k_bits;
   g.hadamard = c->hadamard;
   g.tbq4 = c->scheme == KVQ_TBQ4;
+  g.q40 = c->scheme == KVQ_Q4_0;
   {
     const Tbq4Codebook& cb = tbq4_codebook();
     for (int k = 0; k < 16; ++k) g.cb_level[k] = cb.level[k];
@@ -185,8 +186,9 @@ void plane_sizes(const kvq_config* c, int64_t batch, int64_t max_tokens, uint64_
   } else {
     sz[KVQ_PLANE_K_HI] = pairs * G * 2048;
     sz[KVQ_PLANE_V_HI] = pairs * G * 2048;
-    sz[KVQ_PLANE_K_META] = pairs * G * kGroup * 2;
-    sz[KVQ_PLANE_V_META] = pairs * G * kGroup * 2;
+    const uint64_t per_token = c->scheme == KVQ_Q4_0 ? 4 : 1;   // fp16 scales
+    sz[KVQ_PLANE_K_META] = pairs * G * kGroup * 2 * per_token;
+    sz[KVQ_PLANE_V_META] = pairs * G * kGroup * 2 * per_token;
   }
   if (c->pre_rope_keys) sz[KVQ_PLANE_ROPE] = G * kGroup * 64 * 2 * 4;
 }

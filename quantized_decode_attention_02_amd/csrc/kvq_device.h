@@ -247,6 +247,13 @@ __device__ __forceinline__ void fwht128_row16_signed(float* x, int i, const Mask
   for (int j = 0; j < 8; ++j) x[j] = flip_by(x[j], m, b0 + j);
 }
 
+// Maximum of a non-negative float over a quad of lanes (4q .. 4q + 3), on
+// its bit pattern.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, row_xor<1>(v));
+  return max(v, row_xor<2>(v));
+}
+
 // Maximum of a non-negative float over a 16-lane row, on its bit pattern
 // (for non-negative floats the integer order is the numeric order).
 __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {

@@ -24,12 +24,13 @@ struct Mask128 {
 // value to every launch.
 struct Geom {
   int B, Hq, Hkv, G;           // G = Hq / Hkv
-  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM / KVQ_TBQ4
+  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM / KVQ_TBQ4 / KVQ_Q4_0
   int hi_bits, lo_bits;
   int hadamard, pre_rope;
   int hsigned;                 // 1: the rotation is randomized (a mask is nonzero)
   Mask128 sign_in, sign_out;   // D_in, D_out of D_out H D_in / sqrt(128)
   int tbq4;                    // 1: KVQ_TBQ4 blocks (norm + Lloyd-Max indices)
+  int q40;                     // 1: KVQ_Q4_0 (four 32-value blocks per token)
   float cb_bound[15];          // TBQ4 decision boundaries (fp32 midpoints)
   float cb_level[16];          // TBQ4 levels, ascending
   uint32_t cb_lut[8];          // levels 8..15 (the magnitudes) as hi + lo
@@ -88,7 +89,9 @@ inline int64_t counter_words(int64_t pairs) { return 2 * pairs * kCounterStride;
 ChunkPlan plan_chunks(const Geom& g);
 
 // Schemes with one 128-value block per token (no window, no tiers).
-__host__ __device__ inline bool block_scheme(int scheme) { return scheme == KVQ_BLOCK128_SYM || scheme == KVQ_TBQ4; }
+__host__ __device__ inline bool block_scheme(int scheme) {
+  return scheme == KVQ_BLOCK128_SYM || scheme == KVQ_TBQ4 || scheme == KVQ_Q4_0;
+}
 
 // Launchers (kernels in append.hip, decode.hip, dequant.hip).  Each returns
 // hipGetLastError() after its launches.

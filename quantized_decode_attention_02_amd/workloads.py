@@ -99,6 +99,11 @@ WORKLOADS.append(
     dict(id=5, name="tbq4-randomized-hadamard-gqa32x8-b32-t65536+8192",
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_tbq4(**random_signs(5)), dist="normal", outliers=None))
+# Q4_0-style 32-value blocks (the format table's baseline) at the same shape
+WORKLOADS.append(
+    dict(id=6, name="q4_0-gqa32x8-b32-t65536+8192",
+         batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
+         cfg=_q4_0(), dist="normal", outliers=None))
 
 
 def workload(key):

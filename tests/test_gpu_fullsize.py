@@ -31,6 +31,7 @@ SCHEDULES = {
     3: [131072, 131032] + [1] * 40,
     4: [8192] * 9,
     5: [8192] * 9,
+    6: [8192] * 9,
 }
 
 

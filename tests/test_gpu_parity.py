@@ -29,6 +29,8 @@ VARIANTS = {
     "block128-signed": dict(SIGNS),
     "tbq4": dict(),
     "tbq4-signed": dict(SIGNS),
+    "q4_0": dict(),
+    "q4_0-hadamard": dict(hadamard=True),
 }
 
 
@@ -38,6 +40,8 @@ def make_w(wid, variant, T, batch=2, hq=8, hkv=2, dist="normal", outliers=None):
         cfg = wl._block128(**(kw or {}))
     elif variant.startswith("tbq4"):
         cfg = wl._tbq4(**kw)
+    elif variant.startswith("q4_0"):
+        cfg = wl._q4_0(**kw)
     else:
         cfg = wl._kivi(**kw)
     return wl.custom(wid, batch, hq, hkv, T, cfg, dist=dist, outliers=outliers)
