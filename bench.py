@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "417bee24f3aa62cf67cc50b2d790c1b41286db1167ebb031f81c05e7206531de", "fetch_kib": 665005, "write_kib": 4210,
+    1: {"sources_sha256": "4467ffc66c7fa4d3cd87298cb0d3bae8753c07e5b3f98b4c50fa9e2f5232401c", "fetch_kib": 665043, "write_kib": 4210,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
