@@ -71,16 +71,19 @@ def make_config(**kw):
 BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")
 
 
-def _tile_token_of_byte(key_tile):
-    """Token index whose codes a 4-bit tile byte holds (the lower token of the
-    pair for a value tile, whose bytes hold two tokens of one channel)."""
-    tok = np.zeros(2048, np.int64)
+def _tile_token_of_byte(key_tile, bits=4):
+    """Token index whose codes a 4- or 3-bit tile byte holds (for a value
+    tile, whose bytes hold codes of several tokens of one channel, the first
+    token with bits in the byte)."""
+    rb_k = 128 * bits // 8
+    tok = np.zeros(512 * bits, np.int64)
     if key_tile:
-        for cb in range(64):
+        for cb in range(rb_k):
             for t in range(32):
                 tok[(cb // 16) * 512 + t * 16 + (cb % 16)] = t
     else:
-        tok[:] = np.tile(2 * np.arange(16), 128)
+        rb_v = 32 * bits // 8
+        tok[:] = np.tile((8 * np.arange(rb_v)) // bits, 128)
     return tok
 
 
@@ -144,8 +147,8 @@ class OracleCache:
         vn = np.transpose(v_new, (0, 2, 1, 3))
         c = self.cfg
         if c["scheme"] in BLOCK_SCHEMES:
-            quantize = {"block128": quant.quant_sym128, "tbq4": codebook.quant_tbq4,
-                        "q4_0": quant.quant_sym32}[c["scheme"]]
+            quantize = {"block128": lambda y: quant.quant_sym128(y, c["k_bits"]),
+                        "tbq4": codebook.quant_tbq4, "q4_0": quant.quant_sym32}[c["scheme"]]
             for name, src, nib, sc in (("k", kn, self.k_nib, self.k_sc),
                                        ("v", vn, self.v_nib, self.v_sc)):
                 y = self._source_rows(src)
@@ -199,8 +202,8 @@ class OracleCache:
         K = np.zeros((B, H, t1 - t0, 128), F32)
         V = np.zeros((B, H, t1 - t0, 128), F32)
         if c["scheme"] in BLOCK_SCHEMES:
-            deq = {"block128": quant.dequant_sym128, "tbq4": codebook.dequant_tbq4,
-                   "q4_0": quant.dequant_sym32}[c["scheme"]]
+            deq = {"block128": lambda n, s: quant.dequant_sym128(n, s, c["k_bits"]),
+                   "tbq4": codebook.dequant_tbq4, "q4_0": quant.dequant_sym32}[c["scheme"]]
             K[:] = deq(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
             V[:] = deq(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
         else:
@@ -264,10 +267,11 @@ class OracleCache:
             for plane, nib, sc in ((layout.K_HI, self.k_nib, self.k_sc),
                                    (layout.V_HI, self.v_nib, self.v_sc)):
                 tiles = nib.reshape(B, H, G, 32, 128)
-                im = pair(img[plane]).reshape(B, H, G, 2048)
-                lv = pair(live[plane]).reshape(B, H, G, 2048)
-                tok = np.arange(G)[:, None] * 32 + _tile_token_of_byte(plane == layout.K_HI)[None, :]
-                im[:] = (layout.k_tile if plane == layout.K_HI else layout.v_tile)(tiles, 4)
+                tb = 512 * c["k_bits"]
+                im = pair(img[plane]).reshape(B, H, G, tb)
+                lv = pair(live[plane]).reshape(B, H, G, tb)
+                tok = np.arange(G)[:, None] * 32 + _tile_token_of_byte(plane == layout.K_HI, c["k_bits"])[None, :]
+                im[:] = (layout.k_tile if plane == layout.K_HI else layout.v_tile)(tiles, c["k_bits"])
                 lv[:] = (tok < T)[None, None]
                 meta = layout.K_META if plane == layout.K_HI else layout.V_META
                 pair(img[meta])[:] = sc.reshape(B, H, -1).astype("<f2").view(np.uint8)

@@ -12,6 +12,9 @@ with the library.
 Packing of codes into bytes (canonical):
   4 bits: element 2k -> low nibble of byte k, element 2k+1 -> high nibble.
   2 bits: element 4k+j -> bits [2j, 2j+1] of byte k.
+  3 bits: element i -> bits [3i, 3i+2] of the row read as one little-endian
+          bit string, so eight codes fill three bytes and codes 2, 5 (mod 8)
+          straddle a byte boundary.
 
 Tiles.  Quantized tokens live in tiles of 32 consecutive tokens (one key group):
   key tile   -- token-major: row t = packed codes of token t over the 128
@@ -27,7 +30,8 @@ Planes (all [batch][kv_head][...], row-major, little-endian fp16/fp32):
   0 K_HI   KIVI: key tiles of the high-bit tier.  With a high-bit window of N
            tokens the plane is a ring of N/32 slots and group g uses slot
            g mod (N/32); otherwise it has one slot per group.
-           BLOCK128: key tiles of every group.
+           Block schemes: key tiles of every group (4-bit, or 3-bit for the
+           50-byte block).
   1 V_HI   same for values.
   2 K_LO   KIVI with a high-bit window only: low-bit key tiles, slot g = group g.
   3 V_LO   same for values.
@@ -57,6 +61,17 @@ PLANE_NAMES = ["K_HI", "V_HI", "K_LO", "V_LO", "K_META", "V_META", "K_WIN",
 def pack_rows(codes, bits):
     """Pack the last axis of ``codes`` (uint8 values < 2**bits) canonically."""
     c = np.asarray(codes, dtype=np.uint8)
+    if bits == 3:
+        if c.shape[-1] % 8:
+            raise ValueError("3-bit rows pack 8 codes into 3 bytes")
+        if np.any(c >= 8):
+            raise ValueError("code out of range")
+        g = c.reshape(c.shape[:-1] + (c.shape[-1] // 8, 8)).astype(np.uint32)
+        word = np.zeros(g.shape[:-1], dtype=np.uint32)       # 24 bits per 8 codes
+        for j in range(8):
+            word |= g[..., j] << (3 * j)
+        out = np.stack([(word >> (8 * b)) & 0xFF for b in range(3)], axis=-1).astype(np.uint8)
+        return out.reshape(c.shape[:-1] + (c.shape[-1] * 3 // 8,))
     per = 8 // bits
     if c.shape[-1] % per:
         raise ValueError("row length not a multiple of codes per byte")
@@ -72,6 +87,11 @@ def pack_rows(codes, bits):
 def unpack_rows(packed, bits, n):
     """Inverse of pack_rows: bytes -> n codes per row."""
     p = np.asarray(packed, dtype=np.uint8)
+    if bits == 3:
+        b = p.reshape(p.shape[:-1] + (p.shape[-1] // 3, 3)).astype(np.uint32)
+        word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+        out = np.stack([(word >> (3 * j)) & 7 for j in range(8)], axis=-1)
+        return out.reshape(p.shape[:-1] + (-1,))[..., :n].astype(np.uint8)
     per = 8 // bits
     mask = (1 << bits) - 1
     parts = [(p >> (bits * j)) & mask for j in range(per)]
@@ -153,6 +173,15 @@ def block18(nibbles, s_h):
     return np.concatenate([s, codes], axis=-1)                       # [..., 4, 18]
 
 
+def block50(codes, s_h):
+    """The 50-byte block of one 128-value vector at 3 bits: fp16 scale (LE) +
+    48 code bytes (the format table's "3 bity (50 B / 128)" row)."""
+    s = np.asarray(s_h, dtype="<f2").reshape(-1, 1).view(np.uint8)
+    body = pack_rows(codes, 3).reshape(-1, 48)
+    out = np.concatenate([s.reshape(-1, 2), body], axis=-1)
+    return out.reshape(np.shape(codes)[:-1] + (50,))
+
+
 def gmax(max_tokens):
     return (max_tokens + TILE_TOKENS - 1) // TILE_TOKENS
 
@@ -181,8 +210,8 @@ def plane_sizes(cfg, batch, max_tokens):
         sz[V_WIN] = pairs * RING * 128 * 2
     else:
         per_token = 4 if cfg["scheme"] == "q4_0" else 1     # fp16 per token
-        sz[K_HI] = pairs * G * 512 * 4
-        sz[V_HI] = pairs * G * 512 * 4
+        sz[K_HI] = pairs * G * 512 * cfg["k_bits"]
+        sz[V_HI] = pairs * G * 512 * cfg["v_bits"]
         sz[K_META] = pairs * G * TILE_TOKENS * 2 * per_token
         sz[V_META] = pairs * G * TILE_TOKENS * 2 * per_token
     if cfg["pre_rope"]:

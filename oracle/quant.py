@@ -29,6 +29,9 @@ Readings where the pages are silent (all float32 one op at a time, RNE):
     a = max|y|;  s_h = fp16(fl32(a / 7))
     c = clamp(rint(fl32(y / s_h)), -7, 7);  c = 0 wherever s_h == 0
     stored nibble n = c + 8 (1..15);  y^ = fl32((n - 8) * s_h)  (exact)
+  the same at 3 bits (the 50-byte block, "3 bity (50 B / 128)" in the format
+  table of [trefon] "Przykład: model 27B przy 262K"): s_h = fp16(fl32(a / 3)),
+  c in [-3, 3], stored n = c + 4 (1..7), y^ = fl32((n - 4) * s_h).
   symmetric 32-value blocks, 4 bits ("Q4_0", 18 B per 32 values in the
   format table of [trefon] "Przykład: model 27B przy 262K"): the same
   quantizer over each 32-value slice of a vector, one fp16 scale per slice.
@@ -77,27 +80,30 @@ def dequant_asym(codes, s_h, z_h, axis):
     return ((c * s).astype(F32) + z).astype(F32)
 
 
-def quant_sym128(y):
-    """Symmetric 4-bit quantization of float32 vectors along the last axis (128).
-
-    Returns (nibbles uint8 in 1..15 (or 8 for an all-zero vector), s_h fp16)."""
+def quant_sym128(y, bits=4):
+    """Symmetric quantization of float32 vectors along the last axis (128) at
+    4 or 3 bits.  Returns (codes uint8 in 1 .. 2^bits - 1 (the middle code for
+    an all-zero vector), s_h fp16)."""
     y = np.asarray(y, dtype=F32)
     _check_finite(y)
     if y.shape[-1] != 128:
         raise ValueError("block length must be 128")
+    if bits not in (4, 3):
+        raise ValueError("4 or 3 bits")
+    top = (1 << (bits - 1)) - 1                    # 7 or 3
     a = np.abs(y).max(axis=-1)
-    s_h = (a / F32(7)).astype(F32).astype(F16)
+    s_h = (a / F32(top)).astype(F32).astype(F16)
     sx = s_h.astype(F32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         quo = (y / sx).astype(F32)
     quo = np.where(sx == 0, F32(0), quo)
-    c = np.clip(np.rint(quo), F32(-7), F32(7)).astype(np.int16)
-    return (c + 8).astype(np.uint8), s_h
+    c = np.clip(np.rint(quo), F32(-top), F32(top)).astype(np.int16)
+    return (c + top + 1).astype(np.uint8), s_h
 
 
-def dequant_sym128(nibbles, s_h):
-    """y^ = fl32((n - 8) * s_h), exact."""
-    c = np.asarray(nibbles).astype(np.int16) - 8
+def dequant_sym128(nibbles, s_h, bits=4):
+    """y^ = fl32((n - 2^(bits-1)) * s_h), exact."""
+    c = np.asarray(nibbles).astype(np.int16) - (1 << (bits - 1))
     return (c.astype(F32) * np.asarray(s_h, dtype=F16).astype(F32)[..., None]).astype(F32)
 
 

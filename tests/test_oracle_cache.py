@@ -58,6 +58,7 @@ SIGNS = wl.random_signs(7)
                                        ("block128", dict(**SIGNS)),
                                        ("tbq4", {}), ("tbq4", dict(**SIGNS)),
                                        ("q4_0", {}), ("q4_0", dict(hadamard=True)),
+                                       ("block128", dict(k_bits=3, v_bits=3)),
                                        ("kivi", dict(k_bits=2, v_bits=2)),
                                        ("kivi", dict(pre_rope=True, rope_theta=500000.0)),
                                        ("block128", {})])

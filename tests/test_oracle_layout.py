@@ -91,3 +91,49 @@ def test_meta_images():
     # token 7, dim group 2 at bytes 16*7 + 4*2: (s, z)
     assert mv[16 * 7 + 8:16 * 7 + 10].view("<f2")[0] == sv[7, 2]
     assert mv[16 * 31 + 14:16 * 31 + 16].view("<f2")[0] == zv[31, 3]
+
+
+def test_every_3bit_code_at_every_position():
+    # element i at bits 3i .. 3i + 2 of the little-endian bit string: built
+    # here bit by bit, independently of the packer's 24-bit words
+    for p in range(128):
+        for v in range(8):
+            codes = np.zeros(128, np.uint8)
+            codes[p] = v
+            packed = layout.pack_rows(codes, 3)
+            assert packed.shape == (48,)
+            expect = np.zeros(48, np.uint8)
+            for k in range(3):
+                if (v >> k) & 1:
+                    bit = 3 * p + k
+                    expect[bit // 8] |= 1 << (bit % 8)
+            assert np.array_equal(packed, expect), (p, v)
+            assert np.array_equal(layout.unpack_rows(packed, 3, 128), codes)
+    # all codes at once, random rows, round trip
+    rng = np.random.default_rng(33)
+    rows = rng.integers(0, 8, size=(50, 128)).astype(np.uint8)
+    assert np.array_equal(layout.unpack_rows(layout.pack_rows(rows, 3), 3, 128), rows)
+    with pytest.raises(ValueError):
+        layout.pack_rows(np.array([8] + [0] * 7, np.uint8), 3)
+
+
+def test_3bit_tiles_and_block50():
+    rng = np.random.default_rng(34)
+    codes = rng.integers(0, 8, size=(32, 128)).astype(np.uint8)
+    kt, vt = layout.k_tile(codes, 3), layout.v_tile(codes, 3)
+    assert kt.shape == (1536,) and vt.shape == (1536,)
+    assert np.array_equal(layout.k_tile_decode(kt, 3), codes)
+    assert np.array_equal(layout.v_tile_decode(vt, 3), codes)
+    rows = layout.pack_rows(codes, 3)              # [32, 48]
+    assert kt[2 * 512 + 7 * 16 + 3] == rows[7, 35]
+    # value row d: 12 bytes, token t at bits 3t
+    for d in (0, 64, 127):
+        r = vt[12 * d:12 * d + 12]
+        stream = int.from_bytes(r.tobytes(), "little")
+        assert [(stream >> (3 * t)) & 7 for t in range(32)] == list(codes[:, d])
+    s = np.array([1.5, -0.25], np.float16)
+    img = layout.block50(codes[:2] % 8, s)
+    assert img.shape == (2, 50)
+    assert np.array_equal(img[:, :2].copy().view("<f2")[:, 0], s)
+    assert np.array_equal(img[:, 2:], layout.pack_rows(codes[:2], 3))
+    assert 50 * 8 / 128 == 3.125

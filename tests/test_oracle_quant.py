@@ -189,3 +189,24 @@ def test_symmetric_32_value_blocks():
     assert np.array_equal(img[..., 2:] >> 4, n[:3].reshape(3, 4, 32)[..., 1::2])
     # 18 B per 32 values = 4.5 bits per value (the page's Q4_0 row)
     assert img.shape[-1] * 8 / 32 == 4.5
+
+
+def test_symmetric_block_3bit():
+    rng = np.random.default_rng(14)
+    y = (rng.standard_normal((3000, 128)) * rng.uniform(0.01, 100, (3000, 1))).astype(F32)
+    n, s = quant.quant_sym128(y, 3)
+    yh = quant.dequant_sym128(n, s, 3)
+    assert n.min() >= 1 and n.max() <= 7
+    assert np.all(np.abs(y - yh) <= s.astype(np.float64)[:, None] / 2 * SLACK)
+    am = np.argmax(np.abs(y), axis=1)
+    c_am = n[np.arange(len(y)), am].astype(int) - 4
+    assert np.all(np.abs(c_am) == 3)
+    assert np.all(np.sign(c_am) == np.sign(y[np.arange(len(y)), am]))
+    # brute force: every code is the nearest of the 7 levels (away from ties)
+    c = n.astype(np.float64) - 4
+    q = y.astype(np.float64) / s.astype(np.float64)[:, None]
+    near = np.clip(np.round(q), -3, 3)
+    clear = np.abs(np.abs(q - np.floor(q)) - 0.5) > 1e-4
+    assert np.array_equal(c[clear], near[clear])
+    zn, zs = quant.quant_sym128(np.zeros((1, 128), F32), 3)
+    assert np.all(zn == 4) and zs[0] == 0
