@@ -72,7 +72,9 @@ BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")   # per-token blocks, no window
 
 def block_bytes(cfg):
     """Bytes of one token's 128 values of one tensor in a block scheme."""
-    return 4 * 18 if cfg["scheme"] == "q4_0" else 66
+    if cfg["scheme"] == "q4_0":
+        return 4 * 18
+    return 50 if cfg["k_bits"] == 3 else 66
 
 
 def tier_map(cfg, T):
@@ -109,6 +111,9 @@ def describe_cache(cfg):
         return ("TBQ4: 4-bit indices into 16 Lloyd-Max levels of N(0, 1/sqrt(128)) + fp16 norm "
                 "(66 B/128) after a " + ("randomized " if cfg.get("sign_in") else "")
                 + "Hadamard-128 rotation, no fp16 window")
+    if cfg["scheme"] == "block128" and cfg["k_bits"] == 3:
+        return ("symmetric 3-bit blocks of 128 values + fp16 scale (50 B/128)"
+                + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")
     if cfg["scheme"] == "block128":
         return ("symmetric 4-bit blocks of 128 values + fp16 scale (66 B/128)"
                 + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")

@@ -497,7 +497,9 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
                   ? *reinterpret_cast<const uint4*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + 8 * i)
                   : make_uint4(0, 0, 0, 0);
   }
-  uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * 2048;
+  const int bits = g.hi_bits;            // 4, or 3 for the 50-byte block
+  const int64_t tb = 512 * (int64_t)bits;
+  uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * tb;
 #pragma unroll
   for (int ps = 0; ps < 4; ++ps) {
     const int v = 16 * ps + row, tensor = v >> 5, tok = v & 31;
@@ -543,28 +545,36 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       // Q4_0: the absmax of this lane's 32-value slice (lanes 4s .. 4s + 3 of
       // the row); the 128-block scheme: of the whole row
       const float a = __uint_as_float(g.q40 ? quad_max_u32(m) : row_max_u32(m));
-      sb = float_to_half_bits(a / 7.0f);
+      // levels -top .. top: 7 at 4 bits, 3 at 3 bits (stored code c + top + 1)
+      const float top = bits == 3 ? 3.0f : 7.0f;
+      sb = float_to_half_bits(a / top);
       const float s = half_bits_to_float(sb);
       // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
-      // code clamped to [-7, 7] lie in (-6.75, 6.75).  If any lane came close
-      // to one, the wave redoes its vectors with the division.
+      // code clamped to [-top, top] lie in (-top + 0.25, top - 0.25).  If any
+      // lane came close to one, the wave redoes its vectors with the division.
       float r[8];
       bool risky = false;
       const float rs = s != 0.0f ? 1.0f / s : 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, -6.75f, 6.75f, risky);
+      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, 0.25f - top, top - 0.25f, risky);
       if (__any(risky)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -7.0f), 7.0f) : 0;
-        packed |= (uint32_t)(c + 8) << (4 * j);
+        const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -top), top) : 0;
+        packed |= (uint32_t)(c + (int)top + 1) << (bits * j);
       }
     }
     if (tensor == 0) {
-      if (in) *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;
+      if (in) {
+        if (bits == 3) {   // 24 bits: row bytes 3i .. 3i + 2 (chunks may differ)
+          for (int k = 0; k < 3; ++k) kt[ktile_offset(tok, 3 * i + k)] = (uint8_t)(packed >> (8 * k));
+        } else {
+          *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;
+        }
+      }
     } else {
       vnib[tok][i] = packed;
     }
@@ -582,8 +592,40 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
   // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k + 1 (high)
   // of channel d; a byte with one token outside [T0, T1) keeps that token's
   // stored nibble.  Thread tid builds bytes 8 tid .. 8 tid + 7 (one row d).
-  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * 2048;
-  {
+  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * tb;
+  if (bits == 3) {
+    // 3 bits: row d is the 32 tokens' codes as one 96-bit string, token k at
+    // bits 3k; thread d (< 128) rebuilds it, keeping the bits of tokens
+    // outside [T0, T1)
+    if (tid < kD) {
+      const int d = tid, wd = d >> 3, sh = 3 * (d & 7);
+      uint32_t* row32 = reinterpret_cast<uint32_t*>(vt + 12 * d);
+      const bool whole = tbase >= T0 && tbase + kGroup <= T1;
+      uint32_t out[3] = {0, 0, 0};
+      if (!whole) {
+        out[0] = row32[0];
+        out[1] = row32[1];
+        out[2] = row32[2];
+      }
+      for (int k = 0; k < kGroup; ++k) {
+        const int64_t tk = tbase + k;
+        if (tk < T0 || tk >= T1) continue;
+        const uint32_t code = (vnib[k][wd] >> sh) & 7u;
+        const int bit = 3 * k, w0 = bit >> 5, b0 = bit & 31;
+        out[w0] = (out[w0] & ~(7u << b0)) | (code << b0);
+        if (b0 > 29) {   // the code straddles two words
+          const int nb = 32 - b0;
+          out[w0 + 1] = (out[w0 + 1] & ~(7u >> nb)) | (code >> nb);
+        }
+      }
+      const bool any_in = tbase + kGroup > T0 && tbase < T1;
+      if (any_in) {
+        row32[0] = out[0];
+        row32[1] = out[1];
+        row32[2] = out[2];
+      }
+    }
+  } else {
     const int d = tid >> 1, kb0 = 8 * (tid & 1);
     const int wd = d >> 3, sh = 4 * (d & 7);
     const bool whole = tbase + 2 * kb0 >= T0 && tbase + 2 * kb0 + 16 <= T1;

@@ -100,6 +100,17 @@ __device__ __forceinline__ h4_t as_h4(uint32_t x, uint32_t y) {
   return __builtin_bit_cast(h4_t, v);
 }
 
+// Four 3-bit codes of a bit string (codes 4q .. 4q + 3, code k at bits 3k of
+// the little-endian words w) as the fp16 B operand of one k-step: each code
+// masked into the low bits of a 16-bit half is the exact subnormal n 2^-24.
+__device__ __forceinline__ h4_t codes3_b(const uint32_t* w, int q) {
+  const int bit = 12 * q, d = bit >> 5, sh = bit & 31;
+  const uint32_t x = sh <= 20 ? (w[d] >> sh) : ((w[d] >> sh) | (w[d + 1] << (32 - sh)));
+  const uint32_t a = (x & 7u) | ((x << 13) & 0x00070000u);          // codes 0, 1
+  const uint32_t b = ((x >> 6) & 7u) | ((x << 7) & 0x00070000u);    // codes 2, 3
+  return as_h4(a, b);
+}
+
 // TBQ4 levels of the eight 4-bit codes of a dword, as fp16 pairs in the
 // order the code masks take them: out[0] = (code 0, code 4), out[1] =
 // (1, 5), out[2] = (2, 6), out[3] = (3, 7) (code k = bits 4k .. 4k + 3).
@@ -144,7 +155,10 @@ __device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
 // Value token tl (0..31 in its group) -> (k-step within the group, slot).
 template <int BITS>
 __device__ __forceinline__ void value_slot(int tl, int* kk, int* slot) {
-  if (BITS == 4) {
+  if (BITS == 3) {   // natural order: k-step tl / 4, slot tl % 4
+    *kk = tl >> 2;
+    *slot = tl & 3;
+  } else if (BITS == 4) {
     const int i = tl >> 3, r = tl & 7, j = r & 3, hp = r >> 2;
     *kk = 2 * i + (j >> 1);
     *slot = (j & 1) * 2 + hp;
@@ -283,7 +297,10 @@ __device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos
     const uint8_t* vt = vpair + (int64_t)(gg ? tp.s1 : tp.s0) * TB;
     for (int hf = 0; hf < 2; ++hf) {
       const uint8_t* src = vt + (lane + 64 * hf) * VROW;
-      if (BITS == 4) {
+      if constexpr (BITS == 3) {
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+        r.vc[gg][hf][0] = ok ? s32[0] : 0u; r.vc[gg][hf][1] = ok ? s32[1] : 0u; r.vc[gg][hf][2] = ok ? s32[2] : 0u;
+      } else if (BITS == 4) {
         const uint4 x = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
         r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y; r.vc[gg][hf][2] = x.z; r.vc[gg][hf][3] = x.w;
       } else {
@@ -342,9 +359,11 @@ __device__ __forceinline__ void stage_issue(uint8_t* st, const TilePos& tp, int 
   const bool g1 = tp.nvalid > 32;
   for (int gg = 0; gg < 2; ++gg) {
     const int64_t slot = (gg && g1) ? tp.s1 : tp.s0;
-    for (int k = 0; k < TB / 1024; ++k) {
-      lds_dma16(kpair + slot * TB + k * 1024 + 16 * lane, st + gg * TB + k * 1024);
-      lds_dma16(vpair + slot * TB + k * 1024 + 16 * lane, st + 2 * TB + gg * TB + k * 1024);
+    for (int k = 0; k * 1024 < TB; ++k) {
+      if (k * 1024 + 16 * lane < TB) {   // a 3-bit tile ends half way through a kilobyte
+        lds_dma16(kpair + slot * TB + k * 1024 + 16 * lane, st + gg * TB + k * 1024);
+        lds_dma16(vpair + slot * TB + k * 1024 + 16 * lane, st + 2 * TB + gg * TB + k * 1024);
+      }
     }
   }
 }
@@ -389,7 +408,10 @@ __device__ __forceinline__ void stage_read(TileRaw<BITS, BLOCK>& r, const uint8_
   for (int gg = 0; gg < 2; ++gg)
     for (int hf = 0; hf < 2; ++hf) {
       const uint8_t* src = st + 2 * TB + gg * TB + (lane + 64 * hf) * VROW;
-      if (BITS == 4) {
+      if constexpr (BITS == 3) {
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+        r.vc[gg][hf][0] = s32[0]; r.vc[gg][hf][1] = s32[1]; r.vc[gg][hf][2] = s32[2];
+      } else if (BITS == 4) {
         const uint4 x = *reinterpret_cast<const uint4*>(src);
         r.vc[gg][hf][0] = x.x; r.vc[gg][hf][1] = x.y; r.vc[gg][hf][2] = x.z; r.vc[gg][hf][3] = x.w;
       } else {
@@ -439,7 +461,8 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
   // 16^(j & 1) (4-bit) or 4^(j & 3) (2-bit), j its nibble / crumb position
   // within a 16-bit half of its word; its probability takes the inverse (a
   // power of two: exact)
-  const float inv_f = TBQ ? 1.0f : BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
+  const float inv_f = (TBQ || BITS == 3) ? 1.0f
+                      : BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
   for (int d = 0; d < NDG; ++d)
     for (int m = 0; m < G; ++m) {
       const float x = p[m] * vs[d];
@@ -461,6 +484,25 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
   for (int gg = 0; gg < 2; ++gg) {
     for (int hf = 0; hf < 2; ++hf) {
       const int dg = NDG == 1 ? 0 : (gh + 2 * hf);   // the 32-dim slice of channel lane + 64 hf
+      if constexpr (BITS == 3) {
+        // the channel row's 32 tokens as one 96-bit string, token t at bits
+        // 3t: k-step q takes tokens 4q .. 4q + 3 in natural order
+        const uint32_t w[3] = {vc[gg][hf][0], vc[gg][hf][1], vc[gg][hf][2]};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const h4_t bv = codes3_b(w, q);
+          const int ks = 8 * gg + q;
+          for (int hl = 0; hl < HL; ++hl) {
+            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][hl][row][0]);
+            if (hf == 0) {
+              if (q & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
+            } else {
+              if (q & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
+            }
+          }
+        }
+        continue;
+      }
       for (int u = 0; u < BITS; ++u) {
         const uint32_t x = vc[gg][hf][u];
         // one dword: 8 tokens (4-bit) or 16 tokens (2-bit), two per pr[] (one

@@ -63,7 +63,12 @@ namespace {
 // unpacking in the tile loop).
 template <int BITS>
 __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
-  if (BITS == 4) {
+  if (BITS == 3) {   // 3-bit codes are unpacked in channel order, no factors
+    for (int s = 0; s < 4; ++s) {
+      ch[s] = 4 * ks + s;
+      inv_f[s] = 1.0f;
+    }
+  } else if (BITS == 4) {
     const int i = ks >> 1, par = ks & 1;
     const int base = 8 * i + 2 * par;
     ch[0] = base; ch[1] = base + 4; ch[2] = base + 1; ch[3] = base + 5;
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
   constexpr int NDG = (BLOCK && !Q40) ? 1 : 4;   // value scale groups per token
+  constexpr float COFF = BITS == 3 ? 4.0f : 8.0f;  // symmetric blocks: stored code offset
   constexpr int TB = 512 * BITS;         // tile bytes
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
@@ -256,8 +262,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
       for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-      add0[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh] : BLOCK ? -8.0f * zsum[0] : zsum[gh];
-      add1[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh + 2] : BLOCK ? -8.0f * zsum[0] : zsum[gh + 2];
+      add0[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh] : BLOCK ? -COFF * zsum[0] : zsum[gh];
+      add1[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh + 2] : BLOCK ? -COFF * zsum[0] : zsum[gh + 2];
     }
     write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, TBQ ? 1.0f : 16777216.0f,
                          add0, add1);
@@ -381,7 +387,23 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     f4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     float sq[G];   // Q40: the score so far, slice by slice
     for (int m = 0; m < G; ++m) sq[m] = 0.0f;
-    for (int j = 0; j < NKW; ++j) {
+    if constexpr (BITS == 3) {
+      // the key row as one 384-bit string, channel c at bits 3c: k-step ks
+      // takes channels 4 ks .. 4 ks + 3 in order
+      uint32_t kw3[12];
+      for (int j = 0; j < 3; ++j) {
+        kw3[4 * j] = kc[j].x; kw3[4 * j + 1] = kc[j].y; kw3[4 * j + 2] = kc[j].z; kw3[4 * j + 3] = kc[j].w;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) {
+        const h4_t bk = codes3_b(kw3, ks);
+        for (int hl = 0; hl < HL; ++hl) {
+          if (ks & 1) acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), bk, acc1);
+          else acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), bk, acc0);
+        }
+      }
+    }
+    for (int j = 0; j < (BITS == 3 ? 0 : NKW); ++j) {
       const uint32_t dw[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
       for (int u = 0; u < 4; ++u) {
         const uint32_t xw = dw[u];
@@ -432,7 +454,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       float s;
       if (Q40) s = sq[m];
       else if (TBQ) s = kscale * (dotv * e_scale_blk);
-      else if (BLOCK) s = kscale * (dotv * e_scale_blk - 8.0f * qsum[m]);
+      else if (BLOCK) s = kscale * (dotv * e_scale_blk - COFF * qsum[m]);
       else s = dotv * kscale_grp + bias[m];
       if (!tok_ok) s = -INFINITY;
       p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
@@ -466,6 +488,8 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
     if (g.G == 1) KVQ_FT(1); else if (g.G == 2) KVQ_FT(2); else KVQ_FT(4);
   } else if (g.q40) {
     if (g.G == 1) KVQ_FQ(1); else if (g.G == 2) KVQ_FQ(2); else KVQ_FQ(4);
+  } else if (blk && bits == 3) {
+    if (g.G == 1) KVQ_FN(1, 3, true); else if (g.G == 2) KVQ_FN(2, 3, true); else KVQ_FN(4, 3, true);
   } else if (blk) {
     if (g.G == 1) KVQ_FN(1, 4, true); else if (g.G == 2) KVQ_FN(2, 4, true); else KVQ_FN(4, 4, true);
   } else if (bits == 4) {
@@ -519,6 +543,10 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
       if (g.G == 1) KVQ_MQ(1);
       else if (g.G == 2) KVQ_MQ(2);
       else KVQ_MQ(4);
+    } else if (blk && rp.bits == 3) {
+      if (g.G == 1) KVQ_MF(1, 3, true);
+      else if (g.G == 2) KVQ_MF(2, 3, true);
+      else KVQ_MF(4, 3, true);
     } else if (blk) {
       if (g.G == 1) KVQ_MF(1, 4, true);
       else if (g.G == 2) KVQ_MF(2, 4, true);

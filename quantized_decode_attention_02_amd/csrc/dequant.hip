@@ -4,7 +4,7 @@
 // model latency" — here only for tests and inspection; decode never uses it.
 //   KIVI:     x = fl32(c * s_h + z_h)   (the product is exact, so fused or not
 //                                        gives the same bits)
-//   BLOCK128: y = fl32((n - 8) * s_h)  (exact)
+//   BLOCK128: y = fl32((n - 8) * s_h)  (exact; n - 4 at 3 bits)
 //   TBQ4:     y = fl32(norm * level[n])
 //   Q4_0:     y = fl32((n - 8) * s_h of the value's 32-value slice)  (exact)
 //   window:   the fp16 value.
@@ -32,10 +32,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
     if (block_scheme(g.scheme)) {
       const int64_t grp = t / kGroup;
       const int row = (int)(t % kGroup);
-      const uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + grp) * 2048;
-      const uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 2048;
-      const int kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
-      const int vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
+      const int bits = g.hi_bits;
+      const uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + grp) * 512 * bits;
+      const uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 512 * bits;
+      int kn, vn;
+      if (bits == 3) {   // code at bits 3c of the row's bit string (may straddle a byte)
+        const int kb = (3 * d) >> 3, ks = (3 * d) & 7;
+        const uint32_t k16 = kt[ktile_offset(row, kb)] | (kb + 1 < 48 ? (uint32_t)kt[ktile_offset(row, kb + 1)] << 8 : 0u);
+        kn = (int)((k16 >> ks) & 7u);
+        const int vb = (3 * row) >> 3, vsh = (3 * row) & 7;
+        const uint32_t v16 = vt[d * 12 + vb] | (vb + 1 < 12 ? (uint32_t)vt[d * 12 + vb + 1] << 8 : 0u);
+        vn = (int)((v16 >> vsh) & 7u);
+      } else {
+        kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
+        vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
+      }
       const int per = g.q40 ? 4 : 1;   // fp16 scales per token
       const uint16_t* ks = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META]) + pair * g.gmax * kGroup * per;
       const uint16_t* vs = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META]) + pair * g.gmax * kGroup * per;
@@ -52,8 +63,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
         kv = (float)(kn - 8) * half_bits_to_float(ks[4 * t + (d >> 5)]);
         vv = (float)(vn - 8) * half_bits_to_float(vs[4 * t + (d >> 5)]);
       } else {
-        kv = (float)(kn - 8) * half_bits_to_float(ks[t]);
-        vv = (float)(vn - 8) * half_bits_to_float(vs[t]);
+        const int off = bits == 3 ? 4 : 8;
+        kv = (float)(kn - off) * half_bits_to_float(ks[t]);
+        vv = (float)(vn - off) * half_bits_to_float(vs[t]);
       }
     } else if (t < g.Tq) {
       const int64_t grp = t / kGroup;

@@ -50,7 +50,8 @@ kvq_status validate_config(const kvq_config* c) {
     if (c->fp16_window != kWindow) return KVQ_ERR_UNSUPPORTED;
     if (c->int4_window >= 0 && (c->k_bits != 4 || c->low_bits != 2)) return KVQ_ERR_UNSUPPORTED;
   } else {
-    if (c->k_bits != 4) return KVQ_ERR_UNSUPPORTED;
+    // 3 bits: the 50-byte block of the format table (symmetric block scheme only)
+    if (c->k_bits != 4 && !(c->k_bits == 3 && c->scheme == KVQ_BLOCK128_SYM)) return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != 0 || c->int4_window != -1) return KVQ_ERR_UNSUPPORTED;
     if (c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
     // TBQ4's levels assume the near-normal coordinates of a rotated block
@@ -184,8 +185,8 @@ void plane_sizes(const kvq_config* c, int64_t batch, int64_t max_tokens, uint64_
     sz[KVQ_PLANE_K_WIN] = pairs * kRing * kD * 2;
     sz[KVQ_PLANE_V_WIN] = pairs * kRing * kD * 2;
   } else {
-    sz[KVQ_PLANE_K_HI] = pairs * G * 2048;
-    sz[KVQ_PLANE_V_HI] = pairs * G * 2048;
+    sz[KVQ_PLANE_K_HI] = pairs * G * 512 * c->k_bits;
+    sz[KVQ_PLANE_V_HI] = pairs * G * 512 * c->v_bits;
     const uint64_t per_token = c->scheme == KVQ_Q4_0 ? 4 : 1;   // fp16 scales
     sz[KVQ_PLANE_K_META] = pairs * G * kGroup * 2 * per_token;
     sz[KVQ_PLANE_V_META] = pairs * G * kGroup * 2 * per_token;

@@ -104,6 +104,11 @@ WORKLOADS.append(
     dict(id=6, name="q4_0-gqa32x8-b32-t65536+8192",
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_q4_0(), dist="normal", outliers=None))
+# the 3-bit 50-byte block (format table row "3 bity (50 B / 128)") at the same shape
+WORKLOADS.append(
+    dict(id=7, name="block50-3bit-hadamard-gqa32x8-b32-t65536+8192",
+         batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
+         cfg=_block128(k_bits=3, v_bits=3), dist="normal", outliers=None))
 
 
 def workload(key):

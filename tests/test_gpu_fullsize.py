@@ -32,6 +32,7 @@ SCHEDULES = {
     4: [8192] * 9,
     5: [8192] * 9,
     6: [8192] * 9,
+    7: [8192] * 9,
 }
 
 

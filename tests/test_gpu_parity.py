@@ -27,6 +27,8 @@ VARIANTS = {
     "block128": None,
     "block128-plain": dict(hadamard=False),
     "block128-signed": dict(SIGNS),
+    "block128-3bit": dict(k_bits=3, v_bits=3),
+    "block128-3bit-plain": dict(k_bits=3, v_bits=3, hadamard=False),
     "tbq4": dict(),
     "tbq4-signed": dict(SIGNS),
     "q4_0": dict(),
