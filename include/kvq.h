@@ -57,6 +57,10 @@ typedef enum kvq_status {
  * KVQ_BLOCK128_SYM: each token's 128-value head vector is one block of an
  *   fp16 scale and 128 symmetric 4-bit codes, 66 bytes, 4.125 bits per value
  *   ([trefon] "Przykład: model 27B przy 262K"); every token is quantized.
+ *   With k_bits = 3, the format table's 50-byte block: codes in [-3, 3]
+ *   stored + 4, scale = absmax / 3, 3.125 bits per value; a row's codes are
+ *   one little-endian bit string (code c at bits 3c), so codes straddle
+ *   bytes.
  * KVQ_TBQ4: the same 66-byte container holding an fp16 norm and 128 4-bit
  *   indices into 16 Lloyd-Max levels of N(0, 1/sqrt(128)), taken after the
  *   (randomized) Hadamard rotation, which is required ([trefon] "Jak
@@ -115,8 +119,8 @@ typedef struct kvq_config {
                              "Bajty na token"), q head h reads kv head h / (Hq/Hkv) */
   int32_t scheme;         /* KVQ_KIVI_ASYM, KVQ_BLOCK128_SYM, KVQ_TBQ4 or
                              KVQ_Q4_0 */
-  int32_t k_bits;         /* bits of the high-bit tier: 4 or 2 (block
-                             schemes: 4) */
+  int32_t k_bits;         /* bits of the high-bit tier: 4 or 2 (KIVI); 4 or
+                             3 (BLOCK128); 4 (TBQ4, Q4_0) */
   int32_t v_bits;         /* must equal k_bits */
   int32_t k_group_tokens; /* must be 32 */
   int32_t v_group_dims;   /* must be 32 */
@@ -250,7 +254,8 @@ kvq_status kvq_decode_merge(const kvq_config* cfg, const kvq_cache* cache, const
  * values), the dequantize-first path of [nalar] "Biaya dequantization harus
  * masuk ke model latency", for tests and inspection.
  *   k_out, v_out: device fp32 [batch][t1 - t0][num_kv_heads][128].
- * Bit-exact: x = c * scale + zero (KIVI), (n - 8) * scale (BLOCK128; Q4_0
+ * Bit-exact: x = c * scale + zero (KIVI), (n - 8) * scale (BLOCK128, n - 4 at
+ * 3 bits; Q4_0
  * with the scale of the value's slice), norm * level[n] (TBQ4). */
 kvq_status kvq_dequant(const kvq_config* cfg, const kvq_cache* cache, int64_t t0, int64_t t1,
                        void* k_out, void* v_out, void* stream);
