@@ -152,6 +152,28 @@ __device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(x, y, c, 0, 0, 0);
 }
 
+// A wave's fp16 A-operand tables of the 4x4x4 MFMA (query or probabilities):
+// tables of NKS k-steps, a k-step being HL blocks of 4 rows x 4 halves.  With
+// KPAD each k-step takes 8 bytes more, with TPAD each table 32 bytes more, so
+// that the k-steps one instruction writes (one per group of lanes) and the
+// tables one instruction reads (one per half wave) fall in different LDS
+// banks: for four query heads, 64-byte k-steps put the 16 k-steps a
+// probability write spans into 4 banks.  Tables that are written rarely, or
+// that must stay small enough for three work-groups per compute unit, go
+// without.
+template <int HL, int NKS, bool KPAD = false, bool TPAD = false>
+struct ATab {
+  static constexpr int KS = HL * 16 + (KPAD ? 4 : 0);   // halves per k-step
+  static constexpr int T = NKS * KS + (TPAD ? 16 : 0);  // halves per table
+  _Float16* p;
+  __device__ __forceinline__ _Float16& at(int t, int ks, int hl, int m, int slot) const {
+    return p[t * T + ks * KS + hl * 16 + m * 4 + slot];
+  }
+  __device__ __forceinline__ h4_t& h4(int t, int ks, int hl, int m) const {
+    return *reinterpret_cast<h4_t*>(&p[t * T + ks * KS + hl * 16 + m * 4]);
+  }
+};
+
 // Value token tl (0..31 in its group) -> (k-step within the group, slot).
 template <int BITS>
 __device__ __forceinline__ void value_slot(int tl, int* kk, int* slot) {
@@ -449,10 +471,11 @@ __device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, bool t
   }
 }
 
-// p' = p s into this wave's value A table (PLw = PL[w]); zero-point sums.
-template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false>
+// p' = p s into this wave's value A tables (PLw, one per value scale group);
+// zero-point sums.
+template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false, class PT>
 __device__ __forceinline__ void stage_probs(const float* p, const float* vs, const float* vz,
-                                            _Float16 (*PLw)[16][HL][4][4], float (*zacc)[NDG],
+                                            const PT& PLw, float (*zacc)[NDG],
                                             int tl, int gh) {
   int kk, slot;
   value_slot<BITS>(tl, &kk, &slot);
@@ -468,17 +491,17 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
       const float x = p[m] * vs[d];
       _Float16 hi, lo;
       split_half(x * inv_f, &hi, &lo);
-      PLw[d][ks][0][m][slot] = hi;
-      if (HL == 1) PLw[d][ks][0][G + m][slot] = lo;
-      else PLw[d][ks][1][m][slot] = lo;
+      PLw.at(d, ks, 0, m, slot) = hi;
+      if (HL == 1) PLw.at(d, ks, 0, G + m, slot) = lo;
+      else PLw.at(d, ks, 1, m, slot) = lo;
       zacc[m][d] += BLOCK ? x : p[m] * vz[d];
     }
 }
 
 // O += p' . codes over the tile's value rows: 16 k-steps x 2 halves.
-template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false>
+template <int G, int BITS, bool BLOCK, int HL, int NDG, bool TBQ = false, class PT>
 __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
-                                           _Float16 (*PLw)[16][HL][4][4], int row, int gh,
+                                           const PT& PLw, int row, int gh,
                                            f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3,
                                            const uint32_t* lut = nullptr) {
   for (int gg = 0; gg < 2; ++gg) {
@@ -493,7 +516,7 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
           const h4_t bv = codes3_b(w, q);
           const int ks = 8 * gg + q;
           for (int hl = 0; hl < HL; ++hl) {
-            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][hl][row][0]);
+            const h4_t av = PLw.h4(dg, ks, hl, row);
             if (hf == 0) {
               if (q & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
             } else {
@@ -533,7 +556,7 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
           // of p' (rows G.. of a HL = 1 table carry p's lo half: included)
           for (int hl = 0; hl < HL + (TBQ ? 1 : 0); ++hl) {
             const bool lo_lv = TBQ && hl == HL;
-            const h4_t av = *reinterpret_cast<const h4_t*>(&PLw[dg][ks][lo_lv ? 0 : hl][row][0]);
+            const h4_t av = PLw.h4(dg, ks, lo_lv ? 0 : hl, row);
             const h4_t b = lo_lv ? as_h4(prl[2 * q2], prl[2 * q2 + 1]) : bv;
             if (hf == 0) {
               if (q2 & 1) o2 = mfma4(av, b, o2); else o0 = mfma4(av, b, o0);
@@ -548,12 +571,12 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
 }
 
 // fp16 window values: O += p . V over tokens [base, base + nvalid) of the
-// channel-major value ring, with p in natural token order in PLw[0] (k-step
+// channel-major value ring, with p in natural token order in table 0 of PLw (k-step
 // lane/4, slot lane%4).  Halves of tokens past the window are zeroed (stale
 // ring slots may hold anything).
-template <int HL>
+template <int HL, class PT>
 __device__ __forceinline__ void window_value_mfma(const __half* vring, int64_t base, int nvalid,
-                                                  _Float16 (*PLw)[16][HL][4][4], int lane, int row,
+                                                  const PT& PLw, int lane, int row,
                                                   f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3) {
   for (int kp = 0; kp < 8; ++kp) {    // 8 tokens (two k-steps) per load
     const int64_t t0 = base + 8 * kp;
@@ -573,8 +596,8 @@ __device__ __forceinline__ void window_value_mfma(const __half* vring, int64_t b
         }
       }
       for (int hl = 0; hl < HL; ++hl) {
-        const h4_t a0 = *reinterpret_cast<const h4_t*>(&PLw[0][2 * kp][hl][row][0]);
-        const h4_t a1 = *reinterpret_cast<const h4_t*>(&PLw[0][2 * kp + 1][hl][row][0]);
+        const h4_t a0 = PLw.h4(0, 2 * kp, hl, row);
+        const h4_t a1 = PLw.h4(0, 2 * kp + 1, hl, row);
         if (hf == 0) {
           o0 = mfma4(a0, as_h4(x.x, x.y), o0);
           o2 = mfma4(a1, as_h4(x.z, x.w), o2);
@@ -588,15 +611,15 @@ __device__ __forceinline__ void window_value_mfma(const __half* vring, int64_t b
 }
 
 // fp16 window probabilities in natural token order (k-step lane/4, slot lane%4).
-template <int G, int HL>
-__device__ __forceinline__ void stage_window_probs(const float* p, _Float16 (*PLw)[16][HL][4][4],
+template <int G, int HL, class PT>
+__device__ __forceinline__ void stage_window_probs(const float* p, const PT& PLw,
                                                    int lane) {
   for (int m = 0; m < G; ++m) {
     _Float16 hi, lo;
     split_half(p[m], &hi, &lo);
-    PLw[0][lane >> 2][0][m][lane & 3] = hi;
-    if (HL == 1) PLw[0][lane >> 2][0][G + m][lane & 3] = lo;
-    else PLw[0][lane >> 2][1][m][lane & 3] = lo;
+    PLw.at(0, lane >> 2, 0, m, lane & 3) = hi;
+    if (HL == 1) PLw.at(0, lane >> 2, 0, G + m, lane & 3) = lo;
+    else PLw.at(0, lane >> 2, 1, m, lane & 3) = lo;
   }
 }
 

@@ -117,8 +117,13 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   __shared__ __attribute__((aligned(16))) float qs[QP ? 1 : 4][G][kD];
   // query tables: per group half (KIVI, rebuilt per group) or one (BLOCK,
   // fixed per pair)
-  __shared__ __attribute__((aligned(16))) _Float16 QL[4][BLOCK ? 1 : 2][32][HL][4][4];
-  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
+  // padded tables where four query heads make their writes conflict (the
+  // query table only where it is rebuilt per group); the KIVI 2-bit kernel
+  // drops the table pads to stay within three work-groups per compute unit
+  using QTab = ATab<HL, 32, (G == 4 && !BLOCK), (G == 4 && !BLOCK && BITS == 4)>;
+  using PTab = ATab<HL, 16, G == 4, (G == 4 && NDG > 1 && BITS == 4)>;
+  __shared__ __attribute__((aligned(16))) _Float16 QL[4][(BLOCK ? 1 : 2) * QTab::T];
+  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
   __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -126,12 +131,13 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // tile walk and its addresses stay on the scalar unit
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gh = lane >> 5, tl = lane & 31, row = lane & 3;
-  auto QLw = QL[w];
-  float (*qsw)[kD] = QP ? reinterpret_cast<float (*)[kD]>(&PL[w][0][0][0][0][0]) : qs[QP ? 0 : w];
+  const QTab QLw{QL[w]};
+  const PTab PLw{PL[w]};
+  float (*qsw)[kD] = QP ? reinterpret_cast<float (*)[kD]>(&PL[w][0]) : qs[QP ? 0 : w];
   static_assert(!QP || sizeof(PL[0]) >= sizeof(qs[0]), "the query must fit the probability table");
   const int qh = BLOCK ? 0 : gh;
-  for (int e = lane; e < (int)(sizeof(QL[0]) / 2); e += 64) (&QLw[0][0][0][0][0])[e] = (_Float16)0.0f;
-  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) (&PL[w][0][0][0][0][0])[e] = (_Float16)0.0f;
+  for (int e = lane; e < (int)(sizeof(QL[0]) / 2); e += 64) QL[w][e] = (_Float16)0.0f;
+  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) PL[w][e] = (_Float16)0.0f;
   wave_sync();
 
   float m_run[G], l_acc[G];
@@ -163,9 +169,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       _Float16 hi[4], lo[4];
       for (int i = 0; i < 4; ++i) split_half(ldexpf(qsw[m][4 * tl + i], e_q), &hi[i], &lo[i]);
       const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-      *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][m][0]) = hv;
-      if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][G + m][0]) = lv;
-      else *reinterpret_cast<h4_t*>(&QLw[qh][tl][1][m][0]) = lv;
+      QLw.h4(qh, tl, 0, m) = hv;
+      if (HL == 1) QLw.h4(qh, tl, 0, G + m) = lv;
+      else QLw.h4(qh, tl, 1, m) = lv;
     }
     wave_sync();
     const int64_t base = g.Tq + 64 * (int64_t)w;
@@ -182,8 +188,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         for (int j = 0; j < 4; ++j) {
           const int ks = 8 * c + 2 * j;
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), as_h4(kr[j].x, kr[j].y), acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks + 1][hl][row][0]), as_h4(kr[j].z, kr[j].w), acc1);
+            acc0 = mfma4(QLw.h4(qh, ks, hl, row), as_h4(kr[j].x, kr[j].y), acc0);
+            acc1 = mfma4(QLw.h4(qh, ks + 1, hl, row), as_h4(kr[j].z, kr[j].w), acc1);
           }
         }
       }
@@ -193,10 +199,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         const float s = tok_ok ? dv * unscale : -INFINITY;
         p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
       }
-      stage_window_probs<G, HL>(p, PL[w], lane);
+      stage_window_probs<G, HL>(p, PLw, lane);
       wave_sync();
       const __half* vring = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
-      window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
+      window_value_mfma<HL>(vring, base, nvalid, PLw, lane, row, o0, o1, o2, o3);
     }
     const float zero[G] = {};
     write_partial<G, HL>(a, b, h, a.win_slot + w, lane, m_run, l_acc, o0, o1, o2, o3, 1.0f, zero, zero);
@@ -307,9 +313,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
             _Float16 hi[4], lo[4];
             for (int i = 0; i < 4; ++i) split_half(ldexpf(qv[m][i], e_blk) * kinv[i], &hi[i], &lo[i]);
             const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-            *reinterpret_cast<h4_t*>(&QLw[0][tl][0][m][0]) = hv;
-            if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[0][tl][0][G + m][0]) = lv;
-            else *reinterpret_cast<h4_t*>(&QLw[0][tl][1][m][0]) = lv;
+            QLw.h4(0, tl, 0, m) = hv;
+            if (HL == 1) QLw.h4(0, tl, 0, G + m) = lv;
+            else QLw.h4(0, tl, 1, m) = lv;
           }
         }
         wave_sync();
@@ -376,9 +382,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         _Float16 hi[4], lo[4];
         for (int i = 0; i < 4; ++i) split_half(ldexpf(qp[m][i], e_grp) * kinv[i], &hi[i], &lo[i]);
         const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][m][0]) = hv;
-        if (HL == 1) *reinterpret_cast<h4_t*>(&QLw[qh][tl][0][G + m][0]) = lv;
-        else *reinterpret_cast<h4_t*>(&QLw[qh][tl][1][m][0]) = lv;
+        QLw.h4(qh, tl, 0, m) = hv;
+        if (HL == 1) QLw.h4(qh, tl, 0, G + m) = lv;
+        else QLw.h4(qh, tl, 1, m) = lv;
       }
       wave_sync();
     }
@@ -398,8 +404,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       for (int ks = 0; ks < 32; ++ks) {
         const h4_t bk = codes3_b(kw3, ks);
         for (int hl = 0; hl < HL; ++hl) {
-          if (ks & 1) acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), bk, acc1);
-          else acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][ks][hl][row][0]), bk, acc0);
+          if (ks & 1) acc1 = mfma4(QLw.h4(qh, ks, hl, row), bk, acc1);
+          else acc0 = mfma4(QLw.h4(qh, ks, hl, row), bk, acc0);
         }
       }
     }
@@ -415,12 +421,12 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
           const h4_t b0 = TBQ ? as_h4(lv[0], lv[1]) : as_h4(xw & 0x000F000Fu, xw & 0x00F000F0u);
           const h4_t b1 = TBQ ? as_h4(lv[2], lv[3]) : as_h4(x8 & 0x000F000Fu, x8 & 0x00F000F0u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i + 1][hl][row][0]), b1, acc1);
+            acc0 = mfma4(QLw.h4(qh, 2 * i, hl, row), b0, acc0);
+            acc1 = mfma4(QLw.h4(qh, 2 * i + 1, hl, row), b1, acc1);
           }
           if (TBQ) {   // the levels' lo halves against the query's hi half
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i][0][row][0]), as_h4(ll[0], ll[1]), acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][2 * i + 1][0][row][0]), as_h4(ll[2], ll[3]), acc1);
+            acc0 = mfma4(QLw.h4(qh, 2 * i, 0, row), as_h4(ll[0], ll[1]), acc0);
+            acc1 = mfma4(QLw.h4(qh, 2 * i + 1, 0, row), as_h4(ll[2], ll[3]), acc1);
           }
         } else {
           const uint32_t x10 = xw >> 10;
@@ -429,10 +435,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
           const h4_t b2 = as_h4(xw & 0x03000300u, x10 & 0x00030003u);
           const h4_t b3 = as_h4(x10 & 0x000C000Cu, x10 & 0x00300030u);
           for (int hl = 0; hl < HL; ++hl) {
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i][hl][row][0]), b0, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 1][hl][row][0]), b1, acc1);
-            acc0 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 2][hl][row][0]), b2, acc0);
-            acc1 = mfma4(*reinterpret_cast<const h4_t*>(&QLw[qh][4 * i + 3][hl][row][0]), b3, acc1);
+            acc0 = mfma4(QLw.h4(qh, 4 * i, hl, row), b0, acc0);
+            acc1 = mfma4(QLw.h4(qh, 4 * i + 1, hl, row), b1, acc1);
+            acc0 = mfma4(QLw.h4(qh, 4 * i + 2, hl, row), b2, acc0);
+            acc1 = mfma4(QLw.h4(qh, 4 * i + 3, hl, row), b3, acc1);
           }
         }
       }
@@ -461,9 +467,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     }
 
     // ---------------- p' = p s into the value A table; values: O += p' . codes
-    stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PL[w], zacc, tl, gh);
+    stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PLw, zacc, tl, gh);
     wave_sync();
-    value_mfma<G, BITS, BLOCK, HL, NDG, TBQ>(vc, PL[w], row, gh, o0, o1, o2, o3, lut);
+    value_mfma<G, BITS, BLOCK, HL, NDG, TBQ>(vc, PLw, row, gh, o0, o1, o2, o3, lut);
     wave_sync();
 
     // ---------------- the member's partial when its assignment ends

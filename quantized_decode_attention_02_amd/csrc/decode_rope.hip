@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   // of QA, group of KSZ) fall in different banks.
   __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD + 4];   // [wave][group][head][channel]
   __shared__ __attribute__((aligned(16))) float KSZ[4][2][65][4];      // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
-  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG][16][HL][4][4];
+  using PTab = ATab<HL, 16, G == 4, G == 4>;
+  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform: read it into a scalar register, so that the
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     *reinterpret_cast<float4*>(&DT[jp][d][0]) = *reinterpret_cast<const float4*>(rope_tab + d * 128 + 4 * jp);
   }
   for (int e = lane; e < (int)(sizeof(QA[0]) / 4); e += 64) (&QA[w][0][0][0])[e] = 0.0f;
-  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) (&PL[w][0][0][0][0][0])[e] = (_Float16)0.0f;
+  for (int e = lane; e < (int)(sizeof(PL[0]) / 2); e += 64) PL[w][e] = (_Float16)0.0f;
   lds_barrier();
 
   // the query of (b, h) at q_pos: R(q_pos) q (fp64 angles), scaled; lane j
@@ -198,10 +199,10 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
         const float s = tok_ok ? (acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m]) : -INFINITY;
         p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
       }
-      stage_window_probs<G, HL>(p, PL[w], lane);
+      stage_window_probs<G, HL>(p, PTab{PL[w]}, lane);
       wave_sync();
       const __half* vring = reinterpret_cast<const __half*>(a.p.p[KVQ_PLANE_V_WIN]) + pair * kD * kRing;
-      window_value_mfma<HL>(vring, base, nvalid, PL[w], lane, row, o0, o1, o2, o3);
+      window_value_mfma<HL>(vring, base, nvalid, PTab{PL[w]}, lane, row, o0, o1, o2, o3);
     }
     const float zero[G] = {};
     write_partial<G, HL>(a, b, h, a.win_slot + w, lane, m_run, l_acc, o0, o1, o2, o3, 1.0f, zero, zero);
@@ -313,9 +314,9 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     }
 
     // ---------------- values
-    stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PL[w], zacc, tl, gh);
+    stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PTab{PL[w]}, zacc, tl, gh);
     wave_sync();
-    value_mfma<G, BITS, false, HL, NDG>(c.vc, PL[w], row, gh, o0, o1, o2, o3);
+    value_mfma<G, BITS, false, HL, NDG>(c.vc, PTab{PL[w]}, row, gh, o0, o1, o2, o3);
     wave_sync();
 
     if (ends) flush();
