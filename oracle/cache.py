@@ -9,7 +9,8 @@ trudniej skwantyzować niż wagi"; [nalar] "Pertumbuhan cache dinamis mengubah
 persoalan kalibrasi").  Four schemes:
 
 ``kivi``: keys per channel over 32-token groups, values per token over 32-dim
-  groups, asymmetric, fp16 scale and zero; a fp16 window of recent tokens
+  groups, asymmetric at 4, 3 or 2 bits, fp16 scale and zero (3-bit codes
+  pack as one bit string per tile row, layout.py); a fp16 window of recent tokens
   (tiers.py); optionally a high-bit window with older groups at ``low_bits``
   ([troisinh] "Ý tưởng cốt lõi", "Mixed Precision"); optionally the Hadamard
   rotation before quantizing ([troisinh] "Tại sao nó hoạt động", item 2),

@@ -16,7 +16,9 @@ What the pages fix:
     ([trefon] "Przykład: model 27B przy 262K").
 
 Readings where the pages are silent (all float32 one op at a time, RNE):
-  asymmetric, b bits, Q = 2**b - 1, over a group x:
+  asymmetric, b bits (4, 3 or 2; the page's title names INT4 and INT3 caches,
+  [troisinh] "KV Cache Quantization - Nén cache INT4/INT3"), Q = 2**b - 1,
+  over a group x:
     mn, mx = min(x), max(x)
     s  = fl32(fl32(mx - mn) / Q);  s_h = fp16(s) + (+0.0)
     z_h = fp16(mn) + (+0.0)         (the additions turn -0 into +0: over a

@@ -60,6 +60,8 @@ SIGNS = wl.random_signs(7)
                                        ("q4_0", {}), ("q4_0", dict(hadamard=True)),
                                        ("block128", dict(k_bits=3, v_bits=3)),
                                        ("kivi", dict(k_bits=2, v_bits=2)),
+                                       ("kivi", dict(k_bits=3, v_bits=3)),
+                                       ("kivi", dict(k_bits=3, v_bits=3, hadamard=True)),
                                        ("kivi", dict(pre_rope=True, rope_theta=500000.0)),
                                        ("block128", {})])
 def test_chunking_invariance(scheme, kw):

@@ -33,7 +33,7 @@ def fp16_groups(rng, n, size, kind):
 KINDS = ["normal", "outlier", "student", "tiny", "offset", "signed_zero"]
 
 
-@pytest.mark.parametrize("bits,kind", list(itertools.product([4, 2], KINDS)))
+@pytest.mark.parametrize("bits,kind", list(itertools.product([4, 3, 2], KINDS)))
 def test_asym_roundtrip_bound_fp16_inputs(bits, kind):
     rng = np.random.default_rng([bits, KINDS.index(kind)])
     x = fp16_groups(rng, 2000, 32, kind).astype(F32)
@@ -67,7 +67,7 @@ def test_asym_fp32_inputs_bound():
     # widens by |z_h - min|
     rng = np.random.default_rng(5)
     x = (rng.standard_normal((5000, 32)) * 3).astype(F32)
-    for bits in (4, 2):
+    for bits in (4, 3, 2):
         c, s, z = quant.quant_asym(x, bits, axis=-1)
         xh = quant.dequant_asym(c, s, z, axis=-1)
         mn = x.min(axis=1).astype(np.float64)
@@ -99,7 +99,7 @@ def test_asym_brute_force_nearest_level():
     # tiny groups: every code is the nearest of the 2^b levels z + k s (fp64),
     # unless two levels are (nearly) tied
     rng = np.random.default_rng(7)
-    for bits in (4, 2):
+    for bits in (4, 3, 2):
         Q = 2 ** bits - 1
         x = (rng.standard_normal((3000, 4)) * rng.uniform(0.1, 10, (3000, 1))).astype(F16).astype(F32)
         c, s, z = quant.quant_asym(x, bits, axis=-1)

@@ -83,6 +83,9 @@ def test_own_format_bytes():
     # per cached token per KV head: INT4 KIVI = 2 x (64 code bytes + 16 metadata bytes)
     assert sizes.kivi_bytes_per_token_head(4) == 160
     assert sizes.kivi_bytes_per_token_head(2) == 96
+    # INT3: 48 code bytes + 16 metadata bytes per tensor, 4 bits per value
+    assert sizes.kivi_bytes_per_token_head(3) == 128
+    assert sizes.kivi_bytes_per_token_head(3) * 8 / (2 * 128) == 4
     # the symmetric block is the page's 66-byte block, once for K and once for V
     assert sizes.block128_bytes_per_token_head() == 2 * EX["tbq4_block_bytes"]
     assert sizes.fp16_bytes_per_token_head() == 512
@@ -90,7 +93,7 @@ def test_own_format_bytes():
     assert sizes.kivi_bytes_per_token_head(4) * 8 / (2 * 128) == 5
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_plane_sizes_match_per_token_bytes(bits):
     cfg = make_config(scheme="kivi", k_bits=bits, v_bits=bits, num_q_heads=4, num_kv_heads=2)
     B, T = 3, 32 * 1000
