@@ -53,7 +53,10 @@ typedef enum kvq_status {
  *   trudniej skwantyzować niż wagi"), plus a 128-token fp16 window of recent
  *   tokens ([nalar] "Evaluasi harus memisahkan peningkatan kapasitas dari
  *   dampak model").  Tokens [Tq, length) are fp16 with
- *   Tq = max(0, floor((length - 128) / 32) * 32).
+ *   Tq = max(0, floor((length - 128) / 32) * 32).  Codes have 4, 3 or 2
+ *   bits (the INT4 / INT3 caches of [troisinh] "KV Cache Quantization - Nén
+ *   cache INT4/INT3"); 3-bit rows are one little-endian bit string (code c at
+ *   bits 3c), 3-bit caches have one tier and keys stored after RoPE.
  * KVQ_BLOCK128_SYM: each token's 128-value head vector is one block of an
  *   fp16 scale and 128 symmetric 4-bit codes, 66 bytes, 4.125 bits per value
  *   ([trefon] "Przykład: model 27B przy 262K"); every token is quantized.
@@ -119,8 +122,8 @@ typedef struct kvq_config {
                              "Bajty na token"), q head h reads kv head h / (Hq/Hkv) */
   int32_t scheme;         /* KVQ_KIVI_ASYM, KVQ_BLOCK128_SYM, KVQ_TBQ4 or
                              KVQ_Q4_0 */
-  int32_t k_bits;         /* bits of the high-bit tier: 4 or 2 (KIVI); 4 or
-                             3 (BLOCK128); 4 (TBQ4, Q4_0) */
+  int32_t k_bits;         /* bits of the high-bit tier: 4, 3 or 2 (KIVI); 4
+                             or 3 (BLOCK128); 4 (TBQ4, Q4_0) */
   int32_t v_bits;         /* must equal k_bits */
   int32_t k_group_tokens; /* must be 32 */
   int32_t v_group_dims;   /* must be 32 */

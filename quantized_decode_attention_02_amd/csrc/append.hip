@@ -135,14 +135,42 @@ __device__ void quantize_group(const float (*xk)[kD], const float (*xv)[kD], uin
   }
 }
 
+// Byte cb of a 3-bit row of n codes: bits 8 cb .. 8 cb + 7 of the row read as
+// one little-endian bit string, code i at bits 3i .. 3i + 2.
+template <class Code>
+__device__ __forceinline__ uint8_t row3_byte(Code code, int cb, int n) {
+  const int i0 = (8 * cb) / 3, sh = 8 * cb - 3 * i0;
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k)
+    if (i0 + k < n) w |= (uint32_t)code(i0 + k) << (3 * k);
+  return (uint8_t)(w >> sh);
+}
+
+// Six bytes at dst + o0 (o0 even) as three 16-bit stores.
+__device__ __forceinline__ void store6(uint8_t* dst, int o0, const uint8_t* buf) {
+  uint16_t* d16 = reinterpret_cast<uint16_t*>(dst + o0);
+  for (int k = 0; k < 3; ++k) d16[k] = (uint16_t)(buf[2 * k] | (buf[2 * k + 1] << 8));
+}
+
 // Pack codes into the tile byte images (canonical nibble/crumb order: element
-// 2k in the low nibble of byte k; element 4k+j in bits 2j..2j+1).
+// 2k in the low nibble of byte k; element 4k+j in bits 2j..2j+1; at 3 bits a
+// row is one bit string, row3_byte).
 //   key tile:   token-major rows, byte cb of token t at ktile_offset(t, cb)
 //   value tile: channel-major rows of 32 tokens, row d at d * (4 * bits)
 __device__ void pack_key_tile(const uint8_t (*ck)[kD], uint8_t* dst, int bits, int tid) {
-  const int per_thread = 2 * bits;  // 2048 or 1024 bytes over 256 threads
+  const int per_thread = 2 * bits;  // 2048, 1536 or 1024 bytes over 256 threads
   const int o0 = tid * per_thread;
   uint8_t buf[8];
+  if (bits == 3) {
+    for (int k = 0; k < 6; ++k) {
+      const int o = o0 + k;
+      const int t = (o & 511) >> 4;
+      const int cb = (o >> 9) * 16 + (o & 15);
+      buf[k] = row3_byte([&](int i) { return ck[t][i]; }, cb, kD);
+    }
+    store6(dst, o0, buf);
+    return;
+  }
   for (int k = 0; k < per_thread; ++k) {
     const int o = o0 + k;
     const int t = (o & 511) >> 4;
@@ -171,6 +199,15 @@ __device__ void pack_value_tile(const uint8_t (*cv)[kD], uint8_t* dst, int bits,
   const int rb = 4 * bits;  // bytes per channel row
   const int o0 = tid * per_thread;
   uint8_t buf[8];
+  if (bits == 3) {
+    for (int k = 0; k < 6; ++k) {
+      const int o = o0 + k;
+      const int d = o / rb, kb = o % rb;
+      buf[k] = row3_byte([&](int i) { return cv[i][d]; }, kb, kGroup);
+    }
+    store6(dst, o0, buf);
+    return;
+  }
   for (int k = 0; k < per_thread; ++k) {
     const int o = o0 + k;
     const int d = o / rb, kb = o % rb;

@@ -92,10 +92,11 @@ constexpr bool query_in_prob_table() {
 }
 
 // Waves per SIMD the register allocation must allow: three work-groups per
-// compute unit wherever the LDS allows it (the KIVI G = 4 4-bit stages do not).
+// compute unit wherever the LDS allows it (the KIVI G = 4 4-bit and 3-bit
+// stages do not).
 template <int G, int BITS, bool BLOCK>
 constexpr int decode_min_waves() {
-  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK && BITS == 4) ? 2 : 3);
+  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK && BITS >= 3) ? 2 : 3);
 }
 
 // TBQ (with BLOCK): TBQ4 blocks; codes become their fp16 levels through
@@ -217,6 +218,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   int kch[4];
   float kinv[4];
   key_quad<BITS>(tl, kch, kinv);
+  // KIVI key (s, z) pairs come two adjacent channels per 8-byte load: slots
+  // (0, 2) and (1, 3) at 4 and 2 bits, slots (0, 1) and (2, 3) at 3 bits
+  const int kmc0 = kch[0], kmc1 = BITS == 3 ? kch[2] : kch[1];
   if (TBQ)
     for (int i = 0; i < 4; ++i) kinv[i] = 1.0f;
   uint32_t lut[8];
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   auto issue = [&](const TilePos& tp, int64_t pr) {
     stage_issue<BITS>(stage, tp, lane, kpair_of(pr), vpair_of(pr));
     meta_issue<BITS, BLOCK, false, Q40>(nxt, tp, lane, kmeta_of(pr), vmeta_of(pr), ksc_of(pr), vsc_of(pr),
-                                        scale_end, kch[0], kch[1]);
+                                        scale_end, kmc0, kmc1);
   };
   TileCursor cs;
   cursor_start(a, rank, cs, lane);
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       if (more) issue(nxt_pos, cs.pair);
     } else {
       load_tile<BITS, BLOCK, false, Q40>(cur, cur_pos, lane, kpair_of(pair), vpair_of(pair), kmeta_of(pair),
-                                         vmeta_of(pair), ksc_of(pair), vsc_of(pair), kch[0], kch[1]);
+                                         vmeta_of(pair), ksc_of(pair), vsc_of(pair), kmc0, kmc1);
       more = cursor_next(a, cs, lane, &ends);
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
     }
@@ -354,14 +358,14 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     float bias[G];
     float kscale_grp = 1.0f;
     if (!BLOCK) {
-      const float sK[4] = {half_bits_to_float((uint16_t)(km0.x & 0xFFFF)),
-                           half_bits_to_float((uint16_t)(km1.x & 0xFFFF)),
-                           half_bits_to_float((uint16_t)(km0.y & 0xFFFF)),
-                           half_bits_to_float((uint16_t)(km1.y & 0xFFFF))};
-      const float zK[4] = {half_bits_to_float((uint16_t)(km0.x >> 16)),
-                           half_bits_to_float((uint16_t)(km1.x >> 16)),
-                           half_bits_to_float((uint16_t)(km0.y >> 16)),
-                           half_bits_to_float((uint16_t)(km1.y >> 16))};
+      // (s, z) of slot i's channel: the words of channels kmc0, kmc0 + 1,
+      // kmc1, kmc1 + 1 in slot order
+      const uint32_t mw[4] = {km0.x, BITS == 3 ? km0.y : km1.x, BITS == 3 ? km1.x : km0.y, km1.y};
+      float sK[4], zK[4];
+      for (int i = 0; i < 4; ++i) {
+        sK[i] = half_bits_to_float((uint16_t)(mw[i] & 0xFFFF));
+        zK[i] = half_bits_to_float((uint16_t)(mw[i] >> 16));
+      }
       float qp[G][4];
       float amax = 0.0f;
       for (int m = 0; m < G; ++m) {
@@ -500,6 +504,8 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
     if (g.G == 1) KVQ_FN(1, 4, true); else if (g.G == 2) KVQ_FN(2, 4, true); else KVQ_FN(4, 4, true);
   } else if (bits == 4) {
     if (g.G == 1) KVQ_FN(1, 4, false); else if (g.G == 2) KVQ_FN(2, 4, false); else KVQ_FN(4, 4, false);
+  } else if (bits == 3) {
+    if (g.G == 1) KVQ_FN(1, 3, false); else if (g.G == 2) KVQ_FN(2, 3, false); else KVQ_FN(4, 3, false);
   } else {
     if (g.G == 1) KVQ_FN(1, 2, false); else if (g.G == 2) KVQ_FN(2, 2, false); else KVQ_FN(4, 2, false);
   }
@@ -561,6 +567,10 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
       if (g.G == 1) KVQ_MF(1, 4, false);
       else if (g.G == 2) KVQ_MF(2, 4, false);
       else KVQ_MF(4, 4, false);
+    } else if (rp.bits == 3) {
+      if (g.G == 1) KVQ_MF(1, 3, false);
+      else if (g.G == 2) KVQ_MF(2, 3, false);
+      else KVQ_MF(4, 3, false);
     } else {
       if (g.G == 1) KVQ_MF(1, 2, false);
       else if (g.G == 2) KVQ_MF(2, 2, false);

@@ -15,6 +15,20 @@
 namespace kvq {
 namespace {
 
+// 3-bit tiles: a row's codes are one little-endian bit string, code c at bits
+// 3c .. 3c + 2, so a code may straddle two bytes.  Key rows are 48 bytes of
+// the token-major key tile, value rows 12 bytes per channel.
+__device__ __forceinline__ int key_code3(const uint8_t* kt, int row, int d) {
+  const int kb = (3 * d) >> 3, sh = (3 * d) & 7;
+  const uint32_t w = kt[ktile_offset(row, kb)] | (kb + 1 < 48 ? (uint32_t)kt[ktile_offset(row, kb + 1)] << 8 : 0u);
+  return (int)((w >> sh) & 7u);
+}
+__device__ __forceinline__ int value_code3(const uint8_t* vt, int d, int t) {
+  const int vb = (3 * t) >> 3, sh = (3 * t) & 7;
+  const uint32_t w = vt[d * 12 + vb] | (vb + 1 < 12 ? (uint32_t)vt[d * 12 + vb + 1] << 8 : 0u);
+  return (int)((w >> sh) & 7u);
+}
+
 __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t t0, int64_t nt,
                                                       float* k_out, float* v_out) {
   const int64_t items = (int64_t)g.B * nt * g.Hkv * kD;
@@ -36,13 +50,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       const uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + grp) * 512 * bits;
       const uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + grp) * 512 * bits;
       int kn, vn;
-      if (bits == 3) {   // code at bits 3c of the row's bit string (may straddle a byte)
-        const int kb = (3 * d) >> 3, ks = (3 * d) & 7;
-        const uint32_t k16 = kt[ktile_offset(row, kb)] | (kb + 1 < 48 ? (uint32_t)kt[ktile_offset(row, kb + 1)] << 8 : 0u);
-        kn = (int)((k16 >> ks) & 7u);
-        const int vb = (3 * row) >> 3, vsh = (3 * row) & 7;
-        const uint32_t v16 = vt[d * 12 + vb] | (vb + 1 < 12 ? (uint32_t)vt[d * 12 + vb + 1] << 8 : 0u);
-        vn = (int)((v16 >> vsh) & 7u);
+      if (bits == 3) {
+        kn = key_code3(kt, row, d);
+        vn = value_code3(vt, d, row);
       } else {
         kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
         vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
@@ -73,9 +83,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       int bits;
       const uint8_t* kt = tile_ptr(g, p, KVQ_PLANE_K_HI, KVQ_PLANE_K_LO, pair, grp, &bits);
       const uint8_t* vt = tile_ptr(g, p, KVQ_PLANE_V_HI, KVQ_PLANE_V_LO, pair, grp, &bits);
-      const int per = 8 / bits, mask = (1 << bits) - 1;
-      const int kc = (kt[ktile_offset(row, d / per)] >> (bits * (d % per))) & mask;
-      const int vc = (vt[d * 4 * bits + row / per] >> (bits * (row % per))) & mask;
+      int kc, vc;
+      if (bits == 3) {
+        kc = key_code3(kt, row, d);
+        vc = value_code3(vt, d, row);
+      } else {
+        const int per = 8 / bits, mask = (1 << bits) - 1;
+        kc = (kt[ktile_offset(row, d / per)] >> (bits * (d % per))) & mask;
+        vc = (vt[d * 4 * bits + row / per] >> (bits * (row % per))) & mask;
+      }
       const uint16_t* km = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_K_META] + (pair * g.gmax + grp) * 512);
       const uint16_t* vm = reinterpret_cast<const uint16_t*>(p.p[KVQ_PLANE_V_META] + (pair * g.gmax + grp) * 512);
       const int dg = d >> 5;

@@ -46,9 +46,11 @@ kvq_status validate_config(const kvq_config* c) {
     for (int i = 0; i < 4; ++i)
       if (c->hadamard_sign_in[i] != 0 || c->hadamard_sign_out[i] != 0) return KVQ_ERR_INVALID_ARG;
   if (c->scheme == KVQ_KIVI_ASYM) {
-    if (c->k_bits != 4 && c->k_bits != 2) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_bits != 4 && c->k_bits != 3 && c->k_bits != 2) return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != kWindow) return KVQ_ERR_UNSUPPORTED;
     if (c->int4_window >= 0 && (c->k_bits != 4 || c->low_bits != 2)) return KVQ_ERR_UNSUPPORTED;
+    // 3-bit KIVI: one tier, keys stored after RoPE (or rotated)
+    if (c->k_bits == 3 && c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
   } else {
     // 3 bits: the 50-byte block of the format table (symmetric block scheme only)
     if (c->k_bits != 4 && !(c->k_bits == 3 && c->scheme == KVQ_BLOCK128_SYM)) return KVQ_ERR_UNSUPPORTED;

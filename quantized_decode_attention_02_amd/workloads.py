@@ -109,6 +109,11 @@ WORKLOADS.append(
     dict(id=7, name="block50-3bit-hadamard-gqa32x8-b32-t65536+8192",
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_block128(k_bits=3, v_bits=3), dist="normal", outliers=None))
+# INT3 KIVI (the INT3 cache of [troisinh]'s title) at the Llama-2-7B layer shape
+WORKLOADS.append(
+    dict(id=8, name="int3-kivi-llama2-7b-mha32-b8-t32768-outlier2pct-x15",
+         batch=8, num_q_heads=32, num_kv_heads=32, tokens=32768, prefill=0,
+         cfg=_kivi(k_bits=3, v_bits=3), dist="normal", outliers=("pairs", 82, 15.0)))
 
 
 def workload(key):

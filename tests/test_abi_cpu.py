@@ -71,6 +71,10 @@ def test_config_validation():
     assert status_of(fp16_window=64) == -2
     assert status_of(int4_window=100) == -1
     assert status_of(int4_window=64, k_bits=2, v_bits=2) == -2
+    # 3-bit KIVI: one tier, keys stored after RoPE
+    assert status_of(k_bits=3, v_bits=3) == 0
+    assert status_of(k_bits=3, v_bits=3, int4_window=64) == -2
+    assert status_of(k_bits=3, v_bits=3, pre_rope_keys=1, rope_theta=1e4) == -2
     assert status_of(scheme=7) == -1
     assert status_of(hadamard=2) == -1
     assert status_of(hadamard=1, pre_rope_keys=1) == -2

@@ -33,6 +33,7 @@ SCHEDULES = {
     5: [8192] * 9,
     6: [8192] * 9,
     7: [8192] * 9,
+    8: [32767, 1],
 }
 
 

@@ -19,6 +19,8 @@ SIGNS = wl.random_signs(11)
 VARIANTS = {
     "int4": dict(),
     "int2": dict(k_bits=2, v_bits=2),
+    "int3": dict(k_bits=3, v_bits=3),
+    "int3-hadamard-signed": dict(k_bits=3, v_bits=3, hadamard=True, **SIGNS),
     "int4-hadamard": dict(hadamard=True),
     "int4-prerope": dict(pre_rope=True, rope_theta=500000.0),
     "mixed-hadamard": dict(hadamard=True, hi_window=96),
@@ -80,9 +82,10 @@ def test_streaming(variant, stream):
     check_decode(g, o, w, s, h)
 
 
+@pytest.mark.parametrize("variant", ["int4", "int3"])
 @pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 1), (8, 8)])
-def test_gqa_shapes(hq, hkv):
-    w = make_w(3000 + hq * 10 + hkv, "int4", 777, batch=3, hq=hq, hkv=hkv)
+def test_gqa_shapes(hq, hkv, variant):
+    w = make_w(3000 + hq * 10 + hkv, variant, 777, batch=3, hq=hq, hkv=hkv)
     g, o, s, h = build_pair(w, [777])
     compare_planes(g, o, s, h)
     check_decode(g, o, w, s, h)
