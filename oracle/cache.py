@@ -25,6 +25,7 @@ persoalan kalibrasi").  Four schemes:
 ``q4_0``: every token's 128-vector, optionally rotated, becomes four
   symmetric 4-bit 32-value blocks with an fp16 scale each (18 B per 32 values,
   [trefon] "Przykład: model 27B przy 262K"); no window.
+``q8_0``: the same at 8 bits (34 B per 32 values, the table's Q8_0 row).
 
 Append order (reading; the pages give none): groups that leave the high-bit
 tier are requantized to ``low_bits`` from their dequantized high-bit values
@@ -69,7 +70,7 @@ def make_config(**kw):
 
 
 # per-token 128-value block schemes: nibbles + one fp16 per token and tensor
-BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")
+BLOCK_SCHEMES = ("block128", "tbq4", "q4_0", "q8_0")
 
 
 def _tile_token_of_byte(key_tile, bits=4):
@@ -118,7 +119,7 @@ class OracleCache:
             Tp = G * 32
             self.k_nib = np.zeros((B, H, Tp, 128), np.uint8)
             self.v_nib = np.zeros((B, H, Tp, 128), np.uint8)
-            sc_shape = (B, H, Tp, 4) if c["scheme"] == "q4_0" else (B, H, Tp)
+            sc_shape = (B, H, Tp, 4) if c["scheme"] in ("q4_0", "q8_0") else (B, H, Tp)
             self.k_sc = np.zeros(sc_shape, F16)
             self.v_sc = np.zeros(sc_shape, F16)
 
@@ -149,7 +150,8 @@ class OracleCache:
         c = self.cfg
         if c["scheme"] in BLOCK_SCHEMES:
             quantize = {"block128": lambda y: quant.quant_sym128(y, c["k_bits"]),
-                        "tbq4": codebook.quant_tbq4, "q4_0": quant.quant_sym32}[c["scheme"]]
+                        "tbq4": codebook.quant_tbq4, "q4_0": quant.quant_sym32,
+                        "q8_0": lambda y: quant.quant_sym32(y, 8)}[c["scheme"]]
             for name, src, nib, sc in (("k", kn, self.k_nib, self.k_sc),
                                        ("v", vn, self.v_nib, self.v_sc)):
                 y = self._source_rows(src)
@@ -204,7 +206,8 @@ class OracleCache:
         V = np.zeros((B, H, t1 - t0, 128), F32)
         if c["scheme"] in BLOCK_SCHEMES:
             deq = {"block128": lambda n, s: quant.dequant_sym128(n, s, c["k_bits"]),
-                   "tbq4": codebook.dequant_tbq4, "q4_0": quant.dequant_sym32}[c["scheme"]]
+                   "tbq4": codebook.dequant_tbq4, "q4_0": quant.dequant_sym32,
+                   "q8_0": lambda n, s: quant.dequant_sym32(n, s, 8)}[c["scheme"]]
             K[:] = deq(self.k_nib[:, :, t0:t1], self.k_sc[:, :, t0:t1])
             V[:] = deq(self.v_nib[:, :, t0:t1], self.v_sc[:, :, t0:t1])
         else:
@@ -276,7 +279,7 @@ class OracleCache:
                 lv[:] = (tok < T)[None, None]
                 meta = layout.K_META if plane == layout.K_HI else layout.V_META
                 pair(img[meta])[:] = sc.reshape(B, H, -1).astype("<f2").view(np.uint8)
-                ml = np.repeat(np.arange(G * 32) < T, 2 * (4 if c["scheme"] == "q4_0" else 1))
+                ml = np.repeat(np.arange(G * 32) < T, 2 * (4 if c["scheme"] in ("q4_0", "q8_0") else 1))
                 pair(live[meta])[:] = ml[None, None]
             return img, live
         hs = layout.hi_slots(c, self.max_tokens)

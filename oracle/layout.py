@@ -15,14 +15,15 @@ Packing of codes into bytes (canonical):
   3 bits: element i -> bits [3i, 3i+2] of the row read as one little-endian
           bit string, so eight codes fill three bytes and codes 2, 5 (mod 8)
           straddle a byte boundary.
+  8 bits: element k -> byte k.
 
 Tiles.  Quantized tokens live in tiles of 32 consecutive tokens (one key group):
   key tile   -- token-major: row t = packed codes of token t over the 128
-                channels (64 B at 4 bits, 32 B at 2 bits).  Byte c of row t is
+                channels (128 B at 8 bits, 64 B at 4, 32 B at 2).  Byte c of row t is
                 stored at offset (c // 16) * 512 + t * 16 + (c % 16), so the
                 16-byte chunk j of all 32 rows is one contiguous 512-byte run.
   value tile -- channel-major: row d = packed codes of channel d over the 32
-                tokens (16 B at 4 bits, 8 B at 2 bits), row d at offset
+                tokens (32 B at 8 bits, 16 B at 4, 8 B at 2), row d at offset
                 d * rowbytes.
   A tile holds 512 * bits bytes.
 
@@ -30,15 +31,16 @@ Planes (all [batch][kv_head][...], row-major, little-endian fp16/fp32):
   0 K_HI   KIVI: key tiles of the high-bit tier.  With a high-bit window of N
            tokens the plane is a ring of N/32 slots and group g uses slot
            g mod (N/32); otherwise it has one slot per group.
-           Block schemes: key tiles of every group (4-bit, or 3-bit for the
-           50-byte block).
+           Block schemes: key tiles of every group (4-bit, 3-bit for the
+           50-byte block, 8-bit for Q8_0).
   1 V_HI   same for values.
   2 K_LO   KIVI with a high-bit window only: low-bit key tiles, slot g = group g.
   3 V_LO   same for values.
   4 K_META KIVI: 512 B per group: (s, z) fp16 pairs per channel, channel d at
-           bytes 4d..4d+3.  BLOCK128: one fp16 scale per token.
+           bytes 4d..4d+3.  BLOCK128: one fp16 scale per token; Q4_0 and
+           Q8_0: four per token (32-value slices in order).
   5 V_META KIVI: 512 B per group: token-major, token t and 32-dim group g at
-           bytes 16t + 4g: (s, z).  BLOCK128: one fp16 scale per token.
+           bytes 16t + 4g: (s, z).  Block schemes: as K_META.
   6 K_WIN  KIVI: fp16 key window ring, 160 rows x 128 channels; token t in
            row t mod 160.
   7 V_WIN  KIVI: fp16 value window ring, channel-major: 128 rows (channels) x
@@ -173,6 +175,16 @@ def block18(nibbles, s_h):
     return np.concatenate([s, codes], axis=-1)                       # [..., 4, 18]
 
 
+def block34(codes, s_h):
+    """The 34-byte blocks of one 128-value vector's four 32-value slices at 8
+    bits: per slice an fp16 scale (LE) + 32 code bytes, element k in byte k
+    (the format table's "Q8_0 (34 B / 32)" row)."""
+    n = np.asarray(codes)
+    body = pack_rows(n.reshape(n.shape[:-1] + (4, 32)), 8)           # [..., 4, 32]
+    s = np.asarray(s_h, dtype="<f2").reshape(n.shape[:-1] + (4, 1)).view(np.uint8)
+    return np.concatenate([s, body], axis=-1)                        # [..., 4, 34]
+
+
 def block50(codes, s_h):
     """The 50-byte block of one 128-value vector at 3 bits: fp16 scale (LE) +
     48 code bytes (the format table's "3 bity (50 B / 128)" row)."""
@@ -209,7 +221,7 @@ def plane_sizes(cfg, batch, max_tokens):
         sz[K_WIN] = pairs * RING * 128 * 2
         sz[V_WIN] = pairs * RING * 128 * 2
     else:
-        per_token = 4 if cfg["scheme"] == "q4_0" else 1     # fp16 per token
+        per_token = 4 if cfg["scheme"] in ("q4_0", "q8_0") else 1     # fp16 per token
         sz[K_HI] = pairs * G * 512 * cfg["k_bits"]
         sz[V_HI] = pairs * G * 512 * cfg["v_bits"]
         sz[K_META] = pairs * G * TILE_TOKENS * 2 * per_token

@@ -36,7 +36,10 @@ Readings where the pages are silent (all float32 one op at a time, RNE):
   c in [-3, 3], stored n = c + 4 (1..7), y^ = fl32((n - 4) * s_h).
   symmetric 32-value blocks, 4 bits ("Q4_0", 18 B per 32 values in the
   format table of [trefon] "Przykład: model 27B przy 262K"): the same
-  quantizer over each 32-value slice of a vector, one fp16 scale per slice.
+  quantizer over each 32-value slice of a vector, one fp16 scale per slice;
+  at 8 bits ("Q8_0", 34 B per 32 values, the table's row above it):
+  s_h = fp16(fl32(a / 127)), c in [-127, 127], stored byte c + 128 (1..255),
+  y^ = fl32((n - 128) * s_h).
   No clipping: the full [min, max] range is used.
 """
 
@@ -109,28 +112,33 @@ def dequant_sym128(nibbles, s_h, bits=4):
     return (c.astype(F32) * np.asarray(s_h, dtype=F16).astype(F32)[..., None]).astype(F32)
 
 
-def quant_sym32(y):
-    """Symmetric 4-bit quantization of float32 vectors (last axis 128) in four
-    32-value slices: (nibbles uint8 1..15, s_h fp16 [..., 4])."""
+def quant_sym32(y, bits=4):
+    """Symmetric quantization of float32 vectors (last axis 128) in four
+    32-value slices at 4 bits (Q4_0: codes -7..7 stored + 8, 1..15) or 8 bits
+    (Q8_0: codes -127..127 stored + 128, 1..255): (codes uint8, s_h fp16
+    [..., 4])."""
+    if bits not in (4, 8):
+        raise ValueError("4 or 8 bits")
+    top = (1 << (bits - 1)) - 1                    # 7 or 127
     y = np.asarray(y, dtype=F32)
     _check_finite(y)
     if y.shape[-1] != 128:
         raise ValueError("vector length must be 128")
     ys = y.reshape(y.shape[:-1] + (4, 32))
     a = np.abs(ys).max(axis=-1)
-    s_h = (a / F32(7)).astype(F32).astype(F16)
+    s_h = (a / F32(top)).astype(F32).astype(F16)
     sx = s_h.astype(F32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         quo = (ys / sx).astype(F32)
     quo = np.where(sx == 0, F32(0), quo)
-    c = np.clip(np.rint(quo), F32(-7), F32(7)).astype(np.int16)
-    return (c + 8).astype(np.uint8).reshape(y.shape), s_h
+    c = np.clip(np.rint(quo), F32(-top), F32(top)).astype(np.int16)
+    return (c + top + 1).astype(np.uint8).reshape(y.shape), s_h
 
 
-def dequant_sym32(nibbles, s_h):
-    """y^ = fl32((n - 8) * s_h of the value's slice), exact."""
-    n = np.asarray(nibbles)
-    c = (n.astype(np.int16) - 8).reshape(n.shape[:-1] + (4, 32)).astype(F32)
+def dequant_sym32(codes, s_h, bits=4):
+    """y^ = fl32((n - 2^(bits-1)) * s_h of the value's slice), exact."""
+    n = np.asarray(codes)
+    c = (n.astype(np.int16) - (1 << (bits - 1))).reshape(n.shape[:-1] + (4, 32)).astype(F32)
     y = c * np.asarray(s_h, dtype=F16).astype(F32)[..., None]
     return y.astype(F32).reshape(n.shape)
 

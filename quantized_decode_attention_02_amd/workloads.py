@@ -60,6 +60,10 @@ def _q4_0(**kw):
     return c
 
 
+def _q8_0(**kw):
+    return _q4_0(**dict(dict(scheme="q8_0", k_bits=8, v_bits=8), **kw))
+
+
 def _tbq4(**kw):
     c = dict(scheme="tbq4", k_bits=4, v_bits=4, low_bits=2, hi_window=-1,
              window=0, hadamard=True, pre_rope=False, rope_theta=10000.0)

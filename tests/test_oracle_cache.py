@@ -36,7 +36,8 @@ def test_append_plan_demotion_sets():
 
 
 def small_workload(wid, scheme, T, **kw):
-    cfg = {"kivi": wl._kivi, "block128": wl._block128, "tbq4": wl._tbq4, "q4_0": wl._q4_0}[scheme](**kw)
+    cfg = {"kivi": wl._kivi, "block128": wl._block128, "tbq4": wl._tbq4, "q4_0": wl._q4_0,
+           "q8_0": wl._q8_0}[scheme](**kw)
     return wl.custom(wid, 2, 4, 2, T, cfg)
 
 
@@ -58,6 +59,7 @@ SIGNS = wl.random_signs(7)
                                        ("block128", dict(**SIGNS)),
                                        ("tbq4", {}), ("tbq4", dict(**SIGNS)),
                                        ("q4_0", {}), ("q4_0", dict(hadamard=True)),
+                                       ("q8_0", {}), ("q8_0", dict(hadamard=True)),
                                        ("block128", dict(k_bits=3, v_bits=3)),
                                        ("kivi", dict(k_bits=2, v_bits=2)),
                                        ("kivi", dict(k_bits=3, v_bits=3)),

@@ -210,3 +210,44 @@ def test_symmetric_block_3bit():
     assert np.array_equal(c[clear], near[clear])
     zn, zs = quant.quant_sym128(np.zeros((1, 128), F32), 3)
     assert np.all(zn == 4) and zs[0] == 0
+
+
+def test_symmetric_32_value_blocks_8bit():
+    """Q8_0-style slices: every code is the nearest of the 255 levels k s_h,
+    k in [-127, 127] (fp64 brute force over all levels, away from ties); the
+    absmax element takes the end level of its sign; half-step bound; zero
+    slices; the 34-byte image and 8.5 bits per value (the page's Q8_0 row)."""
+    from oracle import layout
+    rng = np.random.default_rng(15)
+    y = (rng.standard_normal((400, 128)) * rng.uniform(0.01, 100, (400, 4)).repeat(32, axis=1)).astype(F32)
+    y[0, 32:64] = 0.0                                  # an all-zero slice
+    n, s = quant.quant_sym32(y, 8)
+    assert n.shape == y.shape and s.shape == (400, 4)
+    assert n.min() >= 1 and n.max() <= 255
+    assert s[0, 1] == 0 and np.all(n[0, 32:64] == 128)
+    sx = np.repeat(s.astype(np.float64), 32, axis=1)
+    c = n.astype(np.float64) - 128
+    levels = np.arange(-127, 128, dtype=np.float64)
+    for r in range(0, 400, 7):
+        for j in range(128):
+            if sx[r, j] == 0:
+                continue
+            d = np.abs(levels * sx[r, j] - float(y[r, j]))
+            best = np.argsort(d)
+            if d[best[1]] - d[best[0]] < 1e-6 * sx[r, j]:
+                continue
+            assert c[r, j] == levels[best[0]], (r, j)
+    ys = y.reshape(400, 4, 32)
+    am = np.argmax(np.abs(ys), axis=-1)
+    c_am = np.take_along_axis(c.reshape(400, 4, 32), am[..., None], axis=-1)[..., 0]
+    y_am = np.take_along_axis(ys, am[..., None], axis=-1)[..., 0]
+    nz = s != 0
+    assert np.all(np.abs(c_am[nz]) == 127)
+    assert np.all(np.sign(c_am[nz]) == np.sign(y_am[nz]))
+    yh = quant.dequant_sym32(n, s, 8)
+    assert np.all(np.abs(y - yh) <= sx / 2 * SLACK)
+    img = layout.block34(n[:3], s[:3])
+    assert img.shape == (3, 4, 34)
+    assert np.array_equal(img[..., :2].copy().view("<f2")[..., 0], s[:3])
+    assert np.array_equal(img[..., 2:], n[:3].reshape(3, 4, 32))   # element k in byte k
+    assert img.shape[-1] * 8 / 32 == 8.5

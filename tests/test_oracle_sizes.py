@@ -107,3 +107,6 @@ def test_plane_sizes_match_per_token_bytes(bits):
     # four 18-byte blocks per token and tensor
     cfgq = make_config(scheme="q4_0", num_q_heads=4, num_kv_heads=2)
     assert sum(layout.plane_sizes(cfgq, B, T)) == B * 2 * T * 2 * 4 * 18   # K and V
+    # four 34-byte blocks per token and tensor (the page's Q8_0 row)
+    cfg8 = make_config(scheme="q8_0", k_bits=8, v_bits=8, num_q_heads=4, num_kv_heads=2)
+    assert sum(layout.plane_sizes(cfg8, B, T)) == B * 2 * T * 2 * 4 * 34
