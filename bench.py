@@ -67,13 +67,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-BLOCK_SCHEMES = ("block128", "tbq4", "q4_0")   # per-token blocks, no window
+BLOCK_SCHEMES = ("block128", "tbq4", "q4_0", "q8_0")   # per-token blocks, no window
 
 
 def block_bytes(cfg):
     """Bytes of one token's 128 values of one tensor in a block scheme."""
     if cfg["scheme"] == "q4_0":
         return 4 * 18
+    if cfg["scheme"] == "q8_0":
+        return 4 * 34
     return 50 if cfg["k_bits"] == 3 else 66
 
 
@@ -104,6 +106,9 @@ def counter_traffic(wid):
 
 
 def describe_cache(cfg):
+    if cfg["scheme"] == "q8_0":
+        return ("Q8_0-style symmetric 8-bit blocks of 32 values + fp16 scale (34 B/32)"
+                + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")
     if cfg["scheme"] == "q4_0":
         return ("Q4_0-style symmetric 4-bit blocks of 32 values + fp16 scale (18 B/32)"
                 + (" after a Hadamard-128 rotation" if cfg["hadamard"] else "") + ", no fp16 window")

@@ -76,24 +76,28 @@ typedef enum kvq_status {
  *   fp16 scale and 32 symmetric 4-bit codes, 18 bytes per 32 values, 4.5 bits
  *   per value (the Q4_0 row of the format table, [trefon] "Przykład: model
  *   27B przy 262K"); the quantizer of KVQ_BLOCK128_SYM per 32-value slice.
- *   Rotation optional. */
-enum { KVQ_KIVI_ASYM = 0, KVQ_BLOCK128_SYM = 1, KVQ_TBQ4 = 2, KVQ_Q4_0 = 3 };
+ *   Rotation optional.
+ * KVQ_Q8_0: the same four 32-value blocks at 8 bits (k_bits = 8): an fp16
+ *   scale absmax / 127 and 32 codes in [-127, 127] stored as the byte c + 128,
+ *   34 bytes per 32 values, 8.5 bits per value (the Q8_0 row of the same
+ *   table).  Rotation optional. */
+enum { KVQ_KIVI_ASYM = 0, KVQ_BLOCK128_SYM = 1, KVQ_TBQ4 = 2, KVQ_Q4_0 = 3, KVQ_Q8_0 = 4 };
 
 /* Cache planes (caller-allocated device buffers; byte image per plane is the
  * documented layout, sizes from kvq_layout):
  *   K_HI/V_HI   key/value code tiles of the high-bit tier (KIVI; a ring of
  *               int4_window/32 slots when int4_window >= 0) or of every token
- *               (BLOCK128, TBQ4, Q4_0).  A tile is 32 tokens x 128 channels at b bits:
+ *               (BLOCK128, TBQ4, Q4_0, Q8_0).  A tile is 32 tokens x 128 channels at b bits:
  *               keys token-major with 16-byte chunks interleaved across the
  *               32 tokens, values channel-major.
  *   K_LO/V_LO   low-bit tiles (KIVI with int4_window >= 0), one per group.
  *   K_META      KIVI: per group 128 fp16 (scale, zero) pairs, one per
  *               channel.  BLOCK128: one fp16 scale per token; TBQ4: one fp16
- *               norm per token; Q4_0: four fp16 scales per token (32-value
+ *               norm per token; Q4_0, Q8_0: four fp16 scales per token (32-value
  *               slices in order).
  *   V_META      KIVI: per group, token-major: for each of the 32 tokens the
  *               fp16 (scale, zero) of its four 32-dim slices.  BLOCK128: one
- *               fp16 scale per token; TBQ4: one fp16 norm per token; Q4_0:
+ *               fp16 scale per token; TBQ4: one fp16 norm per token; Q4_0, Q8_0:
  *               four fp16 scales per token.
  *   K_WIN       KIVI: fp16 key ring of 160 rows x 128 channels per
  *               (sequence, kv head); token t lives in row t mod 160.
@@ -120,10 +124,10 @@ typedef struct kvq_config {
   int32_t num_q_heads;    /* Hq */
   int32_t num_kv_heads;   /* Hkv; Hq / Hkv must be 1, 2 or 4 (GQA, [trefon]
                              "Bajty na token"), q head h reads kv head h / (Hq/Hkv) */
-  int32_t scheme;         /* KVQ_KIVI_ASYM, KVQ_BLOCK128_SYM, KVQ_TBQ4 or
-                             KVQ_Q4_0 */
+  int32_t scheme;         /* KVQ_KIVI_ASYM, KVQ_BLOCK128_SYM, KVQ_TBQ4,
+                             KVQ_Q4_0 or KVQ_Q8_0 */
   int32_t k_bits;         /* bits of the high-bit tier: 4, 3 or 2 (KIVI); 4
-                             or 3 (BLOCK128); 4 (TBQ4, Q4_0) */
+                             or 3 (BLOCK128); 4 (TBQ4, Q4_0); 8 (Q8_0) */
   int32_t v_bits;         /* must equal k_bits */
   int32_t k_group_tokens; /* must be 32 */
   int32_t v_group_dims;   /* must be 32 */
@@ -208,7 +212,7 @@ kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t len
  * channel, values per token; after the Hadamard rotation if configured);
  * groups leaving the high-bit window are requantized to low_bits from their
  * dequantized values; new groups go straight to the tier of their age.
- * BLOCK128, TBQ4, Q4_0: every new token becomes one block (four for Q4_0).  pre_rope_keys: ROPE rows for
+ * BLOCK128, TBQ4, Q4_0, Q8_0: every new token becomes one block (four for Q4_0 and Q8_0).  pre_rope_keys: ROPE rows for
  * the new positions are written.  Advances cache->length on success.
  * Errors: KVQ_ERR_CAPACITY if length + n_new > max_tokens; n_new == 0 is a
  * no-op.  Output is bit-exact with the documented fp32 round-to-nearest-even
@@ -258,8 +262,8 @@ kvq_status kvq_decode_merge(const kvq_config* cfg, const kvq_cache* cache, const
  * masuk ke model latency", for tests and inspection.
  *   k_out, v_out: device fp32 [batch][t1 - t0][num_kv_heads][128].
  * Bit-exact: x = c * scale + zero (KIVI), (n - 8) * scale (BLOCK128, n - 4 at
- * 3 bits; Q4_0
- * with the scale of the value's slice), norm * level[n] (TBQ4). */
+ * 3 bits; Q4_0, and n - 128 for Q8_0, with the scale of the value's slice),
+ * norm * level[n] (TBQ4). */
 kvq_status kvq_dequant(const kvq_config* cfg, const kvq_cache* cache, int64_t t0, int64_t t1,
                        void* k_out, void* v_out, void* stream);
 

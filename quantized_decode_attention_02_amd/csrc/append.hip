@@ -37,13 +37,16 @@ struct GroupParams {
 // rs = fl32(1 / s) is within 2^-23 |d / s| + 2^-24 |d / s| <= 2^-19
 // (|q| <= 16) of d / s, and the correctly rounded quotient fl32(d / s) is
 // within 2^-20 of it, so both round to the same integer unless q0 lies within
-// 2^-18 of a half integer.  Such a quotient inside (lo, hi) -- the half
-// integers that can move a clamped code lie there -- sets `risky`, and the
-// caller redoes the group with the division; outside, q0 stands.
-__device__ __forceinline__ float quot_fast(float d, float rs, float lo, float hi, bool& risky) {
+// 2^-18 of a half integer (`margin`; for |q| <= 128, 8-bit codes, the same
+// argument gives 1.5 * 2^-16 and 2^-17, and the margin is 2^-14).  Such a
+// quotient inside (lo, hi) -- the half integers that can move a clamped code
+// lie there -- sets `risky`, and the caller redoes the group with the
+// division; outside, q0 stands.
+__device__ __forceinline__ float quot_fast(float d, float rs, float lo, float hi, bool& risky,
+                                           float margin = 0x1p-18f) {
   const float q0 = d * rs;
   const float r = rintf(q0);
-  risky |= (q0 > lo) & (q0 < hi) & (fabsf(q0 - r) >= 0.5f - 0x1p-18f);
+  risky |= (q0 > lo) & (q0 < hi) & (fabsf(q0 - r) >= 0.5f - margin);
   return r;
 }
 
@@ -516,7 +519,8 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
   // The tile's 64 vectors (32 tokens x keys, values) go through 16 rows of
   // 16 lanes in four passes: vector 16 pass + row, lane i of a row holding
   // elements 8i .. 8i + 7, which are also its four packed bytes 4i .. 4i + 3.
-  __shared__ uint32_t vnib[kGroup][16];   // value nibbles of a token, 8 channels a word
+  __shared__ uint32_t vnib[kGroup][32];   // value codes of a token: 8 channels a word (4 bits;
+                                          // 3 bits: 24 bits of 8), 4 a word at 8 bits
   const int tid = threadIdx.x, row = tid >> 4, i = tid & 15;
   const int64_t tile = tile0 + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
                   ? *reinterpret_cast<const uint4*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + 8 * i)
                   : make_uint4(0, 0, 0, 0);
   }
-  const int bits = g.hi_bits;            // 4, or 3 for the 50-byte block
+  const int bits = g.hi_bits;            // 4, 3 for the 50-byte block, 8 for Q8_0
   const int64_t tb = 512 * (int64_t)bits;
   uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * tb;
 #pragma unroll
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       else fwht128_row16(x, i);
     }
     uint16_t sb;
-    uint32_t packed = 0;
+    uint32_t packed = 0, packed_hi = 0;   // codes 0..7 of the lane (packed_hi: 4..7 at 8 bits)
     if (g.tbq4) {
       // TBQ4 ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót"):
       // norm = fp16(min(fl32(sqrt(sum y^2)), 65504)), the sum and the root in
@@ -582,8 +586,10 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       // Q4_0: the absmax of this lane's 32-value slice (lanes 4s .. 4s + 3 of
       // the row); the 128-block scheme: of the whole row
       const float a = __uint_as_float(g.q40 ? quad_max_u32(m) : row_max_u32(m));
-      // levels -top .. top: 7 at 4 bits, 3 at 3 bits (stored code c + top + 1)
-      const float top = bits == 3 ? 3.0f : 7.0f;
+      // levels -top .. top: 7 at 4 bits, 3 at 3 bits, 127 at 8 bits (stored
+      // code c + top + 1)
+      const float top = bits == 3 ? 3.0f : bits == 8 ? 127.0f : 7.0f;
+      const float margin = bits == 8 ? 0x1p-14f : 0x1p-18f;
       sb = float_to_half_bits(a / top);
       const float s = half_bits_to_float(sb);
       // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
@@ -593,7 +599,7 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
       bool risky = false;
       const float rs = s != 0.0f ? 1.0f / s : 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, 0.25f - top, top - 0.25f, risky);
+      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, 0.25f - top, top - 0.25f, risky, margin);
       if (__any(risky)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
@@ -601,17 +607,28 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -top), top) : 0;
-        packed |= (uint32_t)(c + (int)top + 1) << (bits * j);
+        const uint32_t code = (uint32_t)(c + (int)top + 1);
+        if (bits == 8) {
+          if (j < 4) packed |= code << (8 * j);
+          else packed_hi |= code << (8 * (j - 4));
+        } else {
+          packed |= code << (bits * j);
+        }
       }
     }
     if (tensor == 0) {
       if (in) {
         if (bits == 3) {   // 24 bits: row bytes 3i .. 3i + 2 (chunks may differ)
           for (int k = 0; k < 3; ++k) kt[ktile_offset(tok, 3 * i + k)] = (uint8_t)(packed >> (8 * k));
+        } else if (bits == 8) {   // row bytes 8i .. 8i + 7 (one half of a 16-byte chunk)
+          *reinterpret_cast<uint2*>(kt + ktile_offset(tok, 8 * i)) = make_uint2(packed, packed_hi);
         } else {
           *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;
         }
       }
+    } else if (bits == 8) {
+      vnib[tok][2 * i] = packed;
+      vnib[tok][2 * i + 1] = packed_hi;
     } else {
       vnib[tok][i] = packed;
     }
@@ -630,7 +647,28 @@ __global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, 
   // of channel d; a byte with one token outside [T0, T1) keeps that token's
   // stored nibble.  Thread tid builds bytes 8 tid .. 8 tid + 7 (one row d).
   uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * tb;
-  if (bits == 3) {
+  if (bits == 8) {
+    // 8 bits: byte k of row d (32 bytes) is token k's code of channel d;
+    // thread tid builds bytes 16 (tid & 1) .. + 15 of row tid / 2, keeping
+    // the bytes of tokens outside [T0, T1)
+    const int d = tid >> 1, k0 = 16 * (tid & 1);
+    const int wd = 2 * (d >> 3) + ((d & 7) >> 2), sh = 8 * (d & 3);
+    const bool whole = tbase + k0 >= T0 && tbase + k0 + 16 <= T1;
+    uint32_t out[4] = {0, 0, 0, 0};
+    if (!whole) {
+      const uint4 old = *reinterpret_cast<const uint4*>(vt + 32 * d + k0);
+      out[0] = old.x; out[1] = old.y; out[2] = old.z; out[3] = old.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int64_t tk = tbase + k0 + k;
+      if (tk < T0 || tk >= T1) continue;
+      const uint32_t byte = (vnib[k0 + k][wd] >> sh) & 0xFFu;
+      out[k >> 2] = (out[k >> 2] & ~(0xFFu << (8 * (k & 3)))) | (byte << (8 * (k & 3)));
+    }
+    const bool any_in = tbase + k0 + 16 > T0 && tbase + k0 < T1;
+    if (any_in) *reinterpret_cast<uint4*>(vt + 32 * d + k0) = make_uint4(out[0], out[1], out[2], out[3]);
+  } else if (bits == 3) {
     // 3 bits: row d is the 32 tokens' codes as one 96-bit string, token k at
     // bits 3k; thread d (< 128) rebuilds it, keeping the bits of tokens
     // outside [T0, T1)

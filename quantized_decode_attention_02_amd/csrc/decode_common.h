@@ -180,6 +180,10 @@ __device__ __forceinline__ void value_slot(int tl, int* kk, int* slot) {
   if (BITS == 3) {   // natural order: k-step tl / 4, slot tl % 4
     *kk = tl >> 2;
     *slot = tl & 3;
+  } else if (BITS == 8) {   // a dword's bytes 0, 2 then 1, 3: tokens 4k, 4k + 2, 4k + 1, 4k + 3
+    const int j = tl & 3;
+    *kk = tl >> 2;
+    *slot = ((j & 1) << 1) | (j >> 1);
   } else if (BITS == 4) {
     const int i = tl >> 3, r = tl & 7, j = r & 3, hp = r >> 2;
     *kk = 2 * i + (j >> 1);
@@ -319,7 +323,13 @@ __device__ __forceinline__ void load_tile(TileRaw<BITS, BLOCK>& r, const TilePos
     const uint8_t* vt = vpair + (int64_t)(gg ? tp.s1 : tp.s0) * TB;
     for (int hf = 0; hf < 2; ++hf) {
       const uint8_t* src = vt + (lane + 64 * hf) * VROW;
-      if constexpr (BITS == 3) {
+      if constexpr (BITS == 8) {
+        for (int hv = 0; hv < 2; ++hv) {
+          const uint4 x = ok ? *reinterpret_cast<const uint4*>(src + 16 * hv) : make_uint4(0, 0, 0, 0);
+          r.vc[gg][hf][4 * hv] = x.x; r.vc[gg][hf][4 * hv + 1] = x.y;
+          r.vc[gg][hf][4 * hv + 2] = x.z; r.vc[gg][hf][4 * hv + 3] = x.w;
+        }
+      } else if constexpr (BITS == 3) {
         const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
         r.vc[gg][hf][0] = ok ? s32[0] : 0u; r.vc[gg][hf][1] = ok ? s32[1] : 0u; r.vc[gg][hf][2] = ok ? s32[2] : 0u;
       } else if (BITS == 4) {
@@ -430,7 +440,13 @@ __device__ __forceinline__ void stage_read(TileRaw<BITS, BLOCK>& r, const uint8_
   for (int gg = 0; gg < 2; ++gg)
     for (int hf = 0; hf < 2; ++hf) {
       const uint8_t* src = st + 2 * TB + gg * TB + (lane + 64 * hf) * VROW;
-      if constexpr (BITS == 3) {
+      if constexpr (BITS == 8) {
+        for (int hv = 0; hv < 2; ++hv) {
+          const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * hv);
+          r.vc[gg][hf][4 * hv] = x.x; r.vc[gg][hf][4 * hv + 1] = x.y;
+          r.vc[gg][hf][4 * hv + 2] = x.z; r.vc[gg][hf][4 * hv + 3] = x.w;
+        }
+      } else if constexpr (BITS == 3) {
         const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
         r.vc[gg][hf][0] = s32[0]; r.vc[gg][hf][1] = s32[1]; r.vc[gg][hf][2] = s32[2];
       } else if (BITS == 4) {
@@ -484,7 +500,7 @@ __device__ __forceinline__ void stage_probs(const float* p, const float* vs, con
   // 16^(j & 1) (4-bit) or 4^(j & 3) (2-bit), j its nibble / crumb position
   // within a 16-bit half of its word; its probability takes the inverse (a
   // power of two: exact)
-  const float inv_f = (TBQ || BITS == 3) ? 1.0f
+  const float inv_f = (TBQ || BITS == 3 || BITS == 8) ? 1.0f
                       : BITS == 4 ? ((tl & 1) ? 1.0f / 16 : 1.0f) : 1.0f / (float)(1 << (2 * (tl & 3)));
   for (int d = 0; d < NDG; ++d)
     for (int m = 0; m < G; ++m) {
@@ -507,6 +523,26 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
   for (int gg = 0; gg < 2; ++gg) {
     for (int hf = 0; hf < 2; ++hf) {
       const int dg = NDG == 1 ? 0 : (gh + 2 * hf);   // the 32-dim slice of channel lane + 64 hf
+      if constexpr (BITS == 8) {
+        // a dword holds tokens 4u .. 4u + 3 of the channel row, one byte
+        // each: bytes 0 and 2 masked in place, bytes 1 and 3 shifted down
+        // (codes n enter as n * 2^-24, no factors)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t x = vc[gg][hf][u];
+          const h4_t bv = as_h4(x & 0x00FF00FFu, (x >> 8) & 0x00FF00FFu);
+          const int ks = 8 * gg + u;
+          for (int hl = 0; hl < HL; ++hl) {
+            const h4_t av = PLw.h4(dg, ks, hl, row);
+            if (hf == 0) {
+              if (u & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
+            } else {
+              if (u & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
+            }
+          }
+        }
+        continue;
+      }
       if constexpr (BITS == 3) {
         // the channel row's 32 tokens as one 96-bit string, token t at bits
         // 3t: k-step q takes tokens 4q .. 4q + 3 in natural order

@@ -68,6 +68,9 @@ __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
       ch[s] = 4 * ks + s;
       inv_f[s] = 1.0f;
     }
+  } else if (BITS == 8) {   // a dword's bytes 0, 2 then 1, 3 (odd bytes shifted down, no factors)
+    ch[0] = 4 * ks; ch[1] = 4 * ks + 2; ch[2] = 4 * ks + 1; ch[3] = 4 * ks + 3;
+    for (int s = 0; s < 4; ++s) inv_f[s] = 1.0f;
   } else if (BITS == 4) {
     const int i = ks >> 1, par = ks & 1;
     const int base = 8 * i + 2 * par;
@@ -110,7 +113,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
   constexpr int NKW = BITS;              // key uint4 loads per token (64 or 32 bytes)
   constexpr int NDG = (BLOCK && !Q40) ? 1 : 4;   // value scale groups per token
-  constexpr float COFF = BITS == 3 ? 4.0f : 8.0f;  // symmetric blocks: stored code offset
+  // symmetric blocks: stored code offset (c + 4 at 3 bits, c + 8 at 4, c + 128 at 8)
+  constexpr float COFF = BITS == 3 ? 4.0f : BITS == 8 ? 128.0f : 8.0f;
   constexpr int TB = 512 * BITS;         // tile bytes
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
@@ -272,8 +276,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
       for (int d = 0; d < NDG; ++d) zsum[d] = wave_sum64(zacc[m][d]);
-      add0[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh] : BLOCK ? -COFF * zsum[0] : zsum[gh];
-      add1[m] = TBQ ? 0.0f : Q40 ? -8.0f * zsum[gh + 2] : BLOCK ? -COFF * zsum[0] : zsum[gh + 2];
+      add0[m] = TBQ ? 0.0f : Q40 ? -COFF * zsum[gh] : BLOCK ? -COFF * zsum[0] : zsum[gh];
+      add1[m] = TBQ ? 0.0f : Q40 ? -COFF * zsum[gh + 2] : BLOCK ? -COFF * zsum[0] : zsum[gh + 2];
     }
     write_partial<G, HL>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, o0, o1, o2, o3, TBQ ? 1.0f : 16777216.0f,
                          add0, add1);
@@ -418,7 +422,13 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       for (int u = 0; u < 4; ++u) {
         const uint32_t xw = dw[u];
         const int i = 4 * j + u;     // canonical dword index of the row
-        if (BITS == 4) {
+        if (BITS == 8) {   // channels 4i .. 4i + 3, one byte each: k-step i
+          const h4_t bk = as_h4(xw & 0x00FF00FFu, (xw >> 8) & 0x00FF00FFu);
+          for (int hl = 0; hl < HL; ++hl) {
+            if (u & 1) acc1 = mfma4(QLw.h4(qh, i, hl, row), bk, acc1);
+            else acc0 = mfma4(QLw.h4(qh, i, hl, row), bk, acc0);
+          }
+        } else if (BITS == 4) {
           const uint32_t x8 = xw >> 8;
           uint32_t lv[4], ll[4];
           if (TBQ) tbq4_levels(xw, lut, lv, ll);
@@ -446,13 +456,15 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
           }
         }
       }
-      if (Q40) {
-        // slice j done: its scale times (q'.codes - 8 sum q), then the next
-        const uint32_t kw2 = j < 2 ? cur.kq4.x : cur.kq4.y;
-        const float ksj = half_bits_to_float((uint16_t)((kw2 >> (16 * (j & 1))) & 0xFFFF));
+      // a 32-channel slice is one 16-byte piece of the row at 4 bits, two at 8
+      if (Q40 && (BITS != 8 || (j & 1))) {
+        // slice sl done: its scale times (q'.codes - offset sum q), then the next
+        const int sl = BITS == 8 ? j >> 1 : j;
+        const uint32_t kw2 = sl < 2 ? cur.kq4.x : cur.kq4.y;
+        const float ksj = half_bits_to_float((uint16_t)((kw2 >> (16 * (sl & 1))) & 0xFFFF));
         for (int m = 0; m < G; ++m) {
           const float dj = (HL == 1) ? acc0[m] + acc0[G + m] + acc1[m] + acc1[G + m] : acc0[m] + acc1[m];
-          sq[m] += ksj * (dj * e_scale_blk - 8.0f * qsum4[m][j]);
+          sq[m] += ksj * (dj * e_scale_blk - COFF * qsum4[m][sl]);
         }
         acc0 = f4_t{0, 0, 0, 0};
         acc1 = f4_t{0, 0, 0, 0};
@@ -493,11 +505,13 @@ int decode_mfma_wgs_per_cu(const Geom& g, int bits) {
   const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_FN(GG, BB, BL) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, BB, BL>)
 #define KVQ_FT(GG) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, 4, true, true>)
-#define KVQ_FQ(GG) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, 4, true, false, true>)
+#define KVQ_FQ(GG, BB) fn = reinterpret_cast<const void*>(&decode_mfma_kernel<GG, BB, true, false, true>)
   if (g.tbq4) {
     if (g.G == 1) KVQ_FT(1); else if (g.G == 2) KVQ_FT(2); else KVQ_FT(4);
+  } else if (g.q40 && bits == 8) {
+    if (g.G == 1) KVQ_FQ(1, 8); else if (g.G == 2) KVQ_FQ(2, 8); else KVQ_FQ(4, 8);
   } else if (g.q40) {
-    if (g.G == 1) KVQ_FQ(1); else if (g.G == 2) KVQ_FQ(2); else KVQ_FQ(4);
+    if (g.G == 1) KVQ_FQ(1, 4); else if (g.G == 2) KVQ_FQ(2, 4); else KVQ_FQ(4, 4);
   } else if (blk && bits == 3) {
     if (g.G == 1) KVQ_FN(1, 3, true); else if (g.G == 2) KVQ_FN(2, 3, true); else KVQ_FN(4, 3, true);
   } else if (blk) {
@@ -546,15 +560,19 @@ hipError_t launch_decode_mfma(const Geom& g, const Planes& p, const ChunkPlan& c
     const bool blk = g.scheme == KVQ_BLOCK128_SYM;
 #define KVQ_MF(GG, BB, BL) hipLaunchKernelGGL((decode_mfma_kernel<GG, BB, BL>), grid, block, 0, s, a)
 #define KVQ_MT(GG) hipLaunchKernelGGL((decode_mfma_kernel<GG, 4, true, true>), grid, block, 0, s, a)
-#define KVQ_MQ(GG) hipLaunchKernelGGL((decode_mfma_kernel<GG, 4, true, false, true>), grid, block, 0, s, a)
+#define KVQ_MQ(GG, BB) hipLaunchKernelGGL((decode_mfma_kernel<GG, BB, true, false, true>), grid, block, 0, s, a)
     if (g.tbq4) {
       if (g.G == 1) KVQ_MT(1);
       else if (g.G == 2) KVQ_MT(2);
       else KVQ_MT(4);
+    } else if (g.q40 && rp.bits == 8) {
+      if (g.G == 1) KVQ_MQ(1, 8);
+      else if (g.G == 2) KVQ_MQ(2, 8);
+      else KVQ_MQ(4, 8);
     } else if (g.q40) {
-      if (g.G == 1) KVQ_MQ(1);
-      else if (g.G == 2) KVQ_MQ(2);
-      else KVQ_MQ(4);
+      if (g.G == 1) KVQ_MQ(1, 4);
+      else if (g.G == 2) KVQ_MQ(2, 4);
+      else KVQ_MQ(4, 4);
     } else if (blk && rp.bits == 3) {
       if (g.G == 1) KVQ_MF(1, 3, true);
       else if (g.G == 2) KVQ_MF(2, 3, true);

@@ -7,6 +7,7 @@
 //   BLOCK128: y = fl32((n - 8) * s_h)  (exact; n - 4 at 3 bits)
 //   TBQ4:     y = fl32(norm * level[n])
 //   Q4_0:     y = fl32((n - 8) * s_h of the value's 32-value slice)  (exact)
+//   Q8_0:     y = fl32((n - 128) * s_h of the value's 32-value slice)  (exact)
 //   window:   the fp16 value.
 #pragma clang fp contract(off)
 
@@ -53,6 +54,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
       if (bits == 3) {
         kn = key_code3(kt, row, d);
         vn = value_code3(vt, d, row);
+      } else if (bits == 8) {   // one byte per code
+        kn = kt[ktile_offset(row, d)];
+        vn = vt[d * 32 + row];
       } else {
         kn = (kt[ktile_offset(row, d >> 1)] >> (4 * (d & 1))) & 15;
         vn = (vt[d * 16 + (row >> 1)] >> (4 * (row & 1))) & 15;
@@ -70,8 +74,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(Geom g, Planes p, int64_t 
         kv = half_bits_to_float(ks[t]) * kl;
         vv = half_bits_to_float(vs[t]) * vl;
       } else if (g.q40) {
-        kv = (float)(kn - 8) * half_bits_to_float(ks[4 * t + (d >> 5)]);
-        vv = (float)(vn - 8) * half_bits_to_float(vs[4 * t + (d >> 5)]);
+        const int off = bits == 8 ? 128 : 8;
+        kv = (float)(kn - off) * half_bits_to_float(ks[4 * t + (d >> 5)]);
+        vv = (float)(vn - off) * half_bits_to_float(vs[4 * t + (d >> 5)]);
       } else {
         const int off = bits == 3 ? 4 : 8;
         kv = (float)(kn - off) * half_bits_to_float(ks[t]);

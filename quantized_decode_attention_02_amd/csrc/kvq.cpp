@@ -53,7 +53,10 @@ kvq_status validate_config(const kvq_config* c) {
     if (c->k_bits == 3 && c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
   } else {
     // 3 bits: the 50-byte block of the format table (symmetric block scheme only)
-    if (c->k_bits != 4 && !(c->k_bits == 3 && c->scheme == KVQ_BLOCK128_SYM)) return KVQ_ERR_UNSUPPORTED;
+    // 8 bits: Q8_0 (and only Q8_0)
+    if ((c->scheme == KVQ_Q8_0) != (c->k_bits == 8)) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_bits != 4 && c->k_bits != 8 && !(c->k_bits == 3 && c->scheme == KVQ_BLOCK128_SYM))
+      return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != 0 || c->int4_window != -1) return KVQ_ERR_UNSUPPORTED;
     if (c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
     // TBQ4's levels assume the near-normal coordinates of a rotated block
@@ -145,7 +148,7 @@ Geom make_geom(const kvq_config* c, int64_t batch, int64_t max_tokens, int64_t l
   g.lo_bits = (c->scheme == KVQ_KIVI_ASYM && c->int4_window >= 0) ? c->low_bits : c->k_bits;
   g.hadamard = c->hadamard;
   g.tbq4 = c->scheme == KVQ_TBQ4;
-  g.q40 = c->scheme == KVQ_Q4_0;
+  g.q40 = c->scheme == KVQ_Q4_0 || c->scheme == KVQ_Q8_0;
   {
     const Tbq4Codebook& cb = tbq4_codebook();
     for (int k = 0; k < 16; ++k) g.cb_level[k] = cb.level[k];
@@ -189,7 +192,7 @@ void plane_sizes(const kvq_config* c, int64_t batch, int64_t max_tokens, uint64_
   } else {
     sz[KVQ_PLANE_K_HI] = pairs * G * 512 * c->k_bits;
     sz[KVQ_PLANE_V_HI] = pairs * G * 512 * c->v_bits;
-    const uint64_t per_token = c->scheme == KVQ_Q4_0 ? 4 : 1;   // fp16 scales
+    const uint64_t per_token = (c->scheme == KVQ_Q4_0 || c->scheme == KVQ_Q8_0) ? 4 : 1;   // fp16 scales
     sz[KVQ_PLANE_K_META] = pairs * G * kGroup * 2 * per_token;
     sz[KVQ_PLANE_V_META] = pairs * G * kGroup * 2 * per_token;
   }

@@ -24,13 +24,14 @@ struct Mask128 {
 // value to every launch.
 struct Geom {
   int B, Hq, Hkv, G;           // G = Hq / Hkv
-  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM / KVQ_TBQ4 / KVQ_Q4_0
+  int scheme;                  // KVQ_KIVI_ASYM / KVQ_BLOCK128_SYM / KVQ_TBQ4 / KVQ_Q4_0 / KVQ_Q8_0
   int hi_bits, lo_bits;
   int hadamard, pre_rope;
   int hsigned;                 // 1: the rotation is randomized (a mask is nonzero)
   Mask128 sign_in, sign_out;   // D_in, D_out of D_out H D_in / sqrt(128)
   int tbq4;                    // 1: KVQ_TBQ4 blocks (norm + Lloyd-Max indices)
-  int q40;                     // 1: KVQ_Q4_0 (four 32-value blocks per token)
+  int q40;                     // 1: four 32-value blocks per token (KVQ_Q4_0 at 4 bits,
+                               // KVQ_Q8_0 at 8 bits)
   float cb_bound[15];          // TBQ4 decision boundaries (fp32 midpoints)
   float cb_level[16];          // TBQ4 levels, ascending
   uint32_t cb_lut[8];          // levels 8..15 (the magnitudes) as hi + lo
@@ -90,7 +91,7 @@ ChunkPlan plan_chunks(const Geom& g);
 
 // Schemes with one 128-value block per token (no window, no tiers).
 __host__ __device__ inline bool block_scheme(int scheme) {
-  return scheme == KVQ_BLOCK128_SYM || scheme == KVQ_TBQ4 || scheme == KVQ_Q4_0;
+  return scheme == KVQ_BLOCK128_SYM || scheme == KVQ_TBQ4 || scheme == KVQ_Q4_0 || scheme == KVQ_Q8_0;
 }
 
 // Launchers (kernels in append.hip, decode.hip, dequant.hip).  Each returns

@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "_lib", "libkvq.so")
 
-KIVI_ASYM, BLOCK128_SYM, TBQ4, Q4_0 = 0, 1, 2, 3
+KIVI_ASYM, BLOCK128_SYM, TBQ4, Q4_0, Q8_0 = 0, 1, 2, 3, 4
 MAX_PLANES = 16
 NUM_PLANES = 9
 PLANE_NAMES = ["K_HI", "V_HI", "K_LO", "V_LO", "K_META", "V_META", "K_WIN", "V_WIN", "ROPE"]
@@ -93,7 +93,8 @@ def _check(status, what):
 
 def make_config(d):
     """kvq_config from a plain dict (keys as in workloads.library_config)."""
-    scheme = {"kivi": KIVI_ASYM, "block128": BLOCK128_SYM, "tbq4": TBQ4, "q4_0": Q4_0}[d["scheme"]]
+    scheme = {"kivi": KIVI_ASYM, "block128": BLOCK128_SYM, "tbq4": TBQ4, "q4_0": Q4_0,
+              "q8_0": Q8_0}[d["scheme"]]
     return Config(head_dim=d.get("head_dim", 128), num_q_heads=d["num_q_heads"],
                   num_kv_heads=d["num_kv_heads"], scheme=scheme, k_bits=d.get("k_bits", 4),
                   v_bits=d.get("v_bits", 4), k_group_tokens=d.get("group", 32),

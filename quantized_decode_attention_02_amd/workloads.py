@@ -113,6 +113,11 @@ WORKLOADS.append(
     dict(id=7, name="block50-3bit-hadamard-gqa32x8-b32-t65536+8192",
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_block128(k_bits=3, v_bits=3), dist="normal", outliers=None))
+# Q8_0-style 32-value blocks (the format table's 8-bit row) at the block-128 shape
+WORKLOADS.append(
+    dict(id=9, name="q8_0-gqa32x8-b32-t65536+8192",
+         batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
+         cfg=_q8_0(), dist="normal", outliers=None))
 # INT3 KIVI (the INT3 cache of [troisinh]'s title) at the Llama-2-7B layer shape
 WORKLOADS.append(
     dict(id=8, name="int3-kivi-llama2-7b-mha32-b8-t32768-outlier2pct-x15",

@@ -71,6 +71,10 @@ def test_config_validation():
     assert status_of(fp16_window=64) == -2
     assert status_of(int4_window=100) == -1
     assert status_of(int4_window=64, k_bits=2, v_bits=2) == -2
+    # Q8_0 takes 8 bits and only Q8_0 does
+    assert status_of(scheme=4, k_bits=8, v_bits=8, fp16_window=0, int4_window=-1) == 0
+    assert status_of(scheme=4, k_bits=4, v_bits=4, fp16_window=0, int4_window=-1) == -2
+    assert status_of(scheme=3, k_bits=8, v_bits=8, fp16_window=0, int4_window=-1) == -2
     # 3-bit KIVI: one tier, keys stored after RoPE
     assert status_of(k_bits=3, v_bits=3) == 0
     assert status_of(k_bits=3, v_bits=3, int4_window=64) == -2

@@ -34,6 +34,7 @@ SCHEDULES = {
     6: [8192] * 9,
     7: [8192] * 9,
     8: [32767, 1],
+    9: [8192] * 9,
 }
 
 

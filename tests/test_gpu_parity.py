@@ -35,6 +35,8 @@ VARIANTS = {
     "tbq4-signed": dict(SIGNS),
     "q4_0": dict(),
     "q4_0-hadamard": dict(hadamard=True),
+    "q8_0": dict(),
+    "q8_0-hadamard-signed": dict(hadamard=True, **SIGNS),
 }
 
 
@@ -46,6 +48,8 @@ def make_w(wid, variant, T, batch=2, hq=8, hkv=2, dist="normal", outliers=None):
         cfg = wl._tbq4(**kw)
     elif variant.startswith("q4_0"):
         cfg = wl._q4_0(**kw)
+    elif variant.startswith("q8_0"):
+        cfg = wl._q8_0(**kw)
     else:
         cfg = wl._kivi(**kw)
     return wl.custom(wid, batch, hq, hkv, T, cfg, dist=dist, outliers=outliers)
@@ -156,7 +160,7 @@ def tie_tokens(rng, T, hkv, q_levels, s, base):
     return kx.astype(np.float16), vx.astype(np.float16)
 
 
-@pytest.mark.parametrize("variant", ["int4", "int2", "block128-plain"])
+@pytest.mark.parametrize("variant", ["int4", "int2", "block128-plain", "q8_0"])
 def test_rounding_ties(variant):
     """Quotients exactly halfway between two codes: the kernels' reciprocal
     fast path must fall back to the division and round to even like the
@@ -165,7 +169,17 @@ def test_rounding_ties(variant):
     from quantized_decode_attention_02_amd import kvq
     T, hkv = 32 * 6 + 128, 2
     s = 3.0 / 32.0   # an fp16 scale that is not a power of two
-    if variant == "block128-plain":
+    if variant == "q8_0":
+        # 8-bit slices: a = 127 s in every 32-value slice, y = (k + 1/2) s with
+        # k in -127 .. 126 (all exact in fp16)
+        rng = np.random.default_rng(8)
+        k = rng.integers(-127, 127, size=(1, T, hkv, 128))
+        y = (k + 0.5) * s
+        y[..., 0::32] = 127 * s
+        K = y.astype(np.float16)
+        V = (-y).astype(np.float16)
+        assert np.all(K.astype(np.float64) == y)
+    elif variant == "block128-plain":
         # symmetric: a = max |y| = 7 s, y = (k + 1/2) s with k in -7 .. 6
         rng = np.random.default_rng(7)
         k = rng.integers(-7, 7, size=(1, T, hkv, 128))
