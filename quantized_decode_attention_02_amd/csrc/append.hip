@@ -149,88 +149,83 @@ __device__ __forceinline__ uint8_t row3_byte(Code code, int cb, int n) {
   return (uint8_t)(w >> sh);
 }
 
-// Six bytes at dst + o0 (o0 even) as three 16-bit stores.
-__device__ __forceinline__ void store6(uint8_t* dst, int o0, const uint8_t* buf) {
-  uint16_t* d16 = reinterpret_cast<uint16_t*>(dst + o0);
-  for (int k = 0; k < 3; ++k) d16[k] = (uint16_t)(buf[2 * k] | (buf[2 * k + 1] << 8));
-}
-
 // Pack codes into the tile byte images (canonical nibble/crumb order: element
 // 2k in the low nibble of byte k; element 4k+j in bits 2j..2j+1; at 3 bits a
 // row is one bit string, row3_byte).
 //   key tile:   token-major rows, byte cb of token t at ktile_offset(t, cb)
 //   value tile: channel-major rows of 32 tokens, row d at d * (4 * bits)
-__device__ void pack_key_tile(const uint8_t (*ck)[kD], uint8_t* dst, int bits, int tid) {
-  const int per_thread = 2 * bits;  // 2048, 1536 or 1024 bytes over 256 threads
-  const int o0 = tid * per_thread;
-  uint8_t buf[8];
-  if (bits == 3) {
-    for (int k = 0; k < 6; ++k) {
-      const int o = o0 + k;
-      const int t = (o & 511) >> 4;
-      const int cb = (o >> 9) * 16 + (o & 15);
-      buf[k] = row3_byte([&](int i) { return ck[t][i]; }, cb, kD);
-    }
-    store6(dst, o0, buf);
-    return;
+// Each of the 256 threads builds 2 * bits consecutive bytes of the tile image
+// in registers (the loops unroll with constant indices) and stores them.
+template <int BITS>
+__device__ __forceinline__ void store_packed(uint8_t* dst, int o0, const uint32_t* w) {
+  if (BITS == 4) {
+    *reinterpret_cast<uint2*>(dst + o0) = make_uint2(w[0], w[1]);
+  } else if (BITS == 2) {
+    *reinterpret_cast<uint32_t*>(dst + o0) = w[0];
+  } else {   // six bytes at an even offset: three 16-bit stores
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst + o0);
+    d16[0] = (uint16_t)w[0];
+    d16[1] = (uint16_t)(w[0] >> 16);
+    d16[2] = (uint16_t)w[1];
   }
-  for (int k = 0; k < per_thread; ++k) {
+}
+
+template <int BITS>
+__device__ __forceinline__ void pack_key_tile_t(const uint8_t (*ck)[kD], uint8_t* dst, int tid) {
+  constexpr int PT = 2 * BITS;   // 2048, 1536 or 1024 bytes over 256 threads
+  const int o0 = tid * PT;
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
     const int o = o0 + k;
     const int t = (o & 511) >> 4;
     const int cb = (o >> 9) * 16 + (o & 15);
     uint32_t v = 0;
-    if (bits == 4) {
+    if (BITS == 4) {
       v = ck[t][2 * cb] | (ck[t][2 * cb + 1] << 4);
-    } else {
+    } else if (BITS == 2) {
       for (int j = 0; j < 4; ++j) v |= (uint32_t)ck[t][4 * cb + j] << (2 * j);
+    } else {
+      v = row3_byte([&](int i) { return ck[t][i]; }, cb, kD);
     }
-    buf[k] = (uint8_t)v;
+    w[k >> 2] |= v << (8 * (k & 3));
   }
-  if (bits == 4) {
-    uint2 w;
-    w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
-    w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
-    *reinterpret_cast<uint2*>(dst + o0) = w;
-  } else {
-    *reinterpret_cast<uint32_t*>(dst + o0) =
-        buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
+  store_packed<BITS>(dst, o0, w);
+}
+
+template <int BITS>
+__device__ __forceinline__ void pack_value_tile_t(const uint8_t (*cv)[kD], uint8_t* dst, int tid) {
+  constexpr int PT = 2 * BITS;
+  constexpr int RB = 4 * BITS;   // bytes per channel row
+  const int o0 = tid * PT;
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int o = o0 + k;
+    const int d = o / RB, kb = o % RB;
+    uint32_t v = 0;
+    if (BITS == 4) {
+      v = cv[2 * kb][d] | (cv[2 * kb + 1][d] << 4);
+    } else if (BITS == 2) {
+      for (int j = 0; j < 4; ++j) v |= (uint32_t)cv[4 * kb + j][d] << (2 * j);
+    } else {
+      v = row3_byte([&](int i) { return cv[i][d]; }, kb, kGroup);
+    }
+    w[k >> 2] |= v << (8 * (k & 3));
   }
+  store_packed<BITS>(dst, o0, w);
+}
+
+__device__ void pack_key_tile(const uint8_t (*ck)[kD], uint8_t* dst, int bits, int tid) {
+  if (bits == 4) pack_key_tile_t<4>(ck, dst, tid);
+  else if (bits == 3) pack_key_tile_t<3>(ck, dst, tid);
+  else pack_key_tile_t<2>(ck, dst, tid);
 }
 
 __device__ void pack_value_tile(const uint8_t (*cv)[kD], uint8_t* dst, int bits, int tid) {
-  const int per_thread = 2 * bits;
-  const int rb = 4 * bits;  // bytes per channel row
-  const int o0 = tid * per_thread;
-  uint8_t buf[8];
-  if (bits == 3) {
-    for (int k = 0; k < 6; ++k) {
-      const int o = o0 + k;
-      const int d = o / rb, kb = o % rb;
-      buf[k] = row3_byte([&](int i) { return cv[i][d]; }, kb, kGroup);
-    }
-    store6(dst, o0, buf);
-    return;
-  }
-  for (int k = 0; k < per_thread; ++k) {
-    const int o = o0 + k;
-    const int d = o / rb, kb = o % rb;
-    uint32_t v = 0;
-    if (bits == 4) {
-      v = cv[2 * kb][d] | (cv[2 * kb + 1][d] << 4);
-    } else {
-      for (int j = 0; j < 4; ++j) v |= (uint32_t)cv[4 * kb + j][d] << (2 * j);
-    }
-    buf[k] = (uint8_t)v;
-  }
-  if (bits == 4) {
-    uint2 w;
-    w.x = buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
-    w.y = buf[4] | (buf[5] << 8) | (buf[6] << 16) | ((uint32_t)buf[7] << 24);
-    *reinterpret_cast<uint2*>(dst + o0) = w;
-  } else {
-    *reinterpret_cast<uint32_t*>(dst + o0) =
-        buf[0] | (buf[1] << 8) | (buf[2] << 16) | ((uint32_t)buf[3] << 24);
-  }
+  if (bits == 4) pack_value_tile_t<4>(cv, dst, tid);
+  else if (bits == 3) pack_value_tile_t<3>(cv, dst, tid);
+  else pack_value_tile_t<2>(cv, dst, tid);
 }
 
 __device__ __forceinline__ uint8_t* hi_tile(const Geom& g, const Planes& p, int plane,
