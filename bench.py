@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "4467ffc66c7fa4d3cd87298cb0d3bae8753c07e5b3f98b4c50fa9e2f5232401c", "fetch_kib": 665043, "write_kib": 4210,
+    1: {"sources_sha256": "095cfa77418acd3dbf2772a23cdda1db438dfb688cd11fccff0e808db3f8f91b", "fetch_kib": 664620, "write_kib": 4209,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
