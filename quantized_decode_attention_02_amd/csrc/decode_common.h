@@ -64,6 +64,7 @@ struct MfmaArgs {
   int64_t team;         // waves per pair; also the range's partial slots per query head
   int64_t chunk;        // tiles per chunk
   int64_t n_chunks;     // chunks per pair, >= team
+  int64_t n_big;        // chunks [0, n_big) have `chunk` tiles, later ones one tile
   int64_t pwgs;         // work-groups of the quantized tiles
   int64_t slot_base;    // first partial slot of this range
   int64_t wins;         // work-groups of the fp16 window (0 or pairs), launched first
@@ -268,13 +269,25 @@ struct TileCursor {
   uint32_t pend;      // the claim in flight
 };
 
+// Tiles [t, t_stop) of chunk ch: chunks of `chunk` tiles, then single tiles,
+// so that the last claims of a pair are short and its members finish close
+// together.
+__device__ __forceinline__ void chunk_range(const MfmaArgs& a, int64_t ch, int64_t* t, int64_t* t_stop) {
+  if (ch < a.n_big) {
+    *t = ch * a.chunk;
+    *t_stop = min(*t + a.chunk, a.tiles_pp);
+  } else {
+    *t = a.n_big * a.chunk + (ch - a.n_big);
+    *t_stop = *t + 1;
+  }
+}
+
 // First tile of assignment asg: the member's own chunk; its first claim
 // goes out at once.
 __device__ __forceinline__ void cursor_start(const MfmaArgs& a, int64_t asg, TileCursor& c, int lane) {
   c.asg = asg;
   team_member(a, asg, &c.pair, &c.k);
-  c.t = c.k * a.chunk;
-  c.t_stop = min(c.t + a.chunk, a.tiles_pp);
+  chunk_range(a, c.k, &c.t, &c.t_stop);
   c.pend = claim_issue(a.ctr + c.pair * kCounterStride, lane);
 }
 
@@ -290,8 +303,7 @@ __device__ __forceinline__ bool cursor_next(const MfmaArgs& a, TileCursor& c, in
   const int64_t got = claim_value(c.pend);
   const int64_t ch = a.team + got;
   if (ch < a.n_chunks) {
-    c.t = ch * a.chunk;
-    c.t_stop = min(c.t + a.chunk, a.tiles_pp);
+    chunk_range(a, ch, &c.t, &c.t_stop);
     c.pend = claim_issue(a.ctr + c.pair * kCounterStride, lane);
     return true;
   }

@@ -365,6 +365,7 @@ hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& c
     a.team = rp.team;
     a.chunk = rp.chunk;
     a.n_chunks = rp.n_chunks;
+    a.n_big = rp.n_big;
     a.pwgs = rp.pwgs;
     a.slot_base = rp.slot_base;
     a.wins = wins;

@@ -254,8 +254,10 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 // no larger than its pair's tile count.  Chunks are one tile, or two where
 // every member gets at least 8 chunks on average, so that a claim has a
 // tile's time to come back; teams above 2 * kTeamPerChunkTile waves take
-// team / kTeamPerChunkTile tiles per chunk.  The fp16 window rides on the
-// last launch: one more work-group per pair.
+// team / kTeamPerChunkTile tiles per chunk.  The last team tiles of a pair
+// go as single-tile chunks, so that its members' last claims are short and
+// they finish close together.  The fp16 window rides on the last launch:
+// one more work-group per pair.
 #ifndef KVQ_DECODE_CHUNK_MIN
 #define KVQ_DECODE_CHUNK_MIN 1
 #endif
@@ -270,6 +272,10 @@ constexpr int64_t kMinTilesPerWave = KVQ_MIN_TILES_PER_WAVE;
 #define KVQ_TEAM_PER_CHUNK_TILE 16
 #endif
 constexpr int64_t kTeamPerChunkTile = KVQ_TEAM_PER_CHUNK_TILE;
+// Single-tile chunks at the end of a pair's range, per team member.
+#ifndef KVQ_DECODE_TAIL_TILES_PER_MEMBER
+#define KVQ_DECODE_TAIL_TILES_PER_MEMBER 1
+#endif
 
 int occupancy_wgs_per_cu(const void* kernel) {
   static std::mutex mu;
@@ -314,6 +320,7 @@ ChunkPlan plan_chunks(const Geom& g) {
     r.team = 0;
     r.chunk = 1;
     r.n_chunks = 0;
+    r.n_big = 0;
     if (r.tiles_pp > 0) {
       const int per_cu = g.pre_rope ? decode_rope_wgs_per_cu(g, bits) : decode_mfma_wgs_per_cu(g, bits);
       const int64_t cap = 4 * (int64_t)per_cu * device_compute_units();   // waves
@@ -327,7 +334,11 @@ ChunkPlan plan_chunks(const Geom& g) {
       // often than its atomics can be served
       const int64_t wide = team / kTeamPerChunkTile;
       if (wide > r.chunk && r.tiles_pp >= 8 * team * wide) r.chunk = wide;
-      r.n_chunks = (r.tiles_pp + r.chunk - 1) / r.chunk;
+      // the last team * KVQ_DECODE_TAIL_TILES_PER_MEMBER tiles (or fewer) go
+      // as single-tile chunks
+      const int64_t tail = r.chunk > 1 ? team * KVQ_DECODE_TAIL_TILES_PER_MEMBER : 0;
+      r.n_big = r.tiles_pp > tail ? (r.tiles_pp - tail) / r.chunk : 0;
+      r.n_chunks = r.n_big + (r.tiles_pp - r.n_big * r.chunk);
       if (team > r.n_chunks) team = r.n_chunks;
       r.team = team;
       const int64_t waves = pairs * team < cap ? pairs * team : cap;

@@ -61,6 +61,7 @@ struct RangePlan {
   int64_t team;        // waves per pair = partial slots per query head
   int64_t chunk;       // tiles per chunk
   int64_t n_chunks;    // chunks per pair (>= team)
+  int64_t n_big;       // chunks [0, n_big) hold `chunk` tiles, the rest one tile each
   int64_t pwgs;        // work-groups of the quantized tiles
   int64_t slot_base;   // first partial slot
   int window;          // 1: this launch also attends the fp16 window (one
