@@ -237,7 +237,7 @@ struct TileRaw {
   uint4 kmr;        // KIVI, keys before RoPE: (s, z) of channels 4 (lane % 32) .. + 3
   uint4 vm;         // KIVI: (s, z) x 4 of this lane's token
   uint16_t ks16, vs16;   // BLOCK: per-token scales
-  uint2 kq4, vq4;        // BLOCK, Q4_0: the four 32-value slice scales of the token
+  uint2 kq4, vq4;        // BLOCK, Q4_0 / Q8_0: the four 32-value slice scales of the token
 };
 
 struct TilePos {
@@ -480,7 +480,7 @@ __device__ __forceinline__ void wait_stage_read() { asm volatile("s_waitcnt lgkm
 template <int BITS, bool BLOCK, int NDG, bool Q40 = false>
 __device__ __forceinline__ void value_meta(const TileRaw<BITS, BLOCK>& r, bool tok_ok, float* vs,
                                            float* vz) {
-  if (BLOCK && Q40) {   // a scale per 32-dim slice; the code offset 8 comes back in the flush
+  if (BLOCK && Q40) {   // a scale per 32-dim slice; the code offset (8 or 128) comes back in the flush
     const uint32_t vw[2] = {r.vq4.x, r.vq4.y};
     for (int d = 0; d < NDG; ++d) {
       const uint16_t h = (uint16_t)((vw[d >> 1] >> (16 * (d & 1))) & 0xFFFF);

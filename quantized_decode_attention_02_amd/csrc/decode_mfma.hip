@@ -88,7 +88,8 @@ __device__ __forceinline__ void key_quad(int ks, int* ch, float* inv_f) {
 
 // The KIVI G = 4 kernels keep a wave's fp32 query in its probability table
 // (the query is read only while an assignment opens, and every tile rewrites
-// the whole table), which saves 8 KiB of LDS per work-group.
+// every entry the value MFMAs read; the pads are never read), which saves
+// 8 KiB of LDS per work-group.
 template <int G, bool BLOCK>
 constexpr bool query_in_prob_table() {
   return G == 4 && !BLOCK;
@@ -105,9 +106,10 @@ constexpr int decode_min_waves() {
 // TBQ (with BLOCK): TBQ4 blocks; codes become their fp16 levels through
 // tbq4_levels() instead of entering as subnormals, and the block scale is the
 // norm, so there is neither a code offset nor a position factor.
-// Q40 (with BLOCK): Q4_0 blocks; every token has a scale per 32-value slice,
-// so key scores are summed slice by slice (a slice is one uint4 of the key
-// row) and values use four scale groups, as KIVI's per-token values do.
+// Q40 (with BLOCK): Q4_0 (BITS = 4) or Q8_0 (BITS = 8) blocks; every token
+// has a scale per 32-value slice, so key scores are summed slice by slice (a
+// slice is one uint4 of the key row at 4 bits, two at 8) and values use four
+// scale groups, as KIVI's per-token values do.
 template <int G, int BITS, bool BLOCK, bool TBQ = false, bool Q40 = false>
 __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void decode_mfma_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // MFMAs per k-step (hi/lo)
