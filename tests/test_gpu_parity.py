@@ -86,12 +86,15 @@ def test_streaming(variant, stream):
     check_decode(g, o, w, s, h)
 
 
-@pytest.mark.parametrize("variant", ["int4", "int3"])
+@pytest.mark.parametrize("variant", ["int4", "int3", "block128-3bit", "tbq4-signed", "q4_0", "q8_0"])
 @pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 1), (8, 8)])
 def test_gqa_shapes(hq, hkv, variant):
+    # every query-group size (1, 2, 4) of every decode kernel family
     w = make_w(3000 + hq * 10 + hkv, variant, 777, batch=3, hq=hq, hkv=hkv)
+    say(f"gqa {variant} hq={hq} hkv={hkv}")
     g, o, s, h = build_pair(w, [777])
     compare_planes(g, o, s, h)
+    compare_dequant(g, o, s, h)
     check_decode(g, o, w, s, h)
 
 
@@ -160,7 +163,7 @@ def tie_tokens(rng, T, hkv, q_levels, s, base):
     return kx.astype(np.float16), vx.astype(np.float16)
 
 
-@pytest.mark.parametrize("variant", ["int4", "int2", "block128-plain", "q8_0"])
+@pytest.mark.parametrize("variant", ["int4", "int3", "int2", "block128-plain", "q8_0"])
 def test_rounding_ties(variant):
     """Quotients exactly halfway between two codes: the kernels' reciprocal
     fast path must fall back to the division and round to even like the
@@ -189,7 +192,7 @@ def test_rounding_ties(variant):
         V = (-y).astype(np.float16)
         assert np.all(K.astype(np.float64) == y)
     else:
-        q = 15 if variant == "int4" else 3
+        q = {"int4": 15, "int3": 7, "int2": 3}[variant]
         K, V = tie_tokens(np.random.default_rng(5), T, hkv, q, s, base=-0.75)
     w = make_w(3000, variant, T, batch=1, hq=2 * hkv, hkv=hkv)
     cfg = wl.library_config(w)
