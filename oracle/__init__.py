@@ -27,7 +27,8 @@ Sources (the pages this oracle restates; sections are the pages' own headings):
 Modules:
   tiers      -- which tokens are fp16 / high-bit / low-bit for a cache length
   hadamard   -- fixed-order fp32 FWHT-128 and the dense fp64 Sylvester matrix
-  quant      -- asymmetric group quantizer, symmetric 128-block quantizer, dequant
+  quant      -- asymmetric group quantizer (4, 3, 2 bits), symmetric 128-block
+                quantizer (4, 3 bits), symmetric 32-value blocks (Q4_0, Q8_0), dequant
   codebook   -- TBQ4: Lloyd-Max levels of N(0, 1/sqrt(128)), norm + index blocks
   layout     -- the documented byte image of every cache plane, plane sizes
   attention  -- fp64 split-half RoPE and scaled-dot-product decode attention
