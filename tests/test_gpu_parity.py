@@ -264,3 +264,35 @@ def test_workspace_counters_left_zero(variant):
     assert torch.allclose(out3, ref, rtol=1e-4, atol=1e-5)
     assert torch.allclose(out2, g2.decode(q2), rtol=1e-4, atol=1e-5)
     say(f"workspace counters {variant}: clean")
+
+
+@pytest.mark.parametrize("variant", ["int4", "int3", "int2", "mixed-hadamard", "block128-plain",
+                                     "block128-3bit-plain", "tbq4", "q4_0", "q8_0"])
+def test_extreme_magnitudes(variant):
+    """Tokens whose magnitudes span fp16 from the subnormal range (1e-6) to
+    ~1e4, all-zero tokens and constant tokens: scales that are fp16
+    subnormals or large, norms that clamp at 65504 (TBQ4), degenerate groups.
+    Planes and dequant bit-exact, attention within tolerance."""
+    from oracle.cache import OracleCache
+    from quantized_decode_attention_02_amd import kvq
+    T, hkv = 32 * 8 + 128 + 7, 2
+    rng = np.random.default_rng(41)
+    mag = 10.0 ** rng.uniform(-6.0, 3.5, size=(1, T, hkv, 1))
+    K = rng.standard_normal((1, T, hkv, 128)) * mag
+    V = rng.standard_normal((1, T, hkv, 128)) * 10.0 ** rng.uniform(-6.0, 3.5, size=(1, T, hkv, 1))
+    K[:, 5], V[:, 9] = 0.0, 0.0                      # all-zero tokens
+    K[:, 40], V[:, 41] = 0.5, -2.0                   # constant tokens
+    K[:, 64:96, :, 7] = 1e-7                         # a channel group in the subnormal range
+    K, V = K.astype(np.float16), V.astype(np.float16)
+    assert np.all(np.isfinite(K)) and np.all(np.isfinite(V))
+    w = make_w(3700, variant, T, batch=1, hq=2 * hkv, hkv=hkv)
+    cfg = wl.library_config(w)
+    g = kvq.KVCache(cfg, 1, T)
+    g.append(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda())
+    o = OracleCache(cfg, 1, T)
+    o.append(K, V)
+    torch.cuda.synchronize()
+    say(f"extreme magnitudes {variant}")
+    compare_planes(g, o, [0], list(range(hkv)))
+    compare_dequant(g, o, [0], list(range(hkv)))
+    check_decode(g, o, w, [0], list(range(hkv)))
