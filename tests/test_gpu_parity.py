@@ -296,3 +296,57 @@ def test_extreme_magnitudes(variant):
     compare_planes(g, o, [0], list(range(hkv)))
     compare_dequant(g, o, [0], list(range(hkv)))
     check_decode(g, o, w, [0], list(range(hkv)))
+
+
+@pytest.mark.parametrize("variant", ["int4", "mixed-hadamard", "int4-prerope", "q4_0"])
+def test_graph_replay_matches_eager(variant):
+    """A decode step (append one token, split-K partials, merge) captured in a
+    HIP graph and replayed: the library records only its own kernels (no
+    allocation, memset or synchronization), so every replay must give the
+    eager step's planes and output.  Replays are interleaved with eager work
+    and synchronizations; outputs agree to 1e-4 relative (dynamic chunk claims
+    regroup the fp32 sums), planes bit for bit."""
+    from quantized_decode_attention_02_amd import kvq
+    T = 4096 + 33
+    w = make_w(3800, variant, T, batch=2, hq=8, hkv=2)
+    g, o, s, h = build_pair(w, [T - 1, 1])
+    K1, V1 = wl.kv_tokens(w, T - 1, T)
+    k1, v1 = torch.from_numpy(K1).cuda(), torch.from_numpy(V1).cuda()
+    q = torch.from_numpy(wl.queries(w)).cuda()
+    ws = g.new_workspace()
+    out = torch.empty((w["batch"], w["num_q_heads"], 128), dtype=torch.float32, device="cuda")
+
+    def step():
+        g.length = T - 1
+        g.append(k1, v1)
+        g.decode(q, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    planes = [p.clone() if p is not None else None for p in g.planes]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    say(f"graph replay {variant}")
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.allclose(out, ref, rtol=1e-4, atol=1e-5), f"replay {rep}: output differs from eager"
+        for a, b in zip(planes, g.planes):
+            if a is not None:
+                assert torch.equal(a, b), f"replay {rep}: planes differ"
+        eager = g.decode(q)                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.allclose(eager, ref, rtol=1e-4, atol=1e-5)
+    g.length = T
+    check_decode(g, o, w, s, h)
