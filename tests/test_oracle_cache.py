@@ -83,25 +83,31 @@ def test_chunking_invariance(scheme, kw):
     assert np.array_equal(ka, kb) and np.array_equal(va, vb)
 
 
-def test_demotion_requantizes_from_high_bit_values():
-    w = small_workload(901, "kivi", 128 + 96 + 32, hi_window=64)
+@pytest.mark.parametrize("lo", [2, 3])
+def test_demotion_requantizes_from_high_bit_values(lo):
+    # an INT4 window over an INT2 or INT3 low tier
+    w = small_workload(901, "kivi", 128 + 96 + 32, hi_window=64, low_bits=lo)
     K, V = wl.kv_tokens(w, 0, w["tokens"])
     oc = OracleCache(wl.library_config(w), 2, 512)
     oc.append(K[:, :128 + 96], V[:, :128 + 96])        # Tq = 96: groups 0,1,2; hi = 1,2
-    assert list(oc.bits[:3]) == [2, 4, 4]
+    assert list(oc.bits[:3]) == [lo, 4, 4]
     k4 = quant.dequant_k_group(oc.k_codes[:, :, 1], oc.k_s[:, :, 1], oc.k_z[:, :, 1])
     v4 = quant.dequant_v_group(oc.v_codes[:, :, 1], oc.v_s[:, :, 1], oc.v_z[:, :, 1])
     oc.append(K[:, 128 + 96:], V[:, 128 + 96:])        # Tq = 128: group 1 demoted
-    assert list(oc.bits[:4]) == [2, 2, 4, 4]
-    ck, sk, zk = quant.quant_k_group(k4, 2)
-    cv, sv, zv = quant.quant_v_group(v4, 2)
+    assert list(oc.bits[:4]) == [lo, lo, 4, 4]
+    ck, sk, zk = quant.quant_k_group(k4, lo)
+    cv, sv, zv = quant.quant_v_group(v4, lo)
     assert np.array_equal(oc.k_codes[:, :, 1], ck) and np.array_equal(oc.k_s[:, :, 1], sk)
     assert np.array_equal(oc.v_codes[:, :, 1], cv) and np.array_equal(oc.v_z[:, :, 1], zv)
+    assert oc.k_codes[:, :, 1].max() <= 2 ** lo - 1
     # a one-shot build quantizes group 1 straight from its source instead
     one = OracleCache(wl.library_config(w), 2, 512)
     one.append(K, V)
     src = one._source_rows(np.transpose(K, (0, 2, 1, 3))[:, :, 32:64])
-    assert np.array_equal(one.k_codes[:, :, 1], quant.quant_k_group(src, 2)[0])
+    assert np.array_equal(one.k_codes[:, :, 1], quant.quant_k_group(src, lo)[0])
+    # the low-bit planes hold lo-bit tiles: 512 * lo bytes per group
+    sz = layout.plane_sizes(wl.library_config(w) | {"window": 128}, 2, 512)
+    assert sz[layout.K_LO] == 2 * 2 * layout.gmax(512) * 512 * lo
 
 
 def test_window_is_exact_and_quantized_part_close():
