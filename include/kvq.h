@@ -56,7 +56,8 @@ typedef enum kvq_status {
  *   Tq = max(0, floor((length - 128) / 32) * 32).  Codes have 4, 3 or 2
  *   bits (the INT4 / INT3 caches of [troisinh] "KV Cache Quantization - Nén
  *   cache INT4/INT3"); 3-bit rows are one little-endian bit string (code c at
- *   bits 3c), 3-bit caches have one tier and keys stored after RoPE.
+ *   bits 3c); 3-bit codes (a 3-bit cache, or the older tier below an INT4
+ *   window) need keys stored after RoPE.
  * KVQ_BLOCK128_SYM: each token's 128-value head vector is one block of an
  *   fp16 scale and 128 symmetric 4-bit codes, 66 bytes, 4.125 bits per value
  *   ([trefon] "Przykład: model 27B przy 262K"); every token is quantized.
@@ -137,7 +138,7 @@ typedef struct kvq_config {
                              quantized tokens keep k_bits (4) and older ones
                              drop to low_bits ([troisinh] "Ý tưởng cốt lõi",
                              "Mixed Precision").  Block schemes: -1. */
-  int32_t low_bits;       /* 2 (used only when int4_window >= 0) */
+  int32_t low_bits;       /* 2 or 3 (used only when int4_window >= 0) */
   int32_t hadamard;       /* 1: rotate each 128-vector by H_128/sqrt(128)
                              (Sylvester order, fixed fp32 butterfly order
                              h = 1,2,...,64) before quantizing ([troisinh]

@@ -48,9 +48,12 @@ kvq_status validate_config(const kvq_config* c) {
   if (c->scheme == KVQ_KIVI_ASYM) {
     if (c->k_bits != 4 && c->k_bits != 3 && c->k_bits != 2) return KVQ_ERR_UNSUPPORTED;
     if (c->fp16_window != kWindow) return KVQ_ERR_UNSUPPORTED;
-    if (c->int4_window >= 0 && (c->k_bits != 4 || c->low_bits != 2)) return KVQ_ERR_UNSUPPORTED;
-    // 3-bit KIVI: one tier, keys stored after RoPE (or rotated)
-    if (c->k_bits == 3 && c->pre_rope_keys) return KVQ_ERR_UNSUPPORTED;
+    // tiers: INT4 newest, INT2 or INT3 older
+    if (c->int4_window >= 0 && (c->k_bits != 4 || (c->low_bits != 2 && c->low_bits != 3)))
+      return KVQ_ERR_UNSUPPORTED;
+    // 3-bit codes (a 3-bit cache or a 3-bit low tier): keys stored after RoPE (or rotated)
+    if ((c->k_bits == 3 || (c->int4_window >= 0 && c->low_bits == 3)) && c->pre_rope_keys)
+      return KVQ_ERR_UNSUPPORTED;
   } else {
     // 3 bits: the 50-byte block of the format table (symmetric block scheme only)
     // 8 bits: Q8_0 (and only Q8_0)

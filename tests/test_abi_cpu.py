@@ -75,10 +75,14 @@ def test_config_validation():
     assert status_of(scheme=4, k_bits=8, v_bits=8, fp16_window=0, int4_window=-1) == 0
     assert status_of(scheme=4, k_bits=4, v_bits=4, fp16_window=0, int4_window=-1) == -2
     assert status_of(scheme=3, k_bits=8, v_bits=8, fp16_window=0, int4_window=-1) == -2
-    # 3-bit KIVI: one tier, keys stored after RoPE
+    # 3-bit KIVI: a 3-bit cache or a 3-bit tier below the INT4 window, keys
+    # stored after RoPE
     assert status_of(k_bits=3, v_bits=3) == 0
     assert status_of(k_bits=3, v_bits=3, int4_window=64) == -2
     assert status_of(k_bits=3, v_bits=3, pre_rope_keys=1, rope_theta=1e4) == -2
+    assert status_of(int4_window=64, low_bits=3) == 0
+    assert status_of(int4_window=64, low_bits=1) == -2
+    assert status_of(int4_window=64, low_bits=3, pre_rope_keys=1, rope_theta=1e4) == -2
     assert status_of(scheme=7) == -1
     assert status_of(hadamard=2) == -1
     assert status_of(hadamard=1, pre_rope_keys=1) == -2

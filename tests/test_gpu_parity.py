@@ -25,6 +25,8 @@ VARIANTS = {
     "int4-prerope": dict(pre_rope=True, rope_theta=500000.0),
     "mixed-hadamard": dict(hadamard=True, hi_window=96),
     "mixed": dict(hi_window=64),
+    "mixed-int3": dict(hi_window=64, low_bits=3),
+    "mixed-int3-hadamard-signed": dict(hadamard=True, hi_window=96, low_bits=3, **SIGNS),
     "mixed-hadamard-signed": dict(hadamard=True, hi_window=96, **SIGNS),
     "block128": None,
     "block128-plain": dict(hadamard=False),
