@@ -118,6 +118,11 @@ WORKLOADS.append(
     dict(id=9, name="q8_0-gqa32x8-b32-t65536+8192",
          batch=32, num_q_heads=32, num_kv_heads=8, tokens=65536 + 8192, prefill=8192,
          cfg=_q8_0(), dist="normal", outliers=None))
+# the mixed-precision long-context shape with its older tier at INT3 instead of INT2
+WORKLOADS.append(
+    dict(id=10, name="int4x4096-int3-hadamard-gqa32x8-b4-t262144-student3",
+         batch=4, num_q_heads=32, num_kv_heads=8, tokens=262144, prefill=0,
+         cfg=_kivi(hadamard=True, hi_window=4096, low_bits=3), dist="student3", outliers=None))
 # INT3 KIVI (the INT3 cache of [troisinh]'s title) at the Llama-2-7B layer shape
 WORKLOADS.append(
     dict(id=8, name="int3-kivi-llama2-7b-mha32-b8-t32768-outlier2pct-x15",

@@ -35,6 +35,7 @@ SCHEDULES = {
     7: [8192] * 9,
     8: [32767, 1],
     9: [8192] * 9,
+    10: [131072, 131032] + [1] * 40,
 }
 
 
