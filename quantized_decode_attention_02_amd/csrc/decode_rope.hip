@@ -63,6 +63,41 @@ constexpr int key_scale_shift(int c) {
   return BITS == 4 ? 24 - 4 * (c & 1) : 24 - 2 * (c & 3);
 }
 
+// Code k of a key word (channel CPW i + k) as an exact fp32 integer: the
+// codes are moved to byte boundaries (nibbles: k even in the low nibbles,
+// odd in the high ones; crumbs: k mod 4 selects the shift) and converted a
+// byte at a time (v_cvt_f32_ubyte).
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) {   // byte B of v as fp32 (pure ALU)
+  float r;
+  if (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+  else if (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+  else if (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+template <int BITS, int K>
+__device__ __forceinline__ float key_int(uint32_t w) {
+  constexpr int SH = BITS == 4 ? 4 * (K & 1) : 2 * (K & 3);
+  constexpr int BYTE = BITS == 4 ? (K >> 1) : (K >> 2);
+  const uint32_t src = (w >> SH) & (BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u);
+  return ubyte_f32<BYTE>(src);
+}
+template <int BITS>
+__device__ __forceinline__ void codes_int(uint32_t w, float* n) {
+  constexpr int CPW = 32 / BITS;
+  if constexpr (BITS == 4) {
+    n[0] = key_int<4, 0>(w); n[1] = key_int<4, 1>(w); n[2] = key_int<4, 2>(w); n[3] = key_int<4, 3>(w);
+    n[4] = key_int<4, 4>(w); n[5] = key_int<4, 5>(w); n[6] = key_int<4, 6>(w); n[7] = key_int<4, 7>(w);
+  } else {
+    n[0] = key_int<2, 0>(w); n[1] = key_int<2, 1>(w); n[2] = key_int<2, 2>(w); n[3] = key_int<2, 3>(w);
+    n[4] = key_int<2, 4>(w); n[5] = key_int<2, 5>(w); n[6] = key_int<2, 6>(w); n[7] = key_int<2, 7>(w);
+    n[8] = key_int<2, 8>(w); n[9] = key_int<2, 9>(w); n[10] = key_int<2, 10>(w); n[11] = key_int<2, 11>(w);
+    n[12] = key_int<2, 12>(w); n[13] = key_int<2, 13>(w); n[14] = key_int<2, 14>(w); n[15] = key_int<2, 15>(w);
+  }
+  (void)CPW;
+}
+
 template <int G, int BITS>
 __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // value-side MFMAs per k-step (hi/lo of p')
@@ -75,7 +110,9 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   // are padded by 16 bytes so that the rows one read gathers (group and head
   // of QA, group of KSZ) fall in different banks.
   __shared__ __attribute__((aligned(16))) float QA[4][2][4][kD + 4];   // [wave][group][head][channel]
-  __shared__ __attribute__((aligned(16))) float KSZ[4][2][65][4];      // [wave][group][j]: s_j, s_j+64, z_j, z_j+64
+  // [wave][group][j]: the fp16 (s, z) words of channels j and j + 64, as
+  // stored; 66 rows so that the two groups' rows fall in different banks
+  __shared__ __attribute__((aligned(16))) uint32_t KSZ[4][2][66][2];
   using PTab = ATab<HL, 16, G == 4, G == 4>;
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
 
@@ -273,14 +310,12 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     float vs[NDG], vz[NDG];
     value_meta<BITS, false, NDG>(c, tok_ok, vs, vz);
 
-    // key (s, z) of both groups into KSZ (channel ch -> pair ch mod 64, half ch / 64)
+    // key (s, z) words of both groups into KSZ (channel ch -> pair ch mod 64, half ch / 64)
     {
       const uint32_t mw[4] = {c.kmr.x, c.kmr.y, c.kmr.z, c.kmr.w};
       for (int e = 0; e < 4; ++e) {
-        const int ch = 4 * tl + e;   // ch & 3 == e
-        KSZ[w][gh][ch & 63][ch >> 6] =
-            half_bits_to_float((uint16_t)(mw[e] & 0xFFFF)) * (float)(1 << key_scale_shift<BITS>(e));
-        KSZ[w][gh][ch & 63][2 + (ch >> 6)] = half_bits_to_float((uint16_t)(mw[e] >> 16));
+        const int ch = 4 * tl + e;
+        KSZ[w][gh][ch & 63][ch >> 6] = mw[e];
       }
     }
     build_query_rows(c_rows);   // its wave barrier also covers KSZ
@@ -294,16 +329,20 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 2 * BITS; ++i) {   // words of channels [CPW i, CPW (i + 1)) and 64 + ...
-      h2_t pl[CPW / 2], ph[CPW / 2];
-      for (int pp = 0; pp < CPW / 2; ++pp) {
-        pl[pp] = key_part<BITS>(kw[i], pp);
-        ph[pp] = key_part<BITS>(kw[i + 2 * BITS], pp);
-      }
       float xl[CPW], xh[CPW];
-      for (int k = 0; k < CPW; ++k) {
-        const float4 sz = *reinterpret_cast<const float4*>(&KSZ[w][gh][CPW * i + k][0]);
-        xl[k] = __builtin_fmaf((float)key_code<BITS>(pl, k), sz.x, sz.z);   // exact product, one rounding
-        xh[k] = __builtin_fmaf((float)key_code<BITS>(ph, k), sz.y, sz.w);
+      float nl[CPW], nh[CPW];   // the codes as exact fp32 integers
+      codes_int<BITS>(kw[i], nl);
+      codes_int<BITS>(kw[i + 2 * BITS], nh);
+      for (int k = 0; k < CPW; k += 2) {
+        // the (s, z) words of channels k, k + 1 and their partners k + 64, k + 65
+        const uint4 sz = *reinterpret_cast<const uint4*>(&KSZ[w][gh][CPW * i + k][0]);
+        const uint32_t szw[4] = {sz.x, sz.y, sz.z, sz.w};
+        for (int e = 0; e < 2; ++e) {
+          const h2_t lo = __builtin_bit_cast(h2_t, szw[2 * e]), hi = __builtin_bit_cast(h2_t, szw[2 * e + 1]);
+          // x = n s + z with one rounding (the product is exact)
+          xl[k + e] = __builtin_fmaf(nl[k + e], (float)lo.x, (float)lo.y);
+          xh[k + e] = __builtin_fmaf(nh[k + e], (float)hi.x, (float)hi.y);
+        }
       }
       score_pairs(xl, xh, CPW * i, CPW, acc);
     }
