@@ -35,38 +35,6 @@ __device__ __forceinline__ f4_t mfma1(float x, float y, f4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(x, y, c, 0, 0, 0);
 }
 
-// Code c of one key row, channels [8 i, 8 i + 8) (4-bit word i) or
-// [16 i, 16 i + 16) (2-bit word i) in channel order, as the fp16 subnormal
-// c * f * 2^-24 masked in place: part p of the word holds two channels, k and
-// k + CPW / 2, in its low and high halves.  The factor f of channel k is
-// 16^(k & 1) (4-bit) or 4^(k & 3) (2-bit); key_scale_shift() gives the power
-// of two that cancels it together with 2^-24, so that fma(code, s', z) with
-// s' = s * 2^shift is the dequantized key n s + z with one rounding (the
-// product is exact), and the conversion of the code folds into the fma.
-template <int BITS>
-__device__ __forceinline__ h2_t key_part(uint32_t w, int p) {
-  if (BITS == 4) {
-    const uint32_t src = (p & 2) ? (w >> 8) : w;
-    return __builtin_bit_cast(h2_t, src & ((p & 1) ? 0x00F000F0u : 0x000F000Fu));
-  } else {
-    const uint32_t src = (p & 4) ? (w >> 8) : w;
-    return __builtin_bit_cast(h2_t, src & (0x00030003u << (2 * (p & 3))));
-  }
-}
-template <int BITS>
-__device__ __forceinline__ _Float16 key_code(const h2_t* parts, int k) {
-  constexpr int HALF = 16 / BITS;   // channels per half of the word's parts
-  return (k < HALF) ? parts[k % HALF].x : parts[k % HALF].y;
-}
-template <int BITS>
-constexpr int key_scale_shift(int c) {
-  return BITS == 4 ? 24 - 4 * (c & 1) : 24 - 2 * (c & 3);
-}
-
-// Code k of a key word (channel CPW i + k) as an exact fp32 integer: the
-// codes are moved to byte boundaries (nibbles: k even in the low nibbles,
-// odd in the high ones; crumbs: k mod 4 selects the shift) and converted a
-// byte at a time (v_cvt_f32_ubyte).
 template <int B>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) {   // byte B of v as fp32 (pure ALU)
   float r;
