@@ -96,11 +96,12 @@ constexpr bool query_in_prob_table() {
 }
 
 // Waves per SIMD the register allocation must allow: three work-groups per
-// compute unit wherever the LDS allows it (the KIVI G = 4 4-bit and 3-bit
-// stages do not).
+// compute unit wherever the LDS allows it, except for the KIVI G = 4 kernels
+// (the 4-bit and 3-bit stages do not fit three; the 2-bit one would, but at
+// 168 VGPRs it spills, and two work-groups without spills are ~5% faster).
 template <int G, int BITS, bool BLOCK>
 constexpr int decode_min_waves() {
-  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK && BITS >= 3) ? 2 : 3);
+  return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK) ? 2 : 3);
 }
 
 // TBQ (with BLOCK): TBQ4 blocks; codes become their fp16 levels through
