@@ -58,7 +58,7 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
 COUNTERS = {
-    1: {"sources_sha256": "0162d906496e3ec70475f669903b1cf8e190784b9899c2f0b4a922c98d4101d5", "fetch_kib": 664792, "write_kib": 4257,
+    1: {"sources_sha256": "dedb21ad7f0ff33cae4fb052991043fbfb4588953890bdb21078c5a49e0182bf", "fetch_kib": 664792, "write_kib": 4257,
         "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
