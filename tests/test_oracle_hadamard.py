@@ -131,3 +131,38 @@ def test_signed_orthogonal_inverse_and_dot_identity():
     e = np.zeros((1, 128), np.float16)
     e[0, 100] = 64
     assert np.allclose(np.abs(hd.fwht128_f32(e, MASK_IN, MASK_OUT)), 64 / np.sqrt(128), rtol=1e-6)
+
+
+def test_fp32_stage_order_is_pinned():
+    # The butterfly order changes fp32 results (SURVEY reading R9 fixes
+    # h = 1, 2, ..., 64).  For each adjacent pair of stages (h, 2h) the input
+    # x[0] = 1, x[h] = x[3h] = 2^-24 (all fp16-exact) gives, in that order:
+    #   stage h:  x[0] = fl32(1 + 2^-24) = 1 (a tie, to even), x[h] = 1 - 2^-24,
+    #             x[2h] = 2^-24, x[3h] = -2^-24 (all exact);
+    #   stage 2h: x[0] = fl32(1 + 2^-24) = 1, x[h] = 1 - 2^-23, x[2h] = 1 - 2^-24,
+    #             x[3h] = 1 (exact);
+    # every other stage only copies these values (it adds zeros).  With 2h
+    # first, x[0] would end at 1 + 2^-23 instead: stage 2h makes x[h] = 2^-23
+    # exactly, and stage h then adds it to 1 without a tie.  Every order other
+    # than 1, 2, ..., 64 puts some 2h before h, so these six vectors pin it.
+    tiny = 2.0 ** -24
+    for h in (1, 2, 4, 8, 16, 32):
+        x = np.zeros(128, dtype=np.float16)
+        x[0] = 1.0
+        x[h] = tiny
+        x[3 * h] = tiny
+        assert float(x[h]) == tiny   # the smallest fp16 subnormal
+        y = hd.fwht128_f32(x)
+        want = {0: np.float32(1.0), h: np.float32(1.0 - 2.0 ** -23),
+                2 * h: np.float32(1.0 - 2.0 ** -24), 3 * h: np.float32(1.0)}
+        for i, v in want.items():
+            assert y[i] == np.float32(v * hd.C32), (h, i)
+        # the other order would be seen: (1 + 2^-23) C32 rounds to another float
+        assert np.float32(np.float32(1.0 + 2.0 ** -23) * hd.C32) != y[0]
+        # the randomized form flips signs exactly around the same schedule
+        ys = hd.fwht128_f32(x, sign_in=[1, 0, 0, 0], sign_out=[0, 0, 0, 1 << 31])
+        xs = x.copy()
+        xs[0] = -xs[0]
+        yn = hd.fwht128_f32(xs)
+        yn[127] = -yn[127]
+        assert np.array_equal(ys.view(np.uint32), yn.view(np.uint32))

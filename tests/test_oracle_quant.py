@@ -251,3 +251,73 @@ def test_symmetric_32_value_blocks_8bit():
     assert np.array_equal(img[..., :2].copy().view("<f2")[..., 0], s[:3])
     assert np.array_equal(img[..., 2:], n[:3].reshape(3, 4, 32))   # element k in byte k
     assert img.shape[-1] * 8 / 32 == 8.5
+
+
+def _even_neighbour(k):
+    """The code of a quotient k + 1/2 (k >= 0 an integer) under round half to
+    even: k when k is even, k + 1 when it is odd."""
+    return k if k % 2 == 0 else k + 1
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_asym_exact_ties_round_to_even(bits):
+    # A group with min 0 and max Q has s = Q / Q = 1 and z = 0 exactly, so the
+    # element k + 1/2 (fp16-exact) has the quotient k + 1/2 exactly: every
+    # element but the two ends is a tie (SURVEY C1 / R4: round half to even).
+    Q = 2 ** bits - 1
+    rows, want = [], []
+    for r in range(8):
+        ks = [(r + i) % Q for i in range(30)]
+        rows.append([0.0, float(Q)] + [k + 0.5 for k in ks])
+        want.append([0, Q] + [_even_neighbour(k) for k in ks])
+    x = np.array(rows, dtype=F16).astype(F32)
+    c, s, z = quant.quant_asym(x, bits, axis=-1)
+    assert np.all(s == F16(1.0)) and np.all(z == F16(0.0))
+    assert np.array_equal(c.astype(np.int64), np.array(want))
+    # the same groups as KIVI keys (tokens on axis -2) and values (32 dims)
+    xk = np.repeat(x.T[:, :1], 128, axis=1)          # [32 tokens, 128 channels]
+    ck, _, _ = quant.quant_k_group(xk, bits)
+    assert np.array_equal(ck[:, 0].astype(np.int64), np.array(want[0]))
+    xv = np.tile(x[0], 4)[None, :].repeat(32, axis=0)  # every token: four copies of group 0
+    cv, sv, zv = quant.quant_v_group(xv, bits)
+    assert np.all(sv == F16(1.0)) and np.all(zv == F16(0.0))
+    assert np.array_equal(cv[3].astype(np.int64), np.tile(want[0], 4))
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_sym128_exact_ties_round_to_even(bits):
+    # absmax = top gives s = 1 exactly; +-(k + 1/2) are ties, rounded to the
+    # even neighbour with the sign kept (rint(-2.5) = -2); stored c + top + 1.
+    top = (1 << (bits - 1)) - 1
+    vals, want = [float(top), -float(top)], [top, -top]
+    k = 0
+    while len(vals) < 128:
+        kk = k % top
+        sgn = 1 if (k // top) % 2 == 0 else -1
+        vals.append(sgn * (kk + 0.5))
+        want.append(sgn * _even_neighbour(kk))
+        k += 1
+    y = np.array([vals], dtype=F16).astype(F32)
+    c, s = quant.quant_sym128(y, bits)
+    assert s[0] == F16(1.0)
+    assert np.array_equal(c[0].astype(np.int64), np.array(want) + top + 1)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_sym32_exact_ties_round_to_even(bits):
+    # each 32-value slice: absmax = top (s = 1), the rest +-(k + 1/2)
+    top = (1 << (bits - 1)) - 1
+    vals, want = [], []
+    for sl in range(4):
+        vals += [float(top)]
+        want += [top]
+        for i in range(31):
+            kk = (7 * sl + 5 * i) % top
+            sgn = 1 if (i + sl) % 2 == 0 else -1
+            vals.append(sgn * (kk + 0.5))
+            want.append(sgn * _even_neighbour(kk))
+    y = np.array([vals], dtype=F16).astype(F32)
+    assert np.array_equal(np.abs(y[0]) % 1, np.array([0.0] + [0.5] * 31 + ([0.0] + [0.5] * 31) * 3))
+    c, s = quant.quant_sym32(y, bits)
+    assert np.all(s == F16(1.0))
+    assert np.array_equal(c[0].astype(np.int64), np.array(want) + top + 1)
