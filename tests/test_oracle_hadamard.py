@@ -134,8 +134,11 @@ def test_signed_orthogonal_inverse_and_dot_identity():
 
 
 def test_fp32_stage_order_is_pinned():
-    # The butterfly order changes fp32 results (SURVEY reading R9 fixes
-    # h = 1, 2, ..., 64).  For each adjacent pair of stages (h, 2h) the input
+    # The butterfly order changes fp32 results, and the stored codes of a
+    # rotated cache ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw
+    # obrot") are defined by the order h = 1, 2, ..., 64 (the pages give no
+    # schedule; this is the reading the oracle takes).  For each adjacent pair
+    # of stages (h, 2h) the input
     # x[0] = 1, x[h] = x[3h] = 2^-24 (all fp16-exact) gives, in that order:
     #   stage h:  x[0] = fl32(1 + 2^-24) = 1 (a tie, to even), x[h] = 1 - 2^-24,
     #             x[2h] = 2^-24, x[3h] = -2^-24 (all exact);

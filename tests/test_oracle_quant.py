@@ -263,7 +263,8 @@ def _even_neighbour(k):
 def test_asym_exact_ties_round_to_even(bits):
     # A group with min 0 and max Q has s = Q / Q = 1 and z = 0 exactly, so the
     # element k + 1/2 (fp16-exact) has the quotient k + 1/2 exactly: every
-    # element but the two ends is a tie (round half to even).
+    # element but the two ends is a tie, which the fixed fp32 rule rounds half
+    # to even (the pages give no tie rule; this is the reading the oracle takes).
     Q = 2 ** bits - 1
     rows, want = [], []
     for r in range(8):
