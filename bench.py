@@ -13,20 +13,26 @@ Reported (one JSON line on stdout):
                window) / step time, GB/s; inputs resident in HBM
   value is measured over back-to-back steps, where the tail of one step's
   reads is still in the 256 MB Infinity Cache when the next step starts.
-  roofline     the split-K decode kernel alone, cold: algorithmic bytes per
-               launch / its average duration (HIP events on the launch
-               stream) over --cold-steps extra steps, each after a 512 MB read
-               that sweeps the Infinity Cache and the L2s, against the 8 TB/s
-               HBM peak (the back-to-back figure is reported beside it);
-               traffic = counter-measured HBM bytes per launch (null when the
-               kernel sources changed since)
+  roofline     the decode call (split-K partials kernel + merge kernel), cold:
+               algorithmic bytes per call / its average duration (HIP events
+               on the launch stream) over --cold-steps extra steps, each after
+               a 512 MB read that sweeps the Infinity Cache and the L2s,
+               against the 8 TB/s HBM peak (the back-to-back figure and the
+               partials kernel alone are reported beside it); traffic =
+               counter-measured HBM bytes per call (null when the kernel
+               sources changed since)
   append       (chunked-prefill workloads) the workload's multi-token append
                timed apart: (fp16 read + packed write) bytes / time
   cpu_baseline the CPU oracle on the same step (append one token + dequantize
                + fp64 attention) over a bounded sample of the workload's
                (sequence, kv head) pairs, one process per core
 
-    python bench.py [--steps K] [--warmup W] [--workload ID] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload ID] [--sub-workloads 1,4]
+                    [--no-cpu-baseline]
+
+The headline workload defaults to the largest cache that one GPU holds (the
+pre-RoPE GQA layer, 16 x 8 kv heads at T = 131072); the Llama-2-7B-shaped MHA
+layer and the chunked-prefill block cache follow as sub-records.
 """
 
 import argparse
@@ -46,21 +52,23 @@ from quantized_decode_attention_02_amd import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn effective KV GB/s (% of HBM peak) + attended tokens/s, INT4, 1 GPU"
 
-# HBM bytes of one decode-kernel launch from hardware counters (rocprofv3
-# --pmc FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
-# the counter reads for a plain 1 GiB device copy (FETCH_SIZE reads 524300 KiB
-# for 1048576 KiB moved: x2.0; WRITE_SIZE reads 1048576 KiB: x1.0).  Valid only
-# for the kernel sources they were taken with (sha256 over COUNTER_SOURCES);
-# any change there reports traffic as null until the counters are taken again.
+# HBM bytes of one decode call from hardware counters: rocprofv3 --pmc
+# FETCH_SIZE, then WRITE_SIZE (KiB per dispatch), for the partials kernel and
+# the merge kernel of the call, each scaled by what the counter reads for a
+# plain 1 GiB device copy (FETCH_SIZE reads 524300 KiB for 1048576 KiB moved:
+# x2.0; WRITE_SIZE reads 1048576 KiB: x1.0).  Valid only for the kernel
+# sources they were taken with (sha256 over COUNTER_SOURCES); any change there
+# reports traffic as null until the counters are taken again.
 COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
+                   "quantized_decode_attention_02_amd/csrc/decode_rope.hip",
+                   "quantized_decode_attention_02_amd/csrc/decode.hip",
                    "quantized_decode_attention_02_amd/csrc/decode_common.h",
                    "quantized_decode_attention_02_amd/csrc/kvq_device.h",
                    "quantized_decode_attention_02_amd/csrc/kvq_internal.h",
                    "quantized_decode_attention_02_amd/csrc/kvq.cpp"]
-COUNTERS = {
-    1: {"sources_sha256": "dedb21ad7f0ff33cae4fb052991043fbfb4588953890bdb21078c5a49e0182bf", "fetch_kib": 664792, "write_kib": 4257,
-        "fetch_factor": 2.0, "write_factor": 1.0},
-}
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+# workload id -> {"sources_sha256": ..., "kernels": {kernel: [fetch_kib, write_kib]}}
+COUNTERS = {}
 
 
 def log(msg):
@@ -97,12 +105,12 @@ def sources_sha256():
 
 
 def counter_traffic(wid):
-    """Counter-measured HBM bytes per decode launch, or None when the kernel
-    sources differ from those the counters were taken with."""
+    """Counter-measured HBM bytes per decode call (partials + merge), or None
+    when the kernel sources differ from those the counters were taken with."""
     c = COUNTERS.get(wid)
     if c is None or c["sources_sha256"] != sources_sha256():
         return None
-    return int((c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"]) * 1024)
+    return int(sum(f * FETCH_FACTOR + wr * WRITE_FACTOR for f, wr in c["kernels"].values()) * 1024)
 
 
 def describe_cache(cfg):
@@ -222,6 +230,152 @@ def cpu_baseline(w, T, n_pairs, workers):
 
 # ---------------------------------------------------------------------------
 
+def measure(w, args, dev, headline):
+    """Build the workload's cache on the GPU and time it.  Returns the figures
+    of one workload: back-to-back steps, the cold decode call (partials +
+    merge, HIP events on the launch stream, caches swept before each launch)
+    and, for chunked-prefill workloads, the multi-token append."""
+    import torch
+    from quantized_decode_attention_02_amd import kvq
+
+    T = w["tokens"]
+    cfg = wl.library_config(w)
+    decode_only = args.decode_only or (w["cfg"]["scheme"] == "kivi" and w["cfg"]["hi_window"] >= 0)
+    log(f"workload {w['name']}: generating {T} tokens x {w['batch']} seqs x {w['num_kv_heads']} heads")
+    K0, V0 = wl.kv_tokens(w, 0, T - 1)
+    K1, V1 = wl.kv_tokens(w, T - 1, T)
+    q = torch.from_numpy(wl.queries(w)).to(dev)
+    log("uploading")
+    k0, v0 = torch.from_numpy(K0).to(dev), torch.from_numpy(V0).to(dev)
+    del K0, V0
+    k1, v1 = torch.from_numpy(K1).to(dev), torch.from_numpy(V1).to(dev)
+    cache = kvq.KVCache(cfg, w["batch"], T)
+    cache.append(k0, v0)
+    torch.cuda.synchronize()
+    chunk = None
+    if w.get("prefill") and w["cfg"]["scheme"] in BLOCK_SCHEMES:
+        n = w["prefill"]   # the workload's chunked-prefill append: its last n tokens
+        chunk = (n, torch.cat([k0[:, T - n:], k1], 1).contiguous(), torch.cat([v0[:, T - n:], v1], 1).contiguous())
+    del k0, v0
+    log(f"cache built: {cache.length} tokens")
+    stream = torch.cuda.current_stream()
+
+    def ev_pair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    append_rec = None
+    if chunk is not None:
+        # the chunked-prefill append timed apart (it rewrites the same blocks)
+        n, kp, vp = chunk
+        ev_a = [ev_pair() for _ in range(10)]
+        for i in range(12):
+            cache.length = T - n
+            if i >= 2:
+                ev_a[i - 2][0].record(stream)
+            cache.append(kp, vp)
+            if i >= 2:
+                ev_a[i - 2][1].record(stream)
+        torch.cuda.synchronize()
+        a_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
+        rd = w["batch"] * n * w["num_kv_heads"] * 2 * 128 * 2
+        wr = w["batch"] * n * w["num_kv_heads"] * 2 * block_bytes(w["cfg"])
+        append_rec = {"tokens_per_seq": n, "ms": round(a_ms, 5), "read_bytes": rd, "write_bytes": wr,
+                      "gbs": round((rd + wr) / (a_ms / 1e3) / 1e9, 2),
+                      "frac": round((rd + wr) / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"chunked append of {n} tokens: {a_ms:.4f} ms")
+        del kp, vp, chunk
+        cache.length = T - 1
+
+    cache.append(k1, v1)
+    ws = cache.new_workspace()
+    out = torch.empty((w["batch"], w["num_q_heads"], 128), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        # ev: (start, after partials, after merge) on the launch stream
+        if not decode_only:
+            cache.length = T - 1
+            cache.append(k1, v1)
+        if ev is not None:
+            ev[0].record(stream)
+        cache.decode_partials(q, ws, out)
+        if ev is not None:
+            ev[1].record(stream)
+        cache.decode_merge(q, ws, out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def ev3():
+        return tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+
+    steps = args.steps if headline else args.sub_steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [ev3() for _ in range(steps)]
+    log(f"timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    call_warm = float(np.mean([a.elapsed_time(c) for a, b, c in events]))
+
+    # The same steps with the 256 MB Infinity Cache and the L2s swept before
+    # each one by reading a 512 MB buffer (clean lines, so no write-back
+    # competes with the kernels), outside the events.  The roofline figure
+    # uses these cold decode calls.
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    cold = args.cold_steps if headline else max(5, args.cold_steps // 2)
+    ev_c = [ev3() for _ in range(cold)]
+    for e in ev_c:
+        scratch.sum()
+        step(e)
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(c) for a, b, c in ev_c]
+    part_ms = [a.elapsed_time(b) for a, b, c in ev_c]
+    merge_ms = [b.elapsed_time(c) for a, b, c in ev_c]
+    del scratch
+
+    nbytes = decode_bytes(w, T)
+    call = float(np.mean(call_ms))
+    kname = "decode_rope_kernel" if w["cfg"]["pre_rope"] else "decode_mfma_kernel"
+    rec = {
+        "workload": w["name"],
+        "decode_bytes": nbytes,
+        "ms_per_step": round(ms_step, 4),
+        "step": ("split-K decode + merge" if decode_only else "append 1 token/seq + split-K decode + merge"),
+        "value": round(nbytes / (ms_step / 1e3) / 1e9, 2),
+        "attended_tokens_per_s": round(w["batch"] * T / (ms_step / 1e3), 1),
+        "bytes_per_attended_token": round(nbytes / (w["batch"] * T), 2),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (call / 1e3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (call / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic(w["id"]),
+                     "traffic_unit": "HBM bytes per decode call, partials + merge "
+                                     "(FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "algorithmic_bytes": nbytes,
+                     "kernel": f"kvq_decode_attn: {kname} (split-K partials) + decode_merge_kernel",
+                     "kernel_ms_avg": round(call, 5),
+                     "kernel_ms_p10_p90": [round(float(np.percentile(call_ms, 10)), 5),
+                                           round(float(np.percentile(call_ms, 90)), 5)],
+                     "partials_ms_avg": round(float(np.mean(part_ms)), 5),
+                     "merge_ms_avg": round(float(np.mean(merge_ms)), 5),
+                     "caches": "Infinity Cache and L2 swept (512 MB read) before each timed call",
+                     "kernel_ms_avg_back_to_back": round(call_warm, 5),
+                     "achieved_back_to_back": round(nbytes / (call_warm / 1e3) / 1e9, 2)},
+        "cache": describe_cache(w["cfg"]),
+    }
+    if append_rec is not None:
+        rec["append"] = append_rec
+    log(f"{w['name']}: step {ms_step:.4f} ms, decode call {call:.4f} ms cold "
+        f"({rec['roofline']['frac']:.3f} of peak)")
+    del cache, ws, out, q, k1, v1
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,13 +383,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps, each after a 512 MB read that sweeps the caches; the "
-                         "roofline figure is their decode kernel's average")
-    ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--cpu-pairs", type=int, default=64)
+                         "roofline figure is their decode call's average")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="headline workload (default: the largest single-GPU cache, the "
+                         "pre-RoPE GQA layer at T=131072)")
+    ap.add_argument("--sub-workloads", default="1,4",
+                    help="comma-separated workloads measured after the headline and reported "
+                         "under 'sub' (empty: none)")
+    ap.add_argument("--sub-steps", type=int, default=20)
+    ap.add_argument("--cpu-pairs", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time decode (partials + merge) on the built T-token cache without the "
-                         "per-step append (needed for caches with a high-bit window, where "
+                         "per-step append (caches with a high-bit window always run this way: "
                          "replaying the same append would demote a group twice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for "
@@ -257,127 +417,35 @@ def main():
 
     w = wl.workload(args.workload)
     T = w["tokens"]
-    cfg = wl.library_config(w)
-    if w["cfg"]["scheme"] == "kivi" and w["cfg"]["hi_window"] >= 0 and not args.decode_only:
-        raise SystemExit("replaying this workload's append would demote a group twice: "
-                         "use --decode-only")
+    subs = [int(x) for x in args.sub_workloads.split(",") if x.strip()]
 
     cpu = None
     if not args.no_cpu_baseline:
-        ncores = len(os.sched_getaffinity(0))
-        log(f"cpu baseline: {args.cpu_pairs} pairs on up to {min(16, ncores)} processes")
-        cpu = cpu_baseline(w, T, args.cpu_pairs, min(16, ncores))
+        # one process per host core, at most 16 (the host share of one GPU on
+        # the measurement machines, whatever the affinity mask shows)
+        affinity = len(os.sched_getaffinity(0))
+        workers = min(16, affinity)
+        log(f"cpu baseline: {args.cpu_pairs} pairs on {workers} processes "
+            f"(affinity {affinity}, cpu_count {os.cpu_count()})")
+        cpu = cpu_baseline(w, T, args.cpu_pairs, workers)
+        cpu["host_cpus"] = {"affinity": affinity, "cpu_count": os.cpu_count()}
         log(f"cpu baseline {cpu['value']:.3f} GB/s")
 
     import torch
-    from quantized_decode_attention_02_amd import kvq
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    log(f"workload {w['name']}: generating {T} tokens x {w['batch']} seqs x {w['num_kv_heads']} heads")
-    K0, V0 = wl.kv_tokens(w, 0, T - 1)
-    K1, V1 = wl.kv_tokens(w, T - 1, T)
-    q = torch.from_numpy(wl.queries(w)).to(dev)
-    log("uploading")
-    k0, v0 = torch.from_numpy(K0).to(dev), torch.from_numpy(V0).to(dev)
-    del K0, V0
-    k1, v1 = torch.from_numpy(K1).to(dev), torch.from_numpy(V1).to(dev)
-    cache = kvq.KVCache(cfg, w["batch"], T)
-    cache.append(k0, v0)
-    torch.cuda.synchronize()
-    chunk = None
-    if w.get("prefill") and w["cfg"]["scheme"] in BLOCK_SCHEMES:
-        n = w["prefill"]   # the workload's chunked-prefill append: its last n tokens
-        chunk = (n, torch.cat([k0[:, T - n:], k1], 1).contiguous(), torch.cat([v0[:, T - n:], v1], 1).contiguous())
-    del k0, v0
-    log(f"cache built: {cache.length} tokens")
+    head = measure(w, args, dev, headline=True)
+    sub = [measure(wl.workload(s), args, dev, headline=False) for s in subs if s != args.workload]
 
-    append_rec = None
-    if chunk is not None:
-        # the chunked-prefill append timed apart (it rewrites the same blocks)
-        n, kp, vp = chunk
-        ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for i in range(12):
-            cache.length = T - n
-            if i >= 2:
-                ev_a[i - 2][0].record()
-            cache.append(kp, vp)
-            if i >= 2:
-                ev_a[i - 2][1].record()
-        torch.cuda.synchronize()
-        a_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
-        rd = w["batch"] * n * w["num_kv_heads"] * 2 * 128 * 2
-        wr = w["batch"] * n * w["num_kv_heads"] * 2 * block_bytes(w["cfg"])
-        append_rec = {"tokens_per_seq": n, "ms": round(a_ms, 5), "read_bytes": rd, "write_bytes": wr,
-                      "gbs": round((rd + wr) / (a_ms / 1e3) / 1e9, 2),
-                      "frac": round((rd + wr) / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"chunked append of {n} tokens: {a_ms:.4f} ms")
-        del kp, vp, chunk
-        cache.length = T - 1
-
-    cache.append(k1, v1)
-    ws = cache.new_workspace()
-    out = torch.empty((w["batch"], w["num_q_heads"], 128), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if not args.decode_only:
-            cache.length = T - 1
-            cache.append(k1, v1)
-        if ev is not None:
-            ev[0].record(stream)
-        cache.decode_partials(q, ws, out)
-        if ev is not None:
-            ev[1].record(stream)
-        cache.decode_merge(q, ws, out)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = [a.elapsed_time(b) for a, b in events]
-    k_avg = float(np.mean(k_ms))
-
-    # The same steps with the 256 MB Infinity Cache and the L2s swept before
-    # each one by reading a 512 MB buffer (clean lines, so no write-back
-    # competes with the kernel), outside the events.  Back to back, the tail
-    # of one step's reads is still cached when the next step starts; the
-    # roofline figure uses these cold launches.
-    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    ev_c = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.cold_steps)]
-    for e in ev_c:
-        scratch.sum()
-        step(e)
-    torch.cuda.synchronize()
-    k_cold_ms = [a.elapsed_time(b) for a, b in ev_c]
-    k_cold = float(np.mean(k_cold_ms))
-    del scratch
-
-    nbytes = decode_bytes(w, T)
-    value = nbytes / (ms_step / 1e3) / 1e9
-    achieved = nbytes / (k_cold / 1e3) / 1e9
-    achieved_warm = nbytes / (k_avg / 1e3) / 1e9
-    attended = w["batch"] * T / (ms_step / 1e3)
-    kname = "decode_rope_kernel" if w["cfg"]["pre_rope"] else "decode_mfma_kernel"
-    traffic = counter_traffic(w["id"])
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -385,29 +453,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "batch": w["batch"], "q_heads": w["num_q_heads"],
                    "kv_heads": w["num_kv_heads"], "head_dim": 128, "tokens": T,
-                   "cache": describe_cache(w["cfg"]),
-                   "step": ("split-K decode + merge" if args.decode_only else
-                            "append 1 token/seq + split-K decode + merge"),
-                   "decode_bytes": nbytes},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "attended_tokens_per_s": round(attended, 1),
-        "bytes_per_attended_token": round(nbytes / (w["batch"] * T), 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                     "algorithmic_bytes": nbytes,
-                     "kernel": f"{kname} (split-K partials)",
-                     "kernel_ms_avg": round(k_cold, 5),
-                     "kernel_ms_p10_p90": [round(float(np.percentile(k_cold_ms, 10)), 5),
-                                           round(float(np.percentile(k_cold_ms, 90)), 5)],
-                     "caches": "Infinity Cache and L2 swept (512 MB read) before each timed launch",
-                     "kernel_ms_avg_back_to_back": round(k_avg, 5),
-                     "achieved_back_to_back": round(achieved_warm, 2)},
+                   "cache": head["cache"], "step": head["step"], "decode_bytes": head["decode_bytes"]},
+        "pct_hbm_peak": round(100 * head["value"] / HBM_PEAK_GBS, 2),
+        "attended_tokens_per_s": head["attended_tokens_per_s"],
+        "bytes_per_attended_token": head["bytes_per_attended_token"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
     }
-    if append_rec is not None:
-        res["append"] = append_rec
+    if "append" in head:
+        res["append"] = head["append"]
+    if sub:
+        res["sub"] = sub
     print(json.dumps(res), flush=True)
 
 

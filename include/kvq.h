@@ -192,7 +192,10 @@ kvq_status kvq_layout(const kvq_config* cfg, int64_t batch, int64_t max_tokens,
                       kvq_layout_t* out);
 
 /* Bytes of the device workspace kvq_decode_attn needs for `batch` sequences
- * of `length` cached tokens.  Writes *bytes.  The workspace starts with
+ * of `length` cached tokens.  Writes *bytes.  A pure function of (cfg, batch,
+ * length): the size is that of the split-K plan with the most waves a launch
+ * may run at once (8192), which no device's plan exceeds, so the same number
+ * serves every device and call.  The workspace starts with
  * KVQ_COUNTER_BYTES(batch * num_kv_heads) bytes of work counters; the split-K
  * partials follow (running max, sum and 128 accumulators per query head and
  * partial).  The workspace must be all zero before its first use: every

@@ -1,8 +1,7 @@
 // libkvq C ABI: argument validation, plane layout, tier bookkeeping and
-// kernel dispatch.  No device allocation, no synchronization; the only global
-// state is a mutex-guarded cache of kernel occupancies (a pure function of
-// the kernel binary and the device).  The contract of every function is in
-// include/kvq.h.
+// kernel dispatch.  No device allocation, no synchronization and no mutable
+// global state (the TBQ4 codebook is computed once and never changes).  The
+// contract of every function is in include/kvq.h.
 //
 // Sources cited here:
 //   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
@@ -12,8 +11,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <map>
-#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -280,18 +277,14 @@ constexpr int64_t kTeamPerChunkTile = KVQ_TEAM_PER_CHUNK_TILE;
 #define KVQ_DECODE_TAIL_TILES_PER_MEMBER 1
 #endif
 
+// Asked of the runtime on every plan (a pure function of the kernel binary
+// and the current device; nothing is cached).
 int occupancy_wgs_per_cu(const void* kernel) {
-  static std::mutex mu;
-  static std::map<const void*, int> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(kernel);
-  if (it != cache.end()) return it->second;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0) {
     (void)hipGetLastError();
     n = 2;   // no device: a plan that is valid everywhere, if not the fastest
   }
-  cache[kernel] = n;
   return n;
 }
 
@@ -306,6 +299,12 @@ int device_compute_units() {
 }
 
 ChunkPlan plan_chunks(const Geom& g) {
+  // the device's resident waves for the kernel of the widest range (ranges
+  // of one call differ only in code width; each is capped by its own kernel)
+  return plan_chunks(g, -1);
+}
+
+ChunkPlan plan_chunks(const Geom& g, int64_t cap_waves) {
   ChunkPlan cp;
   cp.nr = 0;
   const int64_t pairs = (int64_t)g.B * g.Hkv;
@@ -325,8 +324,12 @@ ChunkPlan plan_chunks(const Geom& g) {
     r.n_chunks = 0;
     r.n_big = 0;
     if (r.tiles_pp > 0) {
-      const int per_cu = g.pre_rope ? decode_rope_wgs_per_cu(g, bits) : decode_mfma_wgs_per_cu(g, bits);
-      const int64_t cap = 4 * (int64_t)per_cu * device_compute_units();   // waves
+      int64_t cap = cap_waves;   // waves
+      if (cap <= 0) {
+        const int per_cu = g.pre_rope ? decode_rope_wgs_per_cu(g, bits) : decode_mfma_wgs_per_cu(g, bits);
+        cap = 4 * (int64_t)per_cu * device_compute_units();
+      }
+      if (cap > kMaxPlanWaves) cap = kMaxPlanWaves;
       int64_t team = pairs <= cap ? cap / pairs : 1;
       const int64_t most = (r.tiles_pp + kMinTilesPerWave - 1) / kMinTilesPerWave;
       if (team > most) team = most;
@@ -399,8 +402,10 @@ kvq_status kvq_workspace_bytes(const kvq_config* cfg, int64_t batch, int64_t len
   kvq_status s = validate_config(cfg);
   if (s != KVQ_OK) return s;
   if (bytes == nullptr || batch <= 0 || batch > 65535 || length < 0) return KVQ_ERR_INVALID_ARG;
+  // the plan of the largest launch any device may run: a team per pair is
+  // never smaller on a larger device, so this covers every device's plan
   const Geom g = make_geom(cfg, batch, length, length);
-  const ChunkPlan cp = plan_chunks(g);
+  const ChunkPlan cp = plan_chunks(g, kMaxPlanWaves);
   *bytes = workspace_need(g, cp);
   return KVQ_OK;
 }

@@ -88,6 +88,15 @@ constexpr int64_t kCounterStride = 64;
 // Workspace words holding the chunk counters of `pairs` pairs.
 inline int64_t counter_words(int64_t pairs) { return 2 * pairs * kCounterStride; }
 
+// Waves a decode launch may run at once, at most (2048 threads per compute
+// unit on 256 compute units).  The workspace size is that of the plan with
+// this many waves, so it depends on (config, batch, length) only; a plan on
+// a device holds at most as many waves and needs no more workspace.
+constexpr int64_t kMaxPlanWaves = 8192;
+
+// Split-K plan for a launch of at most cap_waves waves (<= kMaxPlanWaves).
+ChunkPlan plan_chunks(const Geom& g, int64_t cap_waves);
+// The same with the waves the current device keeps resident.
 ChunkPlan plan_chunks(const Geom& g);
 
 // Schemes with one 128-value block per token (no window, no tiers).

@@ -23,6 +23,8 @@ VARIANTS = {
     "int3-hadamard-signed": dict(k_bits=3, v_bits=3, hadamard=True, **SIGNS),
     "int4-hadamard": dict(hadamard=True),
     "int4-prerope": dict(pre_rope=True, rope_theta=500000.0),
+    "int2-prerope": dict(k_bits=2, v_bits=2, pre_rope=True, rope_theta=500000.0),
+    "mixed-prerope": dict(hi_window=64, low_bits=2, pre_rope=True, rope_theta=500000.0),
     "mixed-hadamard": dict(hadamard=True, hi_window=96),
     "mixed": dict(hi_window=64),
     "mixed-int3": dict(hi_window=64, low_bits=3),
@@ -88,7 +90,8 @@ def test_streaming(variant, stream):
     check_decode(g, o, w, s, h)
 
 
-@pytest.mark.parametrize("variant", ["int4", "int3", "block128-3bit", "tbq4-signed", "q4_0", "q8_0"])
+@pytest.mark.parametrize("variant", ["int4", "int3", "int4-prerope", "int2-prerope", "block128-3bit",
+                                     "tbq4-signed", "q4_0", "q8_0"])
 @pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 1), (8, 8)])
 def test_gqa_shapes(hq, hkv, variant):
     # every query-group size (1, 2, 4) of every decode kernel family
