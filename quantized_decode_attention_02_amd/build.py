@@ -8,7 +8,12 @@ Flags that matter for correctness:
   * ``-fno-gpu-flush-denormals-to-zero`` and
     ``-fhip-fp32-correctly-rounded-divide-sqrt``: IEEE fp32 division and
     denormals, which the bit-exact quantizer relies on;
-  * no fast-math of any kind.
+  * no fast-math of any kind;
+  * ``-mllvm -amdgpu-atomic-optimizer-strategy=None``: the decode kernels'
+    chunk claims are one lane's atomic whose result is read a tile later;
+    the atomic optimizer would rewrite it into a wave-wide form that reads
+    the result back at once, stalling the wave on the atomic's round trip
+    and on every load issued before it.
 """
 
 import os
@@ -38,6 +43,7 @@ def command(out=LIB, defines=()):
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-fno-fast-math", "-Wall", "-Wno-unused-function",
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out] + \
            [os.path.join(CSRC, s) for s in SOURCES]
 
