@@ -42,7 +42,9 @@ typedef enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment or config value */
   KVQ_ERR_UNSUPPORTED = -2, /* a valid but unimplemented combination */
   KVQ_ERR_CAPACITY = -3,    /* length + n_new would exceed max_tokens */
-  KVQ_ERR_WORKSPACE = -4,   /* workspace smaller than kvq_workspace_bytes */
+  KVQ_ERR_WORKSPACE = -4,   /* workspace smaller than the call needs (for
+                               kvq_decode_attn_static: more than its static
+                               array holds) */
   KVQ_ERR_HIP = -5          /* the HIP runtime rejected a launch */
 } kvq_status;
 
@@ -259,6 +261,23 @@ kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache, co
 kvq_status kvq_decode_merge(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                             int64_t q_pos, float sm_scale, void* out, void* workspace,
                             uint64_t workspace_bytes, void* stream);
+
+/* kvq_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * output, accuracy and errors as kvq_decode_attn.  The partials and chunk
+ * counters live in a static device array of KVQ_STATIC_WORKSPACE_BYTES that
+ * each GPU holds from the library's load until the process ends; the call
+ * allocates nothing and starts by clearing the counters with a fill kernel.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other threads) race, and the caller must order
+ * them.  The stream must belong to the current device (KVQ_ERR_INVALID_ARG
+ * otherwise).  KVQ_ERR_WORKSPACE: the call needs more than
+ * KVQ_STATIC_WORKSPACE_BYTES (at most kvq_workspace_bytes of the same
+ * arguments). */
+#define KVQ_STATIC_WORKSPACE_BYTES (32u << 20)
+kvq_status kvq_decode_attn_static(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                  int64_t q_pos, float sm_scale, void* out, void* stream);
 
 /* Dequantize tokens [t0, t1) to fp32 in the stored domain (rotated when
  * hadamard, before RoPE when pre_rope_keys; window tokens are their fp16

@@ -14,10 +14,27 @@
 // query head of its GQA group, the running max m (log2 domain), the sum l of
 // exp2(s - m) and the unnormalized output o[128].  The merge below combines
 // them by log-sum-exp.
+#include <mutex>
+
 #include "kvq_device.h"
+
+// Workspace of kvq_decode_attn_static: split-K partials and chunk counters of
+// a decode call for callers that cannot allocate.  Each GPU holds its own
+// copy from the library's load until the process ends.  In host code this
+// name is only a handle for hipGetSymbolAddress: the device address of the
+// current GPU's copy comes from static_workspace() below, and kernels take
+// that address.
+static __device__ __align__(256) uint8_t scratch[KVQ_STATIC_WORKSPACE_BYTES];
 
 namespace kvq {
 namespace {
+
+// Zeroes n 32-bit words (the chunk counters a decode call starts from).  A
+// kernel rather than hipMemsetAsync, so that the call can be captured in a
+// HIP graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // M = max m_c, L = sum l_c 2^(m_c - M), out = sum o_c 2^(m_c - M) / L.
@@ -136,6 +153,34 @@ hipError_t launch_decode_partials(const Geom& g, const Planes& p, const ChunkPla
   if (cp.n == 0) return hipGetLastError();
   return g.pre_rope ? launch_decode_rope(g, p, cp, q, q_pos, sm_scale, ws, s)
                     : launch_decode_mfma(g, p, cp, q, sm_scale, ws, s);
+}
+
+hipError_t launch_zero_counters(const ChunkPlan& cp, float* ws, hipStream_t s) {
+  if (cp.ctr_floats <= 0) return hipGetLastError();
+  const int64_t blocks = std::min<int64_t>((cp.ctr_floats + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(ws), cp.ctr_floats);
+  return hipGetLastError();
+}
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up once per device with hipGetSymbolAddress and kept: host code never
+// passes the array's name itself to a kernel.
+hipError_t static_workspace(int dev, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,

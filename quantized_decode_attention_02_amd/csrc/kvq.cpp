@@ -497,6 +497,32 @@ kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const 
   return kvq_decode_merge(cfg, cache, q, q_pos, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
+kvq_status kvq_decode_attn_static(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                  int64_t q_pos, float sm_scale, void* out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (st != nullptr) {
+    // the workspace address below is the current device's: the stream must
+    // belong to it
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess) return KVQ_ERR_HIP;
+    if ((int)sdev != dev) return KVQ_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  if (static_workspace(dev, &ws) != hipSuccess) return KVQ_ERR_HIP;
+  DecodeSetup su;
+  // KVQ_ERR_WORKSPACE here: the call needs more than the static array holds
+  const kvq_status s = decode_setup(cfg, cache, q, out, ws, KVQ_STATIC_WORKSPACE_BYTES, sm_scale, &su);
+  if (s != KVQ_OK) return s;
+  float* w = static_cast<float*>(ws);
+  hipError_t e = launch_zero_counters(su.cp, w, st);
+  if (e == hipSuccess)
+    e = launch_decode_partials(su.g, su.p, su.cp, static_cast<const __half*>(q), q_pos, su.scale, w, st);
+  if (e == hipSuccess) e = launch_decode_merge(su.g, su.cp, w, static_cast<float*>(out), st);
+  return from_hip(e);
+}
+
 kvq_status kvq_dequant(const kvq_config* cfg, const kvq_cache* cache, int64_t t0, int64_t t1,
                        void* k_out, void* v_out, void* stream) {
   kvq_status s = validate_config(cfg);

@@ -141,6 +141,11 @@ hipError_t launch_decode_rope(const Geom& g, const Planes& p, const ChunkPlan& c
                               int64_t q_pos, float sm_scale, float* ws, hipStream_t s);
 hipError_t launch_decode_merge(const Geom& g, const ChunkPlan& cp, float* ws, float* out,
                                hipStream_t s);
+// Zeroes the chunk counters at the head of a workspace (a fill kernel).
+hipError_t launch_zero_counters(const ChunkPlan& cp, float* ws, hipStream_t s);
+// Device address of the static workspace on device dev (looked up once per
+// device; dev must be the current device on the first call).
+hipError_t static_workspace(int dev, void** ptr);
 hipError_t launch_dequant(const Geom& g, const Planes& p, int64_t t0, int64_t t1, float* k_out,
                           float* v_out, hipStream_t s);
 

@@ -24,8 +24,9 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WO
 
 # every symbol include/kvq.h declares
 EXPORTS = ["kvq_layout", "kvq_workspace_bytes", "kvq_append", "kvq_decode_attn",
-           "kvq_decode_partials", "kvq_decode_merge", "kvq_dequant", "kvq_strerror",
-           "kvq_abi_version"]
+           "kvq_decode_partials", "kvq_decode_merge", "kvq_dequant", "kvq_decode_attn_static",
+           "kvq_strerror", "kvq_abi_version"]
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 class KvqError(RuntimeError):
@@ -70,10 +71,11 @@ def _load():
     lib.kvq_decode_partials.argtypes = dec
     lib.kvq_decode_merge.argtypes = dec
     lib.kvq_dequant.argtypes = [P(Config), P(CacheStruct), i64, i64, vp, vp, vp]
+    lib.kvq_decode_attn_static.argtypes = [P(Config), P(CacheStruct), vp, i64, ctypes.c_float, vp, vp]
     lib.kvq_strerror.argtypes = [ctypes.c_int]
     lib.kvq_strerror.restype = ctypes.c_char_p
     lib.kvq_abi_version.restype = ctypes.c_int32
-    for name in EXPORTS[:7]:
+    for name in EXPORTS[:8]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -217,6 +219,20 @@ class KVCache:
     def decode_merge(self, q, workspace, out, q_pos=None, sm_scale=0.0, stream=None):
         args, _ = self._decode_args(q, q_pos, sm_scale, out, workspace)
         _check(LIB.kvq_decode_merge(*args, _stream(stream)), "kvq_decode_merge")
+
+    def decode_static(self, q, q_pos=None, sm_scale=0.0, out=None, stream=None):
+        """As decode(), through kvq_decode_attn_static: no workspace argument,
+        the library's static per-GPU array instead (nothing is allocated
+        beyond ``out`` when it is not given)."""
+        _need(q, torch.float16, (self.batch, self.hq, 128), "q")
+        if out is None:
+            out = torch.empty((self.batch, self.hq, 128), dtype=torch.float32, device=q.device)
+        _need(out, torch.float32, (self.batch, self.hq, 128), "out")
+        pos = self.length if q_pos is None else int(q_pos)
+        _check(LIB.kvq_decode_attn_static(ctypes.byref(self.cfg), ctypes.byref(self.struct), _ptr(q), pos,
+                                          ctypes.c_float(sm_scale), _ptr(out), _stream(stream)),
+               "kvq_decode_attn_static")
+        return out
 
     def dequant(self, t0=0, t1=None, stream=None):
         """fp32 [batch, t1 - t0, Hkv, 128] keys and values in the stored domain."""
