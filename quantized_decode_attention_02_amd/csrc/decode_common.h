@@ -159,8 +159,7 @@ __device__ __forceinline__ f4_t mfma4(h4_t x, h4_t y, f4_t c) {
 // that the k-steps one instruction writes (one per group of lanes) and the
 // tables one instruction reads (one per half wave) fall in different LDS
 // banks: for four query heads, 64-byte k-steps put the 16 k-steps a
-// probability write spans into 4 banks.  Tables that are written rarely, or
-// that must stay small enough for three work-groups per compute unit, go
+// probability write spans into 4 banks.  Tables that are written rarely go
 // without.
 template <int HL, int NKS, bool KPAD = false, bool TPAD = false>
 struct ATab {

@@ -126,10 +126,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // query tables: per group half (KIVI, rebuilt per group) or one (BLOCK,
   // fixed per pair)
   // padded tables where four query heads make their writes conflict (the
-  // query table only where it is rebuilt per group); the KIVI 2-bit kernel
-  // drops the table pads to stay within three work-groups per compute unit
-  using QTab = ATab<HL, 32, (G == 4 && !BLOCK), (G == 4 && !BLOCK && BITS == 4)>;
-  using PTab = ATab<HL, 16, G == 4, (G == 4 && NDG > 1 && BITS == 4)>;
+  // query table only where it is rebuilt per group)
+  using QTab = ATab<HL, 32, (G == 4 && !BLOCK), (G == 4 && !BLOCK)>;
+  using PTab = ATab<HL, 16, G == 4, (G == 4 && NDG > 1)>;
   __shared__ __attribute__((aligned(16))) _Float16 QL[4][(BLOCK ? 1 : 2) * QTab::T];
   __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
   __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
