@@ -484,242 +484,6 @@ __global__ __launch_bounds__(256) void window_write_kernel(Geom g, Planes p, con
   }
 }
 
-// Sum of a double over a 16-lane row by an xor butterfly: every lane ends with
-// the same bits (each stage adds the same two partial sums, in either order).
-__device__ __forceinline__ double row_sum_f64(double v) {
-  auto add = [&](auto tag) {
-    constexpr int M = decltype(tag)::value;
-    const uint64_t u = __double_as_longlong(v);
-    const uint32_t lo = row_xor<M>((uint32_t)u), hi = row_xor<M>((uint32_t)(u >> 32));
-    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-  };
-  add(std::integral_constant<int, 1>{});
-  add(std::integral_constant<int, 2>{});
-  add(std::integral_constant<int, 4>{});
-  add(std::integral_constant<int, 8>{});
-  return v;
-}
-
-// ---------------------------------------------------------------------------
-// Symmetric 128-value blocks ([trefon] "Przykład: model 27B przy 262K"; "Jak
-// 4-bitowemu cache to uchodzi: najpierw obrót"): per token vector y (rotated
-// when configured) a = max|y|, s_h = fp16(fl32(a / 7)),
-// c = clamp(rint(fl32(y / s_h)), -7, 7) (0 when s_h == 0), stored nibble c + 8.
-// One work-group per 32-token tile that overlaps [T0, T0 + n_new); tokens of the
-// tile outside that range keep their stored nibbles (value tiles hold two
-// tokens per byte).
-__global__ __launch_bounds__(256) void block128_append_kernel(Geom g, Planes p, const __half* k_new,
-                                                              const __half* v_new, int64_t n_new,
-                                                              int64_t T0, int64_t tile0) {
-  // The tile's 64 vectors (32 tokens x keys, values) go through 16 rows of
-  // 16 lanes in four passes: vector 16 pass + row, lane i of a row holding
-  // elements 8i .. 8i + 7, which are also its four packed bytes 4i .. 4i + 3.
-  __shared__ uint32_t vnib[kGroup][32];   // value codes of a token: 8 channels a word (4 bits;
-                                          // 3 bits: 24 bits of 8), 4 a word at 8 bits
-  const int tid = threadIdx.x, row = tid >> 4, i = tid & 15;
-  const int64_t tile = tile0 + blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t pair = pair_index(g, b, h);
-  const int64_t T1 = T0 + n_new;
-  const int64_t tbase = tile * kGroup;
-
-  uint4 raw[4];   // all four passes in flight at once
-#pragma unroll
-  for (int ps = 0; ps < 4; ++ps) {
-    const int v = 16 * ps + row, tensor = v >> 5, tok = v & 31;
-    const int64_t t = tbase + tok;
-    const __half* src = tensor ? v_new : k_new;
-    raw[ps] = (t >= T0 && t < T1)
-                  ? *reinterpret_cast<const uint4*>(src + (((int64_t)b * n_new + (t - T0)) * g.Hkv + h) * kD + 8 * i)
-                  : make_uint4(0, 0, 0, 0);
-  }
-  const int bits = g.hi_bits;            // 4, 3 for the 50-byte block, 8 for Q8_0
-  const int64_t tb = 512 * (int64_t)bits;
-  uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (pair * g.gmax + tile) * tb;
-#pragma unroll
-  for (int ps = 0; ps < 4; ++ps) {
-    const int v = 16 * ps + row, tensor = v >> 5, tok = v & 31;
-    const int64_t t = tbase + tok;
-    const bool in = t >= T0 && t < T1;
-    const uint32_t w[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __half2float(__ushort_as_half((uint16_t)(w[j] & 0xFFFFu)));
-      x[2 * j + 1] = __half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
-    }
-    if (g.hadamard) {
-      if (g.hsigned) fwht128_row16_signed(x, i, g.sign_in, g.sign_out);
-      else fwht128_row16(x, i);
-    }
-    uint16_t sb;
-    uint32_t packed = 0, packed_hi = 0;   // codes 0..7 of the lane (packed_hi: 4..7 at 8 bits)
-    if (g.tbq4) {
-      // TBQ4 ([trefon] "Jak 4-bitowemu cache to uchodzi: najpierw obrót"):
-      // norm = fp16(min(fl32(sqrt(sum y^2)), 65504)), the sum and the root in
-      // fp64 (squares of fp32 values are exact there; the row's xor
-      // butterfly gives every lane the same sum); index = the number of
-      // level midpoints strictly below fl32(y / norm).
-      double ss = 0.0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fma((double)x[j], (double)x[j], ss);
-      ss = row_sum_f64(ss);
-      sb = float_to_half_bits(fminf((float)sqrt(ss), 65504.0f));
-      const float nrm = half_bits_to_float(sb);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float u = nrm != 0.0f ? x[j] / nrm : 0.0f;
-        uint32_t idx = 0;
-#pragma unroll
-        for (int k = 0; k < 15; ++k) idx += u > g.cb_bound[k] ? 1u : 0u;
-        packed |= idx << (4 * j);
-      }
-    } else {
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-      // Q4_0: the absmax of this lane's 32-value slice (lanes 4s .. 4s + 3 of
-      // the row); the 128-block scheme: of the whole row
-      const float a = __uint_as_float(g.q40 ? quad_max_u32(m) : row_max_u32(m));
-      // levels -top .. top: 7 at 4 bits, 3 at 3 bits, 127 at 8 bits (stored
-      // code c + top + 1)
-      const float top = bits == 3 ? 3.0f : bits == 8 ? 127.0f : 7.0f;
-      const float margin = bits == 8 ? 0x1p-14f : 0x1p-18f;
-      sb = float_to_half_bits(a / top);
-      const float s = half_bits_to_float(sb);
-      // rint(fl32(y / s)) by the reciprocal; the half integers that can move a
-      // code clamped to [-top, top] lie in (-top + 0.25, top - 0.25).  If any
-      // lane came close to one, the wave redoes its vectors with the division.
-      float r[8];
-      bool risky = false;
-      const float rs = s != 0.0f ? 1.0f / s : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = quot_fast(x[j], rs, 0.25f - top, top - 0.25f, risky, margin);
-      if (__any(risky)) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = s != 0.0f ? rintf(x[j] / s) : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = s != 0.0f ? (int)fminf(fmaxf(r[j], -top), top) : 0;
-        const uint32_t code = (uint32_t)(c + (int)top + 1);
-        if (bits == 8) {
-          if (j < 4) packed |= code << (8 * j);
-          else packed_hi |= code << (8 * (j - 4));
-        } else {
-          packed |= code << (bits * j);
-        }
-      }
-    }
-    if (tensor == 0) {
-      if (in) {
-        if (bits == 3) {   // 24 bits: row bytes 3i .. 3i + 2 (chunks may differ)
-          for (int k = 0; k < 3; ++k) kt[ktile_offset(tok, 3 * i + k)] = (uint8_t)(packed >> (8 * k));
-        } else if (bits == 8) {   // row bytes 8i .. 8i + 7 (one half of a 16-byte chunk)
-          *reinterpret_cast<uint2*>(kt + ktile_offset(tok, 8 * i)) = make_uint2(packed, packed_hi);
-        } else {
-          *reinterpret_cast<uint32_t*>(kt + ktile_offset(tok, 4 * i)) = packed;
-        }
-      }
-    } else if (bits == 8) {
-      vnib[tok][2 * i] = packed;
-      vnib[tok][2 * i + 1] = packed_hi;
-    } else {
-      vnib[tok][i] = packed;
-    }
-    if (g.q40) {
-      if (in && (i & 3) == 0) {   // one scale per 32-value slice, slices in order
-        uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
-        sp[(pair * g.gmax * kGroup + t) * 4 + (i >> 2)] = sb;
-      }
-    } else if (in && i == 0) {
-      uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
-      sp[pair * g.gmax * kGroup + t] = sb;
-    }
-  }
-  __syncthreads();
-  // value tile: byte (d, k) holds tokens 2k (low nibble) and 2k + 1 (high)
-  // of channel d; a byte with one token outside [T0, T1) keeps that token's
-  // stored nibble.  Thread tid builds bytes 8 tid .. 8 tid + 7 (one row d).
-  uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (pair * g.gmax + tile) * tb;
-  if (bits == 8) {
-    // 8 bits: byte k of row d (32 bytes) is token k's code of channel d;
-    // thread tid builds bytes 16 (tid & 1) .. + 15 of row tid / 2, keeping
-    // the bytes of tokens outside [T0, T1)
-    const int d = tid >> 1, k0 = 16 * (tid & 1);
-    const int wd = 2 * (d >> 3) + ((d & 7) >> 2), sh = 8 * (d & 3);
-    const bool whole = tbase + k0 >= T0 && tbase + k0 + 16 <= T1;
-    uint32_t out[4] = {0, 0, 0, 0};
-    if (!whole) {
-      const uint4 old = *reinterpret_cast<const uint4*>(vt + 32 * d + k0);
-      out[0] = old.x; out[1] = old.y; out[2] = old.z; out[3] = old.w;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int64_t tk = tbase + k0 + k;
-      if (tk < T0 || tk >= T1) continue;
-      const uint32_t byte = (vnib[k0 + k][wd] >> sh) & 0xFFu;
-      out[k >> 2] = (out[k >> 2] & ~(0xFFu << (8 * (k & 3)))) | (byte << (8 * (k & 3)));
-    }
-    const bool any_in = tbase + k0 + 16 > T0 && tbase + k0 < T1;
-    if (any_in) *reinterpret_cast<uint4*>(vt + 32 * d + k0) = make_uint4(out[0], out[1], out[2], out[3]);
-  } else if (bits == 3) {
-    // 3 bits: row d is the 32 tokens' codes as one 96-bit string, token k at
-    // bits 3k; thread d (< 128) rebuilds it, keeping the bits of tokens
-    // outside [T0, T1)
-    if (tid < kD) {
-      const int d = tid, wd = d >> 3, sh = 3 * (d & 7);
-      uint32_t* row32 = reinterpret_cast<uint32_t*>(vt + 12 * d);
-      const bool whole = tbase >= T0 && tbase + kGroup <= T1;
-      uint32_t out[3] = {0, 0, 0};
-      if (!whole) {
-        out[0] = row32[0];
-        out[1] = row32[1];
-        out[2] = row32[2];
-      }
-      for (int k = 0; k < kGroup; ++k) {
-        const int64_t tk = tbase + k;
-        if (tk < T0 || tk >= T1) continue;
-        const uint32_t code = (vnib[k][wd] >> sh) & 7u;
-        const int bit = 3 * k, w0 = bit >> 5, b0 = bit & 31;
-        out[w0] = (out[w0] & ~(7u << b0)) | (code << b0);
-        if (b0 > 29) {   // the code straddles two words
-          const int nb = 32 - b0;
-          out[w0 + 1] = (out[w0 + 1] & ~(7u >> nb)) | (code >> nb);
-        }
-      }
-      const bool any_in = tbase + kGroup > T0 && tbase < T1;
-      if (any_in) {
-        row32[0] = out[0];
-        row32[1] = out[1];
-        row32[2] = out[2];
-      }
-    }
-  } else {
-    const int d = tid >> 1, kb0 = 8 * (tid & 1);
-    const int wd = d >> 3, sh = 4 * (d & 7);
-    const bool whole = tbase + 2 * kb0 >= T0 && tbase + 2 * kb0 + 16 <= T1;
-    uint32_t out[2] = {0, 0};
-    if (!whole) {
-      const uint2 old = *reinterpret_cast<const uint2*>(vt + 8 * tid);
-      out[0] = old.x;
-      out[1] = old.y;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int kb = kb0 + k;
-      const int64_t t0 = tbase + 2 * kb, t1 = t0 + 1;
-      const bool in0 = t0 >= T0 && t0 < T1, in1 = t1 >= T0 && t1 < T1;
-      uint32_t byte = (out[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-      if (in0) byte = (byte & 0xF0u) | ((vnib[2 * kb][wd] >> sh) & 0xFu);
-      if (in1) byte = (byte & 0x0Fu) | (((vnib[2 * kb + 1][wd] >> sh) & 0xFu) << 4);
-      out[k >> 2] = (out[k >> 2] & ~(0xFFu << (8 * (k & 3)))) | (byte << (8 * (k & 3)));
-    }
-    const bool any_in = tbase + 2 * kb0 + 16 > T0 && tbase + 2 * kb0 < T1;
-    if (any_in) *reinterpret_cast<uint2*>(vt + 8 * tid) = make_uint2(out[0], out[1]);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Split-half RoPE table for pre-RoPE keys ([troisinh] "Tại sao nó hoạt
 // động", item 3): row t holds (cos, sin) of t * theta_j, theta_j =
@@ -788,16 +552,6 @@ hipError_t launch_window_write(const Geom& g, const Planes& p, const __half* k_n
     const int64_t items = 2 * (int64_t)g.B * (w1 - w0) * g.Hkv * 16;
     hipLaunchKernelGGL(window_write_kernel, dim3(grid_for(items)), dim3(256), 0, s, g, p, k_new, v_new,
                        n_new, T0, w0, w1 - w0);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_block128_append(const Geom& g, const Planes& p, const __half* k_new,
-                                  const __half* v_new, int64_t n_new, int64_t T0, hipStream_t s) {
-  if (n_new > 0) {
-    const int64_t tile0 = T0 / kGroup, tile1 = (T0 + n_new + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL(block128_append_kernel, dim3((unsigned)(tile1 - tile0), g.Hkv, g.B), dim3(256), 0,
-                       s, g, p, k_new, v_new, n_new, T0, tile0);
   }
   return hipGetLastError();
 }

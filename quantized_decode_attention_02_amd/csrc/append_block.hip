@@ -1,0 +1,653 @@
+// Quantize-on-append for the block formats: symmetric 128-value blocks at 4
+// or 3 bits, TBQ4, Q4_0 and Q8_0, each optionally after the (randomized)
+// normalized Hadamard rotation.
+//
+// Sources cited here:
+//   [trefon] "Matematyka cache KV: ile kosztuje długi kontekst i co daje
+//            4-bitowy cache" (trefon.com): "Przykład: model 27B przy 262K"
+//            (the block formats and their sizes), "Jak 4-bitowemu cache to
+//            uchodzi: najpierw obrót" (the rotation, TBQ4).
+//
+// Every stored byte is bit-exact with the float32 definitions: the FWHT in
+// its fixed stage order h = 1, 2, ..., 64, one IEEE operation per step, then
+// fl32(1/sqrt(128)) scaling; s_h = fp16(fl32(a / top)) with a the absmax of
+// the (scaled) block; code = clamp(rint(fl32(y / s_h)), -top, top) + top + 1
+// (0 when s_h == 0); TBQ4: n_h = fp16(min(fl32(sqrt(sum y^2) in fp64),
+// 65504)), index = number of fp32 boundaries strictly below fl32(y / n_h).
+//
+// Layout of the work: a wave item is one tensor (keys or values) of one
+// 32-token tile of one (sequence, kv head) pair; each wave takes a
+// contiguous run of items, and lanes v and v + 32 own token v's vector,
+// elements 0..63 and 64..127.  Every FWHT stage but the last stays inside
+// the lane; the last trades half a register set between the two lanes with
+// v_permlane32_swap, after which each lane holds whole (x_e, x_{e+64}) pairs
+// (7.5 fp32 operations an element for the transform, the fp16 -> fp32
+// conversion folded into stage h = 1 by v_fma_mix).  The vectors enter
+// through LDS: the wave reads them with 16-byte loads, four tokens' rows a
+// load, and writes them to its LDS area with the 16-byte chunks of row v
+// rotated by v mod 16 (chunk c at slot c ^ (v & 15)), so that the
+// lane-per-half-row reads hit 16 different bank quads.  The next item's
+// loads are in flight while the current one is computed.  Value codes leave
+// through the same area, transposed from token rows to the channel rows of
+// the value tile.  No work-group barrier after the set-up: waves are
+// independent.
+//
+// Codes come from one fma per end of a bracket: with crs = fl32(c / s_h)
+// (c the scaling, or 1), fma(x, crs (1 -+ 2^-21), 2^23 + top + 1) rounds
+// the bracket's ends to integers, code + offset in the low bits.  The
+// exact quotient fl32(fl32(x c) / s_h) lies strictly inside the bracket
+// (its distance from x crs is below 2^-22 relative), so where both ends
+// round alike it rounds the same way; otherwise -- near a half integer,
+// about one unit of eight codes in 2^14 -- the wave redoes those codes
+// with the division.  A subnormal fp16 scale (the only case where a code
+// can leave [-top, top] before the clamp) always takes the division.
+#pragma clang fp contract(off)
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTr = 36;   // dwords per row of the code transpose: 32 tokens + 4 (rows 36 dwords
+                          // apart: 16 rows read at one offset hit 16 different bank quads)
+
+// fp32 2^23: for |v| < 2^22, fma(x, r, 2^23 + o) is x r + o rounded to an
+// integer (ulp 1 in [2^23, 2^24)), which lands in the low mantissa bits.
+constexpr float kTwo23 = 8388608.0f;
+
+template <int BITS>
+struct Sym {
+  static constexpr int kTop = BITS == 3 ? 3 : (BITS == 8 ? 127 : 7);
+  static constexpr int kRowWords = 4 * BITS;        // dwords of a key row: 12, 16, 32
+  static constexpr int kPer = BITS == 8 ? 4 : 8;    // codes per packed unit
+  static constexpr int kUnits = kD / kPer;          // units: a dword (8 bits: 4 codes, 4 bits:
+                                                    // 8 codes) or a 24-bit group (3 bits: 8 codes)
+};
+
+// One launch: the tokens [T0, T0 + n) of an append whose source rows are
+// (b, t - src_t0, h) of a [batch, src_tokens, Hkv, 128] fp16 array.
+struct SegArgs {
+  const __half* k_new;
+  const __half* v_new;
+  int64_t src_tokens, src_t0;
+  int64_t T0, n;
+  int64_t tile0, n_tiles, n_items;
+};
+
+// Item coordinates (wave-uniform).
+struct Item {
+  int64_t pair, tb;    // tb: first token of the item's tile
+  int b, h, tensor;    // tensor 0: keys, 1: values
+};
+
+__device__ __forceinline__ Item item_at(const Geom& g, int64_t it, int64_t tile0, int64_t n_tiles) {
+  Item r;
+  r.tensor = (int)(it & 1);
+  const int64_t rest = it >> 1;
+  r.pair = rest / n_tiles;
+  r.b = (int)(r.pair / g.Hkv);
+  r.h = (int)(r.pair % g.Hkv);
+  r.tb = (tile0 + rest % n_tiles) * kGroup;
+  return r;
+}
+
+// Pack the low `B`-bit fields of eight words f[0..7] (each a code in its low
+// bits, zero above up to bit 23, anything from bit 24 on) as f[j] << (B j).
+// Shifts of 8 or more push the high garbage out; the low fields go through
+// one masked merge.
+template <int B>
+__device__ __forceinline__ uint32_t pack8(const uint32_t* f) {
+  if (B == 4) {   // nibble pairs as bytes, then the four bytes by byte permutes
+    const uint32_t b01 = (f[1] << 4) | f[0], b23 = (f[3] << 4) | f[2];
+    const uint32_t b45 = (f[5] << 4) | f[4], b67 = (f[7] << 4) | f[6];
+    const uint32_t lo = __builtin_amdgcn_perm(b23, b01, 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b67, b45, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  } else {        // B == 3: 24 bits
+    uint32_t acc = f[7] << 21;
+    acc |= f[6] << 18;
+    acc |= f[5] << 15;
+    acc |= f[4] << 12;
+    acc |= f[3] << 9;
+    const uint32_t lo = (((f[2] << 6) | (f[1] << 3)) | f[0]);
+    return ((lo & 0x1FFu) | acc) & 0xFFFFFFu;
+  }
+}
+__device__ __forceinline__ uint32_t pack4x8(const uint32_t* f) {
+  const uint32_t lo = __builtin_amdgcn_perm(f[1], f[0], 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(f[3], f[2], 0x0C0C0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// (a ^ b) + c in one instruction; opaque to the compiler, which would
+// otherwise split the accumulation of a bracket's disagreement into a
+// compare and select per element.
+__device__ __forceinline__ uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// fp32 of the low (sel 0) or high (sel 1) fp16 half of w, plus or minus the
+// other half, rounded once: v_fma_mix_f32 with the fp16 operands converted
+// exactly inside the instruction (a + b and a - b are the same IEEE
+// operations as fma(a, 1, b) and fma(b, -1, a)).
+__device__ __forceinline__ float mix_sum(uint32_t w) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+  return d;
+}
+__device__ __forceinline__ float mix_diff(uint32_t w) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+  return d;
+}
+
+// 8 x 8 transpose of 4-bit fields: in[i] holds row i (field j at bits 4j);
+// out[j] holds column j (field i at bits 4i).
+__device__ __forceinline__ void transpose_nib8(const uint32_t* in, uint32_t* out) {
+  uint32_t a[8], b[8];
+  // 4 x 4 blocks of fields: the halves of rows i and i + 4
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_amdgcn_perm(in[i + 4], in[i], 0x05040100u);       // lo(i), lo(i + 4)
+    a[i + 4] = __builtin_amdgcn_perm(in[i + 4], in[i], 0x07060302u);   // hi(i), hi(i + 4)
+  }
+  // 2 x 2 blocks: bytes of rows r and r + 2
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = 4 * q + r;
+      b[i] = __builtin_amdgcn_perm(a[i + 2], a[i], 0x06020400u);       // bytes 0, 2 of each
+      b[i + 2] = __builtin_amdgcn_perm(a[i + 2], a[i], 0x07030501u);   // bytes 1, 3 of each
+    }
+  }
+  // single fields: rows r and r + 1
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t x = b[i], y = b[i + 1];
+    b[i] = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+    b[i + 1] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+  }
+  // b[k] now holds column j(k) with its fields in row order
+  out[0] = b[0]; out[1] = b[1]; out[2] = b[2]; out[3] = b[3];
+  out[4] = b[4]; out[5] = b[5]; out[6] = b[6]; out[7] = b[7];
+}
+
+// 4 x 4 transpose of bytes.
+__device__ __forceinline__ void transpose_byte4(const uint32_t* in, uint32_t* out) {
+  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Mask of the fields [lo, hi) of width W in a word whose fields start at
+// bit `first` (fields outside the word ignored).
+__device__ __forceinline__ uint32_t field_mask(int lo, int hi, int first, int W) {
+  const int b0 = min(max(lo * W - first, 0), 32), b1 = min(max(hi * W - first, 0), 32);
+  const uint32_t upto1 = b1 >= 32 ? 0xFFFFFFFFu : ((1u << b1) - 1u);
+  const uint32_t upto0 = b0 >= 32 ? 0xFFFFFFFFu : ((1u << b0) - 1u);
+  return upto1 & ~upto0;
+}
+
+// Value of `v` in the lane 32 apart (the other half of the lane's vector).
+__device__ __forceinline__ uint32_t other_half(uint32_t v, int half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return half ? r[0] : r[1];
+}
+
+template <int BITS, bool Q40, int HAD, bool TBQ>
+__global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, SegArgs a) {
+  constexpr int kTop = Sym<BITS>::kTop;
+  constexpr int kPer = Sym<BITS>::kPer;
+  constexpr int kUnits = Sym<BITS>::kUnits;
+  constexpr int kLU = kUnits / 2;            // units of one lane (half a vector)
+  constexpr int64_t kTileBytes = 512 * BITS;
+  // LDS of one wave: the tile's 32 fp16 vectors, later its value-code transpose
+  constexpr int kWaveLds = (kGroup * kD * 2 > kUnits * kTr * 4) ? kGroup * kD * 2 : kUnits * kTr * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kWaveLds];
+  __shared__ __attribute__((aligned(16))) uint32_t sgn_in[64];    // randomized rotation: fp16 pair
+                                                                   // sign masks (bits 15, 31)
+  __shared__ __attribute__((aligned(16))) uint32_t sgn_out[32];   // negation masks of packed codes
+  __shared__ __attribute__((aligned(16))) uint32_t sgn_f[kD];     // TBQ4: fp32 output sign masks
+  if (HAD == 2) {
+    const int t = threadIdx.x;
+    if (t < 64) {
+      const uint32_t w = mask_word(g.sign_in, t >> 4);
+      const int bit = (2 * t) & 31;
+      sgn_in[t] = (((w >> bit) & 1u) << 15) | (((w >> (bit + 1)) & 1u) << 31);
+    } else if (t < 64 + kUnits && !TBQ) {
+      const int m = t - 64;
+      uint32_t mk = 0;
+      for (int j = 0; j < kPer; ++j) {
+        const int c = kPer * m + j;
+        if ((mask_word(g.sign_out, c >> 5) >> (c & 31)) & 1u) mk |= ((1u << BITS) - 1u) << (BITS * j);
+      }
+      sgn_out[m] = mk;
+    } else if (t >= 128 && TBQ) {
+      const int c = t - 128;
+      sgn_f[c] = ((mask_word(g.sign_out, c >> 5) >> (c & 31)) & 1u) << 31;
+    }
+    __syncthreads();
+  }
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int half = lane >> 5, v = lane & 31;   // vector v of the tile, elements 64 half ..
+  // this wave's items: a contiguous run [i0, i1) of (pair, tile, tensor)
+  // in that order, tensor fastest
+  const int64_t nwaves = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t i0 = gw * a.n_items / nwaves, i1 = (gw + 1) * a.n_items / nwaves;
+  if (i0 >= i1) return;
+  uint8_t* reg = lds + wv * kWaveLds;
+  const int64_t T0 = a.T0, T1 = a.T0 + a.n;
+  const uint32_t rowbytes = (uint32_t)g.Hkv * kD * 2;
+
+  // 16-byte chunk (lane & 15) of the rows of tokens tb + 4 i + (lane >> 4);
+  // rows outside the segment are replaced by the nearest row inside (never
+  // used).  The row offset from the pair's first segment row fits 32 bits.
+#define KVQ_ISSUE_ROWS(it)                                                                      \
+  {                                                                                             \
+    const uint8_t* base_ = reinterpret_cast<const uint8_t*>(                                    \
+        ((it).tensor ? a.v_new : a.k_new) +                                                     \
+        (((int64_t)(it).b * a.src_tokens + (T0 - a.src_t0)) * g.Hkv + (it).h) * kD);             \
+    const int r0_ = (int)((it).tb - T0) + (lane >> 4);                                         \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                             \
+      const int tr_ = min(max(r0_ + 4 * i, 0), (int)a.n - 1);                                   \
+      raw[i] = *reinterpret_cast<const u32x4*>(base_ + ((uint32_t)tr_ * rowbytes +              \
+                                                        16u * (uint32_t)(lane & 15)));          \
+    }                                                                                           \
+  }
+
+  Item cur = item_at(g, i0, a.tile0, a.n_tiles);
+  u32x4 raw[8];
+  KVQ_ISSUE_ROWS(cur)
+  for (int64_t item = i0;; ++item) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4), c = lane & 15;
+      *reinterpret_cast<u32x4*>(reg + row * 256 + 16 * (c ^ (row & 15))) = raw[i];
+    }
+    // the next item's rows (past the last item: this item's again, from L2)
+    Item nit = cur;
+    if (item + 1 < i1) {
+      nit.tensor ^= 1;
+      if (nit.tensor == 0) {
+        nit.tb += kGroup;
+        if (nit.tb == (a.tile0 + a.n_tiles) * kGroup) {
+          nit.tb = a.tile0 * kGroup;
+          ++nit.pair;
+          if (++nit.h == g.Hkv) {
+            nit.h = 0;
+            ++nit.b;
+          }
+        }
+      }
+    }
+    KVQ_ISSUE_ROWS(nit)
+
+    // ---- half a vector: elements 64 half + k in r[k]; fp16 -> fp32 with
+    // stage h = 1, stages 2 .. 32 in the lane, stage 64 with the other half
+    float r[64];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int chunk = 8 * half + c;
+      const u32x4 q = *reinterpret_cast<const u32x4*>(reg + v * 256 + 16 * (chunk ^ (v & 15)));
+      u32x4 sg = {0u, 0u, 0u, 0u};
+      if (HAD == 2) sg = *reinterpret_cast<const u32x4*>(sgn_in + 4 * chunk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = q[k] ^ sg[k];
+        if (HAD) {
+          r[8 * c + 2 * k] = mix_sum(w);
+          r[8 * c + 2 * k + 1] = mix_diff(w);
+        } else {
+          r[8 * c + 2 * k] = __half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
+          r[8 * c + 2 * k + 1] = __half2float(__ushort_as_half((uint16_t)(w >> 16)));
+        }
+      }
+    }
+    if (HAD) {
+#pragma unroll
+      for (int hs = 2; hs < 64; hs <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+          if (j & hs) continue;
+          const float a = r[j], b = r[j + hs];
+          r[j] = a + b;
+          r[j + hs] = a - b;
+        }
+      }
+      // stage 64: the halves trade r[32 ..] of the lower and r[.. 31] of the
+      // upper, so each lane holds pairs (x_e, x_{e+64}) as (r[i], r[32 + i])
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[i]), __float_as_uint(r[32 + i]),
+                                                         false, false);
+        const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+        r[i] = a + b;
+        r[32 + i] = a - b;
+      }
+    }
+    // channel of r[k]: transformed: k + 32 half, +32 for k >= 32 (lower half:
+    // 0..31, 64..95; upper: 32..63, 96..127); plain: 64 half + k
+    auto chan = [&](int k) { return HAD ? k + 32 * half + (k >= 32 ? 32 : 0) : 64 * half + k; };
+
+    // ---- codes (r holds the unscaled transform when rotated: y = fl32(r c))
+    const int64_t t = cur.tb + v;
+    const bool valid = t >= T0 && t < T1;
+    uint32_t U[kLU];       // packed codes: lane unit u = r[kPer u .. kPer u + kPer - 1]
+    uint32_t sbw = 0;      // this lane's fp16 scales (Q4_0 / Q8_0: its two slices)
+    if (TBQ) {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        float y = r[j] * c32();
+        if (HAD == 2) y = __uint_as_float(__float_as_uint(y) ^ sgn_f[chan(j)]);
+        r[j] = y;
+        ss = fma((double)y, (double)y, ss);
+      }
+      const uint64_t sbits = (uint64_t)__double_as_longlong(ss);
+      const uint32_t olo = other_half((uint32_t)sbits, half), ohi = other_half((uint32_t)(sbits >> 32), half);
+      ss = ss + __longlong_as_double((long long)(((uint64_t)ohi << 32) | olo));
+      const uint16_t nb = float_to_half_bits(fminf((float)sqrt(ss), 65504.0f));
+      sbw = nb;
+      const float nrm = half_bits_to_float(nb);
+#pragma unroll
+      for (int u = 0; u < kLU; ++u) {
+        uint32_t f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float uq = nrm != 0.0f ? r[8 * u + j] / nrm : 0.0f;
+          uint32_t idx = 0;
+#pragma unroll
+          for (int k = 0; k < 15; ++k) idx += uq > g.cb_bound[k] ? 1u : 0u;
+          f[j] = idx;
+        }
+        U[u] = pack8<4>(f);
+      }
+    } else {
+      // per slice: a, s_h, 1/s_h folded with the scaling, and a bracket
+      // clo <= c / s_h <= chi around it (relative 2^-21 each way)
+      constexpr int kLS = Q40 ? 2 : 1;   // slices of this lane: r[0..31], r[32..63]
+      float s[kLS], clo[kLS], chi[kLS];
+      bool exact_lane = false;
+#pragma unroll
+      for (int sl = 0; sl < kLS; ++sl) {
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 64 / kLS; ++j) am = fmaxf(am, fabsf(r[sl * (64 / kLS) + j]));
+        if (!Q40) am = fmaxf(am, __uint_as_float(other_half(__float_as_uint(am), half)));
+        const float a = HAD ? am * c32() : am;
+        const uint16_t sb = float_to_half_bits(a / (float)kTop);
+        sbw |= (uint32_t)sb << (16 * sl);
+        s[sl] = half_bits_to_float(sb);
+        const float rs = s[sl] != 0.0f ? 1.0f / s[sl] : 0.0f;
+        const float crs = HAD ? rs * c32() : rs;
+        clo[sl] = crs * (1.0f - 0x1p-21f);
+        chi[sl] = crs * (1.0f + 0x1p-21f);
+        // a subnormal fp16 scale can push quotients past the code range
+        exact_lane |= s[sl] != 0.0f && s[sl] < 0x1p-14f;
+      }
+      const float magic = kTwo23 + (float)(kTop + 1);
+#pragma unroll
+      for (int u = 0; u < kLU; ++u) {
+        const int sl = Q40 ? (kPer * u) / 32 : 0;
+        uint32_t f[8];
+        uint32_t diff = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const float xv = r[kPer * u + j];
+          const uint32_t lo = __float_as_uint(fmaf(xv, clo[sl], magic));
+          const uint32_t hi = __float_as_uint(fmaf(xv, chi[sl], magic));
+          diff = xor_add(lo, hi, diff);
+          f[j] = lo;
+        }
+        // the bracket's ends round alike, so does the exact quotient in
+        // between; otherwise (rare) the wave redoes the unit by division
+        if (__builtin_expect(__any(diff != 0u || exact_lane), 0)) {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            const float y = HAD ? r[kPer * u + j] * c32() : r[kPer * u + j];
+            const float q = s[sl] != 0.0f ? rintf(y / s[sl]) : 0.0f;
+            const int c = (int)fminf(fmaxf(q, (float)-kTop), (float)kTop);
+            f[j] = (uint32_t)(c + kTop + 1);
+          }
+        }
+        uint32_t packed = BITS == 8 ? pack4x8(f) : pack8<BITS>(f);
+        if (HAD == 2) {   // negated coordinates: code 2 (top + 1) - code, fieldwise
+          const uint32_t mk = sgn_out[chan(kPer * u) / kPer];
+          const uint32_t ones = BITS == 8 ? 0x01010101u : (BITS == 4 ? 0x11111111u : 0x249249u);
+          packed = (packed ^ mk) + (mk & ones);
+        }
+        U[u] = packed;
+      }
+    }
+
+    // ---- store: scales, then key rows or value tiles
+    const int64_t tile = cur.tb / kGroup;
+    if (Q40) {   // four slices, two in each half
+      const uint32_t o = other_half(sbw, half);
+      if (valid && half == 0) {   // transformed: slices 0, 2 here, 1, 3 there; plain: 0, 1 | 2, 3
+        uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[cur.tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
+        *reinterpret_cast<uint2*>(sp + (cur.pair * g.gmax * kGroup + t) * 4) =
+            HAD ? make_uint2((sbw & 0xFFFFu) | (o << 16), (sbw >> 16) | (o & 0xFFFF0000u)) : make_uint2(sbw, o);
+      }
+    } else if (valid && half == 0) {
+      uint16_t* sp = reinterpret_cast<uint16_t*>(p.p[cur.tensor ? KVQ_PLANE_V_META : KVQ_PLANE_K_META]);
+      sp[cur.pair * g.gmax * kGroup + t] = (uint16_t)sbw;
+    }
+    if (cur.tensor == 0) {
+      uint8_t* kt = p.p[KVQ_PLANE_K_HI] + (cur.pair * g.gmax + tile) * kTileBytes + v * 16;
+      if (BITS == 3) {
+        // 384-bit row, channel c at bit 3c: this lane's two 96-bit runs
+        // (channels chan(0) .., chan(32) ..) are words 3 chan(0) / 32 ..;
+        // the 16-byte chunks straddle the halves: the lower half writes
+        // chunks 0 and 1, the upper chunk 2, each with words of the other
+        uint32_t A[6];
+        A[0] = U[0] | (U[1] << 24);
+        A[1] = (U[1] >> 8) | (U[2] << 16);
+        A[2] = (U[2] >> 16) | (U[3] << 8);
+        A[3] = U[4] | (U[5] << 24);
+        A[4] = (U[5] >> 8) | (U[6] << 16);
+        A[5] = (U[6] >> 16) | (U[7] << 8);
+        // transformed: lower half = words 0-2, 6-8, upper = 3-5, 9-11;
+        // plain: lower = words 0-5, upper = 6-11
+        if (HAD) {
+          const uint32_t x0 = other_half(A[0], half), x1 = other_half(A[1], half),
+                         x2 = other_half(A[2], half), x5 = other_half(A[5], half);
+          if (valid) {
+            if (half == 0) {
+              *reinterpret_cast<uint4*>(kt) = make_uint4(A[0], A[1], A[2], x0);
+              *reinterpret_cast<uint4*>(kt + 512) = make_uint4(x1, x2, A[3], A[4]);
+            } else {
+              *reinterpret_cast<uint4*>(kt + 1024) = make_uint4(x5, A[3], A[4], A[5]);
+            }
+          }
+        } else {
+          const uint32_t x0 = other_half(A[0], half), x1 = other_half(A[1], half);
+          if (valid) {
+            if (half == 0) {
+              *reinterpret_cast<uint4*>(kt) = make_uint4(A[0], A[1], A[2], A[3]);
+              *reinterpret_cast<uint4*>(kt + 512) = make_uint4(A[4], A[5], x0, x1);
+            } else {
+              *reinterpret_cast<uint4*>(kt + 1024) = make_uint4(A[2], A[3], A[4], A[5]);
+            }
+          }
+        }
+      } else if (valid) {
+        // each run of four units is one 16-byte chunk of the row
+#pragma unroll
+        for (int q = 0; q < kLU / 4; ++q) {
+          const int chunk = chan(4 * kPer * q) * BITS / 128;
+          *reinterpret_cast<uint4*>(kt + chunk * 512) =
+              make_uint4(U[4 * q], U[4 * q + 1], U[4 * q + 2], U[4 * q + 3]);
+        }
+      }
+    } else {
+      // token rows -> channel rows through the LDS area (the row reads above
+      // are complete: their values are in registers; one wave's LDS
+      // operations run in order)
+      uint32_t* tr = reinterpret_cast<uint32_t*>(reg);
+#pragma unroll
+      for (int u = 0; u < kLU; ++u) tr[(chan(kPer * u) / kPer) * kTr + v] = U[u];
+      const int64_t rlo = T0 - cur.tb, rhi = T1 - cur.tb;
+      const int vlo = rlo < 0 ? 0 : (rlo > kGroup ? kGroup : (int)rlo);
+      const int vhi = rhi < 0 ? 0 : (rhi > kGroup ? kGroup : (int)rhi);
+      uint8_t* vt = p.p[KVQ_PLANE_V_HI] + (cur.pair * g.gmax + tile) * kTileBytes;
+      if (BITS == 4) {
+        // lane: channels 8 cg .. 8 cg + 7, tokens 8 tg .. 8 tg + 7
+        const int cg = lane & 15, tg = lane >> 4;
+        const uint32_t* src = tr + cg * kTr + 8 * tg;
+        uint32_t a[8], o[8];
+        const uint4 q0 = *reinterpret_cast<const uint4*>(src), q1 = *reinterpret_cast<const uint4*>(src + 4);
+        a[0] = q0.x; a[1] = q0.y; a[2] = q0.z; a[3] = q0.w;
+        a[4] = q1.x; a[5] = q1.y; a[6] = q1.z; a[7] = q1.w;
+        transpose_nib8(a, o);
+        const int lo = vlo - 8 * tg < 0 ? 0 : vlo - 8 * tg, hi = vhi - 8 * tg > 8 ? 8 : vhi - 8 * tg;
+        if (hi > lo) {
+          const uint32_t mk = field_mask(lo, hi, 0, 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(vt + 16 * (8 * cg + j) + 4 * tg);
+            uint32_t w = o[j];
+            if (mk != 0xFFFFFFFFu) w = (w & mk) | (*dst & ~mk);
+            *dst = w;
+          }
+        }
+      } else if (BITS == 8) {
+        // lane: channels 4 cg .. 4 cg + 3, tokens 16 tq .. 16 tq + 15
+        const int cg = lane & 31, tq = lane >> 5;
+        const uint32_t* src = tr + cg * kTr + 16 * tq;
+        uint32_t o[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint4 q = *reinterpret_cast<const uint4*>(src + 4 * k);
+          const uint32_t in[4] = {q.x, q.y, q.z, q.w};
+          uint32_t out[4];
+          transpose_byte4(in, out);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j][k] = out[j];
+        }
+        if (vhi > 16 * tq && vlo < 16 * tq + 16) {
+          const bool whole = vlo <= 16 * tq && vhi >= 16 * tq + 16;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint4* dst = reinterpret_cast<uint4*>(vt + 32 * (4 * cg + j) + 16 * tq);
+            uint32_t w[4] = {o[j][0], o[j][1], o[j][2], o[j][3]};
+            if (!whole) {
+              const uint4 old = *dst;
+              const uint32_t ol[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const uint32_t mk = field_mask(vlo, vhi, 8 * (16 * tq + 4 * k), 8);
+                w[k] = (w[k] & mk) | (ol[k] & ~mk);
+              }
+            }
+            *dst = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      } else {   // BITS == 3
+        // lane: channels 8 cg + 2 jq, + 1, all 32 tokens; row d is one
+        // 96-bit string, token k at bits 3k
+        const int cg = lane & 15, jq = lane >> 4;
+        const uint32_t* src = tr + cg * kTr;
+        uint32_t a[32];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint4 q = *reinterpret_cast<const uint4*>(src + 4 * k);
+          a[4 * k] = q.x; a[4 * k + 1] = q.y; a[4 * k + 2] = q.z; a[4 * k + 3] = q.w;
+        }
+        if (vhi > vlo) {
+          const bool whole = vlo == 0 && vhi == kGroup;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * jq + e;
+            uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k) {
+              const uint32_t code = (a[k] >> (3 * j)) & 7u;
+              const int bit = 3 * k;
+              o[bit >> 5] |= code << (bit & 31);
+              if ((bit & 31) > 29) o[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+            }
+            uint32_t* dst = reinterpret_cast<uint32_t*>(vt + 12 * (8 * cg + j));
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+              uint32_t val = o[w];
+              if (!whole) {
+                const uint32_t mk = field_mask(vlo, vhi, 32 * w, 3);
+                val = (val & mk) | (dst[w] & ~mk);
+              }
+              dst[w] = val;
+            }
+          }
+        }
+      }
+    }
+    if (item + 1 >= i1) break;
+    cur = nit;
+  }
+#undef KVQ_ISSUE_ROWS
+}
+
+template <int BITS, bool Q40, int HAD, bool TBQ>
+hipError_t launch_one(const Geom& g, const Planes& p, const SegArgs& a, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&block_append_kernel<BITS, Q40, HAD, TBQ>);
+  const int64_t resident = (int64_t)occupancy_wgs_per_cu(fn) * device_compute_units();
+  int64_t wgs = (a.n_items + 3) / 4;
+  if (wgs > resident) wgs = resident;
+  hipLaunchKernelGGL((block_append_kernel<BITS, Q40, HAD, TBQ>), dim3((unsigned)wgs), dim3(256), 0, s, g, p, a);
+  return hipGetLastError();
+}
+
+template <int BITS, bool Q40, bool TBQ>
+hipError_t launch_had(const Geom& g, const Planes& p, const SegArgs& a, hipStream_t s) {
+  if (g.hadamard && g.hsigned) return launch_one<BITS, Q40, 2, TBQ>(g, p, a, s);
+  if (g.hadamard) return launch_one<BITS, Q40, 1, TBQ>(g, p, a, s);
+  if (TBQ) return hipErrorInvalidValue;
+  return launch_one<BITS, Q40, 0, false>(g, p, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_block128_append(const Geom& g, const Planes& p, const __half* k_new,
+                                  const __half* v_new, int64_t n_new, int64_t T0, hipStream_t s) {
+  if (n_new <= 0) return hipSuccess;
+  // segments of whole tiles whose rows lie within 4 GiB of their first row
+  const int64_t row_bytes = (int64_t)g.Hkv * kD * 2;
+  const int64_t seg_tokens = ((((int64_t)1 << 32) - 1) / row_bytes) / kGroup * kGroup;
+  const int64_t T1 = T0 + n_new;
+  for (int64_t ts = T0; ts < T1;) {
+    int64_t te = (ts / kGroup) * kGroup + seg_tokens;
+    if (te > T1) te = T1;
+    SegArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.src_tokens = n_new;
+    a.src_t0 = T0;
+    a.T0 = ts;
+    a.n = te - ts;
+    a.tile0 = ts / kGroup;
+    a.n_tiles = (te + kGroup - 1) / kGroup - a.tile0;
+    a.n_items = (int64_t)g.B * g.Hkv * a.n_tiles * 2;
+    hipError_t e;
+    if (g.tbq4) e = launch_had<4, false, true>(g, p, a, s);
+    else if (g.hi_bits == 8) e = launch_had<8, true, false>(g, p, a, s);
+    else if (g.hi_bits == 3) e = launch_had<3, false, false>(g, p, a, s);
+    else if (g.q40) e = launch_had<4, true, false>(g, p, a, s);
+    else e = launch_had<4, false, false>(g, p, a, s);
+    if (e != hipSuccess) return e;
+    ts = te;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvq
