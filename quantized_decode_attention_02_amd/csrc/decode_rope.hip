@@ -212,36 +212,6 @@ __device__ __forceinline__ void read_value_codes(const uint8_t* stv, int lane, u
   }
 }
 
-// cursor_next (decode_common.h) that leaves the claim of a new chunk to the
-// caller (*claim set), so that the claim has one issue site in the tile loop:
-// the atomic's result then goes straight into the cursor's register, and no
-// register copy (which would wait for the atomic at once) is needed.
-__device__ __forceinline__ bool cursor_next_deferred(const MfmaArgs& a, TileCursor& c, int lane, bool* ends,
-                                                     bool* claim) {
-  *ends = false;
-  *claim = false;
-  if (c.t + 1 < c.t_stop) {
-    ++c.t;
-    return true;
-  }
-  const int64_t got = claim_value(c.pend);
-  const int64_t ch = a.team + got;
-  if (ch < a.n_chunks) {
-    chunk_range(a, ch, &c.t, &c.t_stop);
-    *claim = true;
-    return true;
-  }
-  claim_done(a, a.ctr + c.pair * kCounterStride, got, lane);
-  *ends = true;
-  const int64_t nxt = c.asg + 4 * a.pwgs;
-  if (nxt >= a.pairs * a.team) return false;
-  c.asg = nxt;
-  team_member(a, nxt, &c.pair, &c.k);
-  chunk_range(a, c.k, &c.t, &c.t_stop);
-  *claim = true;
-  return true;
-}
-
 template <int G, int BITS>
 __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // value-side MFMAs per k-step (hi/lo of p')
