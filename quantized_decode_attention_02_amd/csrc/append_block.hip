@@ -53,6 +53,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTr = 36;   // dwords per row of the code transpose: 32 tokens + 4 (rows 36 dwords
                           // apart: 16 rows read at one offset hit 16 different bank quads)
 
+// TBQ4 index lookup: |u| is bucketed by its exponent and top two mantissa
+// bits (buckets 25% wide or less) from 2^-8 up; bucket 0 is [0, 1.25 2^-8),
+// the last everything from 2^-2.  Consecutive decision boundaries of the
+// codebook are more than 25% apart above 0.02, so a bucket holds at most one
+// (checked when the table is built).
+constexpr int kTbqBuckets = 25;
+constexpr int kTbqT0 = (127 - 8) << 2;   // (exponent, 2 mantissa bits) of 2^-8
+
 // fp32 2^23: for |v| < 2^22, fma(x, r, 2^23 + o) is x r + o rounded to an
 // integer (ulp 1 in [2^23, 2^24)), which lands in the low mantissa bits.
 constexpr float kTwo23 = 8388608.0f;
@@ -218,6 +226,47 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
                                                                    // sign masks (bits 15, 31)
   __shared__ __attribute__((aligned(16))) uint32_t sgn_out[32];   // negation masks of packed codes
   __shared__ __attribute__((aligned(16))) uint32_t sgn_f[kD];     // TBQ4: fp32 output sign masks
+  // TBQ4: per (sign, bucket) of u: (the boundary inside, or +inf; the number
+  // of boundaries below the bucket); tbq_exact: the table cannot be used
+  __shared__ __attribute__((aligned(8))) uint2 tbq_tab[2 * kTbqBuckets];
+  __shared__ int tbq_exact;
+  if (TBQ) {
+    const int t = threadIdx.x;
+    if (t == 0) tbq_exact = 0;
+    __syncthreads();
+    if (t < 2 * kTbqBuckets) {
+      const int j = t % kTbqBuckets;
+      const bool neg = t >= kTbqBuckets;
+      // |u| in [lo, hi)
+      const float lo = j == 0 ? 0.0f : ldexpf(1.0f + 0.25f * ((kTbqT0 + j) & 3), ((kTbqT0 + j) >> 2) - 127);
+      const float hi = j == kTbqBuckets - 1 ? INFINITY
+                                            : ldexpf(1.0f + 0.25f * ((kTbqT0 + j + 1) & 3), ((kTbqT0 + j + 1) >> 2) - 127);
+      uint32_t below = 0, inside = 0;
+      float bin = INFINITY;
+      bool near_edge = false;
+      for (int k = 0; k < 15; ++k) {
+        const float b = g.cb_bound[k];
+        // u in [lo, hi) (positive) or (-hi, -lo] (negative)
+        const bool bel = neg ? b <= -hi : b < lo;
+        const bool ins = neg ? (b > -hi && b <= -lo) : (b >= lo && b < hi);
+        below += bel ? 1u : 0u;
+        if (ins) {
+          ++inside;
+          bin = b;
+        } else {
+          // a boundary next to the bucket but outside it: the rounding of
+          // u could cross it without the risk test (on this bucket's
+          // boundary) seeing it.  Zero is no such edge: q and u have the
+          // sign of y.
+          if (j > 0) near_edge |= fabsf(fabsf(b) - lo) < 0x1p-20f;
+          if (j < kTbqBuckets - 1) near_edge |= fabsf(fabsf(b) - hi) < 0x1p-20f;
+        }
+      }
+      tbq_tab[t] = make_uint2(__float_as_uint(bin), below);
+      if (inside > 1 || near_edge) tbq_exact = 1;
+    }
+    __syncthreads();
+  }
   if (HAD == 2) {
     const int t = threadIdx.x;
     if (t < 64) {
@@ -360,16 +409,35 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
       const uint16_t nb = float_to_half_bits(fminf((float)sqrt(ss), 65504.0f));
       sbw = nb;
       const float nrm = half_bits_to_float(nb);
+      const float rn = nrm != 0.0f ? 1.0f / nrm : 0.0f;
+      const bool exact_all = tbq_exact != 0;
 #pragma unroll
       for (int u = 0; u < kLU; ++u) {
         uint32_t f[8];
+        float near = INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float uq = nrm != 0.0f ? r[8 * u + j] / nrm : 0.0f;
-          uint32_t idx = 0;
+          // q = fl32(y fl32(1/n)) is within 3 2^-24 |u| < 2^-22 of
+          // u = fl32(y / n) (|u| <= 1.01); both count the same boundaries
+          // below them unless one lies within 2^-22 of q: that can only be
+          // the boundary of q's bucket (none lies that close to a bucket edge)
+          const float q = r[8 * u + j] * rn;
+          const uint32_t qb = __float_as_uint(q);
+          const int bk = min(max((int)((qb >> 21) & 0x3FFu) - kTbqT0, 0), kTbqBuckets - 1);
+          const uint2 e = tbq_tab[bk + kTbqBuckets * (int)(qb >> 31)];
+          const float bin = __uint_as_float(e.x);
+          f[j] = e.y + (q > bin ? 1u : 0u);
+          near = fminf(near, fabsf(q - bin));
+        }
+        if (__builtin_expect(__any(near < 0x1p-22f || exact_all), 0)) {
 #pragma unroll
-          for (int k = 0; k < 15; ++k) idx += uq > g.cb_bound[k] ? 1u : 0u;
-          f[j] = idx;
+          for (int j = 0; j < 8; ++j) {
+            const float uq = nrm != 0.0f ? r[8 * u + j] / nrm : 0.0f;
+            uint32_t idx = 0;
+#pragma unroll
+            for (int k = 0; k < 15; ++k) idx += uq > g.cb_bound[k] ? 1u : 0u;
+            f[j] = idx;
+          }
         }
         U[u] = pack8<4>(f);
       }
