@@ -252,16 +252,37 @@ def measure(w, args, dev, headline):
     cache = kvq.KVCache(cfg, w["batch"], T)
     cache.append(k0, v0)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def ev_pair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    build_rec = None
+    if w["cfg"]["scheme"] == "kivi":
+        # the one-shot build of the T - 1 token cache from an empty one (a
+        # prefill: group quantization, fp16 window, RoPE table) timed apart
+        ev_b = [ev_pair() for _ in range(3)]
+        for i in range(4):
+            cache.length = 0
+            if i >= 1:
+                ev_b[i - 1][0].record(stream)
+            cache.append(k0, v0)
+            if i >= 1:
+                ev_b[i - 1][1].record(stream)
+        torch.cuda.synchronize()
+        b_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_b]))
+        rd = w["batch"] * w["num_kv_heads"] * (T - 1) * 2 * 128 * 2
+        wr = decode_bytes(w, T - 1)
+        build_rec = {"tokens_per_seq": T - 1, "ms": round(b_ms, 5), "read_bytes": rd, "write_bytes": wr,
+                     "gbs": round((rd + wr) / (b_ms / 1e3) / 1e9, 2),
+                     "frac": round((rd + wr) / (b_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"one-shot build of {T - 1} tokens: {b_ms:.4f} ms")
     chunk = None
     if w.get("prefill") and w["cfg"]["scheme"] in BLOCK_SCHEMES:
         n = w["prefill"]   # the workload's chunked-prefill append: its last n tokens
         chunk = (n, torch.cat([k0[:, T - n:], k1], 1).contiguous(), torch.cat([v0[:, T - n:], v1], 1).contiguous())
     del k0, v0
     log(f"cache built: {cache.length} tokens")
-    stream = torch.cuda.current_stream()
-
-    def ev_pair():
-        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
     append_rec = None
     if chunk is not None:
@@ -369,6 +390,8 @@ def measure(w, args, dev, headline):
     }
     if append_rec is not None:
         rec["append"] = append_rec
+    if build_rec is not None:
+        rec["build"] = build_rec
     log(f"{w['name']}: step {ms_step:.4f} ms, decode call {call:.4f} ms cold "
         f"({rec['roofline']['frac']:.3f} of peak)")
     del cache, ws, out, q, k1, v1
@@ -462,6 +485,8 @@ def main():
     }
     if "append" in head:
         res["append"] = head["append"]
+    if "build" in head:
+        res["build"] = head["build"]
     if sub:
         res["sub"] = sub
     print(json.dumps(res), flush=True)

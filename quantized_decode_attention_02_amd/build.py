@@ -26,7 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvq.so")
-SOURCES = ["kvq.cpp", "append.hip", "append_block.hip", "decode.hip", "decode_mfma.hip", "decode_rope.hip", "dequant.hip"]
+SOURCES = ["kvq.cpp", "append.hip", "append_block.hip", "append_kivi.hip", "decode.hip", "decode_mfma.hip", "decode_rope.hip", "dequant.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

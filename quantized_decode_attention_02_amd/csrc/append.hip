@@ -528,8 +528,20 @@ hipError_t launch_kivi_demote(const Geom& g, const Planes& p, int64_t g0, int64_
 hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_new,
                                 const __half* v_new, int64_t n_new, int64_t T0, int64_t g0,
                                 int64_t g1, int64_t hi_start_new, hipStream_t s) {
-  if (g1 > g0) {
-    hipLaunchKernelGGL(kivi_quantize_kernel, dim3((unsigned)(g1 - g0), g.Hkv, g.B), dim3(256), 0, s, g,
+  // groups wholly from the new tokens go to the group kernel of
+  // append_kivi.hip where it covers the code widths; the others (a group
+  // that starts in the fp16 window, 3-bit codes) come here
+  int64_t gm = g0;
+  if (kivi_groups_supported(g, n_new)) {
+    gm = (T0 + kGroup - 1) / kGroup;
+    gm = gm < g0 ? g0 : (gm > g1 ? g1 : gm);
+    const hipError_t e = launch_kivi_groups(g, p, k_new, v_new, n_new, T0, gm, g1, hi_start_new, s);
+    if (e != hipSuccess) return e;
+  } else {
+    gm = g1;
+  }
+  if (gm > g0) {
+    hipLaunchKernelGGL(kivi_quantize_kernel, dim3((unsigned)(gm - g0), g.Hkv, g.B), dim3(256), 0, s, g,
                        p, k_new, v_new, n_new, T0, g0, hi_start_new);
   }
   return hipGetLastError();

@@ -43,15 +43,10 @@
 // can leave [-top, top] before the clamp) always takes the division.
 #pragma clang fp contract(off)
 
-#include "kvq_device.h"
+#include "append_util.h"
 
 namespace kvq {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kTr = 36;   // dwords per row of the code transpose: 32 tokens + 4 (rows 36 dwords
-                          // apart: 16 rows read at one offset hit 16 different bank quads)
 
 // TBQ4 index lookup: |u| is bucketed by its exponent and top two mantissa
 // bits (buckets 25% wide or less) from 2^-8 up; bucket 0 is [0, 1.25 2^-8),
@@ -61,10 +56,6 @@ constexpr int kTr = 36;   // dwords per row of the code transpose: 32 tokens + 4
 constexpr int kTbqBuckets = 25;
 constexpr int kTbqT0 = (127 - 8) << 2;   // (exponent, 2 mantissa bits) of 2^-8
 
-// fp32 2^23: for |v| < 2^22, fma(x, r, 2^23 + o) is x r + o rounded to an
-// integer (ulp 1 in [2^23, 2^24)), which lands in the low mantissa bits.
-constexpr float kTwo23 = 8388608.0f;
-
 template <int BITS>
 struct Sym {
   static constexpr int kTop = BITS == 3 ? 3 : (BITS == 8 ? 127 : 7);
@@ -72,16 +63,6 @@ struct Sym {
   static constexpr int kPer = BITS == 8 ? 4 : 8;    // codes per packed unit
   static constexpr int kUnits = kD / kPer;          // units: a dword (8 bits: 4 codes, 4 bits:
                                                     // 8 codes) or a 24-bit group (3 bits: 8 codes)
-};
-
-// One launch: the tokens [T0, T0 + n) of an append whose source rows are
-// (b, t - src_t0, h) of a [batch, src_tokens, Hkv, 128] fp16 array.
-struct SegArgs {
-  const __half* k_new;
-  const __half* v_new;
-  int64_t src_tokens, src_t0;
-  int64_t T0, n;
-  int64_t tile0, n_tiles, n_items;
 };
 
 // Item coordinates (wave-uniform).
@@ -99,117 +80,6 @@ __device__ __forceinline__ Item item_at(const Geom& g, int64_t it, int64_t tile0
   r.h = (int)(r.pair % g.Hkv);
   r.tb = (tile0 + rest % n_tiles) * kGroup;
   return r;
-}
-
-// Pack the low `B`-bit fields of eight words f[0..7] (each a code in its low
-// bits, zero above up to bit 23, anything from bit 24 on) as f[j] << (B j).
-// Shifts of 8 or more push the high garbage out; the low fields go through
-// one masked merge.
-template <int B>
-__device__ __forceinline__ uint32_t pack8(const uint32_t* f) {
-  if (B == 4) {   // nibble pairs as bytes, then the four bytes by byte permutes
-    const uint32_t b01 = (f[1] << 4) | f[0], b23 = (f[3] << 4) | f[2];
-    const uint32_t b45 = (f[5] << 4) | f[4], b67 = (f[7] << 4) | f[6];
-    const uint32_t lo = __builtin_amdgcn_perm(b23, b01, 0x0C0C0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(b67, b45, 0x0C0C0400u);
-    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-  } else {        // B == 3: 24 bits
-    uint32_t acc = f[7] << 21;
-    acc |= f[6] << 18;
-    acc |= f[5] << 15;
-    acc |= f[4] << 12;
-    acc |= f[3] << 9;
-    const uint32_t lo = (((f[2] << 6) | (f[1] << 3)) | f[0]);
-    return ((lo & 0x1FFu) | acc) & 0xFFFFFFu;
-  }
-}
-__device__ __forceinline__ uint32_t pack4x8(const uint32_t* f) {
-  const uint32_t lo = __builtin_amdgcn_perm(f[1], f[0], 0x0C0C0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(f[3], f[2], 0x0C0C0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
-// (a ^ b) + c in one instruction; opaque to the compiler, which would
-// otherwise split the accumulation of a bracket's disagreement into a
-// compare and select per element.
-__device__ __forceinline__ uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
-
-// fp32 of the low (sel 0) or high (sel 1) fp16 half of w, plus or minus the
-// other half, rounded once: v_fma_mix_f32 with the fp16 operands converted
-// exactly inside the instruction (a + b and a - b are the same IEEE
-// operations as fma(a, 1, b) and fma(b, -1, a)).
-__device__ __forceinline__ float mix_sum(uint32_t w) {
-  float d;
-  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
-  return d;
-}
-__device__ __forceinline__ float mix_diff(uint32_t w) {
-  float d;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
-  return d;
-}
-
-// 8 x 8 transpose of 4-bit fields: in[i] holds row i (field j at bits 4j);
-// out[j] holds column j (field i at bits 4i).
-__device__ __forceinline__ void transpose_nib8(const uint32_t* in, uint32_t* out) {
-  uint32_t a[8], b[8];
-  // 4 x 4 blocks of fields: the halves of rows i and i + 4
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = __builtin_amdgcn_perm(in[i + 4], in[i], 0x05040100u);       // lo(i), lo(i + 4)
-    a[i + 4] = __builtin_amdgcn_perm(in[i + 4], in[i], 0x07060302u);   // hi(i), hi(i + 4)
-  }
-  // 2 x 2 blocks: bytes of rows r and r + 2
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = 4 * q + r;
-      b[i] = __builtin_amdgcn_perm(a[i + 2], a[i], 0x06020400u);       // bytes 0, 2 of each
-      b[i + 2] = __builtin_amdgcn_perm(a[i + 2], a[i], 0x07030501u);   // bytes 1, 3 of each
-    }
-  }
-  // single fields: rows r and r + 1
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const uint32_t x = b[i], y = b[i + 1];
-    b[i] = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-    b[i + 1] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-  }
-  // b[k] now holds column j(k) with its fields in row order
-  out[0] = b[0]; out[1] = b[1]; out[2] = b[2]; out[3] = b[3];
-  out[4] = b[4]; out[5] = b[5]; out[6] = b[6]; out[7] = b[7];
-}
-
-// 4 x 4 transpose of bytes.
-__device__ __forceinline__ void transpose_byte4(const uint32_t* in, uint32_t* out) {
-  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
-  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
-// Mask of the fields [lo, hi) of width W in a word whose fields start at
-// bit `first` (fields outside the word ignored).
-__device__ __forceinline__ uint32_t field_mask(int lo, int hi, int first, int W) {
-  const int b0 = min(max(lo * W - first, 0), 32), b1 = min(max(hi * W - first, 0), 32);
-  const uint32_t upto1 = b1 >= 32 ? 0xFFFFFFFFu : ((1u << b1) - 1u);
-  const uint32_t upto0 = b0 >= 32 ? 0xFFFFFFFFu : ((1u << b0) - 1u);
-  return upto1 & ~upto0;
-}
-
-// Value of `v` in the lane 32 apart (the other half of the lane's vector).
-__device__ __forceinline__ uint32_t other_half(uint32_t v, int half) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return half ? r[0] : r[1];
 }
 
 template <int BITS, bool Q40, int HAD, bool TBQ>
@@ -319,11 +189,7 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
   u32x4 raw[8];
   KVQ_ISSUE_ROWS(cur)
   for (int64_t item = i0;; ++item) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + (lane >> 4), c = lane & 15;
-      *reinterpret_cast<u32x4*>(reg + row * 256 + 16 * (c ^ (row & 15))) = raw[i];
-    }
+    stage_rows(reg, raw, lane);
     // the next item's rows (past the last item: this item's again, from L2)
     Item nit = cur;
     if (item + 1 < i1) {
@@ -342,52 +208,11 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
     }
     KVQ_ISSUE_ROWS(nit)
 
-    // ---- half a vector: elements 64 half + k in r[k]; fp16 -> fp32 with
-    // stage h = 1, stages 2 .. 32 in the lane, stage 64 with the other half
+    // ---- half a vector: elements 64 half + k in r[k], or half the
+    // unnormalized transform (see read_half)
     float r[64];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int chunk = 8 * half + c;
-      const u32x4 q = *reinterpret_cast<const u32x4*>(reg + v * 256 + 16 * (chunk ^ (v & 15)));
-      u32x4 sg = {0u, 0u, 0u, 0u};
-      if (HAD == 2) sg = *reinterpret_cast<const u32x4*>(sgn_in + 4 * chunk);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = q[k] ^ sg[k];
-        if (HAD) {
-          r[8 * c + 2 * k] = mix_sum(w);
-          r[8 * c + 2 * k + 1] = mix_diff(w);
-        } else {
-          r[8 * c + 2 * k] = __half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
-          r[8 * c + 2 * k + 1] = __half2float(__ushort_as_half((uint16_t)(w >> 16)));
-        }
-      }
-    }
-    if (HAD) {
-#pragma unroll
-      for (int hs = 2; hs < 64; hs <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 64; ++j) {
-          if (j & hs) continue;
-          const float a = r[j], b = r[j + hs];
-          r[j] = a + b;
-          r[j + hs] = a - b;
-        }
-      }
-      // stage 64: the halves trade r[32 ..] of the lower and r[.. 31] of the
-      // upper, so each lane holds pairs (x_e, x_{e+64}) as (r[i], r[32 + i])
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[i]), __float_as_uint(r[32 + i]),
-                                                         false, false);
-        const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
-        r[i] = a + b;
-        r[32 + i] = a - b;
-      }
-    }
-    // channel of r[k]: transformed: k + 32 half, +32 for k >= 32 (lower half:
-    // 0..31, 64..95; upper: 32..63, 96..127); plain: 64 half + k
-    auto chan = [&](int k) { return HAD ? k + 32 * half + (k >= 32 ? 32 : 0) : 64 * half + k; };
+    read_half<HAD>(reg, sgn_in, lane, r);
+    auto chan = [&](int k) { return half_chan<HAD>(k, half); };
 
     // ---- codes (r holds the unscaled transform when rotated: y = fl32(r c))
     const int64_t t = cur.tb + v;

@@ -115,6 +115,12 @@ hipError_t launch_kivi_quantize(const Geom& g, const Planes& p, const __half* k_
                                 int64_t g1, int64_t hi_start_new, hipStream_t s);
 // Appends of 1..kSmallAppendMax tokens: demote, quantize and window copy
 // fused into one launch of one work-group per (sequence, kv head).
+// KIVI groups [g0, g1) that lie wholly in the new tokens, at 4 or 2 bits
+// (append_kivi.hip); supported: the code widths and the source size allow it.
+bool kivi_groups_supported(const Geom& g, int64_t n_new);
+hipError_t launch_kivi_groups(const Geom& g, const Planes& p, const __half* k_new, const __half* v_new,
+                              int64_t n_new, int64_t T0, int64_t g0, int64_t g1, int64_t hi_start_new,
+                              hipStream_t s);
 constexpr int kSmallAppendMax = 32;
 hipError_t launch_kivi_small_append(const Geom& g, const Planes& p, const __half* k_new,
                                     const __half* v_new, int64_t n_new, int64_t T0, int64_t d0,
