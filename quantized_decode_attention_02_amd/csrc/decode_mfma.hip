@@ -338,12 +338,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       // the stage into registers, then the stage and the metadata registers
       // are refilled with the next tile while this one is computed
       wait_stage_landed();
-      bool need_claim = false;
-      more = cursor_next_deferred(a, cs, lane, &ends, &need_claim);
+      more = cursor_next(a, cs, lane, &ends);
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
-      // one issue site for chunk claims: the atomic's result goes straight
-      // into the cursor's register and is first read a chunk later
-      if (need_claim) cs.pend = claim_issue(a.ctr + cs.pair * kCounterStride, lane);
       stage_read<BITS, BLOCK>(cur, stage, lane);
       cur.km0 = nxt.km0; cur.km1 = nxt.km1; cur.vm = nxt.vm; cur.ks16 = nxt.ks16; cur.vs16 = nxt.vs16;
       cur.kq4 = nxt.kq4; cur.vq4 = nxt.vq4;
@@ -352,10 +348,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
     } else {
       load_tile<BITS, BLOCK, false, Q40>(cur, cur_pos, lane, kpair_of(pair), vpair_of(pair), kmeta_of(pair),
                                          vmeta_of(pair), ksc_of(pair), vsc_of(pair), kmc0, kmc1);
-      bool need_claim = false;
-      more = cursor_next_deferred(a, cs, lane, &ends, &need_claim);
+      more = cursor_next(a, cs, lane, &ends);
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
-      if (need_claim) cs.pend = claim_issue(a.ctr + cs.pair * kCounterStride, lane);
     }
     const int nvalid = cur_pos.nvalid;
     const bool tok_ok = lane < nvalid;
