@@ -201,6 +201,167 @@ __device__ __forceinline__ void split_half(float x, _Float16* hi, _Float16* lo) 
   *lo = (_Float16)(x - (float)*hi);
 }
 
+// ---------------------------------------------------------------------------
+// Value side of four query heads on the 16x16x32 f16 MFMA (4- and 2-bit
+// codes).  Per value scale group dg (NDG of them: 32 channels each, or one
+// for the whole row) and key group gg, the A operand is p' = p s of the
+// group's 32 tokens as a 16 x 32 matrix: row 4 hl + m holds the hi (hl = 0)
+// or lo (hl = 1) fp16 half of head m's p'; rows 8..15 repeat rows 0..7 and
+// their sums are never read.  Column k = 8 kc + j: lane group kc = lane / 16
+// covers the 8 tokens whose codes one dword of a channel row holds (at 2
+// bits half of one), j orders them as the masked words do.  B is the codes
+// of 16 channels, one per column (channel 16 cb + lane % 16).  Lane l then
+// holds rows 4 (l / 16) + i of column l % 16: lanes 0..15 the hi sums of
+// heads i = 0..3, lanes 16..31 the lo sums.  One tile is 16 MFMAs (2 groups
+// x 8 channel blocks) where the 4x4x4 shape needs 64 (hi and lo each
+// 4 heads x 4 tokens x 4 channels a block).
+typedef uint32_t u2v_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
+__device__ __forceinline__ f4_t mfma16(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Lane group kc, position j and the inverse place factor of value token tl
+// (0..31 in its group).  4 bits: dword tl / 8 of the row, nibble o = tl % 8,
+// masked word o % 4 (x16 when odd), half o / 4.  2 bits: dword tl / 16,
+// crumb e = tl % 16: lane group 2 (tl / 16) + (e / 4) % 2, masked word e % 4
+// (x4^(e % 4)), half e / 8.
+template <int BITS>
+__device__ __forceinline__ void v16_slot(int tl, int* kc, int* j, float* inv_f) {
+  if (BITS == 4) {
+    const int o = tl & 7;
+    *kc = tl >> 3;
+    *j = 2 * (o & 3) + (o >> 2);
+    *inv_f = (o & 1) ? 1.0f / 16 : 1.0f;
+  } else {
+    const int e = tl & 15, w = e & 3;
+    *kc = 2 * (tl >> 4) + ((e >> 2) & 1);
+    *j = 2 * w + (e >> 3);
+    *inv_f = 1.0f / (float)(1 << (2 * w));
+  }
+}
+
+// Table half offset of (dg, gg, row, column); a table is NDG x 2 x 8 rows
+// of 32 halves.
+__device__ __forceinline__ int v16_at(int dg, int gg, int row, int col) {
+  return ((dg * 2 + gg) * 8 + row) * 32 + col;
+}
+constexpr int v16_halves(int ndg) { return ndg * 2 * 8 * 32; }
+
+// One token's p' of one scale group: hi halves into rows 0..3, lo halves
+// into rows 4..7 (64 bytes a row) of the column at LDS byte address sb.
+// Written as asm, so that the compiler does not first wait for global-to-LDS
+// copies in flight (it cannot tell that they go elsewhere).
+__device__ __forceinline__ void store_p16(uint32_t sb, const _Float16* hi, const _Float16* lo) {
+  asm volatile(
+      "ds_write_b16 %0, %1\n\t"
+      "ds_write_b16 %0, %2 offset:64\n\t"
+      "ds_write_b16 %0, %3 offset:128\n\t"
+      "ds_write_b16 %0, %4 offset:192\n\t"
+      "ds_write_b16 %0, %5 offset:256\n\t"
+      "ds_write_b16 %0, %6 offset:320\n\t"
+      "ds_write_b16 %0, %7 offset:384\n\t"
+      "ds_write_b16 %0, %8 offset:448"
+      ::"v"(sb), "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3])
+      : "memory");
+}
+
+// The lane's A operands of key group gg, av[dg], in one asm block with its
+// own LDS wait.  pvb: the lane's address for (dg, gg) = (0, 0) (row
+// lane % 8, columns 8 (lane / 16) ..); (dg, gg) lies (2 dg + gg) 512 bytes
+// further.
+template <int NDG>
+__device__ __forceinline__ void read_a16(uint32_t pvb, int gg, u4v_t* av) {
+  if (NDG == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(av[0]) : "v"(pvb + 512 * gg) : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(av[0]), "=v"(av[1]), "=v"(av[2]), "=v"(av[3])
+        : "v"(pvb + 512 * gg)
+        : "memory");
+  }
+}
+
+// The B operand of one code dword: four masked words, two codes each (at 2
+// bits from the dword's half the lane group takes).
+template <int BITS>
+__device__ __forceinline__ h8_t codes16_b(uint32_t x, int lane) {
+  u4v_t v;
+  if (BITS == 4) {
+    const uint32_t x8 = x >> 8;
+    v = u4v_t{x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
+  } else {
+    const uint32_t y = x >> (8 * ((lane >> 4) & 1));
+    v = u4v_t{y & 0x00030003u, y & 0x000C000Cu, y & 0x00300030u, y & 0x00C000C0u};
+  }
+  return __builtin_bit_cast(h8_t, v);
+}
+
+// p' = p s of this lane's token into the table (LDS byte address pv), and
+// the zero-point sums (blocks: the sums of p' for the code offset).
+template <int G, int BITS, bool BLOCK, int NDG>
+__device__ __forceinline__ void stage_probs16(const float* p, const float* vs, const float* vz, uint32_t pv,
+                                              float (*zacc)[NDG], int tl, int gh) {
+  int kc, j;
+  float inv_f;
+  v16_slot<BITS>(tl, &kc, &j, &inv_f);
+  const uint32_t sb = pv + 2 * v16_at(0, gh, 0, 8 * kc + j);
+  for (int d = 0; d < NDG; ++d) {
+    _Float16 hi[4], lo[4];
+    for (int m = 0; m < G; ++m) {
+      const float x = p[m] * vs[d];
+      split_half(x * inv_f, &hi[m], &lo[m]);
+      zacc[m][d] += BLOCK ? x : p[m] * vz[d];
+    }
+    store_p16(sb + 1024 * d, hi, lo);
+  }
+}
+
+// O += p' . codes over a tile whose code dwords are in registers,
+// vd[gg][cb] (channel 16 cb + lane % 16, lane group lane / 16).
+template <int BITS, int NDG>
+__device__ __forceinline__ void value_mfma16(const uint32_t (*vd)[8], uint32_t pv, int lane, f4_t* acc) {
+  const uint32_t pvb = pv + 2 * v16_at(0, 0, lane & 7, 8 * (lane >> 4));
+  for (int gg = 0; gg < 2; ++gg) {
+    u4v_t av[NDG];
+    read_a16<NDG>(pvb, gg, av);
+    for (int cb = 0; cb < 8; ++cb) {
+      const h8_t a8 = __builtin_bit_cast(h8_t, av[NDG == 1 ? 0 : cb >> 1]);
+      acc[cb] = mfma16(a8, codes16_b<BITS>(vd[gg][cb], lane), acc[cb]);
+    }
+  }
+}
+
+// Online-softmax step of head m on the 16x16x32 accumulators (as
+// softmax_step: rescale when the running maximum moves).
+template <int G, int NDG>
+__device__ __forceinline__ float softmax_step16(int m, float s, bool tok_ok, float* m_run, float* l_acc,
+                                                f4_t* acc, float (*zacc)[NDG]) {
+  if (__any(s > m_run[m])) {
+    const float mnew = fmaxf(m_run[m], wave_max64(s));
+    const float alpha = (m_run[m] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[m] - mnew);
+    m_run[m] = mnew;
+    l_acc[m] *= alpha;
+    for (int c = 0; c < 8; ++c) acc[c][m] *= alpha;
+    for (int d = 0; d < NDG; ++d) zacc[m][d] *= alpha;
+  }
+  const float p = tok_ok ? __builtin_amdgcn_exp2f(s - m_run[m]) : 0.0f;
+  l_acc[m] += p;
+  return p;
+}
+
 // Online-softmax update of one head for one tile; returns p for this lane.
 template <int G, int HL, int NDG>
 __device__ __forceinline__ float softmax_step(int m, float s, bool tok_ok, float* m_run, float* l_acc,
@@ -232,6 +393,7 @@ template <int BITS, bool BLOCK>
 struct TileRaw {
   uint4 kc[BITS];
   uint32_t vc[2][2][BITS];
+  uint32_t vd[2][8];   // 16x16x32 value side: dword lane / 16 (2 bits: lane / 32) of channel 16 cb + lane % 16
   uint2 km0, km1;   // KIVI, keys after RoPE: (s, z) of the key channels of this lane's k-step
   uint4 kmr;        // KIVI, keys before RoPE: (s, z) of channels 4 (lane % 32) .. + 3
   uint4 vm;         // KIVI: (s, z) x 4 of this lane's token
@@ -500,6 +662,20 @@ __device__ __forceinline__ void stage_read(TileRaw<BITS, BLOCK>& r, const uint8_
     }
 }
 
+// stage_read for the 16x16x32 value side: the key rows as stage_read, the
+// value code dwords as value_mfma16 takes them (4 or 2 bits).
+template <int BITS, bool BLOCK>
+__device__ __forceinline__ void stage_read16(TileRaw<BITS, BLOCK>& r, const uint8_t* st, int lane) {
+  constexpr int TB = 512 * BITS;
+  constexpr int VROW = 4 * BITS;
+  const int gh = lane >> 5, tl = lane & 31;
+  for (int j = 0; j < BITS; ++j) r.kc[j] = *reinterpret_cast<const uint4*>(st + gh * TB + j * 512 + tl * 16);
+  const uint8_t* src = st + 2 * TB + (lane & 15) * VROW + 4 * (lane >> (BITS == 4 ? 4 : 5));
+  for (int gg = 0; gg < 2; ++gg)
+    for (int cb = 0; cb < 8; ++cb)
+      r.vd[gg][cb] = *reinterpret_cast<const uint32_t*>(src + gg * TB + cb * 16 * VROW);
+}
+
 __device__ __forceinline__ void wait_stage_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_stage_read() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -561,88 +737,92 @@ __device__ __forceinline__ void value_mfma(const uint32_t (*vc)[2][BITS],
                                            const PT& PLw, int row, int gh,
                                            f4_t& o0, f4_t& o1, f4_t& o2, f4_t& o3,
                                            const uint32_t* lut = nullptr) {
-  for (int gg = 0; gg < 2; ++gg) {
-    for (int hf = 0; hf < 2; ++hf) {
-      const int dg = NDG == 1 ? 0 : (gh + 2 * hf);   // the 32-dim slice of channel lane + 64 hf
-      if constexpr (BITS == 8) {
-        // a dword holds tokens 4u .. 4u + 3 of the channel row, one byte
-        // each: bytes 0 and 2 masked in place, bytes 1 and 3 shifted down
-        // (codes n enter as n * 2^-24, no factors)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t x = vc[gg][hf][u];
-          const h4_t bv = as_h4(x & 0x00FF00FFu, (x >> 8) & 0x00FF00FFu);
-          const int ks = 8 * gg + u;
-          for (int hl = 0; hl < HL; ++hl) {
-            const h4_t av = PLw.h4(dg, ks, hl, row);
-            if (hf == 0) {
-              if (u & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
-            } else {
-              if (u & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
-            }
-          }
-        }
-        continue;
-      }
-      if constexpr (BITS == 3) {
-        // the channel row's 32 tokens as one 96-bit string, token t at bits
-        // 3t: k-step q takes tokens 4q .. 4q + 3 in natural order
-        const uint32_t w[3] = {vc[gg][hf][0], vc[gg][hf][1], vc[gg][hf][2]};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const h4_t bv = codes3_b(w, q);
-          const int ks = 8 * gg + q;
-          for (int hl = 0; hl < HL; ++hl) {
-            const h4_t av = PLw.h4(dg, ks, hl, row);
-            if (hf == 0) {
-              if (q & 1) o2 = mfma4(av, bv, o2); else o0 = mfma4(av, bv, o0);
-            } else {
-              if (q & 1) o3 = mfma4(av, bv, o3); else o1 = mfma4(av, bv, o1);
-            }
-          }
-        }
-        continue;
-      }
+  if constexpr (BITS == 4 || BITS == 2) {
+    // one dword: 8 tokens (4-bit) or 16 tokens (2-bit), two per pr[] (one per
+    // 16-bit half), masked in place in the low byte of each half: the code of
+    // position j enters as n * 2^-24 times 16^(j & 1) or 4^(j & 3), which
+    // stage_probs divided out of its probability.  Both channel halves of a
+    // dword position are unpacked first; their MFMAs then alternate between
+    // the four accumulators, so that no MFMA waits on the one issued just
+    // before it (each accumulator still sums its terms in the same order).
+    constexpr int NP = (BITS == 4) ? 4 : 8;
+    constexpr int NL = HL + (TBQ ? 1 : 0);
+    for (int gg = 0; gg < 2; ++gg) {
       for (int u = 0; u < BITS; ++u) {
-        const uint32_t x = vc[gg][hf][u];
-        // one dword: 8 tokens (4-bit) or 16 tokens (2-bit), two per pr[] (one
-        // per 16-bit half), masked in place in the low byte of each half: the
-        // code of position j enters as n * 2^-24 times 16^(j & 1) or
-        // 4^(j & 3), which stage_probs divided out of its probability
-        constexpr int NP = (BITS == 4) ? 4 : 8;
-        uint32_t pr[NP];
-        const uint32_t x8 = x >> 8;
-        uint32_t prl[4] = {0, 0, 0, 0};
-        if (TBQ) {
-          tbq4_levels(x, lut, pr, prl);   // the levels themselves, no factors
-        } else if (BITS == 4) {
-          pr[0] = x & 0x000F000Fu;
-          pr[1] = x & 0x00F000F0u;
-          pr[2] = x8 & 0x000F000Fu;
-          pr[3] = x8 & 0x00F000F0u;
-        } else {
-          for (int j = 0; j < 4; ++j) {
-            pr[j] = x & (0x00030003u << (2 * j));
-            pr[4 + j] = x8 & (0x00030003u << (2 * j));
-          }
-        }
-        for (int q2 = 0; q2 < NP / 2; ++q2) {
-          const int ks = 8 * gg + (NP / 2) * u + q2;   // k-step of pairs (2 q2, 2 q2 + 1)
-          const h4_t bv = as_h4(pr[2 * q2], pr[2 * q2 + 1]);
-          // TBQ: one more pass for the levels' lo halves against the hi half
-          // of p' (rows G.. of a HL = 1 table carry p's lo half: included)
-          for (int hl = 0; hl < HL + (TBQ ? 1 : 0); ++hl) {
-            const bool lo_lv = TBQ && hl == HL;
-            const h4_t av = PLw.h4(dg, ks, lo_lv ? 0 : hl, row);
-            const h4_t b = lo_lv ? as_h4(prl[2 * q2], prl[2 * q2 + 1]) : bv;
-            if (hf == 0) {
-              if (q2 & 1) o2 = mfma4(av, b, o2); else o0 = mfma4(av, b, o0);
-            } else {
-              if (q2 & 1) o3 = mfma4(av, b, o3); else o1 = mfma4(av, b, o1);
+        uint32_t pr[2][NP];
+        uint32_t prl[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t x = vc[gg][hf][u];
+          const uint32_t x8 = x >> 8;
+          if (TBQ) {
+            tbq4_levels(x, lut, pr[hf], prl[hf]);   // the levels themselves, no factors
+          } else if (BITS == 4) {
+            pr[hf][0] = x & 0x000F000Fu;
+            pr[hf][1] = x & 0x00F000F0u;
+            pr[hf][2] = x8 & 0x000F000Fu;
+            pr[hf][3] = x8 & 0x00F000F0u;
+          } else {
+            for (int j = 0; j < 4; ++j) {
+              pr[hf][j] = x & (0x00030003u << (2 * j));
+              pr[hf][4 + j] = x8 & (0x00030003u << (2 * j));
             }
           }
         }
+        for (int qp = 0; qp < NP / 4; ++qp)
+          for (int hl = 0; hl < NL; ++hl)
+            for (int q2 = 2 * qp; q2 < 2 * qp + 2; ++q2)
+              for (int hf = 0; hf < 2; ++hf) {
+                const int dg = NDG == 1 ? 0 : (gh + 2 * hf);   // the 32-dim slice of channel lane + 64 hf
+                const int ks = 8 * gg + (NP / 2) * u + q2;    // k-step of pairs (2 q2, 2 q2 + 1)
+                // TBQ: one more pass for the levels' lo halves against the hi
+                // half of p' (rows G.. of a HL = 1 table carry p's lo half:
+                // included)
+                const bool lo_lv = TBQ && hl == HL;
+                const h4_t av = PLw.h4(dg, ks, lo_lv ? 0 : hl, row);
+                const h4_t b = lo_lv ? as_h4(prl[hf][2 * q2], prl[hf][2 * q2 + 1])
+                                     : as_h4(pr[hf][2 * q2], pr[hf][2 * q2 + 1]);
+                if (hf == 0) {
+                  if (q2 & 1) o2 = mfma4(av, b, o2); else o0 = mfma4(av, b, o0);
+                } else {
+                  if (q2 & 1) o3 = mfma4(av, b, o3); else o1 = mfma4(av, b, o1);
+                }
+              }
       }
+    }
+    return;
+  }
+  // 8 bits: a dword holds tokens 4u .. 4u + 3 of the channel row, one byte
+  // each: bytes 0 and 2 masked in place, bytes 1 and 3 shifted down (codes n
+  // enter as n * 2^-24, no factors).  3 bits: the channel row's 32 tokens as
+  // one 96-bit string, token t at bits 3t: k-step q takes tokens
+  // 4q .. 4q + 3 in natural order.  As above, the MFMAs of two k-steps and
+  // both channel halves alternate between the four accumulators.
+  for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+    for (int qp = 0; qp < 4; ++qp) {
+      h4_t bv[2][2];
+      for (int hf = 0; hf < 2; ++hf)
+        for (int j = 0; j < 2; ++j) {
+          const int q = 2 * qp + j;
+          if constexpr (BITS == 8) {
+            const uint32_t x = vc[gg][hf][q];
+            bv[hf][j] = as_h4(x & 0x00FF00FFu, (x >> 8) & 0x00FF00FFu);
+          } else {
+            const uint32_t w[3] = {vc[gg][hf][0], vc[gg][hf][1], vc[gg][hf][2]};
+            bv[hf][j] = codes3_b(w, q);
+          }
+        }
+      for (int hl = 0; hl < HL; ++hl)
+        for (int j = 0; j < 2; ++j)
+          for (int hf = 0; hf < 2; ++hf) {
+            const int dg = NDG == 1 ? 0 : (gh + 2 * hf);
+            const h4_t av = PLw.h4(dg, 8 * gg + 2 * qp + j, hl, row);
+            if (hf == 0) {
+              if (j) o2 = mfma4(av, bv[hf][j], o2); else o0 = mfma4(av, bv[hf][j], o0);
+            } else {
+              if (j) o3 = mfma4(av, bv[hf][j], o3); else o1 = mfma4(av, bv[hf][j], o1);
+            }
+          }
     }
   }
 }
@@ -716,6 +896,27 @@ __device__ __forceinline__ void write_partial(const MfmaArgs& a, int b, int h, i
     const float a1 = (HL == 1) ? o1[m] + o1[G + m] + o3[m] + o3[G + m] : o1[m] + o3[m];
     rec[2 + lane] = a0 * scale + add0[m];
     rec[2 + 64 + lane] = a1 * scale + add1[m];
+    if (lane == 0) {
+      rec[0] = m_run[m];
+      rec[1] = lsum;
+    }
+  }
+}
+
+// The partial of the 16x16x32 accumulators: hi + lo rows (lanes l and
+// l + 16) times `scale`, plus add[m][cb / 2] (add[m][0] for every channel
+// when NDG is 1).
+template <int G, int NDG>
+__device__ __forceinline__ void write_partial16(const MfmaArgs& a, int b, int h, int64_t slot, int lane,
+                                                const float* m_run, const float* l_acc, const f4_t* acc,
+                                                float scale, const float (*add)[NDG]) {
+  for (int m = 0; m < G; ++m) {
+    const float lsum = wave_sum64(l_acc[m]);
+    float* rec = a.ws + (((int64_t)b * a.g.Hq + h * G + m) * a.n_slots + slot) * kPartial;
+    for (int c = 0; c < 8; ++c) {
+      const float v = acc[c][m] + __shfl_xor(acc[c][m], 16);
+      if (lane < 16) rec[2 + 16 * c + lane] = v * scale + add[m][NDG == 1 ? 0 : c >> 1];
+    }
     if (lane == 0) {
       rec[0] = m_run[m];
       rec[1] = lsum;

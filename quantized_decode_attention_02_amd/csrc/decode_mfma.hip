@@ -119,6 +119,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // symmetric blocks: stored code offset (c + 4 at 3 bits, c + 8 at 4, c + 128 at 8)
   constexpr float COFF = BITS == 3 ? 4.0f : BITS == 8 ? 128.0f : 8.0f;
   constexpr int TB = 512 * BITS;         // tile bytes
+  // four query heads at 4 or 2 bits: values on the 16x16x32 MFMA
+  constexpr bool V16 = G == 4 && (BITS == 4 || BITS == 2) && !TBQ && KVQ_DECODE_STAGE;
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
   constexpr bool QP = query_in_prob_table<G, BLOCK>();
@@ -130,7 +132,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   using QTab = ATab<HL, 32, (G == 4 && !BLOCK), (G == 4 && !BLOCK)>;
   using PTab = ATab<HL, 16, G == 4, (G == 4 && NDG > 1)>;
   __shared__ __attribute__((aligned(16))) _Float16 QL[4][(BLOCK ? 1 : 2) * QTab::T];
-  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
+  // (16x16x32 value side: its tables; the window's table 0 overlays them)
+  __shared__ __attribute__((aligned(16))) _Float16
+      PL[4][V16 ? (v16_halves(NDG) > PTab::T ? v16_halves(NDG) : PTab::T) : NDG * PTab::T];
   __shared__ __attribute__((aligned(16))) uint8_t ST[KVQ_DECODE_STAGE ? 4 : 1][stage_bytes<BITS>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // output accumulators: channel lane (o0: even value k-steps, o2: odd) and
   // channel 64 + lane (o1, o3); two chains each so dependent MFMAs interleave
   f4_t o0, o1, o2, o3;
+  f4_t acc16[8];   // V16: channel blocks 0..7 (value_mfma16)
   auto reset = [&]() {
     for (int m = 0; m < G; ++m) {
       m_run[m] = -INFINITY;
@@ -159,6 +164,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
     }
     o0 = f4_t{0, 0, 0, 0}; o1 = o0; o2 = o0; o3 = o0;
+    if (V16)
+      for (int c = 0; c < 8; ++c) acc16[c] = f4_t{0, 0, 0, 0};
   };
   reset();
 
@@ -274,6 +281,17 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
 
   // this member's partial of `pair`
   auto flush = [&]() {
+    if constexpr (V16) {
+      float add[G][NDG];
+      for (int m = 0; m < G; ++m)
+        for (int d = 0; d < NDG; ++d) {
+          const float zs = wave_sum64(zacc[m][d]);
+          add[m][d] = BLOCK ? -COFF * zs : zs;
+        }
+      write_partial16<G, NDG>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, acc16, 16777216.0f, add);
+      reset();
+      return;
+    }
     float add0[G], add1[G];
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
@@ -340,7 +358,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       wait_stage_landed();
       more = cursor_next(a, cs, lane, &ends);
       if (more) tile_at(a, cs.t, slots, ring, nxt_pos);
-      stage_read<BITS, BLOCK>(cur, stage, lane);
+      if constexpr (V16) stage_read16<BITS, BLOCK>(cur, stage, lane);
+      else stage_read<BITS, BLOCK>(cur, stage, lane);
       cur.km0 = nxt.km0; cur.km1 = nxt.km1; cur.vm = nxt.vm; cur.ks16 = nxt.ks16; cur.vs16 = nxt.vs16;
       cur.kq4 = nxt.kq4; cur.vq4 = nxt.vq4;
       wait_stage_read();
@@ -481,13 +500,20 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       else if (BLOCK) s = kscale * (dotv * e_scale_blk - COFF * qsum[m]);
       else s = dotv * kscale_grp + bias[m];
       if (!tok_ok) s = -INFINITY;
-      p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
+      if constexpr (V16) p[m] = softmax_step16<G, NDG>(m, s, tok_ok, m_run, l_acc, acc16, zacc);
+      else p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
     }
 
     // ---------------- p' = p s into the value A table; values: O += p' . codes
-    stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PLw, zacc, tl, gh);
-    wave_sync();
-    value_mfma<G, BITS, BLOCK, HL, NDG, TBQ>(vc, PLw, row, gh, o0, o1, o2, o3, lut);
+    if constexpr (V16) {
+      stage_probs16<G, BITS, BLOCK, NDG>(p, vs, vz, lds_addr(PL[w]), zacc, tl, gh);
+      wave_sync();
+      value_mfma16<BITS, NDG>(cur.vd, lds_addr(PL[w]), lane, acc16);
+    } else {
+      stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PLw, zacc, tl, gh);
+      wave_sync();
+      value_mfma<G, BITS, BLOCK, HL, NDG, TBQ>(vc, PLw, row, gh, o0, o1, o2, o3, lut);
+    }
     wave_sync();
 
     // ---------------- the member's partial when its assignment ends

@@ -96,13 +96,6 @@ __device__ __forceinline__ float half_hi(uint32_t m) {
   return (float)__builtin_bit_cast(h2_t, m).y;
 }
 
-typedef uint32_t u2v_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u4v_t __attribute__((ext_vector_type(4)));
-
-// LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
-}
 
 // A 64-bit LDS store of (x, y) written as asm.  The stores that build the
 // per-tile tables run while the stage's global-to-LDS copies are in flight;
@@ -212,17 +205,79 @@ __device__ __forceinline__ void read_value_codes(const uint8_t* stv, int lane, u
   }
 }
 
+// The lane's code dwords for the B operands, vd[gg][cb] (channel 16 cb +
+// lane % 16, lane group lane / 16), and the A operands of key group 0,
+// a0[dg], in one asm block with its own LDS wait (as read_value_codes).
+// 4 bits: 16-byte rows, dword lane / 16; 2 bits: 8-byte rows, dword
+// lane / 32.  pvb: the lane's A address for (dg, gg) = (0, 0); (dg, gg) is
+// (2 dg + gg) 512 bytes further.
+template <int BITS>
+__device__ __forceinline__ void read_value_codes16(const uint8_t* stv, uint32_t pvb, int lane, uint32_t (*vd)[8],
+                                                   u4v_t* a0) {
+  u2v_t r[8];
+  if (BITS == 4) {
+    const uint32_t base = lds_addr(stv) + 16 * (lane & 15) + 4 * (lane >> 4);
+    asm volatile(
+        "ds_read2st64_b32 %0, %12 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %12 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %12 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %3, %12 offset0:6 offset1:7\n\t"
+        "ds_read2st64_b32 %4, %12 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b32 %5, %12 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b32 %6, %12 offset0:12 offset1:13\n\t"
+        "ds_read2st64_b32 %7, %12 offset0:14 offset1:15\n\t"
+        "ds_read_b128 %8, %13\n\t"
+        "ds_read_b128 %9, %13 offset:1024\n\t"
+        "ds_read_b128 %10, %13 offset:2048\n\t"
+        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
+          "=v"(a0[0]), "=v"(a0[1]), "=v"(a0[2]), "=v"(a0[3])
+        : "v"(base), "v"(pvb)
+        : "memory");
+  } else {
+    const uint32_t b0 = lds_addr(stv) + 8 * (lane & 15) + 4 * (lane >> 5), b1 = b0 + 1024;
+    asm volatile(
+        "ds_read2_b32 %0, %12 offset1:32\n\t"
+        "ds_read2_b32 %1, %12 offset0:64 offset1:96\n\t"
+        "ds_read2_b32 %2, %12 offset0:128 offset1:160\n\t"
+        "ds_read2_b32 %3, %12 offset0:192 offset1:224\n\t"
+        "ds_read2_b32 %4, %13 offset1:32\n\t"
+        "ds_read2_b32 %5, %13 offset0:64 offset1:96\n\t"
+        "ds_read2_b32 %6, %13 offset0:128 offset1:160\n\t"
+        "ds_read2_b32 %7, %13 offset0:192 offset1:224\n\t"
+        "ds_read_b128 %8, %14\n\t"
+        "ds_read_b128 %9, %14 offset:1024\n\t"
+        "ds_read_b128 %10, %14 offset:2048\n\t"
+        "ds_read_b128 %11, %14 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
+          "=v"(a0[0]), "=v"(a0[1]), "=v"(a0[2]), "=v"(a0[3])
+        : "v"(b0), "v"(b1), "v"(pvb)
+        : "memory");
+  }
+  // r[4 gg + c]: channel blocks 2c (.x) and 2c + 1 (.y)
+  for (int gg = 0; gg < 2; ++gg)
+    for (int c = 0; c < 4; ++c) {
+      vd[gg][2 * c] = r[4 * gg + c].x;
+      vd[gg][2 * c + 1] = r[4 * gg + c].y;
+    }
+}
+
 template <int G, int BITS>
 __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   constexpr int HL = (G <= 2) ? 1 : 2;   // value-side MFMAs per k-step (hi/lo of p')
   constexpr int NDG = 4;                 // value scale groups per token
   constexpr int TB = 512 * BITS;         // tile bytes
   constexpr int NW = BITS == 4 ? 2 : 1;  // code dwords per quarter-half of a key row
+  constexpr bool V16 = G == 4;           // value side on the 16x16x32 MFMA
   const Geom& g = a.g;
   __shared__ __attribute__((aligned(16))) float QB[4][2 * kQbGroup];
   __shared__ __attribute__((aligned(16))) float SZ[4][2 * kSzGroup];
   using PTab = ATab<HL, 16, G == 4, G == 4>;
-  __shared__ __attribute__((aligned(16))) _Float16 PL[4][NDG * PTab::T];
+  // p' tables: NDG ATab tables, or (four heads) the 16x16x32 A operands of
+  // 4 scale groups x 2 key groups (the window's table 0 overlays them)
+  __shared__ __attribute__((aligned(16))) _Float16 PL[4][V16 ? v16_halves(NDG) : NDG * PTab::T];
   // the tile stage, keys and values apart: the value half of tile N is still
   // read while the key half of tile N + 1 is in flight into the other array
   __shared__ __attribute__((aligned(16))) uint8_t STK[4][2 * TB];
@@ -290,6 +345,7 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   float m_run[G], l_acc[G];
   float zacc[G][NDG];
   f4_t o0, o1, o2, o3;
+  f4_t acc16[8];   // V16: channel blocks 0..7
   auto reset = [&]() {
     for (int m = 0; m < G; ++m) {
       m_run[m] = -INFINITY;
@@ -297,7 +353,10 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
       for (int d = 0; d < NDG; ++d) zacc[m][d] = 0.0f;
     }
     o0 = f4_t{0, 0, 0, 0}; o1 = o0; o2 = o0; o3 = o0;
+    if (V16)
+      for (int c = 0; c < 8; ++c) acc16[c] = f4_t{0, 0, 0, 0};
   };
+
   reset();
 
   // Scores of one group: the quarter's rotated keys of tokens tau (xa, ya:
@@ -443,6 +502,15 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
   int pb = 0, ph = 0;
   // this member's partial of `pair`
   auto flush = [&]() {
+    if constexpr (V16) {
+      // codes entered as n 2^-24; the zero-point sum of each scale group
+      float zsum[G][NDG];
+      for (int m = 0; m < G; ++m)
+        for (int d = 0; d < NDG; ++d) zsum[m][d] = wave_sum64(zacc[m][d]);
+      write_partial16<G, NDG>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, acc16, 16777216.0f, zsum);
+      reset();
+      return;
+    }
     float add0[G], add1[G];
     for (int m = 0; m < G; ++m) {
       float zsum[NDG];
@@ -492,15 +560,13 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     // read at the top of a later tile, and the waits before then (the value
     // phase's) come a key phase after it
     if (need_claim) cs.pend = claim_issue(a.ctr + cs.pair * kCounterStride, lane);
+    if (more) meta_fetch(nxt, nxt_pos, cs.pair);
     stage_half(stv, vplane, cur_pos, cur_pair);
     // key codes: tokens tau (a) and tau + 16 (b) of both groups, the
     // quarter's low channels then its high channels (NW dwords each)
     uint32_t kc[2][2][4];
     read_key_codes<BITS>(stk, kq, tau, kc);
-    if (more) {
-      stage_half(stk, kplane, nxt_pos, cs.pair);
-      meta_fetch(nxt, nxt_pos, cs.pair);
-    }
+    if (more) stage_half(stk, kplane, nxt_pos, cs.pair);
 
     // SZ of both groups: this lane's four channels (group lane / 32)
     {
@@ -557,7 +623,8 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
     float p[G];
     for (int m = 0; m < G; ++m) {
       const float s = tok_ok ? sel[m] : -INFINITY;
-      p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
+      if constexpr (V16) p[m] = softmax_step16<G, NDG>(m, s, tok_ok, m_run, l_acc, acc16, zacc);
+      else p[m] = softmax_step<G, HL, NDG>(m, s, tok_ok, m_run, l_acc, o0, o1, o2, o3, zacc);
     }
 
     // ---------------- values
@@ -566,13 +633,37 @@ __global__ __launch_bounds__(256, 2) void decode_rope_kernel(MfmaArgs a) {
       meta.vm = cur_vm;
       float vs[NDG], vz[NDG];
       value_meta<BITS, false, NDG>(meta, tok_ok, vs, vz);
-      stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PLw, zacc, tl, gh);
+      if constexpr (V16) {
+        stage_probs16<G, BITS, false, NDG>(p, vs, vz, lds_addr(PL[w]), zacc, tl, gh);
+      } else {
+        stage_probs<G, BITS, false, HL, NDG>(p, vs, vz, PLw, zacc, tl, gh);
+      }
     }
-    // this tile's value copies (and the next tile's key copies and metadata,
-    // issued just after them, a key phase ago) have landed
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this tile's value copies have landed: all but the next tile's key
+    // copies, the last vector memory operations issued (loads return in
+    // order), when there is a next tile
+    if (more) {
+      if constexpr (BITS == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     wave_sync();
-    {
+    if constexpr (V16) {
+      // rows 8..15 of A repeat rows 0..7 (lane & 7)
+      const uint32_t pvb = lds_addr(PL[w]) + 2 * v16_at(0, 0, lane & 7, 8 * (lane >> 4));
+      uint32_t vd[2][8];
+      u4v_t av[2][4];
+      read_value_codes16<BITS>(stv, pvb, lane, vd, av[0]);
+      for (int gg = 0; gg < 2; ++gg) {
+        if (gg == 1) read_a16<4>(pvb, 1, av[1]);
+        for (int d = 0; d < 4; ++d) {
+          const h8_t a8 = __builtin_bit_cast(h8_t, av[gg][d]);
+          acc16[2 * d] = mfma16(a8, codes16_b<BITS>(vd[gg][2 * d], lane), acc16[2 * d]);
+          acc16[2 * d + 1] = mfma16(a8, codes16_b<BITS>(vd[gg][2 * d + 1], lane), acc16[2 * d + 1]);
+        }
+      }
+    } else {
       uint32_t vc[2][2][BITS];
       read_value_codes<BITS>(stv, lane, vc);
       value_mfma<G, BITS, false, HL, NDG>(vc, PLw, lane & 3, lane >> 5, o0, o1, o2, o3);
