@@ -310,13 +310,15 @@ __device__ __forceinline__ h8_t codes16_b(uint32_t x, int lane) {
 }
 
 // p' = p s of this lane's token into the table (LDS byte address pv), and
-// the zero-point sums (blocks: the sums of p' for the code offset).
-template <int G, int BITS, bool BLOCK, int NDG>
+// the zero-point sums (blocks: the sums of p' for the code offset).  TBQ:
+// the B operands are levels, without place factors.
+template <int G, int BITS, bool BLOCK, int NDG, bool TBQ = false>
 __device__ __forceinline__ void stage_probs16(const float* p, const float* vs, const float* vz, uint32_t pv,
                                               float (*zacc)[NDG], int tl, int gh) {
   int kc, j;
   float inv_f;
   v16_slot<BITS>(tl, &kc, &j, &inv_f);
+  if (TBQ) inv_f = 1.0f;
   const uint32_t sb = pv + 2 * v16_at(0, gh, 0, 8 * kc + j);
   for (int d = 0; d < NDG; ++d) {
     _Float16 hi[4], lo[4];
@@ -330,16 +332,26 @@ __device__ __forceinline__ void stage_probs16(const float* p, const float* vs, c
 }
 
 // O += p' . codes over a tile whose code dwords are in registers,
-// vd[gg][cb] (channel 16 cb + lane % 16, lane group lane / 16).
-template <int BITS, int NDG>
-__device__ __forceinline__ void value_mfma16(const uint32_t (*vd)[8], uint32_t pv, int lane, f4_t* acc) {
+// vd[gg][cb] (channel 16 cb + lane % 16, lane group lane / 16).  TBQ: the
+// codes' levels as hi + lo fp16 (tbq4_levels, same order as the masked
+// words), one MFMA for each against both halves of p'.
+template <int BITS, int NDG, bool TBQ = false>
+__device__ __forceinline__ void value_mfma16(const uint32_t (*vd)[8], uint32_t pv, int lane, f4_t* acc,
+                                             const uint32_t* lut = nullptr) {
   const uint32_t pvb = pv + 2 * v16_at(0, 0, lane & 7, 8 * (lane >> 4));
   for (int gg = 0; gg < 2; ++gg) {
     u4v_t av[NDG];
     read_a16<NDG>(pvb, gg, av);
     for (int cb = 0; cb < 8; ++cb) {
       const h8_t a8 = __builtin_bit_cast(h8_t, av[NDG == 1 ? 0 : cb >> 1]);
-      acc[cb] = mfma16(a8, codes16_b<BITS>(vd[gg][cb], lane), acc[cb]);
+      if (TBQ) {
+        uint32_t hi[4], lo[4];
+        tbq4_levels(vd[gg][cb], lut, hi, lo);
+        acc[cb] = mfma16(a8, __builtin_bit_cast(h8_t, u4v_t{hi[0], hi[1], hi[2], hi[3]}), acc[cb]);
+        acc[cb] = mfma16(a8, __builtin_bit_cast(h8_t, u4v_t{lo[0], lo[1], lo[2], lo[3]}), acc[cb]);
+      } else {
+        acc[cb] = mfma16(a8, codes16_b<BITS>(vd[gg][cb], lane), acc[cb]);
+      }
     }
   }
 }

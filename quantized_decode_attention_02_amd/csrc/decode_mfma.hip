@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // symmetric blocks: stored code offset (c + 4 at 3 bits, c + 8 at 4, c + 128 at 8)
   constexpr float COFF = BITS == 3 ? 4.0f : BITS == 8 ? 128.0f : 8.0f;
   constexpr int TB = 512 * BITS;         // tile bytes
-  // four query heads at 4 or 2 bits: values on the 16x16x32 MFMA
-  constexpr bool V16 = G == 4 && (BITS == 4 || BITS == 2) && !TBQ && KVQ_DECODE_STAGE;
+  // four query heads at 4 or 2 bits (TBQ4 included): values on the 16x16x32 MFMA
+  constexpr bool V16 = G == 4 && (BITS == 4 || BITS == 2) && KVQ_DECODE_STAGE;
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
   constexpr bool QP = query_in_prob_table<G, BLOCK>();
@@ -286,9 +286,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       for (int m = 0; m < G; ++m)
         for (int d = 0; d < NDG; ++d) {
           const float zs = wave_sum64(zacc[m][d]);
-          add[m][d] = BLOCK ? -COFF * zs : zs;
+          add[m][d] = TBQ ? 0.0f : BLOCK ? -COFF * zs : zs;
         }
-      write_partial16<G, NDG>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, acc16, 16777216.0f, add);
+      write_partial16<G, NDG>(a, pb, ph, a.slot_base + pk, lane, m_run, l_acc, acc16, TBQ ? 1.0f : 16777216.0f,
+                              add);
       reset();
       return;
     }
@@ -506,9 +507,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
 
     // ---------------- p' = p s into the value A table; values: O += p' . codes
     if constexpr (V16) {
-      stage_probs16<G, BITS, BLOCK, NDG>(p, vs, vz, lds_addr(PL[w]), zacc, tl, gh);
+      stage_probs16<G, BITS, BLOCK, NDG, TBQ>(p, vs, vz, lds_addr(PL[w]), zacc, tl, gh);
       wave_sync();
-      value_mfma16<BITS, NDG>(cur.vd, lds_addr(PL[w]), lane, acc16);
+      value_mfma16<BITS, NDG, TBQ>(cur.vd, lds_addr(PL[w]), lane, acc16, TBQ ? lut : nullptr);
     } else {
       stage_probs<G, BITS, BLOCK, HL, NDG, TBQ>(p, vs, vz, PLw, zacc, tl, gh);
       wave_sync();
