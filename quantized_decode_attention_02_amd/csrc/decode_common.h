@@ -244,7 +244,7 @@ __device__ __forceinline__ void v16_slot(int tl, int* kc, int* j, float* inv_f) 
     const int e = tl & 15, w = e & 3;
     *kc = 2 * (tl >> 4) + ((e >> 2) & 1);
     *j = 2 * w + (e >> 3);
-    *inv_f = 1.0f / (float)(1 << (2 * w));
+    *inv_f = __int_as_float((127 - 2 * w) << 23);   // 4^-w
   }
 }
 
