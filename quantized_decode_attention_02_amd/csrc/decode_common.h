@@ -248,12 +248,15 @@ __device__ __forceinline__ void v16_slot(int tl, int* kc, int* j, float* inv_f) 
   }
 }
 
-// Table half offset of (dg, gg, row, column); a table is NDG x 2 x 8 rows
-// of 32 halves.
+// Table half offset of (dg, gg, row, column); a table is NDG x 2 blocks of
+// 8 rows of 32 halves, each block padded by 32 halves, so that the two key
+// groups' columns (written by the wave's two halves in one store) fall in
+// different LDS banks.  Byte strides: row 64, block 576, scale group 1152.
+constexpr int kV16Blk = 8 * 32 + 32;
 __device__ __forceinline__ int v16_at(int dg, int gg, int row, int col) {
-  return ((dg * 2 + gg) * 8 + row) * 32 + col;
+  return (dg * 2 + gg) * kV16Blk + row * 32 + col;
 }
-constexpr int v16_halves(int ndg) { return ndg * 2 * 8 * 32; }
+constexpr int v16_halves(int ndg) { return ndg * 2 * kV16Blk; }
 
 // One token's p' of one scale group: hi halves into rows 0..3, lo halves
 // into rows 4..7 (64 bytes a row) of the column at LDS byte address sb.
@@ -275,21 +278,21 @@ __device__ __forceinline__ void store_p16(uint32_t sb, const _Float16* hi, const
 
 // The lane's A operands of key group gg, av[dg], in one asm block with its
 // own LDS wait.  pvb: the lane's address for (dg, gg) = (0, 0) (row
-// lane % 8, columns 8 (lane / 16) ..); (dg, gg) lies (2 dg + gg) 512 bytes
+// lane % 8, columns 8 (lane / 16) ..); (dg, gg) lies 1152 dg + 576 gg bytes
 // further.
 template <int NDG>
 __device__ __forceinline__ void read_a16(uint32_t pvb, int gg, u4v_t* av) {
   if (NDG == 1) {
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(av[0]) : "v"(pvb + 512 * gg) : "memory");
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(av[0]) : "v"(pvb + 576 * gg) : "memory");
   } else {
     asm volatile(
         "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:1024\n\t"
-        "ds_read_b128 %2, %4 offset:2048\n\t"
-        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "ds_read_b128 %1, %4 offset:1152\n\t"
+        "ds_read_b128 %2, %4 offset:2304\n\t"
+        "ds_read_b128 %3, %4 offset:3456\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=v"(av[0]), "=v"(av[1]), "=v"(av[2]), "=v"(av[3])
-        : "v"(pvb + 512 * gg)
+        : "v"(pvb + 576 * gg)
         : "memory");
   }
 }
@@ -327,7 +330,7 @@ __device__ __forceinline__ void stage_probs16(const float* p, const float* vs, c
       split_half(x * inv_f, &hi[m], &lo[m]);
       zacc[m][d] += BLOCK ? x : p[m] * vz[d];
     }
-    store_p16(sb + 1024 * d, hi, lo);
+    store_p16(sb + 1152 * d, hi, lo);
   }
 }
 

@@ -210,7 +210,7 @@ __device__ __forceinline__ void read_value_codes(const uint8_t* stv, int lane, u
 // a0[dg], in one asm block with its own LDS wait (as read_value_codes).
 // 4 bits: 16-byte rows, dword lane / 16; 2 bits: 8-byte rows, dword
 // lane / 32.  pvb: the lane's A address for (dg, gg) = (0, 0); (dg, gg) is
-// (2 dg + gg) 512 bytes further.
+// 1152 dg + 576 gg bytes further.
 template <int BITS>
 __device__ __forceinline__ void read_value_codes16(const uint8_t* stv, uint32_t pvb, int lane, uint32_t (*vd)[8],
                                                    u4v_t* a0) {
@@ -227,9 +227,9 @@ __device__ __forceinline__ void read_value_codes16(const uint8_t* stv, uint32_t 
         "ds_read2st64_b32 %6, %12 offset0:12 offset1:13\n\t"
         "ds_read2st64_b32 %7, %12 offset0:14 offset1:15\n\t"
         "ds_read_b128 %8, %13\n\t"
-        "ds_read_b128 %9, %13 offset:1024\n\t"
-        "ds_read_b128 %10, %13 offset:2048\n\t"
-        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "ds_read_b128 %9, %13 offset:1152\n\t"
+        "ds_read_b128 %10, %13 offset:2304\n\t"
+        "ds_read_b128 %11, %13 offset:3456\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
           "=v"(a0[0]), "=v"(a0[1]), "=v"(a0[2]), "=v"(a0[3])
@@ -247,9 +247,9 @@ __device__ __forceinline__ void read_value_codes16(const uint8_t* stv, uint32_t 
         "ds_read2_b32 %6, %13 offset0:128 offset1:160\n\t"
         "ds_read2_b32 %7, %13 offset0:192 offset1:224\n\t"
         "ds_read_b128 %8, %14\n\t"
-        "ds_read_b128 %9, %14 offset:1024\n\t"
-        "ds_read_b128 %10, %14 offset:2048\n\t"
-        "ds_read_b128 %11, %14 offset:3072\n\t"
+        "ds_read_b128 %9, %14 offset:1152\n\t"
+        "ds_read_b128 %10, %14 offset:2304\n\t"
+        "ds_read_b128 %11, %14 offset:3456\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
           "=v"(a0[0]), "=v"(a0[1]), "=v"(a0[2]), "=v"(a0[3])
