@@ -1,5 +1,5 @@
 // Quantize-on-append of whole KIVI groups that come entirely from the new
-// tokens (the bulk of a prefill or of a long append), at 4 or 2 bits.
+// tokens (the bulk of a prefill or of a long append), at 4, 3 or 2 bits.
 //
 // Sources cited here:
 //   [troisinh] "KV Cache Quantization — Nén cache INT4/INT3, mở khóa
@@ -30,7 +30,9 @@
 // (fma(d, fl32(1/s_h) (1 -+ 2^-21), 2^23) at both ends, clamped to [0, Q]):
 // the exact quotient lies strictly inside, so where the ends agree it rounds
 // and clamps the same way; elsewhere the wave redoes those codes with the
-// division.
+// division.  3-bit codes take the 4-bit path as nibbles (top bit clear) up
+// to the transposed rows, whose 4-bit dwords then shrink to 24 bits each
+// (nib_to_3) and join their neighbours' into the 3-bit bit strings.
 #pragma clang fp contract(off)
 
 #include "append_util.h"
@@ -105,6 +107,21 @@ __device__ __forceinline__ uint32_t code_word(float d, float r, float Q) {
 __device__ __forceinline__ uint32_t code_exact(float d, const Grp& gp, float Q) {
   const float c = gp.s != 0.0f ? rintf(d / gp.s) : 0.0f;
   return __float_as_uint(kTwo23 + fminf(fmaxf(c, 0.0f), Q));
+}
+
+// Eight nibbles n_k (bits 4k, each < 8) as eight 3-bit fields (bits 3k):
+// nibble pairs into 6-bit bytes, byte pairs into 12-bit halves, then the
+// halves into 24 bits.
+__device__ __forceinline__ uint32_t nib_to_3(uint32_t x) {
+  const uint32_t y = (x & 0x07070707u) | ((x >> 1) & 0x38383838u);
+  const uint32_t y2 = (y & 0x003F003Fu) | ((y >> 2) & 0x0FC00FC0u);
+  return (y2 & 0xFFFu) | ((y2 >> 4) & 0xFFF000u);
+}
+
+// Dword k (0..2) of a 96-bit run made of four 24-bit pieces, from piece k
+// (own) and piece k + 1 (next).
+__device__ __forceinline__ uint32_t join3(uint32_t own, uint32_t next, int k) {
+  return k == 0 ? (own | (next << 24)) : k == 1 ? ((own >> 8) | (next << 16)) : ((own >> 16) | (next << 8));
 }
 
 template <int HB, int LB, int HAD>
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
           r[j] = y;
         }
       }
-      uint32_t U[8];   // 4 bits: eight 8-channel words; 2 bits: four 16-channel words
+      uint32_t U[8];   // 4 and 3 bits: eight 8-channel nibble words; 2 bits: four 16-channel words
       uint32_t szw[2];
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
@@ -206,11 +223,11 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
         }
         const Grp gp = grp_params(mn, mx, Q);
         szw[sl] = gp.sz;
-        // 8 codes a unit at 4 bits, 16 at 2
+        // 8 codes a unit at 4 and 3 bits, 16 at 2
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (bits == 2 && u >= 2) break;
-          const int n = bits == 4 ? 8 : 16;
+          const int n = bits == 2 ? 16 : 8;
           const int j0 = 32 * sl + n * u;
           uint32_t f[16];
           uint32_t diff = 0;
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
               f[j] = code_exact(r[j0 + j] - gp.z, gp, Q);
             }
           }
-          if (bits == 4) {
+          if (bits != 2) {
             U[4 * sl + u] = pack8<4>(f);
           } else {   // crumb pairs as nibbles, then the nibbles as pack8<4>
             uint32_t nb[8];
@@ -248,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
       }
       // token rows -> channel rows (the rows were read above; this wave's
       // LDS operations run in order)
-      if (bits == 4) {
+      if (bits != 2) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) tr[(half_chan<HAD>(8 * u, half) / 8) * kTr + v] = U[u];
         const int cg = lane & 15, tg = lane >> 4;
@@ -258,8 +275,19 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
         in[0] = q0.x; in[1] = q0.y; in[2] = q0.z; in[3] = q0.w;
         in[4] = q1.x; in[5] = q1.y; in[6] = q1.z; in[7] = q1.w;
         transpose_nib8(in, o);
+        if (bits == 4) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(vt + 16 * (8 * cg + j) + 4 * tg) = o[j];
+          for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(vt + 16 * (8 * cg + j) + 4 * tg) = o[j];
+        } else {
+          // o[j]: tokens 8 tg .. 8 tg + 7 of channel 8 cg + j, bits 24 tg .. of
+          // its 12-byte row; lane + 16 holds the next 8 tokens
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t c = nib_to_3(o[j]);
+            const uint32_t nx = __shfl_down(c, 16);
+            if (tg < 3) *reinterpret_cast<uint32_t*>(vt + 12 * (8 * cg + j) + 4 * tg) = join3(c, nx, tg);
+          }
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) tr[(half_chan<HAD>(16 * u, half) / 16) * kTr + v] = U[u];
@@ -333,12 +361,12 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
         uint2* km = reinterpret_cast<uint2*>(p.p[KVQ_PLANE_K_META] + (cur.pair * g.gmax + cur.grp) * 512);
         km[lane] = make_uint2(g0p.sz, g1p.sz);
       }
-      // codes per token: 4 bits: byte c0 | c1 << 4; 2 bits: nibble c0 | c1 << 2
-      uint32_t tw[8];   // 4 bits: tokens 4j .. 4j + 3 a word; 2 bits: 8j .. 8j + 7
+      // codes per token: 4 and 3 bits: byte c0 | c1 << 4; 2 bits: nibble c0 | c1 << 2
+      uint32_t tw[8];   // 4 and 3 bits: tokens 4j .. 4j + 3 a word; 2 bits: 8j .. 8j + 7
       const uint32_t z0h = g0p.sz >> 16, z1h = g1p.sz >> 16;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int n = bits == 4 ? 4 : 8;
+        const int n = bits == 2 ? 8 : 4;
         if (bits == 2 && q >= 4) break;
         uint32_t f0[8], f1[8], diff = 0;
 #pragma unroll
@@ -365,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
             f1[k] = code_exact(d1, g1p, Q);
           }
         }
-        if (bits == 4) {
+        if (bits != 2) {
           uint32_t by[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) by[k] = (f1[k] << 4) | f0[k];
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
       // (4 or 8) q ..; a token row's word w gathers lanes 4w .. 4w + 3 (4
       // bits, a byte each) or 8w .. 8w + 7 (2 bits, a nibble each).  The
       // column reads above are done (in-order LDS), so the area is free.
-      if (bits == 4) {
+      if (bits != 2) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) tr[q * 64 + lane] = tw[q];
         const int w = lane & 15, q0 = lane >> 4;
@@ -393,8 +421,19 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
           uint32_t o[4];
           transpose_byte4(in, o);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint32_t*>(kt + ktile_offset(4 * q + i, 4 * w)) = o[i];
+          for (int i = 0; i < 4; ++i) {
+            if (bits == 4) {
+              *reinterpret_cast<uint32_t*>(kt + ktile_offset(4 * q + i, 4 * w)) = o[i];
+            } else {
+              // o[i]: channels 8 w .. 8 w + 7 of token 4 q + i, bits 24 w .. of
+              // its 48-byte row; lane + 1 holds channels 8 w + 8 ..
+              const uint32_t c = nib_to_3(o[i]);
+              const uint32_t nx = __shfl_down(c, 1);
+              const int k = w & 3;
+              if (k < 3)
+                *reinterpret_cast<uint32_t*>(kt + ktile_offset(4 * q + i, 4 * (3 * (w >> 2) + k))) = join3(c, nx, k);
+            }
+          }
         }
       } else {
 #pragma unroll
@@ -441,7 +480,9 @@ hipError_t launch_kg_had(const Geom& g, const Planes& p, const KiviArgs& a, hipS
 }  // namespace
 
 bool kivi_groups_supported(const Geom& g, int64_t n_new) {
-  const bool bits_ok = (g.hi_bits == 4 || g.hi_bits == 2) && (g.lo_bits == 4 || g.lo_bits == 2);
+  // one bit width, or an INT4 window over an INT3 or INT2 tier
+  const bool bits_ok = (g.hi_bits == g.lo_bits && g.hi_bits >= 2 && g.hi_bits <= 4) ||
+                       (g.hi_bits == 4 && (g.lo_bits == 3 || g.lo_bits == 2));
   // row offsets from a pair's first new row must fit 32 bits
   const bool offs_ok = n_new * (int64_t)g.Hkv * kD * 2 < ((int64_t)1 << 32);
   return bits_ok && offs_ok;
@@ -461,8 +502,9 @@ hipError_t launch_kivi_groups(const Geom& g, const Planes& p, const __half* k_ne
   a.hi_start = hi_start_new;
   a.n_items = (int64_t)g.B * g.Hkv * a.n_grp * 2;
   if (g.hi_bits == 4 && g.lo_bits == 4) return launch_kg_had<4, 4>(g, p, a, s);
+  if (g.hi_bits == 4 && g.lo_bits == 3) return launch_kg_had<4, 3>(g, p, a, s);
   if (g.hi_bits == 4) return launch_kg_had<4, 2>(g, p, a, s);
-  if (g.lo_bits == 4) return launch_kg_had<2, 4>(g, p, a, s);
+  if (g.hi_bits == 3) return launch_kg_had<3, 3>(g, p, a, s);
   return launch_kg_had<2, 2>(g, p, a, s);
 }
 
