@@ -325,10 +325,10 @@ __device__ __forceinline__ void stage_probs16(const float* p, const float* vs, c
   const uint32_t sb = pv + 2 * v16_at(0, gh, 0, 8 * kc + j);
   for (int d = 0; d < NDG; ++d) {
     _Float16 hi[4], lo[4];
+    const float vsi = vs[d] * inv_f;   // a power of two: p (s / f) = (p s) / f exactly
     for (int m = 0; m < G; ++m) {
-      const float x = p[m] * vs[d];
-      split_half(x * inv_f, &hi[m], &lo[m]);
-      zacc[m][d] += BLOCK ? x : p[m] * vz[d];
+      split_half(p[m] * vsi, &hi[m], &lo[m]);
+      zacc[m][d] += BLOCK ? p[m] * vs[d] : p[m] * vz[d];
     }
     store_p16(sb + 1152 * d, hi, lo);
   }

@@ -275,6 +275,7 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   int64_t pair = -1, pk = 0;
   int pb = 0, ph = 0;
   float qv[G][4];
+  float qabs[4];   // max over the heads of |qv|, per slot
   float qsum[G];
   float qsum4[G][4];   // Q40: sums of the query over each 32-channel slice
   float e_scale_blk = 1.0f;
@@ -316,6 +317,10 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
       const float qmax = wave_query<G>(a, pb, ph, g.hadamard != 0, qsw, lane);
       for (int m = 0; m < G; ++m)
         for (int i = 0; i < 4; ++i) qv[m][i] = qsw[m][kch[i]];
+      for (int i = 0; i < 4; ++i) {
+        qabs[i] = 0.0f;
+        for (int m = 0; m < G; ++m) qabs[i] = fmaxf(qabs[i], fabsf(qv[m][i]));
+      }
       wave_sync();   // the query is read before stage_probs() may overwrite it
       if (BLOCK) {
         // per-token key scales: the query table is fixed for the pair
@@ -399,18 +404,25 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
         for (int i = 0; i < 4; ++i) {
           qp[m][i] = qv[m][i] * sK[i];
           bp += qv[m][i] * zK[i];
-          amax = fmaxf(amax, fabsf(qp[m][i]));
+          if (G <= 2) amax = fmaxf(amax, fabsf(qp[m][i]));
         }
         bias[m] = half_sum(bp);
       }
+      // four heads: max over heads of |q s| is (max over heads of |q|) |s|
+      // (rounding is monotone), one product per channel
+      if (G > 2)
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, qabs[i] * fabsf(sK[i]));
       amax = half_max(amax);
       int ex = 0;
       if (amax > 0.0f) frexpf(amax, &ex);
       const int e_grp = 10 - ex;
       kscale_grp = ldexpf(1.0f, 24 - e_grp);
+      // 2^e_grp and the place factor (both powers of two: exact) per channel
+      float fsc[4];
+      for (int i = 0; i < 4; ++i) fsc[i] = ldexpf(kinv[i], e_grp);
       for (int m = 0; m < G; ++m) {
         _Float16 hi[4], lo[4];
-        for (int i = 0; i < 4; ++i) split_half(ldexpf(qp[m][i], e_grp) * kinv[i], &hi[i], &lo[i]);
+        for (int i = 0; i < 4; ++i) split_half(qp[m][i] * fsc[i], &hi[i], &lo[i]);
         const h4_t hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
         QLw.h4(qh, tl, 0, m) = hv;
         if (HL == 1) QLw.h4(qh, tl, 0, G + m) = lv;
