@@ -282,7 +282,9 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
         const uint16_t sb = float_to_half_bits(a / (float)kTop);
         sbw |= (uint32_t)sb << (16 * sl);
         s[sl] = half_bits_to_float(sb);
-        const float rs = s[sl] != 0.0f ? 1.0f / s[sl] : 0.0f;
+        // v_rcp_f32 is within 1 ulp of 1 / s_h; with the scaling's rounding
+        // the ends below still bracket c / s_h
+        const float rs = s[sl] != 0.0f ? __builtin_amdgcn_rcpf(s[sl]) : 0.0f;
         const float crs = HAD ? rs * c32() : rs;
         clo[sl] = crs * (1.0f - 0x1p-21f);
         chi[sl] = crs * (1.0f + 0x1p-21f);

@@ -27,10 +27,13 @@
 // over the 32 tokens, read as columns of the staged rows (or, rotated, of
 // the fp32 transform written back to LDS); their codes leave transposed into
 // the key tile's token rows.  Codes come from the bracket of append_block.hip
-// (fma(d, fl32(1/s_h) (1 -+ 2^-21), 2^23) at both ends, clamped to [0, Q]):
+// (fma(d, r (1 -+ 2^-21), 2^23) at both ends, r within 1 ulp of 1/s_h, then
+// clamped to [0, Q]):
 // the exact quotient lies strictly inside, so where the ends agree it rounds
 // and clamps the same way; elsewhere the wave redoes those codes with the
-// division.  3-bit codes take the 4-bit path as nibbles (top bit clear) up
+// division.  The bracket's ends are compared before the clamp (equal
+// inputs clamp equally), and fl32(1/s_h) may be v_rcp_f32's (1 ulp): the
+// 2^-21 margin covers it.  3-bit codes take the 4-bit path as nibbles (top bit clear) up
 // to the transposed rows, whose 4-bit dwords then shrink to 24 bits each
 // (nib_to_3) and join their neighbours' into the 3-bit bit strings.
 #pragma clang fp contract(off)
@@ -92,18 +95,22 @@ __device__ __forceinline__ Grp grp_params(float mn, float mx, float Q) {
   r.sz = (uint32_t)sb | ((uint32_t)zb << 16);
   r.s = half_bits_to_float(sb);
   r.z = half_bits_to_float(zb);
-  const float rs = r.s != 0.0f ? 1.0f / r.s : 0.0f;
+  // v_rcp_f32 (within 1 ulp of 1 / s_h): the ends r (1 -+ 2^-21), rounded,
+  // still lie strictly below and above 1 / s_h
+  const float rs = r.s != 0.0f ? __builtin_amdgcn_rcpf(r.s) : 0.0f;
   r.lo = rs * (1.0f - 0x1p-21f);
   r.hi = rs * (1.0f + 0x1p-21f);
   return r;
 }
 
-// The code word of d = fl32(x - z_h) from one end of the bracket: 2^23 +
-// code, clamped to [0, Q].
-__device__ __forceinline__ uint32_t code_word(float d, float r, float Q) {
-  return __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(d, r, kTwo23), kTwo23, kTwo23 + Q));
+// 2^23 + rint(d r) for d = fl32(x - z_h) at one end r of the bracket
+// (unclamped: where the two ends agree unclamped, they agree clamped).
+__device__ __forceinline__ float code_end(float d, float r) { return fmaf(d, r, kTwo23); }
+// The code word from an end: 2^23 + code, clamped to [0, Q].
+__device__ __forceinline__ uint32_t code_clamp(float e, float Q) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(e, kTwo23, kTwo23 + Q));
 }
-// The exact code, 2^23 + code as a word like code_word().
+// The exact code, 2^23 + code as a word like code_clamp().
 __device__ __forceinline__ uint32_t code_exact(float d, const Grp& gp, float Q) {
   const float c = gp.s != 0.0f ? rintf(d / gp.s) : 0.0f;
   return __float_as_uint(kTwo23 + fminf(fmaxf(c, 0.0f), Q));
@@ -235,9 +242,9 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
           for (int j = 0; j < 16; ++j) {
             if (j >= n) break;
             const float d = r[j0 + j] - gp.z;
-            const uint32_t lo = code_word(d, gp.lo, Q), hi = code_word(d, gp.hi, Q);
-            diff = xor_add(lo, hi, diff);
-            f[j] = lo;
+            const float lo = code_end(d, gp.lo), hi = code_end(d, gp.hi);
+            diff = xor_add(__float_as_uint(lo), __float_as_uint(hi), diff);
+            f[j] = code_clamp(lo, Q);
           }
           if (__builtin_expect(__any(diff != 0u), 0)) {
 #pragma unroll
@@ -375,12 +382,12 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
           const int t = n * q + k;
           const float d0 = HAD ? y0[t] - g0p.z : mix_sub<false>(xh[t], z0h);
           const float d1 = HAD ? y1[t] - g1p.z : mix_sub<true>(xh[t], z1h);
-          const uint32_t a0 = code_word(d0, g0p.lo, Q), b0 = code_word(d0, g0p.hi, Q);
-          const uint32_t a1 = code_word(d1, g1p.lo, Q), b1 = code_word(d1, g1p.hi, Q);
-          diff = xor_add(a0, b0, diff);
-          diff = xor_add(a1, b1, diff);
-          f0[k] = a0;
-          f1[k] = a1;
+          const float a0 = code_end(d0, g0p.lo), b0 = code_end(d0, g0p.hi);
+          const float a1 = code_end(d1, g1p.lo), b1 = code_end(d1, g1p.hi);
+          diff = xor_add(__float_as_uint(a0), __float_as_uint(b0), diff);
+          diff = xor_add(__float_as_uint(a1), __float_as_uint(b1), diff);
+          f0[k] = code_clamp(a0, Q);
+          f1[k] = code_clamp(a1, Q);
         }
         if (__builtin_expect(__any(diff != 0u), 0)) {
 #pragma unroll
