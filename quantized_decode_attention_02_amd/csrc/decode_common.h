@@ -1,6 +1,6 @@
-// Pieces shared by the split-K decode kernels on the 4x4x4 fp16 MFMA
-// (decode_mfma.hip: keys stored after RoPE or rotated; decode_rope.hip: keys
-// stored before RoPE).
+// Pieces shared by the split-K decode kernels on the 4x4x4 fp16 MFMA and,
+// for four query heads' values, the 16x16x32 one (decode_mfma.hip: keys
+// stored after RoPE or rotated; decode_rope.hip: keys stored before RoPE).
 //
 // Sources cited here:
 //   [nalar]  "Kuantisasi KV Cache dengan Error Budget yang Eksplisit"
@@ -18,7 +18,8 @@
 // codes of 4 tokens of one channel (value tiles are channel-major): a nibble
 // masked into an fp16 (w & 0x000F000F, ...) is the exact subnormal n * 2^-24,
 // which the epilogue scales back by 2^24 ([nalar] "Error pada value masuk
-// setelah attention probability").
+// setelah attention probability").  The 16x16x32 value side (value_mfma16)
+// keeps these rules with another operand layout.
 #pragma once
 
 #include "kvq_device.h"

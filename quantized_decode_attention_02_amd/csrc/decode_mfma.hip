@@ -34,7 +34,10 @@
 //           would put a 2^-12 relative error on c * s, i.e. on the group's
 //           whole range rather than on the value); zero points add
 //           sum_t p_t z_t.  B is the codes of 4 tokens of one channel (value
-//           tiles are channel-major), unpacked without factors.
+//           tiles are channel-major), unpacked without factors.  Four query
+//           heads at 4 or 2 bits (TBQ4 included) take the 16x16x32 f16
+//           MFMA instead: hi and lo rows of p' in one A operand, 16 channels
+//           x 8 tokens of codes as B (decode_common.h, value_mfma16).
 //   softmax: online in the log2 domain; the running max moves only when a
 //           score exceeds it (one wave vote per tile).
 // The fp16 window of a KIVI cache is one more work-group of the same launch:
