@@ -158,7 +158,9 @@ __global__ __launch_bounds__(256, 2) void block_append_kernel(Geom g, Planes p, 
     __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index is uniform: a scalar register keeps the item walk and its
+  // addresses on the scalar unit
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, v = lane & 31;   // vector v of the tile, elements 64 half ..
   // this wave's items: a contiguous run [i0, i1) of (pair, tile, tensor)
   // in that order, tensor fastest

@@ -131,8 +131,10 @@ __device__ __forceinline__ uint32_t join3(uint32_t own, uint32_t next, int k) {
   return k == 0 ? (own | (next << 24)) : k == 1 ? ((own >> 8) | (next << 16)) : ((own >> 16) | (next << 8));
 }
 
+// Waves per SIMD: the unrotated kernels' 32 KiB of LDS per work-group leave
+// room for three work-groups per compute unit, the rotated ones' for two.
 template <int HB, int LB, int HAD>
-__global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, KiviArgs a) {
+__global__ __launch_bounds__(256, HAD ? 2 : 3) void kivi_group_kernel(Geom g, Planes p, KiviArgs a) {
   // LDS of one wave: the group's 32 fp16 rows; rotated keys: then their
   // fp32 transform, rows of 132 floats (4 of pad: the 16 row writes of one
   // pass hit 16 different bank quads)
@@ -154,7 +156,9 @@ __global__ __launch_bounds__(256, 2) void kivi_group_kernel(Geom g, Planes p, Ki
     __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index is uniform: a scalar register keeps the item walk and its
+  // addresses on the scalar unit
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, v = lane & 31;
   const int64_t nwaves = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wv;
   const int64_t i0 = gw * a.n_items / nwaves, i1 = (gw + 1) * a.n_items / nwaves;

@@ -127,7 +127,12 @@ __device__ __forceinline__ h4_t codes3_b(const uint32_t* w, int q) {
 // themselves are the selectors.  No memory is read.
 __device__ __forceinline__ void tbq4_levels(uint32_t w, const uint32_t* lut, uint32_t* hi, uint32_t* lo) {
   const uint32_t neg = (~w >> 3) & 0x11111111u;                 // code < 8
-  const uint32_t mag = (w & 0x77777777u) ^ ((neg << 3) - neg);  // m per nibble
+  // 7 neg, the nibbles of the codes below 8 set to 7: neg | neg << 1 |
+  // neg << 2 (the bits lie apart), written as asm so that it stays two
+  // full-rate shifts-and-ors rather than becoming an integer multiply
+  uint32_t neg7;
+  asm("v_lshl_or_b32 %0, %1, 1, %1\n\tv_lshl_or_b32 %0, %1, 2, %0" : "=&v"(neg7) : "v"(neg));
+  const uint32_t mag = (w & 0x77777777u) ^ neg7;                // m per nibble
   const uint32_t s_even = mag & 0x0F0F0F0Fu;                    // m of codes 0, 2, 4, 6
   const uint32_t s_odd = (mag >> 4) & 0x0F0F0F0Fu;              // m of codes 1, 3, 5, 7
   // the sign of code k moves from bit 4k to bit 15 or 31 of its pair
