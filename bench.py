@@ -69,26 +69,26 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # workload id -> {"sources_sha256": ..., "kernels": {kernel: [fetch_kib, write_kib]}}
 COUNTERS = {
-    1: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [1077.7, 2208.0], "decode_mfma_kernel<1, 4, false, false, false>": [664681.8, 4257.7]}},
-    2: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [2661.5, 5456.0], "decode_rope_kernel<4, 4>": [1324344.6, 9536.6]}},
-    3: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [4333.7, 8644.0], "decode_mfma_kernel<4, 2, false, false, false>": [387176.0, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11767.3, 4678.5]}},
-    4: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 4, true, false, false>": [1217686.6, 11192.1]}},
-    5: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 4, true, true, false>": [1217777.6, 11192.0]}},
-    6: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [2149.5, 4672.0], "decode_mfma_kernel<4, 4, true, false, true>": [1328332.4, 9000.0]}},
-    7: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [3205.7, 6752.0], "decode_mfma_kernel<4, 3, true, false, false>": [922788.5, 11192.0]}},
-    8: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [1077.5, 2208.0], "decode_mfma_kernel<1, 3, false, false, false>": [532090.6, 4256.3]}},
-    9: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [1125.5, 2592.0], "decode_mfma_kernel<4, 8, true, false, true>": [2507441.8, 6808.0]}},
-    10: {"sources_sha256": "1a580256350b9c45b9d07bbdbb36304dd7000aed24638663fd1667b74e22703a",
-        "kernels": {"decode_merge_kernel": [4333.5, 8644.0], "decode_mfma_kernel<4, 3, false, false, false>": [516144.3, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11769.0, 4677.9]}},
+    1: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [1077.5, 2208.0], "decode_mfma_kernel<1, 4, false, false, false>": [664756.2, 4258.0]}},
+    2: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [2661.5, 5456.0], "decode_rope_kernel<4, 4>": [1324185.1, 9536.2]}},
+    3: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [4333.5, 8644.0], "decode_mfma_kernel<4, 2, false, false, false>": [387168.8, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11769.6, 4678.6]}},
+    4: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [3205.6, 6752.0], "decode_mfma_kernel<4, 4, true, false, false>": [1217692.4, 11192.2]}},
+    5: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 4, true, true, false>": [1217774.9, 11192.0]}},
+    6: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [2149.5, 4672.0], "decode_mfma_kernel<4, 4, true, false, true>": [1328310.0, 9000.0]}},
+    7: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 3, true, false, false>": [922792.1, 11192.0]}},
+    8: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [1077.5, 2208.0], "decode_mfma_kernel<1, 3, false, false, false>": [532084.4, 4256.3]}},
+    9: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [1125.5, 2592.0], "decode_mfma_kernel<4, 8, true, false, true>": [2507461.8, 6808.0]}},
+    10: {"sources_sha256": "db9a51772c5b01ac307df336f56d42913c8e96d001aa26bd5b9721c593c282a6",
+        "kernels": {"decode_merge_kernel": [4333.5, 8644.0], "decode_mfma_kernel<4, 3, false, false, false>": [516133.3, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11769.8, 4678.0]}},
 }
 
 
