@@ -251,7 +251,10 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 // each (low-bit tier, high-bit tier), one launch each.  A launch runs as many
 // waves as fit on the device at once, as a team of equal size per pair (one
 // wave handles several pairs in turn when pairs outnumber waves); a team is
-// no larger than its pair's tile count.  Chunks are one tile, or two where
+// no larger than half its pair's tile count (a wave's set-up, the query and
+// its partial record, then serves at least two tiles: the INT4 window range
+// of an INT4-over-INT2 cache, 64 tiles a pair, took 26 of cfg3's 274 us at one
+// tile a wave).  Chunks are one tile, or two where
 // every member gets at least 8 chunks on average, so that a claim has a
 // tile's time to come back; teams above 2 * kTeamPerChunkTile waves take
 // team / kTeamPerChunkTile tiles per chunk.  The last team tiles of a pair
@@ -265,7 +268,7 @@ kvq_status decode_setup(const kvq_config* cfg, const kvq_cache* cache, const voi
 #define KVQ_DECODE_CHUNK_MAX 2
 #endif
 #ifndef KVQ_MIN_TILES_PER_WAVE
-#define KVQ_MIN_TILES_PER_WAVE 1
+#define KVQ_MIN_TILES_PER_WAVE 2
 #endif
 constexpr int64_t kMinTilesPerWave = KVQ_MIN_TILES_PER_WAVE;
 #ifndef KVQ_TEAM_PER_CHUNK_TILE
