@@ -236,16 +236,24 @@ __device__ __forceinline__ f4_t mfma16(h8_t a, h8_t b, f4_t c) {
 
 // Lane group kc, position j and the inverse place factor of value token tl
 // (0..31 in its group).  4 bits: dword tl / 8 of the row, nibble o = tl % 8,
-// masked word o % 4 (x16 when odd), half o / 4.  2 bits: dword tl / 16,
-// crumb e = tl % 16: lane group 2 (tl / 16) + (e / 4) % 2, masked word e % 4
-// (x4^(e % 4)), half e / 8.
+// masked word o % 4 (x16 when odd), half o / 4.  3 bits: the 24 bits of
+// tokens 8 kc .. 8 kc + 7 of the row's 96-bit string, token o = tl % 8 in
+// masked word o % 4, half o / 4, with the factor its bits keep there
+// (codes16_b): 1, 16, 64, 64 in the low halves, 1, 1, 4, 4 in the high ones.
+// 2 bits: dword tl / 16, crumb e = tl % 16: lane group 2 (tl / 16) +
+// (e / 4) % 2, masked word e % 4 (x4^(e % 4)), half e / 8.
 template <int BITS>
 __device__ __forceinline__ void v16_slot(int tl, int* kc, int* j, float* inv_f) {
-  if (BITS == 4) {
+  if (BITS == 4 || BITS == 3) {
     const int o = tl & 7;
     *kc = tl >> 3;
     *j = 2 * (o & 3) + (o >> 2);
-    *inv_f = (o & 1) ? 1.0f / 16 : 1.0f;
+    if (BITS == 4) {
+      *inv_f = (o & 1) ? 1.0f / 16 : 1.0f;
+    } else {
+      const int e = (o < 4) ? (o == 0 ? 0 : o == 1 ? 4 : 6) : (o < 6 ? 0 : 2);   // log2 of the factor
+      *inv_f = __int_as_float((127 - e) << 23);
+    }
   } else {
     const int e = tl & 15, w = e & 3;
     *kc = 2 * (tl >> 4) + ((e >> 2) & 1);
@@ -304,11 +312,18 @@ __device__ __forceinline__ void read_a16(uint32_t pvb, int gg, u4v_t* av) {
 }
 
 // The B operand of one code dword: four masked words, two codes each (at 2
-// bits from the dword's half the lane group takes).
+// bits from the dword's half the lane group takes; at 3 bits x is the lane
+// group's 24-bit window, code o at bits 3o, each masked word keeps two codes
+// inside the 10 mantissa bits of their halves).
 template <int BITS>
 __device__ __forceinline__ h8_t codes16_b(uint32_t x, int lane) {
   u4v_t v;
-  if (BITS == 4) {
+  if (BITS == 3) {
+    v = u4v_t{(x & 7u) | ((x << 4) & 0x00070000u),   // codes 0, 4 (x1, x1)
+              (x << 1) & 0x00070070u,                 // codes 1, 5 (x16, x1)
+              x & 0x001C01C0u,                        // codes 2, 6 (x64, x4)
+              (x >> 3) & 0x001C01C0u};                // codes 3, 7 (x64, x4)
+  } else if (BITS == 4) {
     const uint32_t x8 = x >> 8;
     v = u4v_t{x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
   } else {
@@ -691,6 +706,20 @@ __device__ __forceinline__ void stage_read16(TileRaw<BITS, BLOCK>& r, const uint
   constexpr int VROW = 4 * BITS;
   const int gh = lane >> 5, tl = lane & 31;
   for (int j = 0; j < BITS; ++j) r.kc[j] = *reinterpret_cast<const uint4*>(st + gh * TB + j * 512 + tl * 16);
+  if (BITS == 3) {
+    // the lane group's 24 bits of the 96-bit row: bits 24 kc .. 24 kc + 23,
+    // from dwords lo and (lo + 1, at most 2)
+    const int kc = lane >> 4, bit = 24 * kc, lo = bit >> 5, sh = bit & 31, hi = lo < 2 ? lo + 1 : 2;
+    const uint8_t* src = st + 2 * TB + (lane & 15) * VROW;
+    for (int gg = 0; gg < 2; ++gg)
+      for (int cb = 0; cb < 8; ++cb) {
+        const uint8_t* row = src + gg * TB + cb * 16 * VROW;
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(row + 4 * lo);
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(row + 4 * hi);
+        r.vd[gg][cb] = sh ? ((a >> sh) | (b << (32 - sh))) : a;
+      }
+    return;
+  }
   const uint8_t* src = st + 2 * TB + (lane & 15) * VROW + 4 * (lane >> (BITS == 4 ? 4 : 5));
   for (int gg = 0; gg < 2; ++gg)
     for (int cb = 0; cb < 8; ++cb)

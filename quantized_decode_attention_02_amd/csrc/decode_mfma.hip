@@ -35,8 +35,8 @@
 //           whole range rather than on the value); zero points add
 //           sum_t p_t z_t.  B is the codes of 4 tokens of one channel (value
 //           tiles are channel-major), unpacked without factors.  Four query
-//           heads at 4 or 2 bits (TBQ4 included) take the 16x16x32 f16
-//           MFMA instead: hi and lo rows of p' in one A operand, 16 channels
+//           heads at 4 or 2 bits (TBQ4 included) and 3-bit blocks take the
+//           16x16x32 f16 MFMA instead: hi and lo rows of p' in one A operand, 16 channels
 //           x 8 tokens of codes as B (decode_common.h, value_mfma16).
 //   softmax: online in the log2 domain; the running max moves only when a
 //           score exceeds it (one wave vote per tile).
@@ -122,8 +122,9 @@ __global__ __launch_bounds__(256, (decode_min_waves<G, BITS, BLOCK>())) void dec
   // symmetric blocks: stored code offset (c + 4 at 3 bits, c + 8 at 4, c + 128 at 8)
   constexpr float COFF = BITS == 3 ? 4.0f : BITS == 8 ? 128.0f : 8.0f;
   constexpr int TB = 512 * BITS;         // tile bytes
-  // four query heads at 4 or 2 bits (TBQ4 included): values on the 16x16x32 MFMA
-  constexpr bool V16 = G == 4 && (BITS == 4 || BITS == 2) && KVQ_DECODE_STAGE;
+  // four query heads at 4 or 2 bits (TBQ4 included) and 3-bit blocks: values on
+  // the 16x16x32 MFMA (3-bit KIVI measured slower there and keeps the 4x4x4)
+  constexpr bool V16 = G == 4 && (BITS == 4 || BITS == 2 || (BITS == 3 && BLOCK)) && KVQ_DECODE_STAGE;
   const Geom& g = a.g;
   // everything per wave: waves never wait for each other
   constexpr bool QP = query_in_prob_table<G, BLOCK>();
