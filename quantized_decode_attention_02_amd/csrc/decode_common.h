@@ -699,7 +699,8 @@ __device__ __forceinline__ void stage_read(TileRaw<BITS, BLOCK>& r, const uint8_
 }
 
 // stage_read for the 16x16x32 value side: the key rows as stage_read, the
-// value code dwords as value_mfma16 takes them (4 or 2 bits).
+// value code dwords as value_mfma16 takes them (4 or 2 bits: whole dwords;
+// 3 bits: each lane group's 24-bit window of the row).
 template <int BITS, bool BLOCK>
 __device__ __forceinline__ void stage_read16(TileRaw<BITS, BLOCK>& r, const uint8_t* st, int lane) {
   constexpr int TB = 512 * BITS;
