@@ -69,25 +69,25 @@ COUNTER_SOURCES = ["quantized_decode_attention_02_amd/csrc/decode_mfma.hip",
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # workload id -> {"sources_sha256": ..., "kernels": {kernel: [fetch_kib, write_kib]}}
 COUNTERS = {
-    1: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    1: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [1077.5, 2208.0], "decode_mfma_kernel<1, 4, false, false, false>": [664775.4, 4258.2]}},
-    2: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    2: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [2661.6, 5456.0], "decode_rope_kernel<4, 4>": [1324162.2, 9536.3]}},
-    3: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    3: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [3293.5, 6564.0], "decode_mfma_kernel<4, 2, false, false, false>": [387172.8, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11764.9, 2503.2]}},
-    4: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    4: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 4, true, false, false>": [1217705.3, 11192.2]}},
-    5: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    5: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 4, true, true, false>": [1217776.5, 11192.0]}},
-    6: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    6: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [2149.5, 4672.0], "decode_mfma_kernel<4, 4, true, false, true>": [1328328.3, 9000.0]}},
-    7: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    7: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [3205.5, 6752.0], "decode_mfma_kernel<4, 3, true, false, false>": [922800.3, 11192.0]}},
-    8: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    8: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [1077.7, 2208.0], "decode_mfma_kernel<1, 3, false, false, false>": [532069.4, 4256.3]}},
-    9: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    9: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [1125.6, 2592.0], "decode_mfma_kernel<4, 8, true, false, true>": [2507460.7, 6808.0]}},
-    10: {"sources_sha256": "6401ec58efeadd7af133d876e675ee65386557ff15160fbc730ddb3da0ca197b",
+    10: {"sources_sha256": "c1c85e570d5573762f42d986c927dd9b29fefb7c787fc01fd3d90f02dba42ba2",
         "kernels": {"decode_merge_kernel": [3293.5, 6564.0], "decode_mfma_kernel<4, 3, false, false, false>": [516146.8, 5410.0], "decode_mfma_kernel<4, 4, false, false, false>": [11765.0, 2503.8]}},
 }
 

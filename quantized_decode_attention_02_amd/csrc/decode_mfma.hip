@@ -101,7 +101,7 @@ constexpr bool query_in_prob_table() {
 // Waves per SIMD the register allocation must allow: three work-groups per
 // compute unit wherever the LDS allows it, except for the KIVI G = 4 kernels
 // (the 4-bit and 3-bit stages do not fit three; the 2-bit one would, but at
-// 168 VGPRs it spills, and two work-groups without spills are ~5% faster).
+// 168 VGPRs it spills, and two work-groups without spills are much faster).
 template <int G, int BITS, bool BLOCK>
 constexpr int decode_min_waves() {
   return KVQ_DECODE_MIN_WAVES > 0 ? KVQ_DECODE_MIN_WAVES : ((G == 4 && !BLOCK) ? 2 : 3);
